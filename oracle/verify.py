@@ -1,0 +1,249 @@
+"""Plain fp64 NumPy oracle of the verification step.
+
+TEST INFRASTRUCTURE: imported only by tests, the smoke check and the bench's
+CPU-baseline leg.  Page abbreviations are listed in oracle/__init__.py.
+
+The step, per sequence, with positions indexed from 0 (target rows p_0..p_gamma,
+draft rows q_0..q_{gamma-1}, drafted tokens x_0..x_{gamma-1}):
+
+  1. p_i = softmax(target_i / T), q_i = softmax(draft_i / T); temperature is applied
+     to both models ([FI] "The loop: draft, verify in one pass, keep a prefix";
+     [NZ] "5. Sampling and evaluation").  T = 0 means argmax, a one-hot
+     distribution ([FI] "Speculative sampling: the accept/reject rule", last
+     paragraphs on temperature).
+  2. Overlap alpha_i = sum_x min(p_i, q_i) = 1 - TV(p_i, q_i) for every draft
+     position ([SD] "How often do we accept?"; [FI] "The acceptance rate is the
+     overlap of p and q", Lemma 3.3).
+  3. Walk the drafts left to right: keep x_i when u_i <= min(1, p_i(x_i)/q_i(x_i)),
+     stop at the first failure; n = number kept ([FI] Algorithm 1, steps 3-4;
+     [SD] "The algorithm").
+  4. If n < gamma, sample from the residual max(0, p_n - q_n) normalised by its
+     sum; otherwise sample the bonus token from p_gamma ([FI] Algorithm 1 step 4
+     and eq. (2); [SD] "Exactness").
+  5. The sample uses its own uniform u_gamma and the inverse CDF in token-index
+     order: the first token whose cumulative weight exceeds u_gamma.
+
+Readings taken where the pages are silent (each is listed in the design notes):
+  * u_gamma is a fresh uniform for the final sample; the rejecting u_n is not reused.
+  * `sample()` is the inverse CDF with a strict ">" in token-index order.
+  * A zero-mass residual (impossible in exact arithmetic after a rejection) falls
+    back to p_n.
+  * Argmax ties go to the lowest token index; alpha in argmax mode is the
+    indicator that the two argmaxes agree.
+  * alpha is reported for every draft position, whatever n is.
+  * p/q uses IEEE semantics: q(x) = 0 < p(x) gives +inf (accept); 0/0 gives NaN,
+    and any comparison with NaN is false (reject).
+"""
+
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+
+# |u_i - min(1, p_i(x_i)/q_i(x_i))| below this marks a decision that fp32 on the
+# GPU and fp64 here may take differently.
+U_BAND = 1e-6
+
+
+# ------------------------------------------------------------------ step 0
+
+def widen(logits: np.ndarray, dtype: str) -> np.ndarray:
+    """Widen logits exactly to float64.  bf16 arrives as uint16 bit patterns."""
+    if dtype == "bf16":
+        bits32 = np.asarray(logits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+        return bits32.view(np.float32).astype(np.float64)
+    if dtype == "f32":
+        return np.asarray(logits, dtype=np.float32).astype(np.float64)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+# ------------------------------------------------------------------ step 1
+
+def softmax(rows: np.ndarray, temperature: float) -> np.ndarray:
+    """softmax(rows / T) along the last axis, in float64.
+
+    The row maximum is subtracted before exponentiating; this changes nothing
+    mathematically and keeps exp in range.
+    """
+    if not temperature > 0.0:
+        raise ValueError("softmax needs T > 0")
+    m = rows.max(axis=-1, keepdims=True)
+    if not np.all(np.isfinite(m)):
+        raise ValueError("row with no finite logit (all -inf, +inf or NaN)")
+    e = np.exp((rows - m) / temperature)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def argmax_first(rows: np.ndarray) -> np.ndarray:
+    """Index of the row maximum, lowest index on ties (-0.0 equals +0.0)."""
+    return np.argmax(rows, axis=-1)
+
+
+# ------------------------------------------------------------------ step 2
+
+def overlap(p: np.ndarray, q: np.ndarray) -> np.ndarray:
+    """alpha = sum_x min(p(x), q(x))."""
+    return np.minimum(p, q).sum(axis=-1)
+
+
+def total_variation(p: np.ndarray, q: np.ndarray) -> np.ndarray:
+    """TV(p, q) = 1/2 sum_x |p(x) - q(x)|."""
+    return 0.5 * np.abs(p - q).sum(axis=-1)
+
+
+# ------------------------------------------------------------------ step 3
+
+def ratio_test(p_x: np.ndarray, q_x: np.ndarray, u: np.ndarray):
+    """Accept iff u <= min(1, p(x)/q(x)).  Returns (accept, min(1, ratio))."""
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ratio = p_x / q_x
+    capped = np.minimum(1.0, ratio)          # NaN propagates, so 0/0 rejects
+    return u <= capped, capped
+
+
+def accepted_prefix(accept: np.ndarray) -> np.ndarray:
+    """n = index of the first rejection along the last axis, or its length."""
+    gamma = accept.shape[-1]
+    if gamma == 0:
+        return np.zeros(accept.shape[:-1], dtype=np.int64)
+    rejected = ~accept
+    return np.where(rejected.any(axis=-1), np.argmax(rejected, axis=-1), gamma)
+
+
+# ------------------------------------------------------------------ step 4
+
+def residual_weights(p_row: np.ndarray, q_row: np.ndarray) -> np.ndarray:
+    """max(0, p - q), not yet normalised."""
+    return np.maximum(0.0, p_row - q_row)
+
+
+# ------------------------------------------------------------------ step 5
+
+def inverse_cdf(probs: np.ndarray, u: np.ndarray):
+    """First token whose cumulative probability exceeds u (token-index order).
+
+    probs: [N, V] normalised weights; u: [N].  If rounding leaves every
+    cumulative sum <= u, the last token with positive weight is taken.
+    Returns (token [N], cdf [N, V]).
+    """
+    cdf = np.cumsum(probs, axis=-1)
+    above = cdf > u[:, None]
+    token = np.argmax(above, axis=-1)
+    none = ~above.any(axis=-1)
+    if none.any():
+        V = probs.shape[-1]
+        last_pos = V - 1 - np.argmax(probs[:, ::-1] > 0, axis=-1)
+        token = np.where(none, last_pos, token)
+    return token, cdf
+
+
+# ------------------------------------------------------------ whole step
+
+@dataclasses.dataclass
+class Result:
+    n_accepted: np.ndarray      # int64 [B]
+    next_token: np.ndarray      # int64 [B]
+    alpha: np.ndarray           # float64 [B, gamma]
+    tv: np.ndarray              # float64 [B, gamma]
+    p_draft: np.ndarray         # float64 [B, gamma]  p_i(x_i)
+    q_draft: np.ndarray         # float64 [B, gamma]  q_i(x_i)
+    u_band: np.ndarray          # bool [B]: an evaluated accept test lies within U_BAND
+    cdf_margin: np.ndarray      # float64 [B]: min_j |u_gamma - cdf_j| of the sampled row
+    residual: np.ndarray        # bool [B]: sampled from a residual (else bonus / argmax)
+    weights: np.ndarray | None  # float64 [B, V] normalised sampling row, if requested
+
+
+def _verify_block(target, draft, tokens, u, temperature, dtype, keep_weights):
+    tl = widen(target, dtype)            # [b, gamma+1, V]
+    dl = widen(draft, dtype)             # [b, gamma, V]
+    nb, g1, V = tl.shape
+    gamma = g1 - 1
+    rows = np.arange(nb)
+    tokens = np.asarray(tokens, dtype=np.int64).reshape(nb, gamma)
+
+    if temperature == 0.0:
+        a = argmax_first(tl)             # target argmax per position
+        d = argmax_first(dl)             # draft argmax per position
+        alpha = (a[:, :gamma] == d).astype(np.float64)
+        p_x = (tokens == a[:, :gamma]).astype(np.float64)
+        q_x = (tokens == d).astype(np.float64)
+        accept = tokens == a[:, :gamma]
+        n = accepted_prefix(accept)
+        t = a[rows, n]
+        weights = None
+        if keep_weights:
+            weights = np.zeros((nb, V))
+            weights[rows, t] = 1.0
+        return Result(n, t, alpha, 1.0 - alpha, p_x, q_x, np.zeros(nb, bool),
+                      np.full(nb, np.inf), np.zeros(nb, bool), weights)
+
+    p = softmax(tl, temperature)         # [b, gamma+1, V]
+    q = softmax(dl, temperature)         # [b, gamma, V]
+    alpha = overlap(p[:, :gamma], q)
+    tv = total_variation(p[:, :gamma], q)
+    p_x = np.take_along_axis(p[:, :gamma], tokens[..., None], axis=-1)[..., 0]
+    q_x = np.take_along_axis(q, tokens[..., None], axis=-1)[..., 0]
+    accept, capped = ratio_test(p_x, q_x, u[:, :gamma])
+    n = accepted_prefix(accept)
+
+    evaluated = np.arange(gamma)[None, :] <= n[:, None]
+    with np.errstate(invalid="ignore"):
+        near = np.abs(u[:, :gamma] - capped) < U_BAND
+    u_band = (near & evaluated).any(axis=-1) if gamma else np.zeros(nb, bool)
+
+    residual = n < gamma
+    w = p[rows, n].copy()                          # bonus row p_gamma when n == gamma
+    if residual.any():
+        idx = np.nonzero(residual)[0]
+        res = residual_weights(p[idx, n[idx]], q[idx, n[idx]])
+        mass = res.sum(axis=-1)
+        ok = mass > 0.0                            # zero mass: keep p_n
+        w[idx[ok]] = res[ok] / mass[ok][:, None]
+    w /= w.sum(axis=-1, keepdims=True)
+    t, cdf = inverse_cdf(w, u[:, gamma].astype(np.float64))
+    margin = np.abs(cdf - u[:, gamma:gamma + 1]).min(axis=-1)
+    return Result(n, t, alpha, tv, p_x, q_x, u_band, margin, residual,
+                  w if keep_weights else None)
+
+
+def verify(target, draft, tokens, uniforms, temperature: float, dtype: str,
+           keep_weights: bool = False, block_elems: int = 1 << 25) -> Result:
+    """Run the verification step for every sequence of the batch.
+
+    target [B, gamma+1, V], draft [B, gamma, V] (float32, or uint16 bf16 bits),
+    tokens int [B, gamma], uniforms float32 [B, gamma+1] in (0, 1).
+    Sequences are independent, so they are processed in blocks to bound memory.
+    """
+    target = np.asarray(target)
+    draft = np.asarray(draft)
+    B, g1, V = target.shape
+    gamma = g1 - 1
+    if draft.shape != (B, gamma, V):
+        raise ValueError("draft must be [B, gamma, V]")
+    if temperature < 0.0 or not np.isfinite(temperature):
+        raise ValueError("temperature must be finite and >= 0")
+    u = np.asarray(uniforms, dtype=np.float32).astype(np.float64).reshape(B, g1)
+    tokens = np.asarray(tokens).reshape(B, gamma)
+    per_seq = max(1, (2 * gamma + 1) * V)
+    step = max(1, block_elems // per_seq)
+    parts = [_verify_block(target[s:s + step], draft[s:s + step], tokens[s:s + step],
+                           u[s:s + step], temperature, dtype, keep_weights)
+             for s in range(0, B, step)]
+    if not parts:
+        z = np.zeros(0)
+        return Result(z.astype(np.int64), z.astype(np.int64), np.zeros((0, gamma)),
+                      np.zeros((0, gamma)), np.zeros((0, gamma)), np.zeros((0, gamma)),
+                      z.astype(bool), z, z.astype(bool), None)
+    cat = lambda f: np.concatenate([getattr(r, f) for r in parts])  # noqa: E731
+    return Result(cat("n_accepted"), cat("next_token"), cat("alpha"), cat("tv"),
+                  cat("p_draft"), cat("q_draft"), cat("u_band"), cat("cdf_margin"),
+                  cat("residual"), cat("weights") if keep_weights else None)
+
+
+def verify_case(case, keep_weights: bool = False, seqs=None) -> Result:
+    """verify() on a workloads.VerifyCase, optionally on a subset of sequences."""
+    if seqs is not None:
+        case = case.subset(seqs)
+    return verify(case.target, case.draft, case.tokens, case.uniforms,
+                  case.temperature, case.dtype, keep_weights)
