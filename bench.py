@@ -1,0 +1,194 @@
+"""Benchmark of the verification step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--algo auto|multipass|fused]
+
+Workload: B=64 sequences, gamma=4 drafts, V=128256, bf16 logits, T=1.  Target
+logits are N(0, 3^2) with 8 peaked tokens per row (+8).  Draft logits are the
+target plus N(0, sigma_b^2), with sigma_b ~ U(0.2, 2) per sequence (seeded,
+synthetic).  One step is one spec_verify call over the whole batch.  The inputs
+are resident in HBM; NSETS copies rotate so that the working set exceeds the
+256 MB last-level cache and every step streams from HBM.
+
+Prints one JSON line (rank 0) with the throughput in verified target rows/s
+(B*(gamma+1) per step).  It also carries:
+  roofline:     algorithmic bytes of one launch / its average HIP-event
+                duration, against 8 TB/s;
+  cpu_baseline: the fp64 oracle (test infrastructure) timed on a bounded
+                sample of the same workload on this host.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "verified logit rows/s (B*(gamma+1) x V) and % of peak HBM GB/s at V=128256"
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ["verify_multipass.hip", "verify_fused.hip", "common.hpp"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        path = os.path.join(ROOT, "speculative_sampling_verification_02_amd", "csrc", name)
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(n_accepted: np.ndarray, gamma: int, V: int, elem: int) -> int:
+    """Bytes the method must read per call: the 2*gamma draft/target rows of every
+    sequence (all overlaps are reported), the bonus row only where every draft was
+    kept, plus tokens, uniforms and outputs."""
+    B = len(n_accepted)
+    rows = 2 * gamma * B + int((n_accepted == gamma).sum())
+    small = 4 * B * gamma + 4 * B * (gamma + 1) + 4 * B * (2 + 3 * gamma)
+    return rows * V * elem + small
+
+
+def cpu_baseline(case, budget_s: float = 12.0) -> dict:
+    """The fp64 oracle as it stands on a sample of the same workload: the first
+    8 sequences, repeated until `budget_s` of CPU time has passed."""
+    from oracle import verify as ov
+    sample = case.subset(np.arange(8))
+    rows = 0
+    t0 = time.perf_counter()
+    while True:
+        ov.verify_case(sample)
+        rows += sample.B * (sample.gamma + 1)
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": rows / dt, "unit": "rows/s", "cores": 1, "kind": "oracle",
+            "sample": f"8 of the {case.B} sequences (rows of {case.V} bf16 logits), "
+                      f"repeated for {dt:.1f} s, single-threaded NumPy fp64"}
+
+
+def load_traffic(algo_name: str):
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = rec.get(algo_name)
+    if not entry or entry.get("source_hash") != kernel_source_hash():
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--algo", default="auto", choices=["auto", "multipass", "fused"])
+    ap.add_argument("--sets", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 1 GiB device copy (for counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the verification step shards by sequence with no communication)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import speculative_sampling_verification_02_amd as sv
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    algo = {"auto": sv.ALGO_AUTO, "multipass": sv.ALGO_MULTIPASS, "fused": sv.ALGO_FUSED}[args.algo]
+    case = W.config3(0, 1.0)
+    B, G, V = case.B, case.gamma, case.V
+    print(f"[bench] generated B={B} gamma={G} V={V} bf16", file=sys.stderr, flush=True)
+
+    def to_dev(a):
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    base = (to_dev(case.target), to_dev(case.draft))
+    sets = [base] + [(base[0].clone(), base[1].clone()) for _ in range(args.sets - 1)]
+    tokens = torch.from_numpy(case.tokens).to(dev)
+    uniforms = torch.from_numpy(case.uniforms).to(dev)
+    ws = torch.empty(sv.workspace_size(B, G, V, sv.SPEC_BF16), dtype=torch.uint8, device=dev)
+    outs = [{k: torch.empty(s, dtype=dt, device=dev) for k, s, dt in (
+        ("n_accepted", (B,), torch.int32), ("next_token", (B,), torch.int32),
+        ("alpha", (B, G), torch.float32), ("p_draft", (B, G), torch.float32),
+        ("q_draft", (B, G), torch.float32))} for _ in sets]
+
+    def step(k):
+        t, d = sets[k % len(sets)]
+        sv.verify(t, d, tokens, uniforms, 1.0, algo=algo, workspace=ws, outputs=outs[k % len(sets)])
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        starts[k].record()
+        step(k)
+        ends[k].record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    launch_ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+
+    ms_per_step = 1e3 * elapsed / args.steps
+    rows = B * (G + 1)
+    n0 = outs[0]["n_accepted"].cpu().numpy()
+    alg = algorithmic_bytes(n0, G, V, 2)
+    avg_launch_s = float(launch_ms.mean()) * 1e-3
+    achieved = alg / avg_launch_s / 1e9
+    algo_name = {sv.ALGO_AUTO: "auto", sv.ALGO_MULTIPASS: "multipass", sv.ALGO_FUSED: "fused"}[algo]
+    traffic = load_traffic(algo_name)
+    line = {
+        "metric": METRIC,
+        "value": rows / (ms_per_step * 1e-3),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"spec_verify B={B} gamma={G} V={V} bf16 logits T=1, Gaussian rows "
+                               "with 8 peaked tokens, per-sequence draft noise",
+                   "B": B, "gamma": G, "V": V, "logits": "bf16", "temperature": 1.0,
+                   "algo": algo_name, "buffer_sets": len(sets)},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "launch_us_mean": 1e3 * float(launch_ms.mean()),
+                     "launch_us_median": 1e3 * float(np.median(launch_ms)),
+                     "alg_bytes": alg, "full_bytes": (2 * G + 1) * V * 2 * B},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(case)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

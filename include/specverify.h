@@ -1,0 +1,167 @@
+/*
+ * specverify.h -- C ABI of the speculative-sampling verification library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Pages cited:
+ *   [FI] intuitivepapers.ai, "Fast Inference from Transformers via Speculative Decoding"
+ *   [SD] nonconvexcard course page, "Speculative Decoding"
+ *   [LH] lihaoran.work article on speculative decoding
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers (hipMalloc'd or torch CUDA tensors),
+ *     row-major, owned by the caller.  They must stay valid until the work
+ *     queued on `stream` has run.  The library keeps no pointer after a call
+ *     returns, allocates no device memory, and holds no global state besides
+ *     the kernels; calls are thread-safe.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Calls are asynchronous: they queue kernels on `stream` and return.
+ *   - Argument errors are detected on the host before anything is queued.
+ *     Nothing is written in that case.  A HIP launch failure returns SPEC_EHIP.
+ *   - Logits must be finite or -inf (-inf means probability 0, for example a
+ *     token masked out before sampling).  Every row needs at least one finite
+ *     logit.  +inf or NaN logits, and rows with no finite logit, are caller
+ *     errors.  The results are then undefined but the kernels still terminate.
+ *   - Outputs are deterministic: the same inputs give bit-identical outputs.
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+enum {
+  SPEC_OK = 0,
+  SPEC_EINVAL = -1,       /* bad argument: NULL pointer, size out of range, bad temperature */
+  SPEC_EUNSUPPORTED = -2, /* unsupported dtype or algorithm */
+  SPEC_ENOSPACE = -3,     /* workspace smaller than the *_workspace_size() query */
+  SPEC_EHIP = -4          /* HIP runtime error while queueing work */
+};
+
+/* Element type of logit tensors. */
+enum { SPEC_F32 = 0, SPEC_BF16 = 1 };
+
+/* Algorithm selector for spec_verify_algo(). */
+enum {
+  SPEC_ALGO_AUTO = 0,      /* the fastest available path for the shape */
+  SPEC_ALGO_MULTIPASS = 1, /* row statistics, then pair overlap, then a per-sequence finish */
+  SPEC_ALGO_FUSED = 2      /* one persistent kernel; every logit is read from HBM once */
+};
+
+#define SPEC_MAX_GAMMA 32
+
+/* Human-readable text for a status code (static storage, never NULL). */
+const char* spec_status_string(int status);
+
+/*
+ * Bytes of device workspace spec_verify() / spec_verify_algo() need for this
+ * shape, for any algorithm.  Returns 0 for invalid arguments.
+ */
+size_t spec_verify_workspace_size(int B, int gamma, int V, int dtype);
+
+/*
+ * spec_verify -- one verification step for a batch of B independent sequences
+ * ([FI] "The loop: draft, verify in one pass, keep a prefix", Algorithm 1
+ * steps 3-4; [SD] "The algorithm").
+ *
+ * For each sequence b, with positions i counted from 0:
+ *   p_i = softmax(target_logits[b][i] / T), i = 0..gamma;
+ *   q_i = softmax(draft_logits[b][i] / T),  i = 0..gamma-1.
+ * The same temperature applies to both models ([FI] "The loop"; nazmi.tech
+ * "5. Sampling and evaluation").
+ *   alpha[b][i] = sum_x min(p_i(x), q_i(x)) = 1 - TV(p_i, q_i) for every i < gamma
+ *     ([SD] "How often do we accept?").
+ *   Drafts are walked left to right.  Draft x_i is kept iff
+ *     uniforms[b][i] <= min(1, p_i(x_i) / q_i(x_i)); the walk stops at the first
+ *     failure.  n_accepted[b] = number kept, in [0, gamma].
+ *   next_token[b] is drawn with uniforms[b][gamma] by inverse CDF in token order
+ *     (the first token whose cumulative weight exceeds u * total).  The weights
+ *     are max(0, p_n - q_n) when n < gamma (the residual, [FI] "Speculative
+ *     sampling: the accept/reject rule", eq. (2)), and p_gamma when every draft
+ *     was kept (the bonus token).
+ *   T == 0 is argmax mode: p_i and q_i are one-hot at the row argmax, with ties
+ *     going to the lowest index.  A draft is kept iff it equals the target
+ *     argmax.  next_token is the target argmax at position n.  alpha is 1 where
+ *     the two argmaxes agree, else 0 ([FI] "Speculative sampling", the
+ *     temperature-to-zero limit; [LH] "What does 'unchanged output' mean?").
+ *     The uniforms are not read.
+ *   A ratio with q_i(x_i) = 0 follows IEEE rules: p > 0 keeps the draft, 0/0 rejects.
+ *
+ * Arguments:
+ *   target_logits  [B][gamma+1][V], dtype
+ *   draft_logits   [B][gamma][V],   dtype (may be NULL when gamma == 0)
+ *   dtype          SPEC_F32 or SPEC_BF16
+ *   draft_tokens   int32 [B][gamma], each in [0, V) (may be NULL when gamma == 0)
+ *   uniforms       float32 [B][gamma+1], each in (0, 1)
+ *   B >= 0, 0 <= gamma <= SPEC_MAX_GAMMA, 1 <= V <= 2^31 - 1
+ *   temperature    0 (argmax) or finite with temperature >= FLT_MIN
+ *   n_accepted     int32 [B] out
+ *   next_token     int32 [B] out
+ *   alpha          float32 [B][gamma] out, or NULL
+ *   p_draft        float32 [B][gamma] out, p_i(x_i), or NULL
+ *   q_draft        float32 [B][gamma] out, q_i(x_i), or NULL
+ *   workspace      device scratch of at least spec_verify_workspace_size() bytes.
+ *                  The library treats it as uninitialised on entry.
+ * Returns SPEC_OK or an error status.  B == 0 returns SPEC_OK and queues nothing.
+ */
+int spec_verify(const void* target_logits, const void* draft_logits, int dtype,
+                const int32_t* draft_tokens, const float* uniforms,
+                int B, int gamma, int V, float temperature,
+                int32_t* n_accepted, int32_t* next_token, float* alpha,
+                float* p_draft, float* q_draft,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/* spec_verify with an explicit algorithm (SPEC_ALGO_*).  All algorithms give the
+ * same outputs up to the floating-point rounding of their reductions. */
+int spec_verify_algo(int algo,
+                     const void* target_logits, const void* draft_logits, int dtype,
+                     const int32_t* draft_tokens, const float* uniforms,
+                     int B, int gamma, int V, float temperature,
+                     int32_t* n_accepted, int32_t* next_token, float* alpha,
+                     float* p_draft, float* q_draft,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * spec_lmhead_logits -- the target pass's final matrix product for the positions
+ * being verified ([FI] "Decoding waits on memory, not arithmetic": every weight
+ * is read once per pass).
+ *   logits[m][v] = sum_k hidden[m][k] * W[k][v], with bf16 inputs and fp32
+ *   accumulation, written as fp32.
+ *   hidden  bf16 [M][d];  W  bf16 [d][V];  logits  float32 [M][V] out.
+ *   1 <= M <= 256, 1 <= d, 1 <= V; d must be a multiple of 32 and V a multiple of 8.
+ */
+int spec_lmhead_logits(const void* hidden, const void* W, int M, int d, int V,
+                       float* logits, void* stream);
+
+/*
+ * spec_lmhead_verify -- LM heads of both models over the verified positions,
+ * followed by spec_verify at `temperature`.
+ *   hidden           bf16 [B*(gamma+1)][d], the target's hidden states at the
+ *                    gamma+1 positions of each sequence
+ *   hidden_draft     bf16 [B*gamma][d], or NULL to use rows 0..gamma-1 of each
+ *                    sequence's block of `hidden`
+ *   W_target, W_draft  bf16 [d][V]
+ *   target_logits    float32 [B][gamma+1][V] out (caller-owned; feeds the verify)
+ *   draft_logits     float32 [B][gamma][V]   out
+ *   other arguments as for spec_verify (the logits are fp32).
+ * Limits: as spec_lmhead_logits for d and V; B*(gamma+1) <= 256.
+ */
+size_t spec_lmhead_workspace_size(int B, int gamma, int d, int V);
+int spec_lmhead_verify(const void* hidden, const void* hidden_draft,
+                       const void* W_target, const void* W_draft,
+                       int B, int gamma, int d, int V,
+                       const int32_t* draft_tokens, const float* uniforms, float temperature,
+                       float* target_logits, float* draft_logits,
+                       int32_t* n_accepted, int32_t* next_token, float* alpha,
+                       float* p_draft, float* q_draft,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECVERIFY_H */

@@ -1,0 +1,223 @@
+"""Speculative-sampling verification on AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding over libspecverify.so, the C ABI declared in
+include/specverify.h.  This module only marshals arguments: it checks tensor
+dtypes, devices and contiguity, allocates outputs and workspace with torch, and
+passes raw device pointers and the current HIP stream.  Every step of the
+verification runs in the library's HIP kernels.  Importing fails loudly if the
+library has not been built; there is no fallback path.
+
+Build the library with `python -m speculative_sampling_verification_02_amd.build`.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libspecverify.so")
+
+SPEC_OK, SPEC_EINVAL, SPEC_EUNSUPPORTED, SPEC_ENOSPACE, SPEC_EHIP = 0, -1, -2, -3, -4
+SPEC_F32, SPEC_BF16 = 0, 1
+ALGO_AUTO, ALGO_MULTIPASS, ALGO_FUSED = 0, 1, 2
+MAX_GAMMA = 32
+
+_c_void_p, _c_int, _c_float, _c_size_t = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+
+# name -> (restype, argtypes); mirrors include/specverify.h
+SIGNATURES = {
+    "spec_status_string": (ctypes.c_char_p, [_c_int]),
+    "spec_verify_workspace_size": (_c_size_t, [_c_int, _c_int, _c_int, _c_int]),
+    "spec_verify": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_void_p, _c_void_p,
+                             _c_int, _c_int, _c_int, _c_float,
+                             _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                             _c_void_p, _c_size_t, _c_void_p]),
+    "spec_verify_algo": (_c_int, [_c_int, _c_void_p, _c_void_p, _c_int, _c_void_p, _c_void_p,
+                                  _c_int, _c_int, _c_int, _c_float,
+                                  _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                  _c_void_p, _c_size_t, _c_void_p]),
+    "spec_lmhead_logits": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_void_p, _c_void_p]),
+    "spec_lmhead_workspace_size": (_c_size_t, [_c_int, _c_int, _c_int, _c_int]),
+    "spec_lmhead_verify": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                    _c_int, _c_int, _c_int, _c_int,
+                                    _c_void_p, _c_void_p, _c_float,
+                                    _c_void_p, _c_void_p,
+                                    _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                    _c_void_p, _c_size_t, _c_void_p]),
+}
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run "
+                          "`python -m speculative_sampling_verification_02_amd.build` first")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+class SpecVerifyError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {lib.spec_status_string(status).decode()} (status {status})")
+
+
+def _check(status: int, where: str) -> None:
+    if status != SPEC_OK:
+        raise SpecVerifyError(status, where)
+
+
+def status_string(status: int) -> str:
+    return lib.spec_status_string(status).decode()
+
+
+# ----------------------------------------------------------- torch plumbing
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return SPEC_F32
+    if t.dtype == torch.bfloat16:
+        return SPEC_BF16
+    raise TypeError(f"logits must be float32 or bfloat16, got {t.dtype}")
+
+
+def _need(t, name, dtype=None, device=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def workspace_size(B: int, gamma: int, V: int, dtype: int = SPEC_BF16) -> int:
+    return int(lib.spec_verify_workspace_size(B, gamma, V, dtype))
+
+
+def verify(target_logits, draft_logits, draft_tokens, uniforms, temperature: float, *,
+           algo: int = ALGO_AUTO, workspace=None, outputs=None):
+    """One verification step on the current stream.
+
+    target_logits [B, gamma+1, V] and draft_logits [B, gamma, V] (float32 or
+    bfloat16, same dtype), draft_tokens int32 [B, gamma], uniforms float32
+    [B, gamma+1]; all on the same GPU.  Returns a dict of GPU tensors:
+    n_accepted int32 [B], next_token int32 [B], alpha / p_draft / q_draft
+    float32 [B, gamma].  `outputs` may supply that dict preallocated.
+    """
+    torch = _torch()
+    dev = target_logits.device
+    _need(target_logits, "target_logits")
+    B, g1, V = target_logits.shape
+    gamma = g1 - 1
+    if tuple(draft_logits.shape) != (B, gamma, V):
+        raise ValueError(f"draft_logits must be [{B}, {gamma}, {V}], got {tuple(draft_logits.shape)}")
+    if draft_logits.dtype != target_logits.dtype:
+        raise TypeError("target_logits and draft_logits must share a dtype")
+    if tuple(draft_tokens.shape) != (B, gamma) or tuple(uniforms.shape) != (B, g1):
+        raise ValueError("draft_tokens must be [B, gamma] and uniforms [B, gamma+1]")
+    _need(draft_logits, "draft_logits", device=dev)
+    _need(draft_tokens, "draft_tokens", torch.int32, dev)
+    _need(uniforms, "uniforms", torch.float32, dev)
+    dt = _dtype_code(target_logits)
+    if outputs is None:
+        outputs = {
+            "n_accepted": torch.empty(B, dtype=torch.int32, device=dev),
+            "next_token": torch.empty(B, dtype=torch.int32, device=dev),
+            "alpha": torch.empty(B, gamma, dtype=torch.float32, device=dev),
+            "p_draft": torch.empty(B, gamma, dtype=torch.float32, device=dev),
+            "q_draft": torch.empty(B, gamma, dtype=torch.float32, device=dev),
+        }
+    need = workspace_size(B, gamma, V, dt)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check(lib.spec_verify_algo(
+        algo, _ptr(target_logits), _ptr(draft_logits), dt, _ptr(draft_tokens), _ptr(uniforms),
+        B, gamma, V, float(temperature),
+        _ptr(outputs["n_accepted"]), _ptr(outputs["next_token"]), _ptr(outputs.get("alpha")),
+        _ptr(outputs.get("p_draft")), _ptr(outputs.get("q_draft")),
+        _ptr(workspace), workspace.numel(), _stream(dev)), "spec_verify")
+    return outputs
+
+
+def lmhead_logits(hidden, W, out=None):
+    """logits[M, V] = hidden[M, d] @ W[d, V] (bf16 in, fp32 accumulate and out)."""
+    torch = _torch()
+    dev = hidden.device
+    _need(hidden, "hidden", torch.bfloat16)
+    _need(W, "W", torch.bfloat16, dev)
+    M, d = hidden.shape
+    V = W.shape[1]
+    if W.shape[0] != d:
+        raise ValueError("W must be [d, V]")
+    if out is None:
+        out = torch.empty(M, V, dtype=torch.float32, device=dev)
+    _need(out, "out", torch.float32, dev)
+    _check(lib.spec_lmhead_logits(_ptr(hidden), _ptr(W), M, d, V, _ptr(out), _stream(dev)),
+           "spec_lmhead_logits")
+    return out
+
+
+def lmhead_verify(hidden, W_target, W_draft, B: int, gamma: int, draft_tokens, uniforms,
+                  temperature: float, hidden_draft=None, workspace=None):
+    """LM heads of both models over the verified positions, then the verification.
+
+    hidden bf16 [B*(gamma+1), d]; W_target / W_draft bf16 [d, V]; hidden_draft
+    bf16 [B*gamma, d] or None (rows 0..gamma-1 of each sequence in `hidden`).
+    Returns the verify outputs plus the fp32 target_logits and draft_logits.
+    """
+    torch = _torch()
+    dev = hidden.device
+    _need(hidden, "hidden", torch.bfloat16)
+    _need(W_target, "W_target", torch.bfloat16, dev)
+    _need(W_draft, "W_draft", torch.bfloat16, dev)
+    if hidden_draft is not None:
+        _need(hidden_draft, "hidden_draft", torch.bfloat16, dev)
+    _need(draft_tokens, "draft_tokens", torch.int32, dev)
+    _need(uniforms, "uniforms", torch.float32, dev)
+    d, V = W_target.shape
+    if tuple(hidden.shape) != (B * (gamma + 1), d):
+        raise ValueError("hidden must be [B*(gamma+1), d]")
+    out = {
+        "target_logits": torch.empty(B, gamma + 1, V, dtype=torch.float32, device=dev),
+        "draft_logits": torch.empty(B, gamma, V, dtype=torch.float32, device=dev),
+        "n_accepted": torch.empty(B, dtype=torch.int32, device=dev),
+        "next_token": torch.empty(B, dtype=torch.int32, device=dev),
+        "alpha": torch.empty(B, gamma, dtype=torch.float32, device=dev),
+        "p_draft": torch.empty(B, gamma, dtype=torch.float32, device=dev),
+        "q_draft": torch.empty(B, gamma, dtype=torch.float32, device=dev),
+    }
+    need = int(lib.spec_lmhead_workspace_size(B, gamma, d, V))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check(lib.spec_lmhead_verify(
+        _ptr(hidden), _ptr(hidden_draft), _ptr(W_target), _ptr(W_draft), B, gamma, d, V,
+        _ptr(draft_tokens), _ptr(uniforms), float(temperature),
+        _ptr(out["target_logits"]), _ptr(out["draft_logits"]),
+        _ptr(out["n_accepted"]), _ptr(out["next_token"]), _ptr(out["alpha"]),
+        _ptr(out["p_draft"]), _ptr(out["q_draft"]),
+        _ptr(workspace), workspace.numel(), _stream(dev)), "spec_lmhead_verify")
+    return out

@@ -1,0 +1,149 @@
+// C ABI of the verification library: argument validation, workspace sizing and
+// dispatch to the kernel paths.  The declarations and the contract of every
+// entry point are in include/specverify.h.
+
+#include <float.h>
+#include <math.h>
+
+#include <algorithm>
+
+#include "specverify.h"
+#include "verify_internal.hpp"
+
+using specv::VerifyArgs;
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+bool valid_shape(int B, int gamma, int V) {
+  if (B < 0 || gamma < 0 || gamma > SPEC_MAX_GAMMA || V < 1) return false;
+  // every kernel indexes blocks and rows with 32-bit grid sizes
+  const size_t rows = (size_t)B * (2 * (size_t)gamma + 1);
+  return rows * (((size_t)V + 8191) / 8192) < (size_t)INT32_MAX;
+}
+
+bool valid_temperature(float T) {
+  if (!std::isfinite(T) || T < 0.f) return false;
+  if (T == 0.f) return true;
+  return T >= FLT_MIN && std::isfinite(kLog2e / T);
+}
+
+int map_hip(hipError_t e) {
+  if (e == hipSuccess) return SPEC_OK;
+  return e == hipErrorNotSupported ? SPEC_EUNSUPPORTED : SPEC_EHIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* spec_status_string(int status) {
+  switch (status) {
+    case SPEC_OK: return "ok";
+    case SPEC_EINVAL: return "invalid argument";
+    case SPEC_EUNSUPPORTED: return "unsupported dtype, algorithm or shape";
+    case SPEC_ENOSPACE: return "workspace too small";
+    case SPEC_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+size_t spec_verify_workspace_size(int B, int gamma, int V, int dtype) {
+  if (!valid_shape(B, gamma, V) || (dtype != SPEC_F32 && dtype != SPEC_BF16)) return 0;
+  size_t bytes = specv::multipass_workspace_bytes(B, gamma, V);
+  bytes = std::max(bytes, specv::fused_workspace_bytes(B, gamma, V, dtype));
+  return std::max<size_t>(bytes, 256);
+}
+
+int spec_verify_algo(int algo, const void* target_logits, const void* draft_logits, int dtype,
+                     const int32_t* draft_tokens, const float* uniforms, int B, int gamma, int V,
+                     float temperature, int32_t* n_accepted, int32_t* next_token, float* alpha,
+                     float* p_draft, float* q_draft, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  if (algo != SPEC_ALGO_AUTO && algo != SPEC_ALGO_MULTIPASS && algo != SPEC_ALGO_FUSED)
+    return SPEC_EUNSUPPORTED;
+  if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_EUNSUPPORTED;
+  if (!valid_shape(B, gamma, V) || !valid_temperature(temperature)) return SPEC_EINVAL;
+  if (B == 0) return SPEC_OK;
+  if (!target_logits || !uniforms || !n_accepted || !next_token) return SPEC_EINVAL;
+  if (gamma > 0 && (!draft_logits || !draft_tokens)) return SPEC_EINVAL;
+  if (workspace_bytes < spec_verify_workspace_size(B, gamma, V, dtype) || !workspace)
+    return SPEC_ENOSPACE;
+
+  VerifyArgs a{};
+  a.target = target_logits;
+  a.draft = draft_logits;
+  a.dtype = dtype;
+  a.tokens = draft_tokens;
+  a.uniforms = uniforms;
+  a.B = B;
+  a.gamma = gamma;
+  a.V = V;
+  a.temperature = temperature;
+  a.k = temperature > 0.f ? kLog2e / temperature : 0.f;
+  a.n_out = n_accepted;
+  a.t_out = next_token;
+  a.alpha = gamma > 0 ? alpha : nullptr;
+  a.p_draft = gamma > 0 ? p_draft : nullptr;
+  a.q_draft = gamma > 0 ? q_draft : nullptr;
+  a.ws = workspace;
+  a.ws_bytes = workspace_bytes;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  const bool fused_ok = specv::fused_supported(B, gamma, V, dtype);
+  if (algo == SPEC_ALGO_FUSED && !fused_ok) return SPEC_EUNSUPPORTED;
+  if (algo == SPEC_ALGO_FUSED || (algo == SPEC_ALGO_AUTO && fused_ok)) return map_hip(specv::fused_launch(a, s));
+  return map_hip(specv::multipass_launch(a, s));
+}
+
+int spec_verify(const void* target_logits, const void* draft_logits, int dtype,
+                const int32_t* draft_tokens, const float* uniforms, int B, int gamma, int V,
+                float temperature, int32_t* n_accepted, int32_t* next_token, float* alpha,
+                float* p_draft, float* q_draft, void* workspace, size_t workspace_bytes,
+                void* stream) {
+  return spec_verify_algo(SPEC_ALGO_AUTO, target_logits, draft_logits, dtype, draft_tokens, uniforms,
+                          B, gamma, V, temperature, n_accepted, next_token, alpha, p_draft, q_draft,
+                          workspace, workspace_bytes, stream);
+}
+
+int spec_lmhead_logits(const void* hidden, const void* W, int M, int d, int V, float* logits,
+                       void* stream) {
+  if (!hidden || !W || !logits) return SPEC_EINVAL;
+  if (M < 1 || M > 256 || d < 32 || d % 32 != 0 || V < 8 || V % 8 != 0) return SPEC_EINVAL;
+  return map_hip(specv::lmhead_launch(hidden, W, M, d, V, 1, 1, logits, static_cast<hipStream_t>(stream)));
+}
+
+size_t spec_lmhead_workspace_size(int B, int gamma, int d, int V) {
+  if (d < 32) return 0;
+  return spec_verify_workspace_size(B, gamma, V, SPEC_F32);
+}
+
+int spec_lmhead_verify(const void* hidden, const void* hidden_draft, const void* W_target,
+                       const void* W_draft, int B, int gamma, int d, int V,
+                       const int32_t* draft_tokens, const float* uniforms, float temperature,
+                       float* target_logits, float* draft_logits, int32_t* n_accepted,
+                       int32_t* next_token, float* alpha, float* p_draft, float* q_draft,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  if (!valid_shape(B, gamma, V) || !valid_temperature(temperature)) return SPEC_EINVAL;
+  if (B == 0) return SPEC_OK;
+  const int M = B * (gamma + 1);
+  if (M > 256 || d < 32 || d % 32 != 0 || V % 8 != 0) return SPEC_EINVAL;
+  if (!hidden || !W_target || !target_logits || (gamma > 0 && (!W_draft || !draft_logits)))
+    return SPEC_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = specv::lmhead_launch(hidden, W_target, M, d, V, 1, 1, target_logits, s);
+  if (e != hipSuccess) return map_hip(e);
+  if (gamma > 0) {
+    // draft rows: either a dense [B*gamma][d] tensor, or rows 0..gamma-1 of
+    // each sequence's gamma+1 block of `hidden`
+    e = hidden_draft ? specv::lmhead_launch(hidden_draft, W_draft, B * gamma, d, V, 1, 1, draft_logits, s)
+                     : specv::lmhead_launch(hidden, W_draft, B * gamma, d, V, gamma + 1, gamma, draft_logits, s);
+    if (e != hipSuccess) return map_hip(e);
+  }
+  return spec_verify(target_logits, draft_logits, SPEC_F32, draft_tokens, uniforms, B, gamma, V,
+                     temperature, n_accepted, next_token, alpha, p_draft, q_draft, workspace,
+                     workspace_bytes, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,43 @@
+// Internal interface between the C ABI layer and the verification kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace specv {
+
+// Everything one verification call needs, validated by the ABI layer.
+struct VerifyArgs {
+  const void* target;      // [B][gamma+1][V]
+  const void* draft;       // [B][gamma][V]
+  int dtype;               // SPEC_F32 / SPEC_BF16
+  const int32_t* tokens;   // [B][gamma]
+  const float* uniforms;   // [B][gamma+1]
+  int B, gamma, V;
+  float temperature;       // 0 = argmax mode
+  float k;                 // log2(e) / T in fp32 (unused in argmax mode)
+  int32_t* n_out;
+  int32_t* t_out;
+  float* alpha;            // may be null
+  float* p_draft;          // may be null
+  float* q_draft;          // may be null
+  void* ws;
+  size_t ws_bytes;
+};
+
+// ---- multi-pass path
+size_t multipass_workspace_bytes(int B, int gamma, int V);
+hipError_t multipass_launch(const VerifyArgs& a, hipStream_t stream);
+
+// ---- fused read-once path
+size_t fused_workspace_bytes(int B, int gamma, int V, int dtype);
+// Returns hipErrorNotSupported when the shape does not fit the fused design.
+hipError_t fused_launch(const VerifyArgs& a, hipStream_t stream);
+bool fused_supported(int B, int gamma, int V, int dtype);
+
+// ---- LM head
+hipError_t lmhead_launch(const void* hidden, const void* W, int M, int d, int V,
+                         int group_in, int group_out, float* out, hipStream_t stream);
+
+}  // namespace specv

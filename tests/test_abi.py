@@ -1,0 +1,89 @@
+"""The C-ABI library without a GPU: it loads, exports every symbol the header
+declares, and rejects bad arguments on the host before any GPU work."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "specverify.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(spec_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_functions()
+    for want in ("spec_verify", "spec_verify_algo", "spec_verify_workspace_size",
+                 "spec_lmhead_logits", "spec_lmhead_verify", "spec_lmhead_workspace_size",
+                 "spec_status_string"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    import speculative_sampling_verification_02_amd as sv
+    lib = ctypes.CDLL(sv.LIB_PATH)
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+        assert name in sv.SIGNATURES, f"binding lacks {name}"
+
+
+def test_status_strings():
+    import speculative_sampling_verification_02_amd as sv
+    assert sv.status_string(0) == "ok"
+    for code in (-1, -2, -3, -4):
+        assert sv.status_string(code) not in ("ok", "unknown status")
+    assert sv.status_string(123) == "unknown status"
+
+
+def test_workspace_query():
+    import speculative_sampling_verification_02_amd as sv
+    assert sv.workspace_size(64, 4, 128256, sv.SPEC_BF16) > 0
+    assert sv.workspace_size(-1, 4, 100, sv.SPEC_BF16) == 0
+    assert sv.workspace_size(1, sv.MAX_GAMMA + 1, 100, sv.SPEC_BF16) == 0
+    assert sv.workspace_size(1, 2, 100, 7) == 0
+    assert sv.workspace_size(0, 2, 100, sv.SPEC_F32) > 0
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+
+
+def _verify(lib, **kw):
+    args = dict(algo=0, target=FAKE, draft=FAKE, dtype=1, tokens=FAKE, u=FAKE, B=2, gamma=3, V=100,
+                T=1.0, n=FAKE, t=FAKE, alpha=None, p=None, q=None, ws=FAKE, ws_bytes=1 << 20, stream=None)
+    args.update(kw)
+    return lib.spec_verify_algo(*args.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), -1), (dict(gamma=-1), -1), (dict(gamma=33), -1), (dict(V=0), -1),
+    (dict(T=-1.0), -1), (dict(T=float("nan")), -1), (dict(T=float("inf")), -1), (dict(T=1e-45), -1),
+    (dict(dtype=5), -2), (dict(algo=9), -2),
+    (dict(target=None), -1), (dict(u=None), -1), (dict(n=None), -1), (dict(t=None), -1),
+    (dict(draft=None), -1), (dict(tokens=None), -1),
+    (dict(ws_bytes=16), -3), (dict(ws=None), -3),
+])
+def test_argument_errors_before_any_gpu_work(kw, status):
+    import speculative_sampling_verification_02_amd as sv
+    assert _verify(sv.lib, **kw) == status
+
+
+def test_empty_batch_is_a_no_op():
+    import speculative_sampling_verification_02_amd as sv
+    assert _verify(sv.lib, B=0, target=None, draft=None, tokens=None, u=None, n=None, t=None,
+                   ws=None, ws_bytes=0) == 0
+
+
+def test_lmhead_argument_errors():
+    import speculative_sampling_verification_02_amd as sv
+    lib = sv.lib
+    assert lib.spec_lmhead_logits(FAKE, FAKE, 0, 64, 64, FAKE, None) == -1
+    assert lib.spec_lmhead_logits(FAKE, FAKE, 257, 64, 64, FAKE, None) == -1
+    assert lib.spec_lmhead_logits(FAKE, FAKE, 4, 60, 64, FAKE, None) == -1
+    assert lib.spec_lmhead_logits(FAKE, FAKE, 4, 64, 63, FAKE, None) == -1
+    assert lib.spec_lmhead_logits(None, FAKE, 4, 64, 64, FAKE, None) == -1

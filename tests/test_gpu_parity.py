@@ -1,0 +1,226 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle, element by
+element, on seeded inputs (rules in tests/parity.py)."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import workloads as W
+from tests import gpu_util, parity
+
+pytestmark = pytest.mark.gpu
+
+ALGOS = {"multipass": 1}
+
+
+def _sv():
+    import speculative_sampling_verification_02_amd as sv
+    return sv
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return gpu_util.device()
+
+
+def _banner(msg):
+    print(f"[parity] {msg}", flush=True)
+
+
+# ------------------------------------------------------- benchmark configs
+
+@pytest.mark.parametrize("algo", list(ALGOS))
+@pytest.mark.parametrize("T", [1.0, 0.0])
+@pytest.mark.parametrize("seed", [1, 2, 3, 4, 5])
+def test_config1(dev, algo, T, seed):
+    case = W.config1(seed, T)
+    rep = parity.check(case, gpu_util.run_case(case, ALGOS[algo], dev=dev), where=f"cfg1 s{seed} T{T}")
+    _banner(f"cfg1 {algo} seed={seed} T={T}: {rep}")
+
+
+@pytest.mark.parametrize("algo", list(ALGOS))
+@pytest.mark.parametrize("T", [0.0, 0.7, 1.0])
+def test_config2(dev, algo, T):
+    case = W.config2(7, T, rounds=6)
+    rep = parity.check(case, gpu_util.run_case(case, ALGOS[algo], dev=dev), where=f"cfg2 T{T}")
+    _banner(f"cfg2 {algo} T={T}: {rep}")
+
+
+@pytest.mark.parametrize("algo", list(ALGOS))
+@pytest.mark.parametrize("T", [1.0, 0.0])
+def test_config3_full_size(dev, algo, T):
+    case = W.config3(1, T)
+    gpu = gpu_util.run_case(case, ALGOS[algo], dev=dev)
+    rep = parity.check(case, gpu, where=f"cfg3 T{T}")
+    _banner(f"cfg3 {algo} T={T}: {rep}")
+    assert rep.u_band + rep.cdf_ambiguous <= max(2, case.B // 10)
+
+
+@pytest.mark.parametrize("algo", list(ALGOS))
+@pytest.mark.parametrize("T", [1.0, 0.0])
+def test_config5_full_size_sampled(dev, algo, T):
+    case = W.config5(1, T)
+    gpu = gpu_util.run_case(case, ALGOS[algo], dev=dev)
+    # every sequence is independent: check a spread of 24 plus the confidently-wrong ones
+    rng = np.random.default_rng(5)
+    seqs = set(rng.choice(case.B, 24, replace=False).tolist())
+    tl = W.as_f32(case.target[:, :case.gamma], "bf16")
+    for b in range(case.B):
+        if len(seqs) >= 32:
+            break
+        if np.any(case.tokens[b] == tl[b].argmin(-1)):
+            seqs.add(b)
+    seqs = np.array(sorted(seqs))
+    rep = parity.check(case, gpu, seqs=seqs, where=f"cfg5 T{T}")
+    _banner(f"cfg5 {algo} T={T}: {rep}")
+    # properties over the whole batch
+    assert np.all((gpu["n_accepted"] >= 0) & (gpu["n_accepted"] <= case.gamma))
+    assert np.all((gpu["next_token"] >= 0) & (gpu["next_token"] < case.V))
+    assert np.all((gpu["alpha"] >= 0) & (gpu["alpha"] <= 1 + 1e-5))
+
+
+# ------------------------------------------------ shapes, tails, edge cases
+
+SHAPES = [
+    # B, gamma, V, dtype, T     (kChunk = 8192 tokens)
+    (3, 5, 8192 * 3 + 77, "f32", 1.0),     # V % 4 != 0: scalar loads, ragged last chunk
+    (3, 5, 8192 * 3 + 77, "bf16", 0.7),    # odd V in bf16: unaligned rows
+    (2, 4, 8192 * 2 + 8, "bf16", 1.0),     # vector loads, 8-token last chunk
+    (2, 4, 8192 * 2 + 4, "f32", 0.0),
+    (4, 0, 1000, "f32", 1.0),              # no drafts: plain sampling from p_0
+    (2, 32, 300, "bf16", 1.3),             # the largest gamma
+    (5, 3, 1, "f32", 1.0),                 # one-token vocabulary
+    (3, 2, 7, "bf16", 0.0),
+    (3, 6, 5000, "f32", 1e-3),             # cold temperature
+    (3, 6, 5000, "bf16", 10.0),            # hot temperature
+    (7, 1, 40000, "bf16", 1.0),
+]
+
+
+@pytest.mark.parametrize("algo", list(ALGOS))
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "B{}g{}V{}{}T{}".format(*s))
+def test_shapes(dev, algo, shape):
+    B, G, V, dt, T = shape
+    case = W.gaussian_case(B, G, V, dt, T, seed=B * 1000 + G * 10 + V % 97, target_std=2.5,
+                           draft_scale=0.9, draft_noise=0.8)
+    rep = parity.check(case, gpu_util.run_case(case, ALGOS[algo], dev=dev), where=str(shape))
+    _banner(f"shape {shape} {algo}: {rep}")
+
+
+@pytest.mark.parametrize("algo", list(ALGOS))
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_masked_logits(dev, algo, dt):
+    """-inf logits (a top-k style mask): masked tokens have probability 0."""
+    rng = np.random.default_rng(9)
+    B, G, V, keep = 6, 4, 9000, 40
+    case = W.gaussian_case(B, G, V, "f32", 1.0, seed=9)
+    tl, dl = case.target.copy(), case.draft.copy()
+    for arr in (tl, dl):
+        thresh = np.sort(arr, axis=-1)[..., -keep][..., None]
+        arr[arr < thresh] = -np.inf
+    tokens = case.tokens.copy()
+    for b in range(B):
+        for i in range(G):
+            if rng.random() < 0.3:   # a token the target masked: p = 0, must reject
+                tokens[b, i] = int(np.nonzero(np.isinf(tl[b, i]))[0][0])
+            elif rng.random() < 0.3:  # q = 0 < p: must accept
+                cand = np.nonzero(np.isinf(dl[b, i]) & np.isfinite(tl[b, i]))[0]
+                if len(cand):
+                    tokens[b, i] = int(cand[0])
+    if dt == "bf16":
+        tl, dl = W.f32_to_bf16_bits(tl), W.f32_to_bf16_bits(dl)
+    case = W.VerifyCase("masked", tl, dl, dt, tokens, case.uniforms, 1.0)
+    gpu = gpu_util.run_case(case, ALGOS[algo], dev=dev)
+    rep = parity.check(case, gpu, where=f"masked {dt}")
+    _banner(f"masked {dt} {algo}: {rep}")
+
+
+@pytest.mark.parametrize("algo", list(ALGOS))
+def test_identical_draft_accepts_everything(dev, algo):
+    case = W.gaussian_case(4, 6, 20000, "bf16", 1.0, seed=3)
+    case = W.VerifyCase("same", case.target, case.target[:, :6].copy(), "bf16", case.tokens, case.uniforms, 1.0)
+    gpu = gpu_util.run_case(case, ALGOS[algo], dev=dev)
+    assert np.all(gpu["n_accepted"] == 6)
+    np.testing.assert_allclose(gpu["alpha"], 1.0, atol=1e-5)
+    parity.check(case, gpu, where="identical")
+
+
+@pytest.mark.parametrize("algo", list(ALGOS))
+def test_argmax_ties_lowest_index(dev, algo):
+    rng = np.random.default_rng(4)
+    B, G, V = 8, 3, 20000
+    tl = rng.integers(0, 4, size=(B, G + 1, V)).astype(np.float32)   # every max is tied
+    dl = rng.integers(0, 4, size=(B, G, V)).astype(np.float32)
+    tl[0, 0, :] = -0.0
+    tl[0, 0, 5] = 0.0                                                 # -0 and +0 tie
+    tokens = np.where(rng.random((B, G)) < 0.5, tl[:, :G].argmax(-1), 7).astype(np.int32)
+    for dt in ("f32", "bf16"):
+        t, d = (tl, dl) if dt == "f32" else (W.f32_to_bf16_bits(tl), W.f32_to_bf16_bits(dl))
+        case = W.VerifyCase("ties", t, d, dt, tokens, np.full((B, G + 1), 0.5, np.float32), 0.0)
+        parity.check(case, gpu_util.run_case(case, ALGOS[algo], dev=dev), where=f"ties {dt}")
+
+
+@pytest.mark.parametrize("algo", list(ALGOS))
+def test_out_of_range_token_is_rejected(dev, algo):
+    case = W.gaussian_case(3, 3, 3000, "f32", 1.0, seed=5)
+    case.tokens[:, 0] = np.array([-1, 3000, 1 << 30], np.int32)
+    gpu = gpu_util.run_case(case, ALGOS[algo], dev=dev)
+    assert np.all(gpu["n_accepted"] == 0)
+    assert np.all(gpu["p_draft"][:, 0] == 0) and np.all(gpu["q_draft"][:, 0] == 0)
+    assert np.all((gpu["next_token"] >= 0) & (gpu["next_token"] < 3000))
+
+
+@pytest.mark.parametrize("algo", list(ALGOS))
+def test_deterministic(dev, algo):
+    case = W.config3(2, 1.0, B=16, V=50000)
+    t = gpu_util.case_tensors(case, dev)
+    a = gpu_util.run_case(case, ALGOS[algo], tensors=t, dev=dev)
+    b = gpu_util.run_case(case, ALGOS[algo], tensors=t, dev=dev)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+
+
+# ----------------------------------- accepted-prefix statistics at full size
+
+@pytest.mark.parametrize("T", [0.0, 0.7, 1.0])
+def test_config2_accept_length_statistics(dev, T):
+    """10^4 rounds of config 2 on the GPU.  The mean tokens per round must match
+    1 + sum_k prod_{i<k} alpha_i, the expected yield with the round's own
+    per-position overlaps (at T = 0 it is exact per round), and the histogram
+    must match the averaged per-round distribution."""
+    import torch
+    import scipy.stats
+    sv = _sv()
+    G, V, rounds, chunk = 7, 32128, 10000, 2000
+    gen = torch.Generator(device=dev).manual_seed(1234 + int(T * 10))
+    tokens_per_round, expected, pmf_sum = [], [], np.zeros(G + 1)
+    for _ in range(rounds // chunk):
+        tl = torch.randn(chunk, G + 1, V, device=dev, generator=gen) * 3.0
+        dl = 0.8 * tl[:, :G] + 0.5 * torch.randn(chunk, G, V, device=dev, generator=gen)
+        if T > 0:
+            g = -torch.log(-torch.log(torch.rand(chunk, G, V, device=dev, generator=gen).clamp_(1e-30, 1 - 1e-7)))
+            x = torch.argmax(dl / T + g, dim=-1).to(torch.int32)
+            del g
+        else:
+            x = torch.argmax(dl, dim=-1).to(torch.int32)
+        u = torch.rand(chunk, G + 1, device=dev, generator=gen).clamp_(2 ** -24, 1 - 2 ** -24)
+        out = sv.verify(tl, dl.contiguous(), x.contiguous(), u.contiguous(), T, algo=1)
+        n = out["n_accepted"].cpu().numpy().astype(np.int64)
+        a = out["alpha"].cpu().numpy().astype(np.float64)
+        run = np.cumprod(a, axis=1)                            # P(first k drafts kept), k = 1..G
+        expected.append(1.0 + run.sum(axis=1))
+        reach = np.concatenate([np.ones((chunk, 1)), run], axis=1)   # P(n >= k), k = 0..G
+        pmf_sum += (reach - np.concatenate([run, np.zeros((chunk, 1))], axis=1)).sum(axis=0)
+        tokens_per_round.append(n + 1)
+        del tl, dl
+    tok = np.concatenate(tokens_per_round)
+    exp_ = np.concatenate(expected)
+    if T == 0:
+        assert np.array_equal(tok, exp_.astype(np.int64))
+        return
+    se = tok.std() / np.sqrt(rounds)
+    _banner(f"cfg2 MC T={T}: mean tokens {tok.mean():.4f} vs expected {exp_.mean():.4f} (se {se:.4f})")
+    assert abs(tok.mean() - exp_.mean()) < 4 * se
+    counts = np.bincount(tok - 1, minlength=G + 1)
+    assert scipy.stats.chisquare(counts, pmf_sum * rounds / pmf_sum.sum()).pvalue > 1e-4
