@@ -24,8 +24,11 @@ LIB = os.path.join(PKG, "libspecverify.so")
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops.
+# -fno-honor-nans: logits are finite or -inf by contract and no kernel relies
+# on NaN propagation (the 0/0 ratio case is handled explicitly; sentinels are
+# compared as integers), so min/max need no NaN canonicalisation.
 COMMON_FLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fno-honor-nans",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
     "-I", INCLUDE, "-I", CSRC,

@@ -91,9 +91,12 @@ int spec_verify_algo(int algo, const void* target_logits, const void* draft_logi
   a.ws_bytes = workspace_bytes;
   hipStream_t s = static_cast<hipStream_t>(stream);
 
-  const bool fused_ok = specv::fused_supported(B, gamma, V, dtype);
-  if (algo == SPEC_ALGO_FUSED && !fused_ok) return SPEC_EUNSUPPORTED;
-  if (algo == SPEC_ALGO_FUSED || (algo == SPEC_ALGO_AUTO && fused_ok)) return map_hip(specv::fused_launch(a, s));
+  if (algo == SPEC_ALGO_FUSED) return map_hip(specv::fused_launch(a, s));
+  if (algo == SPEC_ALGO_AUTO && specv::fused_supported(B, gamma, V, dtype)) {
+    // the fused path declines unaligned rows and teams that cannot be resident
+    const hipError_t e = specv::fused_launch(a, s);
+    if (e != hipErrorNotSupported) return map_hip(e);
+  }
   return map_hip(specv::multipass_launch(a, s));
 }
 

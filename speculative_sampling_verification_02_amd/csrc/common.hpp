@@ -22,11 +22,16 @@ struct F32 {
   static constexpr int kVec = 4;  // elements per 16-byte load
   __device__ static inline float at(const storage* p, size_t j) { return p[j]; }
   // Unpack one 16-byte vector into kVec floats.
+  // The empty asm pins each value to a register: without it a run of these
+  // copies is merged into one memcpy out of the raw buffer, which then has to
+  // live in scratch memory instead of registers.
   __device__ static inline void unpack(const u32x4& v, float* out) {
-    out[0] = __uint_as_float(v.x);
-    out[1] = __uint_as_float(v.y);
-    out[2] = __uint_as_float(v.z);
-    out[3] = __uint_as_float(v.w);
+    uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      asm("" : "+v"(w[k]));
+      out[k] = __uint_as_float(w[k]);
+    }
   }
 };
 
@@ -52,26 +57,70 @@ __device__ inline u32x4 load_stream(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
+// Ordinary cached 16-byte load (for data read again shortly after).
+__device__ inline u32x4 load_cached(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ------------------------------------------------------------ wave reductions
+//
+// All-reduce across a wave64 with DPP lane moves inside each 16-lane row
+// (xor 1, xor 2, half-row mirror, row mirror), then the four row results
+// combined in row order through readlane.  Every step combines two values with
+// a commutative operation, so all lanes end with bit-identical results and the
+// order of operations is fixed: results are reproducible run to run.
+
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <-> 7 - i within each 8 lanes
+constexpr int kDppMirror = 0x140;      // lane i <-> 15 - i within each 16 lanes
+
+template <int CTRL>
+__device__ inline int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ inline float dpp_f(float v) {
+  return __int_as_float(dpp_i<CTRL>(__float_as_int(v)));
+}
+template <int CTRL>
+__device__ inline double dpp_d(double v) {
+  const long long b = __double_as_longlong(v);
+  const int lo = dpp_i<CTRL>((int)(b & 0xffffffffll)), hi = dpp_i<CTRL>((int)(b >> 32));
+  return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+}
+__device__ inline float lane_f(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+__device__ inline double lane_d(double v, int lane) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane((int)(b & 0xffffffffll), lane);
+  const int hi = __builtin_amdgcn_readlane((int)(b >> 32), lane);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+}
 
 __device__ inline float wave_max(float v) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+  v = fmaxf(v, dpp_f<kDppXor1>(v));
+  v = fmaxf(v, dpp_f<kDppXor2>(v));
+  v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp_f<kDppMirror>(v));
+  return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
 }
 
 __device__ inline float wave_sum(float v) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  v += dpp_f<kDppXor1>(v);
+  v += dpp_f<kDppXor2>(v);
+  v += dpp_f<kDppHalfMirror>(v);
+  v += dpp_f<kDppMirror>(v);
+  return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
 }
 
 __device__ inline double wave_sum(double v) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  v += dpp_d<kDppXor1>(v);
+  v += dpp_d<kDppXor2>(v);
+  v += dpp_d<kDppHalfMirror>(v);
+  v += dpp_d<kDppMirror>(v);
+  return (lane_d(v, 0) + lane_d(v, 16)) + (lane_d(v, 32) + lane_d(v, 48));
 }
 
 // (value, index) with "greater value wins, lower index breaks ties".
@@ -86,24 +135,61 @@ __device__ inline ArgMax argmax_better(ArgMax a, ArgMax b) {
   return a;
 }
 
-__device__ inline ArgMax wave_argmax(ArgMax a) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) {
-    ArgMax b{__shfl_xor(a.v, o, kWave), __shfl_xor(a.i, o, kWave)};
-    a = argmax_better(a, b);
-  }
-  return a;
+template <int CTRL>
+__device__ inline ArgMax dpp_argmax(ArgMax a) {
+  return argmax_better(a, ArgMax{dpp_f<CTRL>(a.v), dpp_i<CTRL>(a.i)});
 }
 
-// Inclusive scan across the wave in lane order.
+__device__ inline ArgMax wave_argmax(ArgMax a) {
+  a = dpp_argmax<kDppXor1>(a);
+  a = dpp_argmax<kDppXor2>(a);
+  a = dpp_argmax<kDppHalfMirror>(a);
+  a = dpp_argmax<kDppMirror>(a);
+  ArgMax r{lane_f(a.v, 0), __builtin_amdgcn_readlane(a.i, 0)};
+  r = argmax_better(r, ArgMax{lane_f(a.v, 16), __builtin_amdgcn_readlane(a.i, 16)});
+  r = argmax_better(r, ArgMax{lane_f(a.v, 32), __builtin_amdgcn_readlane(a.i, 32)});
+  r = argmax_better(r, ArgMax{lane_f(a.v, 48), __builtin_amdgcn_readlane(a.i, 48)});
+  return r;
+}
+
+// Inclusive scan across the wave in lane order: Kogge-Stone with DPP row
+// shifts inside each 16-lane row (lanes shifted in from outside the row read
+// 0), then the totals of the earlier rows, read with readlane, added in row
+// order.
+constexpr int kDppShr1 = 0x111, kDppShr2 = 0x112, kDppShr4 = 0x114, kDppShr8 = 0x118;
+
+template <int CTRL>
+__device__ inline float dpp_shr_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+template <int CTRL>
+__device__ inline double dpp_shr_d(double v) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(b & 0xffffffffll), CTRL, 0xF, 0xF, true);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(b >> 32), CTRL, 0xF, 0xF, true);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+}
+
 __device__ inline float wave_inclusive_scan(float v) {
   const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    float t = __shfl_up(v, o, kWave);
-    if (lane >= o) v += t;
-  }
-  return v;
+  v += dpp_shr_f<kDppShr1>(v);
+  v += dpp_shr_f<kDppShr2>(v);
+  v += dpp_shr_f<kDppShr4>(v);
+  v += dpp_shr_f<kDppShr8>(v);
+  const float t0 = lane_f(v, 15), t1 = lane_f(v, 31), t2 = lane_f(v, 47);
+  const float before = lane < 16 ? 0.f : lane < 32 ? t0 : lane < 48 ? t0 + t1 : (t0 + t1) + t2;
+  return lane < 16 ? v : before + v;
+}
+
+__device__ inline double wave_inclusive_scan(double v) {
+  const int lane = threadIdx.x & (kWave - 1);
+  v += dpp_shr_d<kDppShr1>(v);
+  v += dpp_shr_d<kDppShr2>(v);
+  v += dpp_shr_d<kDppShr4>(v);
+  v += dpp_shr_d<kDppShr8>(v);
+  const double t0 = lane_d(v, 15), t1 = lane_d(v, 31), t2 = lane_d(v, 47);
+  const double before = lane < 16 ? 0.0 : lane < 32 ? t0 : lane < 48 ? t0 + t1 : (t0 + t1) + t2;
+  return lane < 16 ? v : before + v;
 }
 
 // ------------------------------------------------------- workgroup reductions
@@ -134,6 +220,55 @@ __device__ inline float block_sum(float v, float* lds) {
   return r;
 }
 
+// Two independent reductions sharing one pair of barriers.  `lds` must hold
+// 2 * kMaxWaves entries.
+__device__ inline float2 block_max2(float a, float b, float* lds) {
+  const int wid = threadIdx.x / kWave, nw = blockDim.x / kWave;
+  a = wave_max(a);
+  b = wave_max(b);
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0) {
+    lds[wid] = a;
+    lds[kMaxWaves + wid] = b;
+  }
+  __syncthreads();
+  float ra = lds[0], rb = lds[kMaxWaves];
+  for (int w = 1; w < nw; ++w) {
+    ra = fmaxf(ra, lds[w]);
+    rb = fmaxf(rb, lds[kMaxWaves + w]);
+  }
+  return make_float2(ra, rb);
+}
+
+__device__ inline float2 block_sum2(float a, float b, float* lds) {
+  const int wid = threadIdx.x / kWave, nw = blockDim.x / kWave;
+  a = wave_sum(a);
+  b = wave_sum(b);
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0) {
+    lds[wid] = a;
+    lds[kMaxWaves + wid] = b;
+  }
+  __syncthreads();
+  float ra = lds[0], rb = lds[kMaxWaves];
+  for (int w = 1; w < nw; ++w) {
+    ra += lds[w];
+    rb += lds[kMaxWaves + w];
+  }
+  return make_float2(ra, rb);
+}
+
+__device__ inline double block_sum(double v, double* lds) {
+  const int wid = threadIdx.x / kWave, nw = blockDim.x / kWave;
+  v = wave_sum(v);
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0) lds[wid] = v;
+  __syncthreads();
+  double r = lds[0];
+  for (int w = 1; w < nw; ++w) r += lds[w];
+  return r;
+}
+
 __device__ inline ArgMax block_argmax(ArgMax a, float* ldsv, int* ldsi) {
   const int wid = threadIdx.x / kWave, nw = blockDim.x / kWave;
   a = wave_argmax(a);
@@ -156,7 +291,8 @@ __device__ inline float block_scan(float v, float* lds, float* excl, float* tota
   const int wid = threadIdx.x / kWave, nw = blockDim.x / kWave;
   const int lane = threadIdx.x & (kWave - 1);
   const float inc = wave_inclusive_scan(v);
-  float prev = __shfl_up(inc, 1, kWave);
+  // previous lane's inclusive value (DPP wave_shr:1; lane 0 reads 0)
+  float prev = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(inc), 0x138, 0xF, 0xF, true));
   if (lane == 0) prev = 0.f;
   __syncthreads();
   if (lane == kWave - 1) lds[wid] = inc;
@@ -168,6 +304,158 @@ __device__ inline float block_scan(float v, float* lds, float* excl, float* tota
   *total = all;
   *excl = (lane == 0) ? before : before + prev;
   return before + inc;
+}
+
+// ------------------------------------------------------ inverse-CDF search
+
+// Inverse-CDF search over a token range: the first token j in [lo, hi) whose
+// running weight (from 0 at lo) exceeds theta.  `weight(j, x)` gives the
+// weight of token j with logit x in row `r0` (and `x1` from row `r1` for the
+// residual).  If rounding leaves the whole chunk at or below theta, the last
+// token with positive weight is returned.  Called by the whole workgroup.
+template <class E, bool VEC, int kThreads, class W>
+__device__ int range_search(const typename E::storage* r0, const typename E::storage* r1, int lo,
+                            int hi, float theta, W&& weight, float* lds_f, int* lds_i) {
+  constexpr int kPer = VEC ? E::kVec : 1;
+  constexpr int step = kThreads * kPer;
+  __shared__ int found;
+  if (threadIdx.x == 0) found = -1;
+  int last_pos = -1;  // per thread: last index with positive weight seen
+  float carry = 0.f;
+  for (int base = lo; base < hi; base += step) {
+    const int j0 = base + threadIdx.x * kPer;
+    float w[kPer];
+    float s = 0.f;
+#pragma unroll
+    for (int t = 0; t < kPer; ++t) w[t] = 0.f;
+    if (j0 < hi) {
+      float x0[kPer], x1[kPer];
+      if constexpr (VEC) {
+        E::unpack(load_cached(r0 + j0), x0);
+        if (r1) E::unpack(load_cached(r1 + j0), x1);
+      } else {
+        x0[0] = E::at(r0, j0);
+        if (r1) x1[0] = E::at(r1, j0);
+      }
+#pragma unroll
+      for (int t = 0; t < kPer; ++t) {
+        w[t] = weight(x0[t], r1 ? x1[t] : 0.f);
+        if (w[t] > 0.f) last_pos = j0 + t;
+        s += w[t];
+      }
+    }
+    float excl, total;
+    const float incl = block_scan(s, lds_f, &excl, &total);
+    const float start = carry + excl, end = carry + incl;
+    if (start <= theta && theta < end) {
+      float run = start;
+      int pick = -1, lastp = -1;
+#pragma unroll
+      for (int t = 0; t < kPer; ++t) {
+        if (w[t] > 0.f) lastp = j0 + t;
+        run += w[t];
+        if (pick < 0 && run > theta) pick = j0 + t;
+      }
+      found = pick >= 0 ? pick : lastp;  // exactly one thread owns theta
+    }
+    carry += total;
+    __syncthreads();
+    if (found >= 0) break;
+  }
+  const int f = found;
+  __syncthreads();
+  if (f >= 0) return f;
+  // rounding guard: the last positive-weight token of the chunk
+  // (callers keep hi - lo below 2^24, so offsets compare exactly as floats)
+  ArgMax lp{last_pos >= 0 ? (float)(last_pos - lo) : -1.f, last_pos};
+  lp = block_argmax(lp, lds_f, lds_i);
+  return lp.i;
+}
+
+// Inverse-CDF search over one tile of kThreads * PER tokens starting at
+// tile_lo (16-byte aligned rows, V a multiple of kVec).  Thread t owns the PER
+// consecutive tokens from tile_lo + t * PER.  All loads are issued before the
+// scan, and one workgroup scan over the thread sums locates the owner of
+// theta, so the search costs one memory round trip and one scan.  Returns the
+// first token whose running weight (from 0 at tile_lo, in token order)
+// exceeds theta.  If rounding leaves the whole tile at or below theta, the last
+// token with positive weight is returned.  Called by the whole workgroup
+// (blockDim.x == kThreads).
+template <class E, int PER, int kThreads, class W>
+__device__ int tile_search(const typename E::storage* r0, const typename E::storage* r1, int tile_lo, int V,
+                           float theta, W&& weight, float* lds_f, int* lds_i) {
+  constexpr int NS = PER / E::kVec;
+  __shared__ int found;
+  const int base = tile_lo + (int)threadIdx.x * PER;
+  u32x4 raw0[NS], raw1[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int j0 = base + s * E::kVec;
+    raw0[s] = j0 < V ? load_cached(r0 + j0) : u32x4{0u, 0u, 0u, 0u};
+    raw1[s] = (r1 && j0 < V) ? load_cached(r1 + j0) : u32x4{0u, 0u, 0u, 0u};
+  }
+  if (threadIdx.x == 0) found = -1;
+  float w[PER];
+  float sum = 0.f;
+  int last_pos = -1;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int j0 = base + s * E::kVec;
+    float x0[E::kVec], x1[E::kVec];
+    E::unpack(raw0[s], x0);
+    E::unpack(raw1[s], x1);
+#pragma unroll
+    for (int v = 0; v < E::kVec; ++v) {
+      const float wv = j0 < V ? weight(x0[v], x1[v]) : 0.f;
+      w[s * E::kVec + v] = wv;
+      if (wv > 0.f) last_pos = j0 + v;
+      sum += wv;
+    }
+  }
+  float excl, total;
+  const float incl = block_scan(sum, lds_f, &excl, &total);
+  if (excl <= theta && theta < incl) {  // exactly one thread owns theta
+    float run = excl;
+    int pick = -1, lastp = -1;
+#pragma unroll
+    for (int v = 0; v < PER; ++v) {
+      if (w[v] > 0.f) lastp = base + v;
+      run += w[v];
+      if (pick < 0 && run > theta) pick = base + v;
+    }
+    found = pick >= 0 ? pick : lastp;
+  }
+  __syncthreads();
+  const int f = found;
+  __syncthreads();
+  if (f >= 0) return f;
+  // rounding guard: the last positive-weight token of the tile (offsets inside
+  // the tile are small, so they compare exactly as floats)
+  ArgMax lp{last_pos >= 0 ? (float)(last_pos - tile_lo) : -1.f, last_pos};
+  lp = block_argmax(lp, lds_f, lds_i);
+  return lp.i;
+}
+
+// Row normaliser from nch chunk partials (max m_c, sum S_c relative to m_c),
+// computed by one wave in a fixed order: M = max m_c and
+// S = sum_c S_c exp2((m_c - M) k) accumulated in fp64.  Call from all 64
+// lanes of one wave; every lane gets the result.
+struct WaveNorm {
+  float M;
+  double S;
+};
+
+__device__ inline WaveNorm wave_row_norm(const float2* st, int nch, float k) {
+  const int lane = threadIdx.x & (kWave - 1);
+  float M = -INFINITY;
+  for (int c = lane; c < nch; c += kWave) M = fmaxf(M, st[c].x);
+  M = wave_max(M);
+  double S = 0.0;
+  for (int c = lane; c < nch; c += kWave) {
+    const float2 v = st[c];
+    if (v.x != -INFINITY) S += (double)v.y * (double)fast_exp2((v.x - M) * k);
+  }
+  return WaveNorm{M, wave_sum(S)};
 }
 
 }  // namespace specv

@@ -3,16 +3,21 @@
 // Three launches on one stream:
 //   K1 row_stats     per (row, chunk of kChunk tokens): the chunk maximum m_c and
 //                    S_c = sum exp2((l - m_c) k), or the chunk argmax at T = 0.
-//   K2 pair_overlap  per (draft position, chunk): the two rows' global
-//                    normalisers from K1's partials, then the chunk's share of
-//                    alpha = sum min(p, q) and of the residual mass sum max(0, p - q).
-//   K3 finish        per sequence: ratio tests, accepted prefix, alpha totals,
-//                    then the inverse-CDF sample.  It locates the chunk that
-//                    holds the sample from the chunk masses and scans only that chunk.
+//                    The chunk is read once into registers.
+//   K2 pair_overlap  per (draft position, chunk): the two rows' normalisers from
+//                    K1's partials (one wave, fixed order), then the chunk's
+//                    share of alpha = sum min(p, q) and of the residual mass
+//                    sum max(0, p - q).
+//   K3 finish        per sequence: fp64 ratio tests, accepted prefix, alpha
+//                    totals, then the inverse-CDF sample.  It locates the chunk
+//                    holding the sample from the chunk masses and scans only that chunk.
+// K2 and K3 combine a row's partials with the same function, so they see
+// bit-identical normalisers.
 //
-// Each logit is read by K1 and again by K2 (the overlap needs both rows'
-// normalisers before any element can be compared), and one chunk per sequence
-// is read by K3.  The fused path reads every logit once.
+// Each logit is read by K1 and again by K2, because the overlap needs both
+// rows' normalisers before any element can be compared.  K3 reads one chunk
+// per sequence.  The fused path reads every logit once.  This path accepts any
+// row alignment and any V.
 //
 // Page abbreviations: [FI] intuitivepapers.ai "Fast Inference from Transformers
 // via Speculative Decoding"; [SD] nonconvexcard "Speculative Decoding".
@@ -31,7 +36,7 @@ constexpr int kChunk = 8192;  // tokens per chunk; a multiple of 256 * 8
 
 __host__ __device__ inline int num_chunks(int V) { return (V + kChunk - 1) / kChunk; }
 
-// Row numbering shared by K1..K3: target rows first, then draft rows.
+// Row numbering shared by every kernel here: target rows first, then draft rows.
 __device__ inline size_t target_row(int b, int i, int gamma) { return (size_t)b * (gamma + 1) + i; }
 __device__ inline size_t draft_row(int b, int i, int gamma, int B) {
   return (size_t)B * (gamma + 1) + (size_t)b * gamma + i;
@@ -44,26 +49,49 @@ __device__ inline const typename E::storage* row_ptr(const VerifyArgs& a, size_t
   return static_cast<const typename E::storage*>(a.draft) + (row - nt) * (size_t)a.V;
 }
 
-// Visit the elements [lo, hi) of a row owned by this thread, in a fixed order:
-// vector steps of kThreads * kVec tokens, thread t taking the t-th vector.
-// `VEC` requires a 16-byte aligned row base and V a multiple of kVec.
-template <class E, bool VEC, class F>
-__device__ inline void for_chunk(const typename E::storage* row, int lo, int hi, F&& f) {
-  if constexpr (VEC) {
-    constexpr int step = kThreads * E::kVec;
-    for (int base = lo; base < hi; base += step) {
-      const int j0 = base + threadIdx.x * E::kVec;
-      if (j0 < hi) {
-        float x[E::kVec];
-        E::unpack(load_stream(row + j0), x);
-#pragma unroll
-        for (int k = 0; k < E::kVec; ++k) f(j0 + k, x[k]);
-      }
-    }
-  } else {
-    for (int j = lo + threadIdx.x; j < hi; j += kThreads) f(j, E::at(row, j));
+// A row's normaliser: maximum, 1/S in fp32 and S in fp64.
+struct RowNorm {
+  float M;
+  float invS;
+  double S;
+};
+
+// This thread's kPer tokens of a chunk in registers, visited in a fixed order:
+// vector steps of kThreads * kVec tokens, thread t taking the t-th vector of
+// each step.  Needs a 16-byte aligned row base and V a multiple of kVec.
+// Tokens at or past `hi` read as -inf.
+template <class E>
+struct ChunkRegs {
+  static constexpr int kPer = kChunk / kThreads;
+  static constexpr int NS = kPer / E::kVec;
+  float x[kPer];
+  __device__ inline int token(int lo, int t) const {
+    return lo + ((t / E::kVec) * kThreads + (int)threadIdx.x) * E::kVec + t % E::kVec;
   }
-}
+  u32x4 raw[NS];
+  // Issue the chunk's loads without waiting for them.
+  __device__ inline void issue(const typename E::storage* row, int lo, int hi) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int j0 = lo + (s * kThreads + (int)threadIdx.x) * E::kVec;
+      raw[s] = j0 < hi ? load_stream(row + j0) : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  __device__ inline void unpack(int lo, int hi) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int j0 = lo + (s * kThreads + (int)threadIdx.x) * E::kVec;
+      float t[E::kVec];
+      E::unpack(raw[s], t);
+#pragma unroll
+      for (int v = 0; v < E::kVec; ++v) x[s * E::kVec + v] = j0 < hi ? t[v] : -INFINITY;
+    }
+  }
+  __device__ inline void load(const typename E::storage* row, int lo, int hi) {
+    issue(row, lo, hi);
+    unpack(lo, hi);
+  }
+};
 
 // ------------------------------------------------------------------ K1
 
@@ -77,196 +105,155 @@ __global__ __launch_bounds__(kThreads) void row_stats_kernel(VerifyArgs a, float
   const int lo = c * kChunk, hi = min(a.V, lo + kChunk);
   const auto* r = row_ptr<E>(a, row);
 
-  if constexpr (ARGMAX) {
-    ArgMax best{-INFINITY, 0x7fffffff};
-    for_chunk<E, VEC>(r, lo, hi, [&](int j, float x) { best = argmax_better(best, ArgMax{x, j}); });
-    best = block_argmax(best, lds_f, lds_i);
-    if (threadIdx.x == 0) stats[blockIdx.x] = make_float2(best.v, __int_as_float(best.i));
-  } else {
-    float m = -INFINITY;
-    for_chunk<E, VEC>(r, lo, hi, [&](int, float x) { m = fmaxf(m, x); });
-    m = block_max(m, lds_f);
-    float s = 0.f;
-    if (m != -INFINITY) {
-      const float k = a.k;
-      for_chunk<E, VEC>(r, lo, hi, [&](int, float x) { s += fast_exp2((x - m) * k); });
+  if constexpr (VEC) {
+    ChunkRegs<E> ch;
+    ch.load(r, lo, hi);
+    if constexpr (ARGMAX) {
+      ArgMax best{-INFINITY, 0x7fffffff};
+#pragma unroll
+      for (int t = 0; t < ChunkRegs<E>::kPer; ++t) best = argmax_better(best, ArgMax{ch.x[t], ch.token(lo, t)});
+      best = block_argmax(best, lds_f, lds_i);
+      if (threadIdx.x == 0) stats[blockIdx.x] = make_float2(best.v, __int_as_float(best.i));
+    } else {
+      // four independent chains keep the dependency chains short
+      float m0 = -INFINITY, m1 = -INFINITY, m2 = -INFINITY, m3 = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < ChunkRegs<E>::kPer; t += 4) {
+        m0 = fmaxf(m0, ch.x[t]);
+        m1 = fmaxf(m1, ch.x[t + 1]);
+        m2 = fmaxf(m2, ch.x[t + 2]);
+        m3 = fmaxf(m3, ch.x[t + 3]);
+      }
+      const float M = block_max(fmaxf(fmaxf(m0, m1), fmaxf(m2, m3)), lds_f);
+      float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int t = 0; t < ChunkRegs<E>::kPer; t += 4) {
+          s0 += fast_exp2((ch.x[t] - M) * a.k);
+          s1 += fast_exp2((ch.x[t + 1] - M) * a.k);
+          s2 += fast_exp2((ch.x[t + 2] - M) * a.k);
+          s3 += fast_exp2((ch.x[t + 3] - M) * a.k);
+        }
+      }
+      const float s = block_sum((s0 + s1) + (s2 + s3), lds_f);
+      if (threadIdx.x == 0) stats[blockIdx.x] = make_float2(M, s);
     }
-    s = block_sum(s, lds_f);
-    if (threadIdx.x == 0) stats[blockIdx.x] = make_float2(m, s);
+  } else {
+    // unaligned rows: scalar loads, two sweeps over the chunk (the second hits cache)
+    if constexpr (ARGMAX) {
+      ArgMax best{-INFINITY, 0x7fffffff};
+      for (int j = lo + threadIdx.x; j < hi; j += kThreads) best = argmax_better(best, ArgMax{E::at(r, j), j});
+      best = block_argmax(best, lds_f, lds_i);
+      if (threadIdx.x == 0) stats[blockIdx.x] = make_float2(best.v, __int_as_float(best.i));
+    } else {
+      float m = -INFINITY;
+      for (int j = lo + threadIdx.x; j < hi; j += kThreads) m = fmaxf(m, E::at(r, j));
+      const float M = block_max(m, lds_f);
+      float s = 0.f;
+      if (M != -INFINITY)
+        for (int j = lo + threadIdx.x; j < hi; j += kThreads) s += fast_exp2((E::at(r, j) - M) * a.k);
+      s = block_sum(s, lds_f);
+      if (threadIdx.x == 0) stats[blockIdx.x] = make_float2(M, s);
+    }
   }
 }
 
-// Global normaliser of one row from its chunk partials, always in chunk order
-// so that every kernel that calls it gets bit-identical values.
-struct RowNorm {
-  float M;      // row maximum
-  float invS;   // 1 / sum exp2((l - M) k), rounded to fp32
-  double S;     // the sum, fp64
-};
-
-__device__ inline double chunk_weight(float2 st, float M, float k) {
-  // S_c rescaled from the chunk maximum to the row maximum.
-  if (st.x == -INFINITY) return 0.0;
-  return (double)st.y * exp2(((double)st.x - (double)M) * (double)k);
-}
-
-__device__ inline RowNorm combine_row(const float2* st, int nch, float k) {
-  float M = -INFINITY;
-  for (int c = 0; c < nch; ++c) M = fmaxf(M, st[c].x);
-  double S = 0.0;
-  for (int c = 0; c < nch; ++c) S += chunk_weight(st[c], M, k);
-  return RowNorm{M, (float)(1.0 / S), S};
-}
-
-__device__ inline ArgMax combine_argmax(const float2* st, int nch) {
-  ArgMax best{-INFINITY, 0x7fffffff};
-  for (int c = 0; c < nch; ++c) best = argmax_better(best, ArgMax{st[c].x, __float_as_int(st[c].y)});
-  return best;
+// Row normaliser from the row's K1 partials, computed by one wave.
+__device__ inline RowNorm row_norm(const float2* stats, size_t row, int nch, float k) {
+  const WaveNorm w = wave_row_norm(stats + row * nch, nch, k);
+  return RowNorm{w.M, (float)(1.0 / w.S), w.S};
 }
 
 // p_j and q_j in fp32 from a logit and its row normaliser.  K2 and K3 use this
 // one expression so the residual weights they see are bit-identical.
-__device__ inline float prob(float x, float M, float invS, float k) {
-  return fast_exp2((x - M) * k) * invS;
-}
+__device__ inline float prob(float x, float M, float invS, float k) { return fast_exp2((x - M) * k) * invS; }
 
 // ------------------------------------------------------------------ K2
 
 template <class E, bool VEC>
 __global__ __launch_bounds__(kThreads) void pair_overlap_kernel(VerifyArgs a, const float2* stats,
                                                                 float2* pair_stats) {
-  __shared__ float lds_f[kMaxWaves];
-  __shared__ float norm[4];
+  __shared__ float lds_f[2 * kMaxWaves];
+  __shared__ RowNorm norm_s[2];
   const int nch = num_chunks(a.V);
   const int pair = blockIdx.x / nch;  // b * gamma + i
   const int c = blockIdx.x % nch;
   const int b = pair / a.gamma, i = pair % a.gamma;
   const size_t rp = target_row(b, i, a.gamma), rq = draft_row(b, i, a.gamma, a.B);
-  if (threadIdx.x == 0) {
-    RowNorm np = combine_row(stats + rp * nch, nch, a.k);
-    RowNorm nq = combine_row(stats + rq * nch, nch, a.k);
-    norm[0] = np.M; norm[1] = np.invS; norm[2] = nq.M; norm[3] = nq.invS;
-  }
-  __syncthreads();
-  const float Mp = norm[0], invSp = norm[1], Mq = norm[2], invSq = norm[3], k = a.k;
+  const float k = a.k;
   const int lo = c * kChunk, hi = min(a.V, lo + kChunk);
   const auto* p_row = row_ptr<E>(a, rp);
   const auto* q_row = row_ptr<E>(a, rq);
+  ChunkRegs<E> cp, cq;
+  if constexpr (VEC) {
+    cp.issue(p_row, lo, hi);  // in flight while the normalisers are combined
+    cq.issue(q_row, lo, hi);
+  }
+  const int wid = threadIdx.x / kWave;
+  if (wid < 2) {
+    const RowNorm n = row_norm(stats, wid == 0 ? rp : rq, nch, k);
+    if ((threadIdx.x & (kWave - 1)) == 0) norm_s[wid] = n;
+  }
+  __syncthreads();
+  const RowNorm np = norm_s[0], nq = norm_s[1];
 
   float acc_min = 0.f, acc_res = 0.f;
   if constexpr (VEC) {
-    constexpr int step = kThreads * E::kVec;
-    for (int base = lo; base < hi; base += step) {
-      const int j0 = base + threadIdx.x * E::kVec;
-      if (j0 < hi) {
-        float xp[E::kVec], xq[E::kVec];
-        E::unpack(load_stream(p_row + j0), xp);
-        E::unpack(load_stream(q_row + j0), xq);
+    cp.unpack(lo, hi);
+    cq.unpack(lo, hi);
+    float mn[2] = {0.f, 0.f}, rs[2] = {0.f, 0.f};
 #pragma unroll
-        for (int t = 0; t < E::kVec; ++t) {
-          const float p = prob(xp[t], Mp, invSp, k), q = prob(xq[t], Mq, invSq, k);
-          acc_min += fminf(p, q);
-          acc_res += fmaxf(p - q, 0.f);
-        }
-      }
+    for (int t = 0; t < ChunkRegs<E>::kPer; ++t) {
+      const float p = prob(cp.x[t], np.M, np.invS, k), q = prob(cq.x[t], nq.M, nq.invS, k);
+      mn[t & 1] += fminf(p, q);
+      rs[t & 1] += fmaxf(p - q, 0.f);
     }
+    acc_min = mn[0] + mn[1];
+    acc_res = rs[0] + rs[1];
   } else {
     for (int j = lo + threadIdx.x; j < hi; j += kThreads) {
-      const float p = prob(E::at(p_row, j), Mp, invSp, k), q = prob(E::at(q_row, j), Mq, invSq, k);
+      const float p = prob(E::at(p_row, j), np.M, np.invS, k), q = prob(E::at(q_row, j), nq.M, nq.invS, k);
       acc_min += fminf(p, q);
       acc_res += fmaxf(p - q, 0.f);
     }
   }
-  acc_min = block_sum(acc_min, lds_f);
-  acc_res = block_sum(acc_res, lds_f);
-  if (threadIdx.x == 0) pair_stats[blockIdx.x] = make_float2(acc_min, acc_res);
+  const float2 r = block_sum2(acc_min, acc_res, lds_f);
+  if (threadIdx.x == 0) pair_stats[blockIdx.x] = r;
 }
 
 // ------------------------------------------------------------------ K3
-
-// Inverse-CDF search inside one chunk: the first token j in [lo, hi) whose
-// running weight (from 0 at lo) exceeds theta.  `weight(j, x)` gives the
-// weight of token j with logit x in row `r0` (and `x1` from row `r1` for the
-// residual).  If rounding leaves the whole chunk at or below theta, the last
-// token with positive weight is returned.  Called by the whole workgroup.
-template <class E, bool VEC, class W>
-__device__ int chunk_search(const typename E::storage* r0, const typename E::storage* r1, int lo,
-                            int hi, float theta, W&& weight, float* lds_f, int* lds_i) {
-  constexpr int kPer = VEC ? E::kVec : 1;
-  constexpr int step = kThreads * kPer;
-  __shared__ int found;
-  if (threadIdx.x == 0) found = -1;
-  int last_pos = -1;  // per thread: last index with positive weight seen
-  float carry = 0.f;
-  for (int base = lo; base < hi; base += step) {
-    const int j0 = base + threadIdx.x * kPer;
-    float w[kPer];
-    float s = 0.f;
-#pragma unroll
-    for (int t = 0; t < kPer; ++t) w[t] = 0.f;
-    if (j0 < hi) {
-      float x0[kPer], x1[kPer];
-      if constexpr (VEC) {
-        E::unpack(load_stream(r0 + j0), x0);
-        if (r1) E::unpack(load_stream(r1 + j0), x1);
-      } else {
-        x0[0] = E::at(r0, j0);
-        if (r1) x1[0] = E::at(r1, j0);
-      }
-#pragma unroll
-      for (int t = 0; t < kPer; ++t) {
-        w[t] = weight(x0[t], r1 ? x1[t] : 0.f);
-        if (w[t] > 0.f) last_pos = j0 + t;
-        s += w[t];
-      }
-    }
-    float excl, total;
-    const float incl = block_scan(s, lds_f, &excl, &total);
-    const float start = carry + excl, end = carry + incl;
-    if (start <= theta && theta < end) {
-      float run = start;
-      int pick = -1, lastp = -1;
-#pragma unroll
-      for (int t = 0; t < kPer; ++t) {
-        if (w[t] > 0.f) lastp = j0 + t;
-        run += w[t];
-        if (pick < 0 && run > theta) pick = j0 + t;
-      }
-      found = pick >= 0 ? pick : lastp;  // exactly one thread owns theta
-    }
-    carry += total;
-    __syncthreads();
-    if (found >= 0) break;
-  }
-  const int f = found;
-  __syncthreads();
-  if (f >= 0) return f;
-  // rounding guard: the last positive-weight token of the chunk
-  // (offsets inside a chunk are < kChunk, so they compare exactly as floats)
-  ArgMax lp{last_pos >= 0 ? (float)(last_pos - lo) : -1.f, last_pos};
-  lp = block_argmax(lp, lds_f, lds_i);
-  return lp.i;
-}
 
 template <class E, bool VEC>
 __global__ __launch_bounds__(kThreads) void finish_kernel(VerifyArgs a, const float2* stats,
                                                           const float2* pair_stats) {
   __shared__ float lds_f[kMaxWaves];
   __shared__ int lds_i[kMaxWaves];
+  __shared__ double lds_d[kMaxWaves];
   __shared__ int accept_s[SPEC_MAX_GAMMA];
-  __shared__ int n_s;
-  __shared__ int row_s, chunk_s, residual_s;
-  __shared__ float theta_s, norm_s[4];
+  __shared__ float mass_s[kThreads];
+  __shared__ double prefix_s;
+  __shared__ int n_s, chunk_s;
+  __shared__ float theta_s;
   const int b = blockIdx.x, G = a.gamma, nch = num_chunks(a.V);
   const float k = a.k;
   const int tid = threadIdx.x;
   const float* u = a.uniforms + (size_t)b * (G + 1);
 
   if (a.temperature == 0.f) {
-    // ---- argmax mode
+    // ---- argmax mode: combine each row's chunk argmaxes
     __shared__ int amax_t[SPEC_MAX_GAMMA + 1], amax_d[SPEC_MAX_GAMMA];
-    if (tid <= G) amax_t[tid] = combine_argmax(stats + target_row(b, tid, G) * nch, nch).i;
-    if (tid < G) amax_d[tid] = combine_argmax(stats + draft_row(b, tid, G, a.B) * nch, nch).i;
+    if (tid <= G) {
+      const float2* st = stats + target_row(b, tid, G) * nch;
+      ArgMax best{-INFINITY, 0x7fffffff};
+      for (int c = 0; c < nch; ++c) best = argmax_better(best, ArgMax{st[c].x, __float_as_int(st[c].y)});
+      amax_t[tid] = best.i;
+    }
+    if (tid < G) {
+      const float2* st = stats + draft_row(b, tid, G, a.B) * nch;
+      ArgMax best{-INFINITY, 0x7fffffff};
+      for (int c = 0; c < nch; ++c) best = argmax_better(best, ArgMax{st[c].x, __float_as_int(st[c].y)});
+      amax_d[tid] = best.i;
+    }
     __syncthreads();
     if (tid < G) {
       const int x = a.tokens[(size_t)b * G + tid];
@@ -286,100 +273,124 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(VerifyArgs a, const fl
     return;
   }
 
-  // ---- ratio tests ([FI] Algorithm 1 step 3; [SD] "The algorithm"), in fp64
-  if (tid < G) {
-    const size_t rp = target_row(b, tid, G), rq = draft_row(b, tid, G, a.B);
-    const RowNorm np = combine_row(stats + rp * nch, nch, k);
-    const RowNorm nq = combine_row(stats + rq * nch, nch, k);
-    const int x = a.tokens[(size_t)b * G + tid];
-    double px = 0.0, qx = 0.0;
-    if (x >= 0 && x < a.V) {
-      const double lp = (double)E::at(row_ptr<E>(a, rp), x);
-      const double lq = (double)E::at(row_ptr<E>(a, rq), x);
-      px = exp2((lp - (double)np.M) * (double)k) / np.S;
-      qx = exp2((lq - (double)nq.M) * (double)k) / nq.S;
-    }
-    const double ratio = px / qx;  // IEEE: p/0 = inf (accept), 0/0 = NaN (reject)
-    const double uu = (double)u[tid];
-    accept_s[tid] = (ratio >= 1.0) || (uu <= ratio);
-    const size_t o = (size_t)b * G + tid;
-    if (a.p_draft) a.p_draft[o] = (float)px;
-    if (a.q_draft) a.q_draft[o] = (float)qx;
-    if (a.alpha) {
-      double al = 0.0;
-      const float2* ps = pair_stats + ((size_t)b * G + tid) * nch;
-      for (int c = 0; c < nch; ++c) al += (double)ps[c].x;
-      a.alpha[o] = (float)al;
+  // ---- ratio tests ([FI] Algorithm 1 step 3; [SD] "The algorithm"), in fp64.
+  // Wave w handles draft positions w, w + 4, ...; lane 0 does the test.
+  const int wid = tid / kWave, lane = tid & (kWave - 1), nw = kThreads / kWave;
+  for (int i = wid; i < G; i += nw) {
+    const size_t rp = target_row(b, i, G), rq = draft_row(b, i, G, a.B);
+    const RowNorm np = row_norm(stats, rp, nch, k), nq = row_norm(stats, rq, nch, k);
+    const size_t o = (size_t)b * G + i;
+    double al = 0.0;
+    for (int c = lane; c < nch; c += kWave) al += (double)pair_stats[o * nch + c].x;
+    al = wave_sum(al);
+    if (lane == 0) {
+      const int x = a.tokens[o];
+      double px = 0.0, qx = 0.0;
+      if (x >= 0 && x < a.V) {
+        px = exp2(((double)E::at(row_ptr<E>(a, rp), x) - (double)np.M) * (double)k) / np.S;
+        qx = exp2(((double)E::at(row_ptr<E>(a, rq), x) - (double)nq.M) * (double)k) / nq.S;
+      }
+      // q(x) = 0 keeps the draft when p(x) > 0 (ratio +inf) and rejects it
+      // when p(x) = 0 (0/0)
+      if (qx > 0.0) {
+        const double ratio = px / qx;
+        accept_s[i] = (ratio >= 1.0) || ((double)u[i] <= ratio);
+      } else {
+        accept_s[i] = px > 0.0;
+      }
+      if (a.p_draft) a.p_draft[o] = (float)px;
+      if (a.q_draft) a.q_draft[o] = (float)qx;
+      if (a.alpha) a.alpha[o] = (float)al;
     }
   }
   __syncthreads();
-
-  // ---- accepted prefix and the row to sample from
   if (tid == 0) {
     int n = 0;
     while (n < G && accept_s[n]) ++n;
     n_s = n;
-    const double uf = (double)u[G];
-    int residual = 0, chunk = nch - 1;
-    double theta = 0.0;
-    if (n < G) {
-      // residual max(0, p_n - q_n) ([FI] eq. (2); [SD] "Exactness")
-      const float2* ps = pair_stats + ((size_t)b * G + n) * nch;
-      double Sw = 0.0;
-      for (int c = 0; c < nch; ++c) Sw += (double)ps[c].y;
-      if (Sw > 0.0) {
-        residual = 1;
-        theta = uf * Sw;
-        double P = 0.0;
-        for (int c = 0; c < nch; ++c) {
-          const double w = (double)ps[c].y;
-          if (w > 0.0) chunk = c;
-          if (P + w > theta && w > 0.0) { chunk = c; break; }
-          P += w;
+  }
+  __syncthreads();
+  const int n = n_s;
+
+  // ---- the sampled row's chunk masses, in chunk order: the residual
+  // max(0, p_n - q_n) ([FI] eq. (2); [SD] "Exactness") when a draft was
+  // rejected, else p_gamma (the bonus token).  A residual with no mass
+  // (impossible in exact arithmetic after a rejection) falls back to p_n.
+  const float2* res_st = n < G ? pair_stats + ((size_t)b * G + n) * nch : nullptr;
+  const float2* row_st = stats + target_row(b, n, G) * nch;
+  __shared__ RowNorm norm_s[2];
+  if (wid < 2 && (wid == 0 || n < G)) {
+    const RowNorm nr = row_norm(stats, wid == 0 ? target_row(b, n, G) : draft_row(b, n, G, a.B), nch, k);
+    if (lane == 0) norm_s[wid] = nr;
+  }
+  __syncthreads();
+  const RowNorm np = norm_s[0];
+  double part = 0.0;
+  if (res_st)
+    for (int c = tid; c < nch; c += kThreads) part += (double)res_st[c].y;
+  const bool residual = res_st && block_sum(part, lds_d) > 0.0;
+  // chunk c's mass: R_c for the residual, S_c rescaled to the row maximum for p_n
+  auto mass = [&](int c) -> float {
+    if (residual) return res_st[c].y;
+    const float2 v = row_st[c];
+    return v.x == -INFINITY ? 0.f : v.y * fast_exp2((v.x - np.M) * k);
+  };
+  part = 0.0;
+  for (int c = tid; c < nch; c += kThreads) part += (double)mass(c);
+  const double theta = (double)u[G] * block_sum(part, lds_d);
+
+  // ---- locate the chunk holding theta: stage up to kThreads masses in LDS
+  // with one parallel load, then scan them in order on one thread.
+  if (tid == 0) {
+    prefix_s = 0.0;
+    chunk_s = -1;
+  }
+  int last = 0;
+  for (int base = 0; base < nch; base += kThreads) {
+    const int c = base + tid;
+    mass_s[tid] = c < nch ? mass(c) : 0.f;
+    __syncthreads();
+    if (tid == 0 && chunk_s < 0) {
+      double P = prefix_s;
+      for (int j = 0; j < kThreads && base + j < nch; ++j) {
+        const double w = (double)mass_s[j];
+        if (w > 0.0) {
+          last = base + j;
+          if (P + w > theta) {
+            chunk_s = base + j;
+            break;
+          }
         }
-        theta_s = (float)(theta - P);
-        const RowNorm np = combine_row(stats + target_row(b, n, G) * nch, nch, k);
-        const RowNorm nq = combine_row(stats + draft_row(b, n, G, a.B) * nch, nch, k);
-        norm_s[0] = np.M; norm_s[1] = np.invS; norm_s[2] = nq.M; norm_s[3] = nq.invS;
-      }
-    }
-    if (!residual) {
-      // bonus token from p_gamma, or p_n if the residual carried no mass
-      const float2* st = stats + target_row(b, n, G) * nch;
-      const RowNorm np = combine_row(st, nch, k);
-      theta = uf * np.S;
-      double P = 0.0;
-      for (int c = 0; c < nch; ++c) {
-        const double w = chunk_weight(st[c], np.M, k);
-        if (w > 0.0) chunk = c;
-        if (P + w > theta && w > 0.0) { chunk = c; break; }
         P += w;
       }
-      theta_s = (float)(theta - P);
-      norm_s[0] = np.M;
+      prefix_s = P;
     }
-    residual_s = residual;
-    chunk_s = chunk;
-    row_s = n;
+    __syncthreads();
+    if (chunk_s >= 0) break;
+  }
+  if (tid == 0) {
+    if (chunk_s < 0) chunk_s = last;  // rounding guard: theta past every chunk
+    theta_s = (float)(theta - prefix_s);
   }
   __syncthreads();
 
-  const int n = row_s, c = chunk_s;
-  const int lo = c * kChunk, hi = min(a.V, lo + kChunk);
-  const float theta = theta_s;
+  const int c = chunk_s, lo = c * kChunk, hi = min(a.V, lo + kChunk);
+  const auto* p_row = row_ptr<E>(a, target_row(b, n, G));
   int t;
-  if (residual_s) {
-    const float Mp = norm_s[0], invSp = norm_s[1], Mq = norm_s[2], invSq = norm_s[3];
-    t = chunk_search<E, VEC>(row_ptr<E>(a, target_row(b, n, G)), row_ptr<E>(a, draft_row(b, n, G, a.B)),
-                             lo, hi, theta,
-                             [&](float xp, float xq) {
-                               return fmaxf(prob(xp, Mp, invSp, k) - prob(xq, Mq, invSq, k), 0.f);
-                             },
-                             lds_f, lds_i);
+  if (residual) {
+    const RowNorm nq = norm_s[1];
+    const auto* q_row = row_ptr<E>(a, draft_row(b, n, G, a.B));
+    auto w = [&](float xp, float xq) { return fmaxf(prob(xp, np.M, np.invS, k) - prob(xq, nq.M, nq.invS, k), 0.f); };
+    if constexpr (VEC)
+      t = tile_search<E, kChunk / kThreads, kThreads>(p_row, q_row, lo, a.V, theta_s, w, lds_f, lds_i);
+    else
+      t = range_search<E, false, kThreads>(p_row, q_row, lo, hi, theta_s, w, lds_f, lds_i);
   } else {
-    const float M = norm_s[0];
-    t = chunk_search<E, VEC>(row_ptr<E>(a, target_row(b, n, G)), nullptr, lo, hi, theta,
-                             [&](float xp, float) { return fast_exp2((xp - M) * k); }, lds_f, lds_i);
+    auto w = [&](float xp, float) { return fast_exp2((xp - np.M) * k); };
+    if constexpr (VEC)
+      t = tile_search<E, kChunk / kThreads, kThreads>(p_row, nullptr, lo, a.V, theta_s, w, lds_f, lds_i);
+    else
+      t = range_search<E, false, kThreads>(p_row, nullptr, lo, hi, theta_s, w, lds_f, lds_i);
   }
   if (tid == 0) {
     a.n_out[b] = n;
@@ -387,30 +398,44 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(VerifyArgs a, const fl
   }
 }
 
+struct Layout {
+  size_t stats, pair_stats, total;
+};
+
+Layout layout(int B, int gamma, int V) {
+  const size_t nch = num_chunks(V), rows = (size_t)B * (2 * gamma + 1);
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  Layout L{};
+  L.stats = 0;
+  L.pair_stats = up(rows * nch * sizeof(float2));
+  L.total = up(L.pair_stats + (size_t)B * gamma * nch * sizeof(float2));
+  return L;
+}
+
 template <class E, bool VEC>
 hipError_t launch_typed(const VerifyArgs& a, hipStream_t s) {
   const int nch = num_chunks(a.V);
   const size_t rows = (size_t)a.B * (2 * a.gamma + 1);
-  float2* stats = static_cast<float2*>(a.ws);
-  float2* pair_stats = stats + rows * nch;
+  const Layout L = layout(a.B, a.gamma, a.V);
+  char* ws = static_cast<char*>(a.ws);
+  float2* stats = reinterpret_cast<float2*>(ws + L.stats);
+  float2* pair_stats = reinterpret_cast<float2*>(ws + L.pair_stats);
   const bool argmax = a.temperature == 0.f;
   const dim3 blk(kThreads);
-  if (argmax)
+  if (argmax) {
     row_stats_kernel<E, VEC, true><<<dim3(rows * nch), blk, 0, s>>>(a, stats);
-  else
+  } else {
     row_stats_kernel<E, VEC, false><<<dim3(rows * nch), blk, 0, s>>>(a, stats);
-  if (!argmax && a.gamma > 0)
-    pair_overlap_kernel<E, VEC><<<dim3((size_t)a.B * a.gamma * nch), blk, 0, s>>>(a, stats, pair_stats);
+    if (a.gamma > 0)
+      pair_overlap_kernel<E, VEC><<<dim3((size_t)a.B * a.gamma * nch), blk, 0, s>>>(a, stats, pair_stats);
+  }
   finish_kernel<E, VEC><<<dim3(a.B), blk, 0, s>>>(a, stats, pair_stats);
   return hipGetLastError();
 }
 
 }  // namespace
 
-size_t multipass_workspace_bytes(int B, int gamma, int V) {
-  const size_t nch = num_chunks(V);
-  return ((size_t)B * (2 * gamma + 1) + (size_t)B * gamma) * nch * sizeof(float2);
-}
+size_t multipass_workspace_bytes(int B, int gamma, int V) { return layout(B, gamma, V).total; }
 
 hipError_t multipass_launch(const VerifyArgs& a, hipStream_t s) {
   const size_t esz = a.dtype == SPEC_BF16 ? 2 : 4;

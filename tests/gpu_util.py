@@ -33,6 +33,12 @@ def run_case(case, algo, tensors=None, dev=None):
     import speculative_sampling_verification_02_amd as sv
     dev = dev or device()
     t = tensors or case_tensors(case, dev)
-    out = sv.verify(t["target"], t["draft"], t["tokens"], t["uniforms"], case.temperature, algo=algo)
+    try:
+        out = sv.verify(t["target"], t["draft"], t["tokens"], t["uniforms"], case.temperature, algo=algo)
+    except sv.SpecVerifyError as e:
+        if e.status == sv.SPEC_EUNSUPPORTED and algo == sv.ALGO_FUSED:
+            import pytest
+            pytest.skip("the fused path declines this shape (unaligned rows or too long a row)")
+        raise
     torch.cuda.synchronize(dev)
     return {k: v.cpu().numpy() for k, v in out.items()}

@@ -11,7 +11,7 @@ from tests import gpu_util, parity
 
 pytestmark = pytest.mark.gpu
 
-ALGOS = {"multipass": 1}
+ALGOS = {"multipass": 1, "fused": 2}
 
 
 def _sv():
@@ -54,7 +54,8 @@ def test_config3_full_size(dev, algo, T):
     gpu = gpu_util.run_case(case, ALGOS[algo], dev=dev)
     rep = parity.check(case, gpu, where=f"cfg3 T{T}")
     _banner(f"cfg3 {algo} T={T}: {rep}")
-    assert rep.u_band + rep.cdf_ambiguous <= max(2, case.B // 10)
+    # ambiguous rows are allowed to differ (validly); actual differences stay rare
+    assert rep.token_mismatch_valid <= max(1, case.B // 20)
 
 
 @pytest.mark.parametrize("algo", list(ALGOS))
