@@ -120,7 +120,7 @@ def main() -> int:
     sets = [base] + [(base[0].clone(), base[1].clone()) for _ in range(args.sets - 1)]
     tokens = torch.from_numpy(case.tokens).to(dev)
     uniforms = torch.from_numpy(case.uniforms).to(dev)
-    ws = torch.empty(sv.workspace_size(B, G, V, sv.SPEC_BF16), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(sv.workspace_size(B, G, V, sv.SPEC_BF16), dtype=torch.uint8, device=dev)
     outs = [{k: torch.empty(s, dtype=dt, device=dev) for k, s, dt in (
         ("n_accepted", (B,), torch.int32), ("next_token", (B,), torch.int32),
         ("alpha", (B, G), torch.float32), ("p_draft", (B, G), torch.float32),

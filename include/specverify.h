@@ -22,6 +22,11 @@
  *     logit.  +inf or NaN logits, and rows with no finite logit, are caller
  *     errors.  The results are then undefined but the kernels still terminate.
  *   - Outputs are deterministic: the same inputs give bit-identical outputs.
+ *   - Workspace: the caller zero-fills it once before its first use (for
+ *     example torch.zeros).  Every call that completes leaves it all-zero
+ *     again, so it can be reused for any later call, of any shape up to its
+ *     size, without clearing.  Two calls that may run at the same time need
+ *     two workspaces.
  */
 #ifndef SPECVERIFY_H
 #define SPECVERIFY_H
@@ -59,7 +64,7 @@ const char* spec_status_string(int status);
 
 /*
  * Bytes of device workspace spec_verify() / spec_verify_algo() need for this
- * shape, for any algorithm.  Returns 0 for invalid arguments.
+ * shape, for any algorithm and either dtype.  Returns 0 for invalid arguments.
  */
 size_t spec_verify_workspace_size(int B, int gamma, int V, int dtype);
 
@@ -90,6 +95,12 @@ size_t spec_verify_workspace_size(int B, int gamma, int V, int dtype);
  *     temperature-to-zero limit; [LH] "What does 'unchanged output' mean?").
  *     The uniforms are not read.
  *   A ratio with q_i(x_i) = 0 follows IEEE rules: p > 0 keeps the draft, 0/0 rejects.
+ *   A draft token outside [0, V) is rejected (it has p = q = 0).
+ *   n_accepted[b] = next_token[b] = -1 reports that the fused path gave up
+ *     waiting on a partner workgroup (about a second of polling; only possible
+ *     when another kernel occupies the device's compute units at the same
+ *     time).  That sequence has no result and the workspace must be zero-filled
+ *     again before its next use.
  *
  * Arguments:
  *   target_logits  [B][gamma+1][V], dtype
@@ -104,8 +115,9 @@ size_t spec_verify_workspace_size(int B, int gamma, int V, int dtype);
  *   alpha          float32 [B][gamma] out, or NULL
  *   p_draft        float32 [B][gamma] out, p_i(x_i), or NULL
  *   q_draft        float32 [B][gamma] out, q_i(x_i), or NULL
- *   workspace      device scratch of at least spec_verify_workspace_size() bytes.
- *                  The library treats it as uninitialised on entry.
+ *   workspace      device scratch of at least spec_verify_workspace_size() bytes,
+ *                  all-zero on entry (see the conventions above); all-zero on
+ *                  return of the queued work.
  * Returns SPEC_OK or an error status.  B == 0 returns SPEC_OK and queues nothing.
  */
 int spec_verify(const void* target_logits, const void* draft_logits, int dtype,

@@ -127,6 +127,13 @@ def verify(target_logits, draft_logits, draft_tokens, uniforms, temperature: flo
     [B, gamma+1]; all on the same GPU.  Returns a dict of GPU tensors:
     n_accepted int32 [B], next_token int32 [B], alpha / p_draft / q_draft
     float32 [B, gamma].  `outputs` may supply that dict preallocated.
+
+    `workspace` is a uint8 GPU tensor of at least workspace_size() bytes that
+    is all-zero before its first use; every completed call leaves it zero, so
+    one tensor serves a whole serving loop.  Without one, a zeroed tensor is
+    allocated for this call.  n_accepted = -1 marks a sequence whose result
+    was lost because the device was shared (see include/specverify.h); the
+    workspace must then be zeroed again.
     """
     torch = _torch()
     dev = target_logits.device
@@ -153,7 +160,7 @@ def verify(target_logits, draft_logits, draft_tokens, uniforms, temperature: flo
         }
     need = workspace_size(B, gamma, V, dt)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)
     _check(lib.spec_verify_algo(
         algo, _ptr(target_logits), _ptr(draft_logits), dt, _ptr(draft_tokens), _ptr(uniforms),
         B, gamma, V, float(temperature),
@@ -212,7 +219,7 @@ def lmhead_verify(hidden, W_target, W_draft, B: int, gamma: int, draft_tokens, u
     }
     need = int(lib.spec_lmhead_workspace_size(B, gamma, d, V))
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)
     _check(lib.spec_lmhead_verify(
         _ptr(hidden), _ptr(hidden_draft), _ptr(W_target), _ptr(W_draft), B, gamma, d, V,
         _ptr(draft_tokens), _ptr(uniforms), float(temperature),

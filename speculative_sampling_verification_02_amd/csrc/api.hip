@@ -49,11 +49,12 @@ const char* spec_status_string(int status) {
   }
 }
 
+// Both paths start their scratch at the workspace's base and both leave all
+// of it zero when they complete (the fused path needs zero slots on entry).
 size_t spec_verify_workspace_size(int B, int gamma, int V, int dtype) {
   if (!valid_shape(B, gamma, V) || (dtype != SPEC_F32 && dtype != SPEC_BF16)) return 0;
-  size_t bytes = specv::multipass_workspace_bytes(B, gamma, V);
-  bytes = std::max(bytes, specv::fused_workspace_bytes(B, gamma, V, dtype));
-  return std::max<size_t>(bytes, 256);
+  return std::max<size_t>(256, std::max(specv::fused_workspace_bytes(B, gamma, V),
+                                        specv::multipass_workspace_bytes(B, gamma, V)));
 }
 
 int spec_verify_algo(int algo, const void* target_logits, const void* draft_logits, int dtype,

@@ -27,6 +27,12 @@
 // outputs.  Compute workgroups never wait for finishers, and finishers of pair
 // items wait only for compute workgroups, so every wait ends.
 //
+// The exchange slots live in the caller's workspace.  Zero means "not yet
+// published"; the last reader of each slot sets it back to zero, so a call
+// that completes leaves the workspace as it found it (all zero) and no clearing
+// launch is needed.  Every wait is bounded; a wait that gives up publishes a
+// poison word downstream and the sequence reports n_accepted = -1.
+//
 // Page abbreviations: [FI] intuitivepapers.ai "Fast Inference from Transformers
 // via Speculative Decoding"; [SD] nonconvexcard "Speculative Decoding".
 
@@ -59,9 +65,13 @@ constexpr int kMaxTeam = 128;            // longest supported row: 128 tiles
 constexpr unsigned kSpinIters = 1u << 20;
 
 // Published partials are 64-bit words.  A word whose low 32 bits are kEmpty
-// (a quiet NaN) has not been written yet: the first float of every published
-// word is a maximum, an argmax value or an overlap share, never NaN.
-constexpr uint32_t kEmpty = 0x7fc00000u;
+// has not been written yet.  The low word of every published word is nonzero:
+// floats are stored with +0.0 replaced by -0.0 (same value), and the pair
+// result carries a marker bit.  kPoison (a NaN pattern no computation here
+// produces) marks a slot whose producer gave up waiting.
+constexpr uint32_t kEmpty = 0u;
+constexpr uint32_t kPoison = 0xffffffffu;
+constexpr uint32_t kResMark = 2u;  // pair result: bit 0 = accepted, bit 1 = published
 
 struct FusedParams {
   VerifyArgs a;
@@ -73,8 +83,7 @@ struct FusedParams {
   int nfin;       // finisher workgroups
   uint64_t* part1;     // [n_items][K][2]  (max, sum) of p and q, or argmax (value, index)
   uint64_t* part2;     // [n_pairs][K]     (overlap share, residual mass share)
-  uint64_t* pair_res;  // [n_pairs]        (accept flag, sampled token)
-  unsigned* err;       // [1]              set if a wait gave up
+  uint64_t* pair_res;  // [n_pairs]        (accept flag | kResMark, sampled token)
 };
 
 // ------------------------------------------------------------- cross-WG sync
@@ -87,13 +96,19 @@ struct FusedParams {
 // no read-modify-write atomic anywhere: atomics to one address serialise
 // across the device and cost about as much as the work they coordinate.
 
+// Bits of a float for the low word of a published slot: never kEmpty.
+__device__ inline uint32_t nz_bits(float a) {
+  const uint32_t u = __float_as_uint(a);
+  return u == 0u ? 0x80000000u : u;
+}
 __device__ inline uint64_t pack2(float a, float b) {
-  return (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32);
+  return (uint64_t)nz_bits(a) | ((uint64_t)__float_as_uint(b) << 32);
 }
 __device__ inline uint64_t pack2i(uint32_t a, uint32_t b) { return (uint64_t)a | ((uint64_t)b << 32); }
 __device__ inline float lo_f(uint64_t v) { return __uint_as_float((uint32_t)v); }
 __device__ inline float hi_f(uint64_t v) { return __uint_as_float((uint32_t)(v >> 32)); }
 __device__ inline bool published(uint64_t v) { return (uint32_t)v != kEmpty; }
+__device__ inline bool poisoned(uint64_t v) { return (uint32_t)v == kPoison; }
 
 __device__ inline void st_u64(uint64_t* p, uint64_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -103,39 +118,48 @@ __device__ inline uint64_t ld_u64(const uint64_t* p) {
 }
 
 // Wave 0 polls n consecutive 64-bit slots until every one is published and
-// copies them to lds[0..n).  Gives up after kSpinIters polls and sets *err, so
-// the kernel always terminates.  Called by the whole workgroup.
-__device__ inline void gather(const uint64_t* slots, int n, uint64_t* lds, unsigned* err) {
+// copies them to lds[0..n).  Returns true, uniformly over the workgroup, if all
+// arrived and none is poisoned.  Gives up after kSpinIters polls, so the kernel
+// always terminates.  Called by the whole workgroup.
+__device__ inline bool gather(const uint64_t* slots, int n, uint64_t* lds) {
+  __shared__ int ok_s;
   if (threadIdx.x < kWave) {
     const int lane = threadIdx.x;
     unsigned it = 0;
-    for (int base = 0; base < n; base += kWave) {
+    bool ok = true;
+    for (int base = 0; base < n && ok; base += kWave) {
       const int c = base + lane;
       while (true) {
-        const uint64_t v = c < n ? ld_u64(slots + c) : pack2i(0u, 0u);
+        const uint64_t v = c < n ? ld_u64(slots + c) : pack2i(1u, 0u);
         if (c < n) lds[c] = v;
-        if (__all(published(v))) break;
+        if (__all(published(v))) {
+          ok = !__any(poisoned(v));
+          break;
+        }
         __builtin_amdgcn_s_sleep(1);
         if (++it >= kSpinIters) {
-          __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          ok = false;
           break;
         }
       }
     }
+    if (lane == 0) ok_s = ok;
   }
   __syncthreads();
+  return ok_s != 0;
 }
 
 // gather() over two slot ranges at once: [a, a + na) -> la and [b, b + nb) -> lb.
-__device__ inline void gather2(const uint64_t* a, int na, uint64_t* la, const uint64_t* b, int nb, uint64_t* lb,
-                               unsigned* err) {
+__device__ inline bool gather2(const uint64_t* a, int na, uint64_t* la, const uint64_t* b, int nb, uint64_t* lb) {
+  __shared__ int ok_s;
   if (threadIdx.x < kWave) {
     const int lane = threadIdx.x, n = na + nb;
     unsigned it = 0;
-    for (int base = 0; base < n; base += kWave) {
+    bool ok = true;
+    for (int base = 0; base < n && ok; base += kWave) {
       const int c = base + lane;
       while (true) {
-        uint64_t v = pack2i(0u, 0u);
+        uint64_t v = pack2i(1u, 0u);
         if (c < na) {
           v = ld_u64(a + c);
           la[c] = v;
@@ -143,16 +167,28 @@ __device__ inline void gather2(const uint64_t* a, int na, uint64_t* la, const ui
           v = ld_u64(b + (c - na));
           lb[c - na] = v;
         }
-        if (__all(published(v))) break;
+        if (__all(published(v))) {
+          ok = !__any(poisoned(v));
+          break;
+        }
         __builtin_amdgcn_s_sleep(1);
         if (++it >= kSpinIters) {
-          __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          ok = false;
           break;
         }
       }
     }
+    if (lane == 0) ok_s = ok;
   }
   __syncthreads();
+  return ok_s != 0;
+}
+
+// Set n slots back to kEmpty (wave 0).  Only the last reader of a slot clears
+// it, after its own gather has returned the slot's data.
+__device__ inline void clear_slots(uint64_t* slots, int n) {
+  if (threadIdx.x < kWave)
+    for (int c = threadIdx.x; c < n; c += kWave) st_u64(slots + c, 0ull);
 }
 
 // ------------------------------------------------------------- tile loading
@@ -416,7 +452,10 @@ __device__ __attribute__((always_inline)) void pair_compute_sample(const FusedPa
   }
 
   // wait for the other tiles of this pair; the poll returns their partials
-  gather(P.part1 + (size_t)item * K * 2, 2 * K, w1, P.err);
+  if (!gather(P.part1 + (size_t)item * K * 2, 2 * K, w1)) {
+    if (threadIdx.x == 0) st_u64(P.part2 + (size_t)item * K + rank, pack2i(kPoison, 0u));
+    return;
+  }
   unpack_part1(w1, K, st1);
   Norm np, nq;
   team_norm2(st1, K, k, &np, &nq);
@@ -457,21 +496,21 @@ __device__ __attribute__((always_inline)) void single_pass_compute(const FusedPa
     unpack_tile<E, PER>(raw.q, lo, a.V, xq);
     const ArgMax ap = block_argmax(thread_argmax<E, PER>(xp, lo), lds_f, lds_i);
     const ArgMax aq = block_argmax(thread_argmax<E, PER>(xq, lo), lds_f, lds_i);
-    w0 = pack2i(__float_as_uint(ap.v), (uint32_t)ap.i);
-    w1 = pack2i(__float_as_uint(aq.v), (uint32_t)aq.i);
+    w0 = pack2i(nz_bits(ap.v), (uint32_t)ap.i);
+    w1 = pack2i(nz_bits(aq.v), (uint32_t)aq.i);
   } else {
     float x[PER];
     unpack_tile<E, PER>(raw.p, lo, a.V, x);
     if constexpr (ARGMAX) {
       const ArgMax ab = block_argmax(thread_argmax<E, PER>(x, lo), lds_f, lds_i);
-      w0 = pack2i(__float_as_uint(ab.v), (uint32_t)ab.i);
+      w0 = pack2i(nz_bits(ab.v), (uint32_t)ab.i);
     } else {
       const float m = thread_max<PER>(x);
       const float sm = thread_exp_sum<PER, false>(x, m, a.k);
       const float4 bl = block_lse2(m, sm, -INFINITY, 0.f, a.k, lds_f);
       w0 = pack2(bl.x, bl.y);
     }
-    w1 = pack2i(0u, 0u);
+    w1 = pack2i(0x80000000u, 0u);  // unused second word: (-0, 0), published
   }
   if (threadIdx.x == 0) {
     uint64_t* mine = P.part1 + ((size_t)item * K + rank) * 2;
@@ -511,7 +550,11 @@ __device__ void finish_pair(const FusedParams& P, int item) {
   const size_t o = (size_t)b * G + i;
 
   if constexpr (ARGMAX) {
-    gather(P.part1 + (size_t)item * K * 2, 2 * K, w1, P.err);
+    if (!gather(P.part1 + (size_t)item * K * 2, 2 * K, w1)) {
+      if (threadIdx.x == 0) st_u64(P.pair_res + item, pack2i(kPoison, 0u));
+      return;
+    }
+    clear_slots(P.part1 + (size_t)item * K * 2, 2 * K);
     if (threadIdx.x == 0) {
       // keep x iff it is the target's argmax; alpha is the indicator that the
       // two argmaxes agree ([FI] "Speculative sampling", temperature to zero)
@@ -520,7 +563,7 @@ __device__ void finish_pair(const FusedParams& P, int item) {
       if (a.alpha) a.alpha[o] = gp.i == gq.i ? 1.f : 0.f;
       if (a.p_draft) a.p_draft[o] = x == gp.i ? 1.f : 0.f;
       if (a.q_draft) a.q_draft[o] = x == gq.i ? 1.f : 0.f;
-      st_u64(P.pair_res + item, pack2i(x == gp.i ? 1u : 0u, (uint32_t)gp.i));
+      st_u64(P.pair_res + item, pack2i((x == gp.i ? 1u : 0u) | kResMark, (uint32_t)gp.i));
     }
     return;
   } else {
@@ -536,7 +579,13 @@ __device__ void finish_pair(const FusedParams& P, int item) {
     }
     // part2 is published after part1 by every tile; polling both in one pass
     // returns once both are complete
-    gather2(P.part1 + (size_t)item * K * 2, 2 * K, w1, P.part2 + (size_t)item * K, K, w2, P.err);
+    if (!gather2(P.part1 + (size_t)item * K * 2, 2 * K, w1, P.part2 + (size_t)item * K, K, w2)) {
+      if (threadIdx.x == 0) st_u64(P.pair_res + item, pack2i(kPoison, 0u));
+      return;
+    }
+    // every member has published part2, so every member is done reading part1
+    clear_slots(P.part1 + (size_t)item * K * 2, 2 * K);
+    clear_slots(P.part2 + (size_t)item * K, K);
     unpack_part1(w1, K, st1);
     Norm np, nq;
     team_norm2(st1, K, k, &np, &nq);
@@ -604,7 +653,7 @@ __device__ void finish_pair(const FusedParams& P, int item) {
           return fast_exp2((xp - Mp) * k);
         }, lds_f, lds_i);
     }
-    if (threadIdx.x == 0) st_u64(P.pair_res + item, pack2i((uint32_t)acc_s, (uint32_t)t));
+    if (threadIdx.x == 0) st_u64(P.pair_res + item, pack2i((uint32_t)acc_s | kResMark, (uint32_t)t));
   }
 }
 
@@ -623,9 +672,11 @@ __device__ void finish_bonus(const FusedParams& P, int item) {
   const int b = item - P.n_pairs;
   const float k = a.k;
   const auto* row = trow<E>(a, b, G);
-  gather(P.part1 + (size_t)item * K * 2, 2 * K, w1, P.err);
-  int t_bonus;
-  if constexpr (ARGMAX) {
+  const bool ok1 = gather(P.part1 + (size_t)item * K * 2, 2 * K, w1);
+  if (ok1) clear_slots(P.part1 + (size_t)item * K * 2, 2 * K);
+  int t_bonus = -1;
+  if (!ok1) {
+  } else if constexpr (ARGMAX) {
     t_bonus = combine_argmax(w1, K, 0).i;
   } else {
     unpack_part1(w1, K, st1);
@@ -641,12 +692,18 @@ __device__ void finish_bonus(const FusedParams& P, int item) {
                                             lds_i);
   }
   // the sequence's pair results (published by other finishers)
-  gather(P.pair_res + (size_t)b * G, G, res, P.err);
+  const bool ok2 = gather(P.pair_res + (size_t)b * G, G, res);
+  if (ok2) clear_slots(P.pair_res + (size_t)b * G, G);
   if (threadIdx.x == 0) {
-    int n = 0;
-    while (n < G && (uint32_t)res[n] != 0u) ++n;
-    a.n_out[b] = n;
-    a.t_out[b] = n < G ? (int)(uint32_t)(res[n] >> 32) : t_bonus;
+    if (ok1 && ok2) {
+      int n = 0;
+      while (n < G && ((uint32_t)res[n] & 1u) != 0u) ++n;
+      a.n_out[b] = n;
+      a.t_out[b] = n < G ? (int)(uint32_t)(res[n] >> 32) : t_bonus;
+    } else {
+      a.n_out[b] = -1;  // a wait gave up (the device was shared): no result
+      a.t_out[b] = -1;
+    }
   }
 }
 
@@ -701,13 +758,6 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedParams P) {
   }
 }
 
-// Fill n 32-bit words with `v` (the empty sentinel), and clear the error word.
-__global__ void fill_words(uint32_t* p, size_t n, uint32_t v, unsigned* err) {
-  for (size_t j = blockIdx.x * (size_t)blockDim.x + threadIdx.x; j < n; j += (size_t)gridDim.x * blockDim.x)
-    p[j] = v;
-  if (blockIdx.x == 0 && threadIdx.x == 0) *err = 0u;
-}
-
 constexpr int kFinisherDiv = SPECV_FUSED_FIN_DIV;
 
 template <class E>
@@ -720,20 +770,21 @@ int tiles_for(int V, int dtype) {
   return (V + tile - 1) / tile;
 }
 
+// Slot layout.  The size does not depend on the dtype (both use the larger
+// tile count), so one zeroed workspace serves calls of either dtype.
 struct Layout {
-  size_t off_err, off_part1, off_part2, off_res, end_words, total;
+  size_t off_part1, off_part2, off_res, total;
 };
 
-Layout layout(int B, int gamma, int V, int dtype) {
-  const size_t K = tiles_for(V, dtype), n_items = (size_t)B * (gamma + 1), n_pairs = (size_t)B * gamma;
+Layout layout(int B, int gamma, int V) {
+  const size_t K = std::max(tiles_for(V, SPEC_BF16), tiles_for(V, SPEC_F32));
+  const size_t n_items = (size_t)B * (gamma + 1), n_pairs = (size_t)B * gamma;
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   Layout L{};
-  L.off_err = 0;
-  L.off_part1 = 256;
-  L.off_part2 = L.off_part1 + 16 * n_items * K;
-  L.off_res = L.off_part2 + 8 * n_pairs * K;
-  L.end_words = L.off_res + 8 * n_pairs;
-  L.total = up(L.end_words);
+  L.off_part1 = 0;
+  L.off_part2 = up(L.off_part1 + 16 * n_items * K);
+  L.off_res = up(L.off_part2 + 8 * n_pairs * K);
+  L.total = up(L.off_res + 8 * n_pairs);
   return L;
 }
 
@@ -751,7 +802,7 @@ hipError_t resident_blocks(Kern kern, long* out) {
 template <class E, bool ARGMAX>
 hipError_t launch(const VerifyArgs& a, hipStream_t s) {
   constexpr int PER = per_thread<E>();
-  const Layout L = layout(a.B, a.gamma, a.V, a.dtype);
+  const Layout L = layout(a.B, a.gamma, a.V);
   char* ws = static_cast<char*>(a.ws);
   FusedParams P{};
   P.a = a;
@@ -759,7 +810,6 @@ hipError_t launch(const VerifyArgs& a, hipStream_t s) {
   P.K = (a.V + P.tile - 1) / P.tile;
   P.n_pairs = a.B * a.gamma;
   P.n_items = a.B * (a.gamma + 1);
-  P.err = reinterpret_cast<unsigned*>(ws + L.off_err);
   P.part1 = reinterpret_cast<uint64_t*>(ws + L.off_part1);
   P.part2 = reinterpret_cast<uint64_t*>(ws + L.off_part2);
   P.pair_res = reinterpret_cast<uint64_t*>(ws + L.off_res);
@@ -774,16 +824,13 @@ hipError_t launch(const VerifyArgs& a, hipStream_t s) {
   P.nteams = (int)std::min<long>(P.n_items, (resident - P.nfin) / P.K);
   if (P.nteams < 1) return hipErrorNotSupported;
 
-  const size_t words = (L.end_words - L.off_part1) / 4;
-  const unsigned fill_blocks = (unsigned)std::min<size_t>(1024, (words + 255) / 256);
-  fill_words<<<fill_blocks, 256, 0, s>>>(reinterpret_cast<uint32_t*>(ws + L.off_part1), words, kEmpty, P.err);
   kern<<<dim3(P.nteams * P.K + P.nfin), dim3(kThreads), 0, s>>>(P);
   return hipGetLastError();
 }
 
 }  // namespace
 
-size_t fused_workspace_bytes(int B, int gamma, int V, int dtype) { return layout(B, gamma, V, dtype).total; }
+size_t fused_workspace_bytes(int B, int gamma, int V) { return layout(B, gamma, V).total; }
 
 bool fused_supported(int B, int gamma, int V, int dtype) {
   const int vec = dtype == SPEC_BF16 ? BF16::kVec : F32::kVec;

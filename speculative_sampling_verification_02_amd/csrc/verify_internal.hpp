@@ -31,7 +31,9 @@ size_t multipass_workspace_bytes(int B, int gamma, int V);
 hipError_t multipass_launch(const VerifyArgs& a, hipStream_t stream);
 
 // ---- fused read-once path
-size_t fused_workspace_bytes(int B, int gamma, int V, int dtype);
+// Exchange slots of the fused path: all zero before a call, and all zero again
+// after a call that completes.  A multiple of 256 bytes.
+size_t fused_workspace_bytes(int B, int gamma, int V);
 // Returns hipErrorNotSupported when the shape does not fit the fused design.
 hipError_t fused_launch(const VerifyArgs& a, hipStream_t stream);
 bool fused_supported(int B, int gamma, int V, int dtype);

@@ -223,9 +223,22 @@ __global__ __launch_bounds__(kThreads) void pair_overlap_kernel(VerifyArgs a, co
 
 // ------------------------------------------------------------------ K3
 
+// Zero sequence b's row and pair statistics.  The finish block of b is their
+// only reader; it calls this after its last read, so every call leaves the
+// workspace all-zero, as the fused path's exchange slots require.
+__device__ inline void clear_sequence_stats(const VerifyArgs& a, float2* stats, float2* pair_stats, int b, int nch) {
+  const int G = a.gamma;
+  const float2 z = make_float2(0.f, 0.f);
+  for (int r = 0; r < 2 * G + 1; ++r) {
+    const size_t row = r <= G ? target_row(b, r, G) : draft_row(b, r - G - 1, G, a.B);
+    for (int c = threadIdx.x; c < nch; c += kThreads) stats[row * nch + c] = z;
+  }
+  if (a.temperature != 0.f)
+    for (int j = threadIdx.x; j < G * nch; j += kThreads) pair_stats[(size_t)b * G * nch + j] = z;
+}
+
 template <class E, bool VEC>
-__global__ __launch_bounds__(kThreads) void finish_kernel(VerifyArgs a, const float2* stats,
-                                                          const float2* pair_stats) {
+__global__ __launch_bounds__(kThreads) void finish_kernel(VerifyArgs a, float2* stats, float2* pair_stats) {
   __shared__ float lds_f[kMaxWaves];
   __shared__ int lds_i[kMaxWaves];
   __shared__ double lds_d[kMaxWaves];
@@ -264,6 +277,7 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(VerifyArgs a, const fl
       if (a.q_draft) a.q_draft[o] = (x == amax_d[tid]) ? 1.f : 0.f;
     }
     __syncthreads();
+    clear_sequence_stats(a, stats, pair_stats, b, nch);
     if (tid == 0) {
       int n = 0;
       while (n < G && accept_s[n]) ++n;
@@ -373,6 +387,7 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(VerifyArgs a, const fl
     theta_s = (float)(theta - prefix_s);
   }
   __syncthreads();
+  clear_sequence_stats(a, stats, pair_stats, b, nch);  // no statistic is read after this
 
   const int c = chunk_s, lo = c * kChunk, hi = min(a.V, lo + kChunk);
   const auto* p_row = row_ptr<E>(a, target_row(b, n, G));

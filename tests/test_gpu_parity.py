@@ -225,3 +225,28 @@ def test_config2_accept_length_statistics(dev, T):
     assert abs(tok.mean() - exp_.mean()) < 4 * se
     counts = np.bincount(tok - 1, minlength=G + 1)
     assert scipy.stats.chisquare(counts, pmf_sum * rounds / pmf_sum.sum()).pvalue > 1e-4
+
+
+# ------------------------------------------------------- workspace contract
+
+@pytest.mark.parametrize("T", [1.0, 0.0])
+def test_workspace_reused_across_shapes_and_paths(dev, T):
+    """One zeroed workspace serves calls of different shapes, dtypes and paths in
+    a row; every fused call leaves its exchange slots zero again."""
+    import torch
+    sv = _sv()
+    cases = [W.gaussian_case(3, 4, 40000, "bf16", T, seed=11), W.gaussian_case(2, 2, 20000, "f32", T, seed=12),
+             W.gaussian_case(5, 6, 33000, "bf16", T, seed=13)]
+    need = max(sv.workspace_size(c.B, c.gamma, c.V, sv.SPEC_BF16) for c in cases)
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+    for rep in range(2):
+        for j, case in enumerate(cases):
+            algo = ALGOS["fused"] if (rep + j) % 2 == 0 else ALGOS["multipass"]
+            t = gpu_util.case_tensors(case, dev)
+            out = sv.verify(t["target"], t["draft"], t["tokens"], t["uniforms"], case.temperature,
+                            algo=algo, workspace=ws)
+            torch.cuda.synchronize(dev)
+            got = {k: v.cpu().numpy() for k, v in out.items()}
+            parity.check(case, got, where=f"ws reuse rep{rep} case{j} algo{algo}")
+            assert (got["n_accepted"] >= 0).all()
+            assert int(ws.count_nonzero()) == 0, f"algo {algo} left the workspace dirty"
