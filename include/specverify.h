@@ -141,10 +141,12 @@ int spec_verify_algo(int algo,
  * spec_lmhead_logits -- the target pass's final matrix product for the positions
  * being verified ([FI] "Decoding waits on memory, not arithmetic": every weight
  * is read once per pass).
- *   logits[m][v] = sum_k hidden[m][k] * W[k][v], with bf16 inputs and fp32
- *   accumulation, written as fp32.
+ *   logits[m][v] = sum_k hidden[m][k] * W[k][v], with bf16 inputs, products
+ *   exact in fp32, fp32 accumulation (matrix cores), written as fp32.
  *   hidden  bf16 [M][d];  W  bf16 [d][V];  logits  float32 [M][V] out.
- *   1 <= M <= 256, 1 <= d, 1 <= V; d must be a multiple of 32 and V a multiple of 8.
+ *   1 <= M <= 256; d >= 32 and a multiple of 32; V >= 8 and a multiple of 8.
+ *   All three pointers 16-byte aligned.  W is read once per 64 rows of M.
+ *   Returns SPEC_EINVAL for any other shape or alignment.
  */
 int spec_lmhead_logits(const void* hidden, const void* W, int M, int d, int V,
                        float* logits, void* stream);
@@ -160,7 +162,10 @@ int spec_lmhead_logits(const void* hidden, const void* W, int M, int d, int V,
  *   target_logits    float32 [B][gamma+1][V] out (caller-owned; feeds the verify)
  *   draft_logits     float32 [B][gamma][V]   out
  *   other arguments as for spec_verify (the logits are fp32).
- * Limits: as spec_lmhead_logits for d and V; B*(gamma+1) <= 256.
+ * Both products run in one launch (for B*(gamma+1) <= 64), then the verification
+ * on the fp32 logits.  Limits and alignment as spec_lmhead_logits for d, V and
+ * every pointer; B*(gamma+1) <= 256.  The workspace is that of spec_verify for
+ * SPEC_F32 (spec_lmhead_workspace_size), zero on entry as there.
  */
 size_t spec_lmhead_workspace_size(int B, int gamma, int d, int V);
 int spec_lmhead_verify(const void* hidden, const void* hidden_draft,

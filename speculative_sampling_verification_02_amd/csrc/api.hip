@@ -111,15 +111,19 @@ int spec_verify(const void* target_logits, const void* draft_logits, int dtype,
                           workspace, workspace_bytes, stream);
 }
 
+static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
 int spec_lmhead_logits(const void* hidden, const void* W, int M, int d, int V, float* logits,
                        void* stream) {
   if (!hidden || !W || !logits) return SPEC_EINVAL;
-  if (M < 1 || M > 256 || d < 32 || d % 32 != 0 || V < 8 || V % 8 != 0) return SPEC_EINVAL;
-  return map_hip(specv::lmhead_launch(hidden, W, M, d, V, 1, 1, logits, static_cast<hipStream_t>(stream)));
+  if (M < 1 || M > 256 || !specv::lmhead_shape_ok(d, V)) return SPEC_EINVAL;
+  if (!aligned16(hidden) || !aligned16(W) || !aligned16(logits)) return SPEC_EINVAL;
+  const specv::LMHeadJob job{hidden, W, logits, M, 1, 1};
+  return map_hip(specv::lmhead_launch(&job, 1, d, V, static_cast<hipStream_t>(stream)));
 }
 
 size_t spec_lmhead_workspace_size(int B, int gamma, int d, int V) {
-  if (d < 32) return 0;
+  if (!specv::lmhead_shape_ok(d, V)) return 0;
   return spec_verify_workspace_size(B, gamma, V, SPEC_F32);
 }
 
@@ -132,19 +136,26 @@ int spec_lmhead_verify(const void* hidden, const void* hidden_draft, const void*
   if (!valid_shape(B, gamma, V) || !valid_temperature(temperature)) return SPEC_EINVAL;
   if (B == 0) return SPEC_OK;
   const int M = B * (gamma + 1);
-  if (M > 256 || d < 32 || d % 32 != 0 || V % 8 != 0) return SPEC_EINVAL;
+  if (M > 256 || !specv::lmhead_shape_ok(d, V)) return SPEC_EINVAL;
   if (!hidden || !W_target || !target_logits || (gamma > 0 && (!W_draft || !draft_logits)))
     return SPEC_EINVAL;
+  if (!aligned16(hidden) || !aligned16(W_target) || !aligned16(target_logits) ||
+      (gamma > 0 && (!aligned16(W_draft) || !aligned16(draft_logits) ||
+                     (hidden_draft && !aligned16(hidden_draft)))))
+    return SPEC_EINVAL;
+  if (workspace_bytes < spec_lmhead_workspace_size(B, gamma, d, V) || !workspace) return SPEC_ENOSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = specv::lmhead_launch(hidden, W_target, M, d, V, 1, 1, target_logits, s);
-  if (e != hipSuccess) return map_hip(e);
+  // Both heads in one launch.  Draft rows are either a dense [B*gamma][d]
+  // tensor, or rows 0..gamma-1 of each sequence's gamma+1 block of `hidden`.
+  specv::LMHeadJob jobs[2] = {{hidden, W_target, target_logits, M, 1, 1}, {}};
+  int njobs = 1;
   if (gamma > 0) {
-    // draft rows: either a dense [B*gamma][d] tensor, or rows 0..gamma-1 of
-    // each sequence's gamma+1 block of `hidden`
-    e = hidden_draft ? specv::lmhead_launch(hidden_draft, W_draft, B * gamma, d, V, 1, 1, draft_logits, s)
-                     : specv::lmhead_launch(hidden, W_draft, B * gamma, d, V, gamma + 1, gamma, draft_logits, s);
-    if (e != hipSuccess) return map_hip(e);
+    jobs[1] = hidden_draft ? specv::LMHeadJob{hidden_draft, W_draft, draft_logits, B * gamma, 1, 1}
+                           : specv::LMHeadJob{hidden, W_draft, draft_logits, B * gamma, gamma + 1, gamma};
+    njobs = 2;
   }
+  const hipError_t e = specv::lmhead_launch(jobs, njobs, d, V, s);
+  if (e != hipSuccess) return map_hip(e);
   return spec_verify(target_logits, draft_logits, SPEC_F32, draft_tokens, uniforms, B, gamma, V,
                      temperature, n_accepted, next_token, alpha, p_draft, q_draft, workspace,
                      workspace_bytes, stream);

@@ -39,7 +39,18 @@ hipError_t fused_launch(const VerifyArgs& a, hipStream_t stream);
 bool fused_supported(int B, int gamma, int V, int dtype);
 
 // ---- LM head
-hipError_t lmhead_launch(const void* hidden, const void* W, int M, int d, int V,
-                         int group_in, int group_out, float* out, hipStream_t stream);
+// One head of the product: out[m][v] = sum_k hidden[r(m)][k] W[k][v] for
+// m < M, with hidden row r(m) = (m / group_out) * group_in + m % group_out
+// (group_in = group_out = 1 reads the rows in order).
+struct LMHeadJob {
+  const void* hidden;  // bf16 [rows][d], 16-byte aligned
+  const void* W;       // bf16 [d][V], 16-byte aligned
+  float* out;          // [M][V], 16-byte aligned
+  int M, group_in, group_out;
+};
+// d a multiple of 32, V a multiple of 8.
+bool lmhead_shape_ok(int d, int V);
+// One launch per 64 output rows computes one or two heads (sharing d and V).
+hipError_t lmhead_launch(const LMHeadJob* jobs, int njobs, int d, int V, hipStream_t stream);
 
 }  // namespace specv

@@ -59,10 +59,25 @@ class VerifyCase:
 # ---------------------------------------------------------------- helpers
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
-    """Round float32 to bf16 (nearest, ties to even); returns uint16 bits."""
-    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
-    rounding = ((b >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
-    return ((b + rounding) >> np.uint32(16)).astype(np.uint16)
+    """Round float32 to bf16 (nearest, ties to even); returns uint16 bits.
+
+    Works in chunks of 4M values with in-place operations, so gigabyte-sized
+    weight matrices convert without gigabyte-sized temporaries.
+    """
+    b = np.ascontiguousarray(x, dtype=np.float32).reshape(-1).view(np.uint32)
+    out = np.empty(b.shape, dtype=np.uint16)
+    chunk = 1 << 22
+    t = np.empty(min(chunk, b.size), dtype=np.uint32)
+    for lo in range(0, b.size, chunk):
+        src = b[lo:lo + chunk]
+        tt = t[:src.size]
+        np.right_shift(src, np.uint32(16), out=tt)
+        np.bitwise_and(tt, np.uint32(1), out=tt)
+        np.add(tt, np.uint32(0x7FFF), out=tt)
+        np.add(tt, src, out=tt)
+        np.right_shift(tt, np.uint32(16), out=tt)
+        out[lo:lo + src.size] = tt
+    return out.reshape(np.shape(x))
 
 
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
@@ -213,6 +228,39 @@ class LMHeadCase:
         return np.array([b * g1 + i for b in range(self.B) for i in range(self.gamma)], dtype=np.int64)
 
 
+def _normal_bf16_weights(seed: int, d: int, V: int, std: float, noise_std: float,
+                         blocks: int = 32, workers: int = 8):
+    """W_p ~ N(0, std^2) and W_q = W_p + N(0, noise_std^2), both [d, V] bf16 bits.
+
+    The rows are cut into `blocks` blocks; block j draws from its own stream
+    spawned from (seed, 0x40) and is converted on a worker thread (numpy's
+    generators release the GIL), so a gigabyte matrix takes seconds.  The
+    result depends only on the seed and the shape, never on `workers`.
+    """
+    children = np.random.SeedSequence([seed, 0x40]).spawn(blocks)
+    wp = np.empty((d, V), dtype=np.uint16)
+    wq = np.empty((d, V), dtype=np.uint16)
+    bounds = [(j * d // blocks, (j + 1) * d // blocks) for j in range(blocks)]
+
+    def work(j):
+        lo, hi = bounds[j]
+        if hi <= lo:
+            return
+        rng = np.random.default_rng(children[j])
+        p32 = rng.standard_normal((hi - lo, V), dtype=np.float32)
+        p32 *= np.float32(std)
+        n32 = rng.standard_normal((hi - lo, V), dtype=np.float32)
+        n32 *= np.float32(noise_std)
+        n32 += p32
+        wp[lo:hi] = f32_to_bf16_bits(p32)
+        wq[lo:hi] = f32_to_bf16_bits(n32)
+
+    import concurrent.futures
+    with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
+        list(ex.map(work, range(blocks)))
+    return wp, wq
+
+
 def config4(seed: int = 0, temperature: float = 1.0, B: int = 8, gamma: int = 4,
             d: int = 4096, V: int = 128256) -> LMHeadCase:
     """Fused LM head + verify: hidden [B(gamma+1), d] ~ N(0,1); W_p ~ N(0, 0.02^2);
@@ -221,18 +269,18 @@ def config4(seed: int = 0, temperature: float = 1.0, B: int = 8, gamma: int = 4,
     Drafted tokens are Gumbel-max samples from the draft head's own fp32 logits,
     as the draft model would have produced them.
     """
-    rng = np.random.default_rng([seed, 0x40])
+    rng = np.random.default_rng([seed, 0x41])
     M = B * (gamma + 1)
-    hidden32 = rng.standard_normal((M, d), dtype=np.float32)
-    wp32 = rng.standard_normal((d, V), dtype=np.float32) * np.float32(0.02)
-    wq32 = wp32 + rng.standard_normal((d, V), dtype=np.float32) * np.float32(0.005)
-    hidden, wp, wq = f32_to_bf16_bits(hidden32), f32_to_bf16_bits(wp32), f32_to_bf16_bits(wq32)
-    del hidden32, wp32, wq32
+    hidden = f32_to_bf16_bits(rng.standard_normal((M, d), dtype=np.float32))
+    wp, wq = _normal_bf16_weights(seed, d, V, 0.02, 0.005)
     case = LMHeadCase(hidden, wp, wq, B, gamma, np.zeros((B, gamma), np.int32),
                       make_uniforms(seed, B, gamma), float(temperature))
     hq = bf16_bits_to_f32(hidden[case.draft_hidden_rows()])
-    draft_logits = (hq @ bf16_bits_to_f32(wq)).reshape(B, gamma, V)
-    case.tokens = gumbel_max_tokens(draft_logits, temperature, np.random.default_rng([seed, 0x70CE]))
+    draft_logits = np.zeros((B * gamma, V), dtype=np.float32)
+    for lo in range(0, d, 512):
+        draft_logits += hq[:, lo:lo + 512] @ bf16_bits_to_f32(wq[lo:lo + 512])
+    case.tokens = gumbel_max_tokens(draft_logits.reshape(B, gamma, V), temperature,
+                                    np.random.default_rng([seed, 0x70CE]))
     return case
 
 
