@@ -1,31 +1,40 @@
 // Fused read-once verification path for gfx950.
 //
 // One persistent kernel whose grid fits the device's residency limit, so all
-// of its workgroups run at once.  The vocabulary is cut into tiles of
-// PER * 256 tokens.  Most workgroups form compute teams of K = ceil(V / tile).
-// A team owns one work item at a time, one tile per workgroup:
+// of its workgroups run at once.  Each row is cut into wave tiles of
+// kWave * PER contiguous tokens, and each wave owns one wave tile.  A workgroup
+// holds four waves, so its tile is four adjacent wave tiles.  Most workgroups
+// form compute teams of K = ceil(V / (4 * kWave * PER)).  A team owns one
+// work item at a time, one tile per workgroup:
 //   pair item (b, i), i < gamma:  tiles of target row p_i and draft row q_i
 //   bonus item b:                 tiles of target row p_gamma
 // Teams step through the items round-robin.  Every logit is read from HBM once.
 //
-// Pair item, T > 0 (the only place a compute workgroup waits):
-//   1. Load the tile's two rows.  Keep e = exp2((l - m_t) k) per token in
-//      registers (m_t = the thread's maximum; k = log2(e) / T).
-//   2. Publish the tile's (max, sum) of both rows.  Wait until all K tiles of
-//      the pair have published.
-//   3. Every member combines the K partials in the same order.  It then forms
-//      its share of alpha = sum min(p, q) and of the residual mass
-//      sum max(0, p - q) from the registers, and publishes both.
-// Argmax-mode pairs and bonus items publish a single partial per tile.
+// Waves work on their own: every reduction is a wave-level DPP reduction and
+// every partial is published per wave, so a compute workgroup meets at a
+// barrier once per pair item and never otherwise.
 //
-// The remaining workgroups are finishers.  A finisher waits until all K tiles
-// of an item have published.  It then computes alpha and the fp64 ratio test,
-// and draws the item's sample: the residual of a rejected pair, or the bonus
-// token.  To draw it, it finds the tile holding u * mass and scans that tile
-// again with all loads issued up front.  The finisher of a sequence's bonus
-// item then waits for the sequence's pair results, forms n and writes the
-// outputs.  Compute workgroups never wait for finishers, and finishers of pair
-// items wait only for compute workgroups, so every wait ends.
+// Pair item, T > 0 (the only place a compute workgroup waits):
+//   1. Load the wave tile of both rows.  Keep e = exp2((l - m_t) k) per token
+//      in registers (m_t = the thread's maximum; k = log2(e) / T).
+//   2. Publish the wave's (max, sum) of both rows.
+//   3. Wave 0 waits until all 4K waves of the team have published, combines
+//      the partials in one fixed order and hands both row normalisers to the
+//      other waves through LDS (one barrier that waits on LDS only, so no
+//      global load is held up by it).
+//   4. Each wave forms its share of alpha = sum min(p, q) and of the residual
+//      mass sum max(0, p - q) from its registers and publishes both.
+// Argmax-mode pairs and bonus items publish a single partial per wave.
+//
+// The remaining workgroups are finishers.  A finisher waits until all wave
+// tiles of an item have published.  It then computes alpha and the fp64 ratio
+// test, and draws the item's sample: the residual of a rejected pair, or the
+// bonus token.  To draw it, it finds the wave tile holding u * mass from the
+// per-wave masses and scans that one tile (kWave * PER tokens) again.  The
+// finisher of a sequence's bonus item then waits for the sequence's pair
+// results, forms n and writes the outputs.  Compute workgroups never wait for
+// finishers, and finishers of pair items wait only for compute workgroups, so
+// every wait ends.
 //
 // The exchange slots live in the caller's workspace.  Zero means "not yet
 // published"; the last reader of each slot sets it back to zero, so a call
@@ -40,6 +49,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "common.hpp"
 #include "specverify.h"
@@ -48,20 +58,26 @@
 namespace specv {
 namespace {
 
-// Tokens per thread per row (the tile is 256 times this), the share of
-// resident workgroups that finish items (1 / SPECV_FUSED_FIN_DIV), and whether
-// a compute workgroup double-buffers its tiles across items.
+// Tokens per thread per row (the wave tile is kWave times this) and the share
+// of resident workgroups that finish items (1 / SPECV_FUSED_FIN_DIV).
 #ifndef SPECV_FUSED_PER
 #define SPECV_FUSED_PER 32
 #endif
 #ifndef SPECV_FUSED_FIN_DIV
 #define SPECV_FUSED_FIN_DIV 8
 #endif
-#ifndef SPECV_FUSED_PREFETCH
-#define SPECV_FUSED_PREFETCH 0
+// Stage the next bf16 item in LDS while the current one is computed (1) or
+// load each item when its turn comes (0).
+#ifndef SPECV_FUSED_STAGE
+#define SPECV_FUSED_STAGE 1
+#endif
+// Minimum waves per SIMD the register allocation must allow (1: no limit).
+#ifndef SPECV_FUSED_MIN_WAVES
+#define SPECV_FUSED_MIN_WAVES 1
 #endif
 constexpr int kThreads = 256;
-constexpr int kMaxTeam = 128;            // longest supported row: 128 tiles
+constexpr int kWavesPerGroup = kThreads / kWave;
+constexpr int kMaxWaveTiles = 256;  // longest supported row: 256 wave tiles
 constexpr unsigned kSpinIters = 1u << 20;
 
 // Published partials are 64-bit words.  A word whose low 32 bits are kEmpty
@@ -75,14 +91,14 @@ constexpr uint32_t kResMark = 2u;  // pair result: bit 0 = accepted, bit 1 = pub
 
 struct FusedParams {
   VerifyArgs a;
-  int K;          // tiles per row: the team size
-  int tile;       // tokens per tile
+  int K;          // workgroups per team
+  int W;          // wave tiles per row slot range: 4 K (the last few may lie past V)
   int n_pairs;    // B * gamma
   int n_items;    // B * (gamma + 1): pairs, then one bonus item per sequence
   int nteams;     // compute teams
   int nfin;       // finisher workgroups
-  uint64_t* part1;     // [n_items][K][2]  (max, sum) of p and q, or argmax (value, index)
-  uint64_t* part2;     // [n_pairs][K]     (overlap share, residual mass share)
+  uint64_t* part1;     // [n_items][W][2]  (max, sum) of p and q, or argmax (value, index)
+  uint64_t* part2;     // [n_pairs][W]     (overlap share, residual mass share)
   uint64_t* pair_res;  // [n_pairs]        (accept flag | kResMark, sampled token)
 };
 
@@ -117,90 +133,80 @@ __device__ inline uint64_t ld_u64(const uint64_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Wave 0 polls n consecutive 64-bit slots until every one is published and
-// copies them to lds[0..n).  Returns true, uniformly over the workgroup, if all
-// arrived and none is poisoned.  Gives up after kSpinIters polls, so the kernel
-// always terminates.  Called by the whole workgroup.
-__device__ inline bool gather(const uint64_t* slots, int n, uint64_t* lds) {
-  __shared__ int ok_s;
-  if (threadIdx.x < kWave) {
-    const int lane = threadIdx.x;
-    unsigned it = 0;
-    bool ok = true;
-    for (int base = 0; base < n && ok; base += kWave) {
-      const int c = base + lane;
-      while (true) {
-        const uint64_t v = c < n ? ld_u64(slots + c) : pack2i(1u, 0u);
-        if (c < n) lds[c] = v;
-        if (__all(published(v))) {
-          ok = !__any(poisoned(v));
-          break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-        if (++it >= kSpinIters) {
-          ok = false;
-          break;
-        }
-      }
-    }
-    if (lane == 0) ok_s = ok;
-  }
-  __syncthreads();
-  return ok_s != 0;
+// Workgroup barrier for LDS data only: the fences order LDS accesses, so the
+// barrier waits for this wave's LDS operations but not for its outstanding
+// global loads (a full __syncthreads() would drain those too).
+__device__ inline void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// gather() over two slot ranges at once: [a, a + na) -> la and [b, b + nb) -> lb.
+// One wave polls n consecutive 64-bit slots until every one is published and
+// copies them to lds[0..n).  Returns true, uniformly over the wave, if all
+// arrived and none is poisoned.  Gives up after kSpinIters polls, so the
+// kernel always terminates.  Called by all lanes of one wave.
+__device__ inline bool wave_poll(const uint64_t* a, int na, uint64_t* la, const uint64_t* b, int nb,
+                                 uint64_t* lb) {
+  const int lane = threadIdx.x & (kWave - 1), n = na + nb;
+  unsigned it = 0;
+  for (int base = 0; base < n; base += kWave) {
+    const int c = base + lane;
+    while (true) {
+      uint64_t v = pack2i(1u, 0u);
+      if (c < na) {
+        v = ld_u64(a + c);
+        la[c] = v;
+      } else if (c < n) {
+        v = ld_u64(b + (c - na));
+        lb[c - na] = v;
+      }
+      if (__all(published(v))) {
+        if (__any(poisoned(v))) return false;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+      if (++it >= kSpinIters) return false;
+    }
+  }
+  return true;
+}
+
+// Whole-workgroup wait: wave 0 polls, then a barrier.  Finishers only.
 __device__ inline bool gather2(const uint64_t* a, int na, uint64_t* la, const uint64_t* b, int nb, uint64_t* lb) {
   __shared__ int ok_s;
   if (threadIdx.x < kWave) {
-    const int lane = threadIdx.x, n = na + nb;
-    unsigned it = 0;
-    bool ok = true;
-    for (int base = 0; base < n && ok; base += kWave) {
-      const int c = base + lane;
-      while (true) {
-        uint64_t v = pack2i(1u, 0u);
-        if (c < na) {
-          v = ld_u64(a + c);
-          la[c] = v;
-        } else if (c < n) {
-          v = ld_u64(b + (c - na));
-          lb[c - na] = v;
-        }
-        if (__all(published(v))) {
-          ok = !__any(poisoned(v));
-          break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-        if (++it >= kSpinIters) {
-          ok = false;
-          break;
-        }
-      }
-    }
-    if (lane == 0) ok_s = ok;
+    const bool ok = wave_poll(a, na, la, b, nb, lb);
+    if (threadIdx.x == 0) ok_s = ok;
   }
   __syncthreads();
   return ok_s != 0;
 }
+__device__ inline bool gather(const uint64_t* slots, int n, uint64_t* lds) {
+  return gather2(slots, n, lds, nullptr, 0, nullptr);
+}
 
 // Set n slots back to kEmpty (wave 0).  Only the last reader of a slot clears
-// it, after its own gather has returned the slot's data.
+// it, after its own poll has returned the slot's data.
 __device__ inline void clear_slots(uint64_t* slots, int n) {
   if (threadIdx.x < kWave)
     for (int c = threadIdx.x; c < n; c += kWave) st_u64(slots + c, 0ull);
 }
 
 // ------------------------------------------------------------- tile loading
+//
+// Wave tile c of a row is tokens [c * kWave * PER, (c + 1) * kWave * PER).
+// Lane l holds vectors s = 0 .. PER / kVec - 1 at token
+// tile_lo + (s * kWave + l) * kVec, so each load instruction of a wave reads
+// 1 KiB of contiguous memory.
 
-// This thread's PER tokens of a row tile, in token order within each
-// 256 * kVec step.  Tokens >= V read as -inf.  load_raw only issues the loads,
-// so both rows of a pair can be in flight before either is unpacked.
 template <class E, int PER>
 struct RawTile {
   static constexpr int NS = PER / E::kVec;
   u32x4 v[NS];
 };
+
+__device__ inline int wave_lane() { return threadIdx.x & (kWave - 1); }
 
 // The loads are unconditional: a vector past the end of the row reads the
 // row's last vector instead (V >= kVec), and unpack_tile masks it to -inf.
@@ -209,14 +215,14 @@ template <class E, int PER>
 __device__ inline void load_raw(const typename E::storage* row, int tile_lo, int V, RawTile<E, PER>& r) {
 #pragma unroll
   for (int s = 0; s < RawTile<E, PER>::NS; ++s) {
-    const int j0 = tile_lo + (s * kThreads + (int)threadIdx.x) * E::kVec;
+    const int j0 = tile_lo + (s * kWave + wave_lane()) * E::kVec;
     r.v[s] = load_stream(row + min(j0, V - E::kVec));
   }
 }
 
 template <class E, int PER>
 __device__ inline void unpack_tile(const RawTile<E, PER>& r, int tile_lo, int V, float (&x)[PER]) {
-  if (tile_lo + kThreads * PER <= V) {  // the whole tile is in range: no per-token select
+  if (tile_lo + kWave * PER <= V) {  // the whole tile is in range: no per-token select
 #pragma unroll
     for (int s = 0; s < RawTile<E, PER>::NS; ++s) {
       float t[E::kVec];
@@ -228,7 +234,7 @@ __device__ inline void unpack_tile(const RawTile<E, PER>& r, int tile_lo, int V,
   }
 #pragma unroll
   for (int s = 0; s < RawTile<E, PER>::NS; ++s) {
-    const int j0 = tile_lo + (s * kThreads + (int)threadIdx.x) * E::kVec;
+    const int j0 = tile_lo + (s * kWave + wave_lane()) * E::kVec;
     float t[E::kVec];
     E::unpack(r.v[s], t);
 #pragma unroll
@@ -236,22 +242,16 @@ __device__ inline void unpack_tile(const RawTile<E, PER>& r, int tile_lo, int V,
   }
 }
 
-template <class E, int PER>
-__device__ inline void load_tile(const typename E::storage* row, int tile_lo, int V, float (&x)[PER]) {
-  RawTile<E, PER> r;
-  load_raw<E, PER>(row, tile_lo, V, r);
-  unpack_tile<E, PER>(r, tile_lo, V, x);
+template <int KVEC>
+__device__ inline int tile_token(int tile_lo, int idx) {
+  return tile_lo + ((idx / KVEC) * kWave + wave_lane()) * KVEC + idx % KVEC;
 }
 
-__device__ inline int tile_token(int tile_lo, int idx, int kvec) {
-  return tile_lo + ((idx / kvec) * kThreads + (int)threadIdx.x) * kvec + idx % kvec;
-}
-
-// Thread maximum with four independent max chains (short dependency chains).
+// Thread maximum with independent max chains (three-input maxima: half an
+// instruction per token).
 template <int PER>
 __device__ inline float thread_max(const float (&x)[PER]) {
   static_assert(PER % 4 == 0, "PER must be a multiple of 4");
-  // three-input maxima (v_max3_f32): half an instruction per token
   float m0 = fmaxf(x[0], x[1]), m1 = fmaxf(x[2], x[3]);
 #pragma unroll
   for (int i = 4; i < PER; i += 4) {
@@ -289,86 +289,74 @@ __device__ inline float thread_exp_sum(float (&x)[PER], float m, float k) {
   return (s0 + s1) + (s2 + s3);
 }
 
-// The thread's (max, sum) -> the workgroup's (max, sum) relative to that max,
-// for two rows at once: returns (M_p, S_p, M_q, S_q).
-__device__ inline float4 block_lse2(float mp, float sp, float mq, float sq, float k, float* lds) {
-  const float2 M = block_max2(mp, mq, lds);
-  const float wp = mp == -INFINITY ? 0.f : sp * fast_exp2((mp - M.x) * k);
-  const float wq = mq == -INFINITY ? 0.f : sq * fast_exp2((mq - M.y) * k);
-  const float2 S = block_sum2(wp, wq, lds);
-  return make_float4(M.x, S.x, M.y, S.y);
+// The threads' (max m, sum s relative to m) -> the wave's (max, sum relative
+// to that max), identical in every lane.
+__device__ inline float2 wave_lse(float m, float s, float k) {
+  const float M = wave_max(m);
+  const float w = m == -INFINITY ? 0.f : s * fast_exp2((m - M) * k);
+  return make_float2(M, wave_sum(w));
 }
 
 template <class E, int PER>
 __device__ inline ArgMax thread_argmax(const float (&x)[PER], int tile_lo) {
   ArgMax best{-INFINITY, 0x7fffffff};
 #pragma unroll
-  for (int i = 0; i < PER; ++i) best = argmax_better(best, ArgMax{x[i], tile_token(tile_lo, i, E::kVec)});
+  for (int i = 0; i < PER; ++i) best = argmax_better(best, ArgMax{x[i], tile_token<E::kVec>(tile_lo, i)});
   return best;
 }
 
-// Row normaliser over the K staged tiles, combined in one fixed order so that
-// every workgroup that calls it gets bit-identical values.  `sel` picks the
-// (max, sum) half of the float4 partial: 0 -> (x, y), 1 -> (z, w).
-struct Norm {
-  float M;
-  float invS;
-  double S;
+// Row normalisers of both rows of an item from its W published word pairs
+// (lds[2c] = (max, sum) of p in wave tile c, lds[2c + 1] the same for q):
+// M = max_c m_c and S = sum_c s_c exp2((m_c - M) k) in fp64, in one fixed
+// order.  Called by all lanes of one wave; every lane gets the result.
+struct Norm2 {
+  float Mp, Mq;
+  double Sp, Sq;
 };
 
-// Normalisers of both rows (sel 0: (x, y) halves, sel 1: (z, w) halves) from
-// the K staged partials, computed by wave 0 in one fixed order.
-__device__ inline void team_norm2(const float4* st, int K, float k, Norm* np, Norm* nq) {
-  __shared__ float sM[2];
-  __shared__ double sS[2];
-  if (threadIdx.x < kWave) {
-    float Mp = -INFINITY, Mq = -INFINITY;
-    for (int c = threadIdx.x; c < K; c += kWave) {
-      Mp = fmaxf(Mp, st[c].x);
-      Mq = fmaxf(Mq, st[c].z);
-    }
-    Mp = wave_max(Mp);
-    Mq = wave_max(Mq);
-    double Sp = 0.0, Sq = 0.0;
-    for (int c = threadIdx.x; c < K; c += kWave) {
-      const float4 v = st[c];
-      if (v.x != -INFINITY) Sp += (double)v.y * (double)fast_exp2((v.x - Mp) * k);
-      if (v.z != -INFINITY) Sq += (double)v.w * (double)fast_exp2((v.z - Mq) * k);
-    }
-    Sp = wave_sum(Sp);
-    Sq = wave_sum(Sq);
-    if (threadIdx.x == 0) {
-      sM[0] = Mp;
-      sM[1] = Mq;
-      sS[0] = Sp;
-      sS[1] = Sq;
-    }
+__device__ inline Norm2 wave_norm2(const uint64_t* w, int W, float k) {
+  const int lane = wave_lane();
+  float Mp = -INFINITY, Mq = -INFINITY;
+  for (int c = lane; c < W; c += kWave) {
+    Mp = fmaxf(Mp, lo_f(w[2 * c]));
+    Mq = fmaxf(Mq, lo_f(w[2 * c + 1]));
   }
-  __syncthreads();
-  *np = Norm{sM[0], (float)(1.0 / sS[0]), sS[0]};
-  *nq = Norm{sM[1], (float)(1.0 / sS[1]), sS[1]};
-  __syncthreads();
+  Mp = wave_max(Mp);
+  Mq = wave_max(Mq);
+  double Sp = 0.0, Sq = 0.0;
+  for (int c = lane; c < W; c += kWave) {
+    const float mp = lo_f(w[2 * c]), mq = lo_f(w[2 * c + 1]);
+    if (mp != -INFINITY) Sp += (double)hi_f(w[2 * c]) * (double)fast_exp2((mp - Mp) * k);
+    if (mq != -INFINITY) Sq += (double)hi_f(w[2 * c + 1]) * (double)fast_exp2((mq - Mq) * k);
+  }
+  return Norm2{Mp, Mq, wave_sum(Sp), wave_sum(Sq)};
 }
 
-// Tile holding theta among K tile masses in tile order: wave 0 scans the
+// Mass of wave tile c of the p row, relative to the row maximum M.
+__device__ inline double p_tile_mass(const uint64_t* w, int c, float M, float k) {
+  const float m = lo_f(w[2 * c]);
+  return m == -INFINITY ? 0.0 : (double)hi_f(w[2 * c]) * (double)fast_exp2((m - M) * k);
+}
+
+// Tile holding theta among W tile masses in tile order: wave 0 scans the
 // masses (fp64, fixed order) and takes the first tile whose running mass
 // exceeds theta.  *tile and *rest (theta minus the mass before that tile) are
 // LDS variables, valid for the whole workgroup on return.  If rounding leaves
 // theta past every tile, the last tile with mass is taken.  Called by the
 // whole workgroup.
 template <class MassFn>
-__device__ inline void wave_pick_tile(int K, double theta, MassFn mass, int* tile, float* rest) {
+__device__ inline void wave_pick_tile(int W, double theta, MassFn mass, int* tile, float* rest) {
   if (threadIdx.x < kWave) {
     const int lane = threadIdx.x;
     double carry = 0.0;
     int pick = -1, last = 0;
     float left = 0.f;
-    for (int base = 0; base < K; base += kWave) {
+    for (int base = 0; base < W; base += kWave) {
       const int c = base + lane;
-      const double w = c < K ? mass(c) : 0.0;
+      const double w = c < W ? mass(c) : 0.0;
       const double incl = carry + wave_inclusive_scan(w);
-      const unsigned long long hit = __ballot(c < K && w > 0.0 && incl > theta);
-      const unsigned long long pos = __ballot(c < K && w > 0.0);
+      const unsigned long long hit = __ballot(c < W && w > 0.0 && incl > theta);
+      const unsigned long long pos = __ballot(c < W && w > 0.0);
       if (pos) last = base + 63 - __clzll(pos);
       if (hit) {
         const int l = __ffsll((long long)hit) - 1;
@@ -388,11 +376,8 @@ __device__ inline void wave_pick_tile(int K, double theta, MassFn mass, int* til
 }
 
 // ------------------------------------------------------ compute workgroups
-// A compute workgroup only streams its tile and publishes partials.  It
-// never waits for a finisher.  Its loop is software-pipelined: the next
-// item's tile loads are issued before the current item is processed (two
-// register buffers, used alternately), so the load latency overlaps the
-// current item's arithmetic and wait.
+// A compute workgroup only streams its tiles and publishes partials.  It
+// never waits for a finisher.
 
 template <class E>
 __device__ inline const typename E::storage* trow(const VerifyArgs& a, int b, int i) {
@@ -403,16 +388,15 @@ __device__ inline const typename E::storage* drow(const VerifyArgs& a, int b, in
   return static_cast<const typename E::storage*>(a.draft) + ((size_t)b * a.gamma + i) * (size_t)a.V;
 }
 
-// The raw tiles of one item: both rows of a pair, or the bonus row in `p`.
+// The raw wave tiles of one item: both rows of a pair, or the bonus row in `p`.
 template <class E, int PER>
 struct RawPair {
   RawTile<E, PER> p, q;
 };
 
 template <class E, int PER>
-__device__ __attribute__((always_inline)) void issue_item(const FusedParams& P, int item, int rank, RawPair<E, PER>& r) {
+__device__ __attribute__((always_inline)) void issue_item(const FusedParams& P, int item, int lo, RawPair<E, PER>& r) {
   const VerifyArgs& a = P.a;
-  const int lo = rank * P.tile;
   const bool pair = item < P.n_pairs;
   const int b = pair ? item / a.gamma : item - P.n_pairs;
   const int i = pair ? item % a.gamma : a.gamma;
@@ -420,47 +404,53 @@ __device__ __attribute__((always_inline)) void issue_item(const FusedParams& P, 
   if (pair) load_raw<E, PER>(drow<E>(a, b, i), lo, a.V, r.q);
 }
 
-// LDS view of an item's published first partials.
-__device__ inline void unpack_part1(const uint64_t* w, int K, float4* st) {
-  for (int c = threadIdx.x; c < K; c += kThreads)
-    st[c] = make_float4(lo_f(w[2 * c]), hi_f(w[2 * c]), lo_f(w[2 * c + 1]), hi_f(w[2 * c + 1]));
-  __syncthreads();
-}
+// Row normalisers handed from wave 0 to the other waves, double-buffered by
+// item parity: a buffer is rewritten two items later, after every wave has
+// passed the barrier of the item in between.
+struct NormMsg {
+  float Mp, Mq, invSp, invSq;
+  int ok;
+};
 
 // Pair item, T > 0: the tile stays in registers across the team's one wait.
 template <class E, int PER>
-__device__ __attribute__((always_inline)) void pair_compute_sample(const FusedParams& P, int item, int rank, const RawPair<E, PER>& raw) {
-  __shared__ float lds_f[2 * kMaxWaves];
-  __shared__ uint64_t w1[2 * kMaxTeam];
-  __shared__ float4 st1[kMaxTeam];
+__device__ __attribute__((always_inline)) void pair_compute_sample(const FusedParams& P, int item, int c, int lo,
+                                                                   int parity, const RawPair<E, PER>& raw,
+                                                                   uint64_t* w1, NormMsg* msg) {
   const VerifyArgs& a = P.a;
-  const int G = a.gamma, K = P.K;
-  const int b = item / G, i = item % G;
   const float k = a.k;
-  const int lo = rank * P.tile;
 
   float ep[PER], eq[PER];
   unpack_tile<E, PER>(raw.p, lo, a.V, ep);
   unpack_tile<E, PER>(raw.q, lo, a.V, eq);
   const float mp = thread_max<PER>(ep), mq = thread_max<PER>(eq);
   const float sp = thread_exp_sum<PER, true>(ep, mp, k), sq = thread_exp_sum<PER, true>(eq, mq, k);
-  const float4 bl = block_lse2(mp, sp, mq, sq, k, lds_f);
-  uint64_t* mine = P.part1 + ((size_t)item * K + rank) * 2;
-  if (threadIdx.x == 0) {
-    st_u64(mine, pack2(bl.x, bl.y));
-    st_u64(mine + 1, pack2(bl.z, bl.w));
+  const float2 lp = wave_lse(mp, sp, k), lq = wave_lse(mq, sq, k);
+  uint64_t* part1 = P.part1 + (size_t)item * P.W * 2;
+  if (wave_lane() == 0) {
+    st_u64(part1 + 2 * c, pack2(lp.x, lp.y));
+    st_u64(part1 + 2 * c + 1, pack2(lq.x, lq.y));
   }
 
-  // wait for the other tiles of this pair; the poll returns their partials
-  if (!gather(P.part1 + (size_t)item * K * 2, 2 * K, w1)) {
-    if (threadIdx.x == 0) st_u64(P.part2 + (size_t)item * K + rank, pack2i(kPoison, 0u));
+  // wave 0 waits for the whole team's partials and forms the normalisers
+  if (threadIdx.x < kWave) {
+    const bool ok = wave_poll(part1, 2 * P.W, w1, nullptr, 0, nullptr);
+    NormMsg m{0.f, 0.f, 0.f, 0.f, 0};
+    if (ok) {
+      const Norm2 n = wave_norm2(w1, P.W, k);
+      m = NormMsg{n.Mp, n.Mq, (float)(1.0 / n.Sp), (float)(1.0 / n.Sq), 1};
+    }
+    if (threadIdx.x == 0) msg[parity] = m;
+  }
+  lds_barrier();
+  const NormMsg m = msg[parity];
+  uint64_t* mine2 = P.part2 + (size_t)item * P.W + c;
+  if (!m.ok) {
+    if (wave_lane() == 0) st_u64(mine2, pack2i(kPoison, 0u));
     return;
   }
-  unpack_part1(w1, K, st1);
-  Norm np, nq;
-  team_norm2(st1, K, k, &np, &nq);
-  const float fp = mp == -INFINITY ? 0.f : fast_exp2((mp - np.M) * k) * np.invS;
-  const float fq = mq == -INFINITY ? 0.f : fast_exp2((mq - nq.M) * k) * nq.invS;
+  const float fp = mp == -INFINITY ? 0.f : fast_exp2((mp - m.Mp) * k) * m.invSp;
+  const float fq = mq == -INFINITY ? 0.f : fast_exp2((mq - m.Mq) * k) * m.invSq;
   float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
   if (fp > 0.f && fq > 0.f) {
     // sum min(ep fp, eq fq) = fq * sum min(ep (fp / fq), eq); ep <= 1, so the
@@ -476,55 +466,121 @@ __device__ __attribute__((always_inline)) void pair_compute_sample(const FusedPa
   }
   const float alpha_t = ((a0 + a1) + (a2 + a3)) * fq;
   const float res_t = fmaxf(sp * fp - alpha_t, 0.f);  // sum max(0, p - q) = sum p - sum min(p, q)
-  const float2 c2 = block_sum2(alpha_t, res_t, lds_f);
-  const float alpha_c = c2.x, res_c = c2.y;
-  if (threadIdx.x == 0) st_u64(P.part2 + (size_t)item * K + rank, pack2(alpha_c, res_c));
+  const float alpha_w = wave_sum(alpha_t), res_w = wave_sum(res_t);
+  if (wave_lane() == 0) st_u64(mine2, pack2(alpha_w, res_w));
 }
 
 // Pair item at T = 0, or a bonus item: one pass, no waiting.
 template <class E, int PER, bool ARGMAX>
-__device__ __attribute__((always_inline)) void single_pass_compute(const FusedParams& P, int item, int rank, const RawPair<E, PER>& raw) {
-  __shared__ float lds_f[2 * kMaxWaves];
-  __shared__ int lds_i[kMaxWaves];
+__device__ __attribute__((always_inline)) void single_pass_compute(const FusedParams& P, int item, int c, int lo,
+                                                                   const RawPair<E, PER>& raw) {
   const VerifyArgs& a = P.a;
-  const int G = a.gamma, K = P.K;
-  const int lo = rank * P.tile;
   uint64_t w0, w1;
   if (item < P.n_pairs) {  // argmax pair
     float xp[PER], xq[PER];
     unpack_tile<E, PER>(raw.p, lo, a.V, xp);
     unpack_tile<E, PER>(raw.q, lo, a.V, xq);
-    const ArgMax ap = block_argmax(thread_argmax<E, PER>(xp, lo), lds_f, lds_i);
-    const ArgMax aq = block_argmax(thread_argmax<E, PER>(xq, lo), lds_f, lds_i);
+    const ArgMax ap = wave_argmax(thread_argmax<E, PER>(xp, lo));
+    const ArgMax aq = wave_argmax(thread_argmax<E, PER>(xq, lo));
     w0 = pack2i(nz_bits(ap.v), (uint32_t)ap.i);
     w1 = pack2i(nz_bits(aq.v), (uint32_t)aq.i);
   } else {
     float x[PER];
     unpack_tile<E, PER>(raw.p, lo, a.V, x);
     if constexpr (ARGMAX) {
-      const ArgMax ab = block_argmax(thread_argmax<E, PER>(x, lo), lds_f, lds_i);
+      const ArgMax ab = wave_argmax(thread_argmax<E, PER>(x, lo));
       w0 = pack2i(nz_bits(ab.v), (uint32_t)ab.i);
     } else {
       const float m = thread_max<PER>(x);
       const float sm = thread_exp_sum<PER, false>(x, m, a.k);
-      const float4 bl = block_lse2(m, sm, -INFINITY, 0.f, a.k, lds_f);
-      w0 = pack2(bl.x, bl.y);
+      const float2 l = wave_lse(m, sm, a.k);
+      w0 = pack2(l.x, l.y);
     }
     w1 = pack2i(0x80000000u, 0u);  // unused second word: (-0, 0), published
   }
-  if (threadIdx.x == 0) {
-    uint64_t* mine = P.part1 + ((size_t)item * K + rank) * 2;
+  if (wave_lane() == 0) {
+    uint64_t* mine = P.part1 + ((size_t)item * P.W + c) * 2;
     st_u64(mine, w0);
     st_u64(mine + 1, w1);
   }
 }
 
+// Wait until this wave's vector memory operations are complete (vmcnt(0);
+// the other counters are left alone).
+__device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// bf16 compute loop with the next item staged in LDS.  Waves 1..3 copy the
+// next item's tiles (all four waves' tiles) from HBM straight into LDS while
+// the current item is computed from registers; wave 0 issues no global loads,
+// so its polls of the exchange slots never wait behind them (vector memory
+// operations of a wave complete in order).  Per item:
+//   every wave copies its raw vectors from the stage; barrier (stage free);
+//   waves 1..3 start the next item's copy; compute; waves 1..3 wait for their
+//   copies; barrier (stage full).
+// Each of the 2 * 4 * NS wave loads of an item moves 1 KiB of one row into
+// 1 KiB of LDS, lane l writing bytes [16 l, 16 l + 16).
+template <int PER>
+constexpr int stage_vectors() { return 2 * kWavesPerGroup * (PER / BF16::kVec) * kWave; }
+
+template <int PER, bool ARGMAX>
+__device__ __attribute__((always_inline)) void compute_loop_staged(const FusedParams& P, int team, int rank,
+                                                                   u32x4* stage, uint64_t* w1, NormMsg* msg) {
+  using E = BF16;
+  constexpr int NS = PER / E::kVec;
+  constexpr int kLoads = 2 * kWavesPerGroup * NS;
+  const VerifyArgs& a = P.a;
+  const int wave = threadIdx.x / kWave, lane = wave_lane();
+  const int c = rank * kWavesPerGroup + wave;
+  const int lo = c * kWave * PER;
+
+  auto issue = [&](int item) {  // waves 1..3
+    const bool pair = item < P.n_pairs;
+    const int b = pair ? item / a.gamma : item - P.n_pairs;
+    const int i = pair ? item % a.gamma : a.gamma;
+    const E::storage* prow = trow<E>(a, b, i);
+    const E::storage* qrow = pair ? drow<E>(a, b, i) : prow;
+    const int n = pair ? kLoads : kLoads / 2;
+    for (int l = wave - 1; l < n; l += kWavesPerGroup - 1) {
+      const int r = l / (kWavesPerGroup * NS), w = (l / NS) % kWavesPerGroup, v = l % NS;
+      const int j0 = (rank * kWavesPerGroup + w) * kWave * PER + (v * kWave + lane) * E::kVec;
+      const E::storage* src = (r == 0 ? prow : qrow) + min(j0, a.V - E::kVec);
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)&stage[l * kWave], 16, 0, 0);
+    }
+  };
+
+  int item = team;
+  if (wave != 0 && item < P.n_items) issue(item);
+  if (wave != 0) wait_vmem();
+  lds_barrier();
+  int parity = 0;
+  while (item < P.n_items) {
+    RawPair<E, PER> A;
+#pragma unroll
+    for (int v = 0; v < NS; ++v) {
+      A.p.v[v] = stage[(wave * NS + v) * kWave + lane];
+      A.q.v[v] = stage[((kWavesPerGroup + wave) * NS + v) * kWave + lane];
+    }
+    lds_barrier();
+    const int next = item + P.nteams;
+    if (wave != 0 && next < P.n_items) issue(next);
+    if (!ARGMAX && item < P.n_pairs) {
+      pair_compute_sample<E, PER>(P, item, c, lo, parity, A, w1, msg);
+      parity ^= 1;
+    } else {
+      single_pass_compute<E, PER, ARGMAX>(P, item, c, lo, A);
+    }
+    if (wave != 0) wait_vmem();
+    lds_barrier();
+    item = next;
+  }
+}
+
 // ---------------------------------------------------- finisher workgroups
 
-// Combine K argmax partials (value, index) in tile order.
-__device__ inline ArgMax combine_argmax(const uint64_t* w, int K, int half) {
+// Combine W argmax partials (value, index) in tile order.
+__device__ inline ArgMax combine_argmax(const uint64_t* w, int W, int half) {
   ArgMax g{-INFINITY, 0x7fffffff};
-  for (int c = 0; c < K; ++c) {
+  for (int c = 0; c < W; ++c) {
     const uint64_t v = w[2 * c + half];
     g = argmax_better(g, ArgMax{lo_f(v), (int)(uint32_t)(v >> 32)});
   }
@@ -534,31 +590,34 @@ __device__ inline ArgMax combine_argmax(const uint64_t* w, int K, int half) {
 // Pair item: alpha, the ratio test and, after a rejection, the residual
 // sample.  Publishes (accept, token) for the sequence's bonus finisher.
 template <class E, int PER, bool ARGMAX>
-__device__ void finish_pair(const FusedParams& P, int item) {
+__device__ void finish_pair(const FusedParams& P, int item, uint64_t* w1, uint64_t* w2) {
+  constexpr int kSearchPer = kWave * PER / kThreads;  // tokens per thread in a one-tile search
   __shared__ float lds_f[kMaxWaves];
   __shared__ int lds_i[kMaxWaves];
-  __shared__ uint64_t w1[2 * kMaxTeam], w2[kMaxTeam];
-  __shared__ float4 st1[kMaxTeam];
   __shared__ int tile_s, acc_s;
   __shared__ float rest_s;
+  __shared__ float Mp_s, Mq_s;
+  __shared__ double Sp_s, Sq_s, alpha_s, sw_s;
   const VerifyArgs& a = P.a;
-  const int G = a.gamma, K = P.K;
+  const int G = a.gamma, W = P.W;
   const int b = item / G, i = item % G;
   const float k = a.k;
   const auto* prow = trow<E>(a, b, i);
   const auto* qrow = drow<E>(a, b, i);
   const size_t o = (size_t)b * G + i;
+  uint64_t* part1 = P.part1 + (size_t)item * W * 2;
+  uint64_t* part2 = P.part2 + (size_t)item * W;
 
   if constexpr (ARGMAX) {
-    if (!gather(P.part1 + (size_t)item * K * 2, 2 * K, w1)) {
+    if (!gather(part1, 2 * W, w1)) {
       if (threadIdx.x == 0) st_u64(P.pair_res + item, pack2i(kPoison, 0u));
       return;
     }
-    clear_slots(P.part1 + (size_t)item * K * 2, 2 * K);
+    clear_slots(part1, 2 * W);
     if (threadIdx.x == 0) {
       // keep x iff it is the target's argmax; alpha is the indicator that the
       // two argmaxes agree ([FI] "Speculative sampling", temperature to zero)
-      const ArgMax gp = combine_argmax(w1, K, 0), gq = combine_argmax(w1, K, 1);
+      const ArgMax gp = combine_argmax(w1, W, 0), gq = combine_argmax(w1, W, 1);
       const int x = a.tokens[o];
       if (a.alpha) a.alpha[o] = gp.i == gq.i ? 1.f : 0.f;
       if (a.p_draft) a.p_draft[o] = x == gp.i ? 1.f : 0.f;
@@ -577,39 +636,42 @@ __device__ void finish_pair(const FusedParams& P, int item) {
         lq = E::at(qrow, x);
       }
     }
-    // part2 is published after part1 by every tile; polling both in one pass
+    // part2 is published after part1 by every wave; polling both in one pass
     // returns once both are complete
-    if (!gather2(P.part1 + (size_t)item * K * 2, 2 * K, w1, P.part2 + (size_t)item * K, K, w2)) {
+    if (!gather2(part1, 2 * W, w1, part2, W, w2)) {
       if (threadIdx.x == 0) st_u64(P.pair_res + item, pack2i(kPoison, 0u));
       return;
     }
-    // every member has published part2, so every member is done reading part1
-    clear_slots(P.part1 + (size_t)item * K * 2, 2 * K);
-    clear_slots(P.part2 + (size_t)item * K, K);
-    unpack_part1(w1, K, st1);
-    Norm np, nq;
-    team_norm2(st1, K, k, &np, &nq);
-    // alpha and the residual mass (wave 0, fixed order), and the tile holding
-    // u * mass, found with a wave-wide prefix scan of the tile masses
-    __shared__ double alpha_s, sw_s;
+    // every wave has published part2, so every wave is done reading part1
+    clear_slots(part1, 2 * W);
+    clear_slots(part2, W);
+    // normalisers, alpha and the residual mass (wave 0, fixed order)
     if (threadIdx.x < kWave) {
+      const Norm2 n = wave_norm2(w1, W, k);
       double al = 0.0, sw = 0.0;
-      for (int c = threadIdx.x; c < K; c += kWave) {
+      for (int c = threadIdx.x; c < W; c += kWave) {
         al += (double)lo_f(w2[c]);
         sw += (double)hi_f(w2[c]);
       }
       al = wave_sum(al);
       sw = wave_sum(sw);
       if (threadIdx.x == 0) {
+        Mp_s = n.Mp;
+        Mq_s = n.Mq;
+        Sp_s = n.Sp;
+        Sq_s = n.Sq;
         alpha_s = al;
         sw_s = sw;
       }
     }
+    __syncthreads();
+    const float Mp = Mp_s, Mq = Mq_s;
+    const double Sp = Sp_s, Sq = Sq_s;
     if (threadIdx.x == 0) {
       double px = 0.0, qx = 0.0;
       if (x >= 0 && x < a.V) {
-        px = exp2(((double)lp - (double)np.M) * (double)k) / np.S;
-        qx = exp2(((double)lq - (double)nq.M) * (double)k) / nq.S;
+        px = exp2(((double)lp - (double)Mp) * (double)k) / Sp;
+        qx = exp2(((double)lq - (double)Mq) * (double)k) / Sq;
       }
       // accept iff u <= min(1, p(x) / q(x)) ([FI] Algorithm 1 step 3; [SD]
       // "The algorithm").  q(x) = 0 keeps the draft when p(x) > 0 (the ratio
@@ -623,33 +685,31 @@ __device__ void finish_pair(const FusedParams& P, int item) {
       }
       if (a.p_draft) a.p_draft[o] = (float)px;
       if (a.q_draft) a.q_draft[o] = (float)qx;
+      if (a.alpha) a.alpha[o] = (float)alpha_s;
     }
     __syncthreads();
-    if (threadIdx.x == 0 && a.alpha) a.alpha[o] = (float)alpha_s;
     const int acc_i = acc_s;
     int mode = 0;
     if (!acc_i) {
       const double uf = (double)a.uniforms[(size_t)b * (G + 1) + G];
       if (sw_s > 0.0) {
         mode = 1;  // residual max(0, p_i - q_i) ([FI] eq. (2); [SD] "Exactness")
-        wave_pick_tile(K, uf * sw_s, [&](int c) { return (double)hi_f(w2[c]); }, &tile_s, &rest_s);
+        wave_pick_tile(W, uf * sw_s, [&](int c) { return (double)hi_f(w2[c]); }, &tile_s, &rest_s);
       } else {
         mode = 2;  // no residual mass: sample p_i itself
-        wave_pick_tile(K, uf * np.S, [&](int c) {
-          return st1[c].x == -INFINITY ? 0.0 : (double)st1[c].y * (double)fast_exp2((st1[c].x - np.M) * k);
-        }, &tile_s, &rest_s);
+        wave_pick_tile(W, uf * Sp, [&](int c) { return p_tile_mass(w1, c, Mp, k); }, &tile_s, &rest_s);
       }
     }
     int t = 0;
     if (mode) {
-      const float Mp = np.M, invSp = np.invS, Mq = nq.M, invSq = nq.invS;
-      const int tlo = tile_s * P.tile;
+      const float invSp = (float)(1.0 / Sp), invSq = (float)(1.0 / Sq);
+      const int tlo = tile_s * kWave * PER;
       if (mode == 1)
-        t = tile_search<E, PER, kThreads>(prow, qrow, tlo, a.V, rest_s, [&](float xp, float xq) {
+        t = tile_search<E, kSearchPer, kThreads>(prow, qrow, tlo, a.V, rest_s, [&](float xp, float xq) {
           return fmaxf(fast_exp2((xp - Mp) * k) * invSp - fast_exp2((xq - Mq) * k) * invSq, 0.f);
         }, lds_f, lds_i);
       else
-        t = tile_search<E, PER, kThreads>(prow, nullptr, tlo, a.V, rest_s, [&](float xp, float) {
+        t = tile_search<E, kSearchPer, kThreads>(prow, nullptr, tlo, a.V, rest_s, [&](float xp, float) {
           return fast_exp2((xp - Mp) * k);
         }, lds_f, lds_i);
     }
@@ -660,36 +720,40 @@ __device__ void finish_pair(const FusedParams& P, int item) {
 // Bonus item: the token from p_gamma ([FI] Algorithm 1 step 4), then the
 // sequence's outputs once every pair result of the sequence is published.
 template <class E, int PER, bool ARGMAX>
-__device__ void finish_bonus(const FusedParams& P, int item) {
+__device__ void finish_bonus(const FusedParams& P, int item, uint64_t* w1, uint64_t* res) {
+  constexpr int kSearchPer = kWave * PER / kThreads;
   __shared__ float lds_f[kMaxWaves];
   __shared__ int lds_i[kMaxWaves];
-  __shared__ uint64_t w1[2 * kMaxTeam], res[SPEC_MAX_GAMMA];
-  __shared__ float4 st1[kMaxTeam];
   __shared__ int tile_s;
-  __shared__ float rest_s;
+  __shared__ float rest_s, M_s;
+  __shared__ double S_s;
   const VerifyArgs& a = P.a;
-  const int G = a.gamma, K = P.K;
+  const int G = a.gamma, W = P.W;
   const int b = item - P.n_pairs;
   const float k = a.k;
   const auto* row = trow<E>(a, b, G);
-  const bool ok1 = gather(P.part1 + (size_t)item * K * 2, 2 * K, w1);
-  if (ok1) clear_slots(P.part1 + (size_t)item * K * 2, 2 * K);
+  uint64_t* part1 = P.part1 + (size_t)item * W * 2;
+  const bool ok1 = gather(part1, 2 * W, w1);
+  if (ok1) clear_slots(part1, 2 * W);
   int t_bonus = -1;
   if (!ok1) {
   } else if constexpr (ARGMAX) {
-    t_bonus = combine_argmax(w1, K, 0).i;
+    t_bonus = combine_argmax(w1, W, 0).i;
   } else {
-    unpack_part1(w1, K, st1);
-    Norm n, unused;
-    team_norm2(st1, K, k, &n, &unused);
+    if (threadIdx.x < kWave) {
+      const Norm2 n = wave_norm2(w1, W, k);
+      if (threadIdx.x == 0) {
+        M_s = n.Mp;
+        S_s = n.Sp;
+      }
+    }
+    __syncthreads();
+    const float M = M_s;
     const double uf = (double)a.uniforms[(size_t)b * (G + 1) + G];
-    wave_pick_tile(K, uf * n.S, [&](int c) {
-      return st1[c].x == -INFINITY ? 0.0 : (double)st1[c].y * (double)fast_exp2((st1[c].x - n.M) * k);
-    }, &tile_s, &rest_s);
-    const float M = n.M;
-    t_bonus = tile_search<E, PER, kThreads>(row, nullptr, tile_s * P.tile, a.V, rest_s,
-                                            [&](float xp, float) { return fast_exp2((xp - M) * k); }, lds_f,
-                                            lds_i);
+    wave_pick_tile(W, uf * S_s, [&](int c) { return p_tile_mass(w1, c, M, k); }, &tile_s, &rest_s);
+    t_bonus = tile_search<E, kSearchPer, kThreads>(row, nullptr, tile_s * kWave * PER, a.V, rest_s,
+                                                   [&](float xp, float) { return fast_exp2((xp - M) * k); },
+                                                   lds_f, lds_i);
   }
   // the sequence's pair results (published by other finishers)
   const bool ok2 = gather(P.pair_res + (size_t)b * G, G, res);
@@ -709,81 +773,84 @@ __device__ void finish_bonus(const FusedParams& P, int item) {
 
 // --------------------------------------------------------------- the kernel
 
-template <class E, int PER, bool ARGMAX>
-__device__ __attribute__((always_inline)) void compute_item(const FusedParams& P, int item, int rank, const RawPair<E, PER>& raw) {
-  if (!ARGMAX && item < P.n_pairs)
-    pair_compute_sample<E, PER>(P, item, rank, raw);
-  else
-    single_pass_compute<E, PER, ARGMAX>(P, item, rank, raw);
-}
+// LDS of one workgroup.  Region A is the bf16 stage on a compute workgroup and
+// the finisher's copies of an item's slots on a finisher (a workgroup is one
+// or the other); the compute workgroup's poll buffer and normaliser messages
+// follow it.
+template <class E, int PER>
+struct Pool {
+  static constexpr bool kStaged = std::is_same<E, BF16>::value && SPECV_FUSED_STAGE;
+  static constexpr int kFinBytes = (3 * kMaxWaveTiles + SPEC_MAX_GAMMA) * 8;
+  static constexpr int kStageBytes = kStaged ? stage_vectors<PER>() * 16 : 0;
+  static constexpr int kABytes = kStageBytes > kFinBytes ? kStageBytes : kFinBytes;
+  static constexpr int kBytes = kABytes + 2 * kMaxWaveTiles * 8 + 2 * (int)sizeof(NormMsg);
+};
 
 template <class E, int PER, bool ARGMAX>
-__global__ __launch_bounds__(kThreads) void fused_kernel(FusedParams P) {
+__global__ __launch_bounds__(kThreads, SPECV_FUSED_MIN_WAVES) void fused_kernel(FusedParams P) {
+  using L = Pool<E, PER>;
+  __shared__ __align__(16) unsigned char pool[L::kBytes];
+  uint64_t* poll_buf = reinterpret_cast<uint64_t*>(pool + L::kABytes);
+  NormMsg* msg = reinterpret_cast<NormMsg*>(pool + L::kABytes + 2 * kMaxWaveTiles * 8);
+  uint64_t* fin_w1 = reinterpret_cast<uint64_t*>(pool);
+  uint64_t* fin_w2 = fin_w1 + 2 * kMaxWaveTiles;
+  uint64_t* fin_res = fin_w2 + kMaxWaveTiles;
   const int ncompute = P.nteams * P.K;
   if ((int)blockIdx.x < ncompute) {
     const int team = blockIdx.x / P.K, rank = blockIdx.x % P.K;
-#if SPECV_FUSED_PREFETCH
-    // two register buffers: the next item's loads are in flight while this
-    // item is computed
-    RawPair<E, PER> A, B;
-    int item = team;
-    if (item < P.n_items) issue_item<E, PER>(P, item, rank, A);
-    while (item < P.n_items) {
-      int next = item + P.nteams;
-      if (next < P.n_items) issue_item<E, PER>(P, next, rank, B);
-      compute_item<E, PER, ARGMAX>(P, item, rank, A);
-      item = next;
-      if (item >= P.n_items) break;
-      next = item + P.nteams;
-      if (next < P.n_items) issue_item<E, PER>(P, next, rank, A);
-      compute_item<E, PER, ARGMAX>(P, item, rank, B);
-      item = next;
+    if constexpr (L::kStaged) {
+      compute_loop_staged<PER, ARGMAX>(P, team, rank, reinterpret_cast<u32x4*>(pool), poll_buf, msg);
+    } else {
+      const int c = rank * kWavesPerGroup + (int)threadIdx.x / kWave;  // this wave's tile
+      const int lo = c * kWave * PER;
+      int parity = 0;
+      for (int item = team; item < P.n_items; item += P.nteams) {
+        RawPair<E, PER> A;
+        issue_item<E, PER>(P, item, lo, A);
+        if (!ARGMAX && item < P.n_pairs) {
+          pair_compute_sample<E, PER>(P, item, c, lo, parity, A, poll_buf, msg);
+          parity ^= 1;
+        } else {
+          single_pass_compute<E, PER, ARGMAX>(P, item, c, lo, A);
+        }
+      }
     }
-#else
-    for (int item = team; item < P.n_items; item += P.nteams) {
-      RawPair<E, PER> A;
-      issue_item<E, PER>(P, item, rank, A);
-      compute_item<E, PER, ARGMAX>(P, item, rank, A);
-    }
-#endif
   } else {
     // pairs precede bonus items in the item order, so a finisher never waits
     // on an item it has yet to finish itself
     for (int item = blockIdx.x - ncompute; item < P.n_items; item += P.nfin) {
       if (item < P.n_pairs)
-        finish_pair<E, PER, ARGMAX>(P, item);
+        finish_pair<E, PER, ARGMAX>(P, item, fin_w1, fin_w2);
       else
-        finish_bonus<E, PER, ARGMAX>(P, item);
+        finish_bonus<E, PER, ARGMAX>(P, item, fin_w1, fin_res);
     }
   }
 }
 
 constexpr int kFinisherDiv = SPECV_FUSED_FIN_DIV;
+constexpr int kPer = SPECV_FUSED_PER;
+static_assert(kPer % 8 == 0 && (kWave * kPer) % kThreads == 0, "tile shape");
 
-template <class E>
-constexpr int per_thread() {
-  return SPECV_FUSED_PER;
+// Workgroups per team and wave-tile slots per row for a row of V tokens.
+int groups_for(int V) {
+  const int group_tokens = kThreads * kPer;
+  return (V + group_tokens - 1) / group_tokens;
 }
 
-int tiles_for(int V, int dtype) {
-  const int tile = kThreads * (dtype == SPEC_BF16 ? per_thread<BF16>() : per_thread<F32>());
-  return (V + tile - 1) / tile;
-}
-
-// Slot layout.  The size does not depend on the dtype (both use the larger
-// tile count), so one zeroed workspace serves calls of either dtype.
+// Slot layout; the same for both dtypes, so one zeroed workspace serves calls
+// of either.
 struct Layout {
   size_t off_part1, off_part2, off_res, total;
 };
 
 Layout layout(int B, int gamma, int V) {
-  const size_t K = std::max(tiles_for(V, SPEC_BF16), tiles_for(V, SPEC_F32));
+  const size_t W = (size_t)groups_for(V) * kWavesPerGroup;
   const size_t n_items = (size_t)B * (gamma + 1), n_pairs = (size_t)B * gamma;
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   Layout L{};
   L.off_part1 = 0;
-  L.off_part2 = up(L.off_part1 + 16 * n_items * K);
-  L.off_res = up(L.off_part2 + 8 * n_pairs * K);
+  L.off_part2 = up(L.off_part1 + 16 * n_items * W);
+  L.off_res = up(L.off_part2 + 8 * n_pairs * W);
   L.total = up(L.off_res + 8 * n_pairs);
   return L;
 }
@@ -801,20 +868,19 @@ hipError_t resident_blocks(Kern kern, long* out) {
 
 template <class E, bool ARGMAX>
 hipError_t launch(const VerifyArgs& a, hipStream_t s) {
-  constexpr int PER = per_thread<E>();
   const Layout L = layout(a.B, a.gamma, a.V);
   char* ws = static_cast<char*>(a.ws);
   FusedParams P{};
   P.a = a;
-  P.tile = kThreads * PER;
-  P.K = (a.V + P.tile - 1) / P.tile;
+  P.K = groups_for(a.V);
+  P.W = P.K * kWavesPerGroup;
   P.n_pairs = a.B * a.gamma;
   P.n_items = a.B * (a.gamma + 1);
   P.part1 = reinterpret_cast<uint64_t*>(ws + L.off_part1);
   P.part2 = reinterpret_cast<uint64_t*>(ws + L.off_part2);
   P.pair_res = reinterpret_cast<uint64_t*>(ws + L.off_res);
 
-  auto kern = fused_kernel<E, PER, ARGMAX>;
+  auto kern = fused_kernel<E, kPer, ARGMAX>;
   long resident = 0;
   hipError_t e = resident_blocks(kern, &resident);
   if (e != hipSuccess) return e;
@@ -823,7 +889,6 @@ hipError_t launch(const VerifyArgs& a, hipStream_t s) {
   P.nfin = (int)std::min<long>(P.n_items, std::max<long>(1, resident / kFinisherDiv));
   P.nteams = (int)std::min<long>(P.n_items, (resident - P.nfin) / P.K);
   if (P.nteams < 1) return hipErrorNotSupported;
-
   kern<<<dim3(P.nteams * P.K + P.nfin), dim3(kThreads), 0, s>>>(P);
   return hipGetLastError();
 }
@@ -834,7 +899,8 @@ size_t fused_workspace_bytes(int B, int gamma, int V) { return layout(B, gamma, 
 
 bool fused_supported(int B, int gamma, int V, int dtype) {
   const int vec = dtype == SPEC_BF16 ? BF16::kVec : F32::kVec;
-  return B >= 1 && V % vec == 0 && tiles_for(V, dtype) <= kMaxTeam && (size_t)B * (gamma + 1) < (1u << 30);
+  return B >= 1 && V % vec == 0 && groups_for(V) * kWavesPerGroup <= kMaxWaveTiles &&
+         (size_t)B * (gamma + 1) < (1u << 30);
 }
 
 hipError_t fused_launch(const VerifyArgs& a, hipStream_t s) {
