@@ -18,9 +18,12 @@
  *   - Argument errors are detected on the host before anything is queued.
  *     Nothing is written in that case.  A HIP launch failure returns SPEC_EHIP.
  *   - Logits must be finite or -inf (-inf means probability 0, for example a
- *     token masked out before sampling).  Every row needs at least one finite
- *     logit.  +inf or NaN logits, and rows with no finite logit, are caller
- *     errors.  The results are then undefined but the kernels still terminate.
+ *     token masked out before sampling), and at T > 0 every finite logit l
+ *     must keep l * log2(e) / T finite in fp32 (the scaled logit the softmax
+ *     is taken of).  Every row needs at least one finite logit.  +inf or NaN
+ *     logits, scaled logits that overflow, and rows with no finite logit are
+ *     caller errors.  The results are then undefined but the kernels still
+ *     terminate.
  *   - Outputs are deterministic: the same inputs give bit-identical outputs.
  *   - Workspace: the caller zero-fills it once before its first use (for
  *     example torch.zeros).  Every call that completes leaves it all-zero

@@ -15,8 +15,8 @@
 // barrier once per pair item and never otherwise.
 //
 // Pair item, T > 0 (the only place a compute workgroup waits):
-//   1. Load the wave tile of both rows.  Keep e = exp2((l - m_t) k) per token
-//      in registers (m_t = the thread's maximum; k = log2(e) / T).
+//   1. Load the wave tile of both rows.  Keep e = exp2(l k - c_t) per token
+//      in registers (c_t = the thread's maximum times k; k = log2(e) / T).
 //   2. Publish the wave's (max, sum) of both rows.
 //   3. Wave 0 waits until all 4K waves of the team have published, combines
 //      the partials in one fixed order and hands both row normalisers to the
@@ -71,6 +71,15 @@ namespace {
 #ifndef SPECV_FUSED_STAGE
 #define SPECV_FUSED_STAGE 1
 #endif
+// Place each compute team's workgroups on one XCD (workgroups are dispatched
+// to the 8 XCDs round-robin by index), and poll a team's partials through that
+// XCD's L2 before falling back to device-scope polls.
+#ifndef SPECV_FUSED_XCD_TEAMS
+#define SPECV_FUSED_XCD_TEAMS 0
+#endif
+#ifndef SPECV_FUSED_L2_POLL
+#define SPECV_FUSED_L2_POLL 0
+#endif
 // Minimum waves per SIMD the register allocation must allow (1: no limit).
 #ifndef SPECV_FUSED_MIN_WAVES
 #define SPECV_FUSED_MIN_WAVES 1
@@ -97,6 +106,7 @@ struct FusedParams {
   int n_items;    // B * (gamma + 1): pairs, then one bonus item per sequence
   int nteams;     // compute teams
   int nfin;       // finisher workgroups
+  int xcd_teams;  // nonzero: team t lives on XCD t % 8 (grid = 8 * per-XCD share)
   uint64_t* part1;     // [n_items][W][2]  (max, sum) of p and q, or argmax (value, index)
   uint64_t* part2;     // [n_pairs][W]     (overlap share, residual mass share)
   uint64_t* pair_res;  // [n_pairs]        (accept flag | kResMark, sampled token)
@@ -132,6 +142,15 @@ __device__ inline void st_u64(uint64_t* p, uint64_t v) {
 __device__ inline uint64_t ld_u64(const uint64_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// 64-bit load through this XCD's L2 (sc0: bypasses only the CU's L1).  It sees
+// every store made through the same L2; a store from another XCD may stay
+// invisible to it, so a poll built on it falls back to ld_u64.
+__device__ inline uint64_t ld_u64_l2(const uint64_t* base, int idx) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint64_t*>(base), (short)0, 0x7fffffff, 0x00020000);
+  return __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(r, idx * 8, 0, 1));
+}
+constexpr unsigned kL2Polls = 64;
 
 // Workgroup barrier for LDS data only: the fences order LDS accesses, so the
 // barrier waits for this wave's LDS operations but not for its outstanding
@@ -146,6 +165,7 @@ __device__ inline void lds_barrier() {
 // copies them to lds[0..n).  Returns true, uniformly over the wave, if all
 // arrived and none is poisoned.  Gives up after kSpinIters polls, so the
 // kernel always terminates.  Called by all lanes of one wave.
+template <bool L2FIRST = false>
 __device__ inline bool wave_poll(const uint64_t* a, int na, uint64_t* la, const uint64_t* b, int nb,
                                  uint64_t* lb) {
   const int lane = threadIdx.x & (kWave - 1), n = na + nb;
@@ -155,7 +175,7 @@ __device__ inline bool wave_poll(const uint64_t* a, int na, uint64_t* la, const 
     while (true) {
       uint64_t v = pack2i(1u, 0u);
       if (c < na) {
-        v = ld_u64(a + c);
+        v = (L2FIRST && it < kL2Polls) ? ld_u64_l2(a, c) : ld_u64(a + c);
         la[c] = v;
       } else if (c < n) {
         v = ld_u64(b + (c - na));
@@ -261,16 +281,23 @@ __device__ inline float thread_max(const float (&x)[PER]) {
   return fmaxf(m0, m1);
 }
 
-// sum_i exp2((x_i - m) k) over four independent accumulators.  With KEEP the
-// exponentials replace x in place.  m == -inf (no finite logit) gives 0.
+// Exponents are kept in the scaled domain y = l * k (k = log2(e) / T): a
+// maximum m becomes c = m * k, rounded once, and a token's weight relative to
+// it is exp2(fma(l, k, -c)) -- one instruction for the argument.  Every later
+// combination subtracts the same rounded c values, so that rounding cancels
+// exactly.  This needs l * k finite for every logit (|l| log2(e) / T below
+// FLT_MAX), which holds whenever l / T is representable at all.
+
+// sum_i exp2(l_i k - c) over four independent accumulators.  With KEEP the
+// weights replace x in place.  c == -inf (no finite logit) gives 0.
 template <int PER, bool KEEP>
-__device__ inline float thread_exp_sum(float (&x)[PER], float m, float k) {
+__device__ inline float thread_exp_sum(float (&x)[PER], float c, float k) {
   float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
-  if (m != -INFINITY) {
+  if (c != -INFINITY) {
 #pragma unroll
     for (int i = 0; i < PER; i += 4) {
-      const float e0 = fast_exp2((x[i] - m) * k), e1 = fast_exp2((x[i + 1] - m) * k);
-      const float e2 = fast_exp2((x[i + 2] - m) * k), e3 = fast_exp2((x[i + 3] - m) * k);
+      const float e0 = fast_exp2(fmaf(x[i], k, -c)), e1 = fast_exp2(fmaf(x[i + 1], k, -c));
+      const float e2 = fast_exp2(fmaf(x[i + 2], k, -c)), e3 = fast_exp2(fmaf(x[i + 3], k, -c));
       if (KEEP) {
         x[i] = e0;
         x[i + 1] = e1;
@@ -289,12 +316,12 @@ __device__ inline float thread_exp_sum(float (&x)[PER], float m, float k) {
   return (s0 + s1) + (s2 + s3);
 }
 
-// The threads' (max m, sum s relative to m) -> the wave's (max, sum relative
-// to that max), identical in every lane.
-__device__ inline float2 wave_lse(float m, float s, float k) {
-  const float M = wave_max(m);
-  const float w = m == -INFINITY ? 0.f : s * fast_exp2((m - M) * k);
-  return make_float2(M, wave_sum(w));
+// The threads' (scaled max c, sum s relative to c) -> the wave's (scaled max,
+// sum relative to it), identical in every lane.
+__device__ inline float2 wave_lse(float c, float s) {
+  const float C = wave_max(c);
+  const float w = c == -INFINITY ? 0.f : s * fast_exp2(c - C);
+  return make_float2(C, wave_sum(w));
 }
 
 template <class E, int PER>
@@ -306,15 +333,15 @@ __device__ inline ArgMax thread_argmax(const float (&x)[PER], int tile_lo) {
 }
 
 // Row normalisers of both rows of an item from its W published word pairs
-// (lds[2c] = (max, sum) of p in wave tile c, lds[2c + 1] the same for q):
-// M = max_c m_c and S = sum_c s_c exp2((m_c - M) k) in fp64, in one fixed
-// order.  Called by all lanes of one wave; every lane gets the result.
+// (lds[2c] = (scaled max, sum) of p in wave tile c, lds[2c + 1] the same for
+// q): M = max_c m_c and S = sum_c s_c exp2(m_c - M) in fp64, in one fixed
+// order; M is in the scaled domain (a logit times k).  Called by all lanes of one wave; every lane gets the result.
 struct Norm2 {
   float Mp, Mq;
   double Sp, Sq;
 };
 
-__device__ inline Norm2 wave_norm2(const uint64_t* w, int W, float k) {
+__device__ inline Norm2 wave_norm2(const uint64_t* w, int W) {
   const int lane = wave_lane();
   float Mp = -INFINITY, Mq = -INFINITY;
   for (int c = lane; c < W; c += kWave) {
@@ -326,16 +353,16 @@ __device__ inline Norm2 wave_norm2(const uint64_t* w, int W, float k) {
   double Sp = 0.0, Sq = 0.0;
   for (int c = lane; c < W; c += kWave) {
     const float mp = lo_f(w[2 * c]), mq = lo_f(w[2 * c + 1]);
-    if (mp != -INFINITY) Sp += (double)hi_f(w[2 * c]) * (double)fast_exp2((mp - Mp) * k);
-    if (mq != -INFINITY) Sq += (double)hi_f(w[2 * c + 1]) * (double)fast_exp2((mq - Mq) * k);
+    if (mp != -INFINITY) Sp += (double)hi_f(w[2 * c]) * (double)fast_exp2(mp - Mp);
+    if (mq != -INFINITY) Sq += (double)hi_f(w[2 * c + 1]) * (double)fast_exp2(mq - Mq);
   }
   return Norm2{Mp, Mq, wave_sum(Sp), wave_sum(Sq)};
 }
 
-// Mass of wave tile c of the p row, relative to the row maximum M.
-__device__ inline double p_tile_mass(const uint64_t* w, int c, float M, float k) {
+// Mass of wave tile c of the p row, relative to the row's scaled maximum M.
+__device__ inline double p_tile_mass(const uint64_t* w, int c, float M) {
   const float m = lo_f(w[2 * c]);
-  return m == -INFINITY ? 0.0 : (double)hi_f(w[2 * c]) * (double)fast_exp2((m - M) * k);
+  return m == -INFINITY ? 0.0 : (double)hi_f(w[2 * c]) * (double)fast_exp2(m - M);
 }
 
 // Tile holding theta among W tile masses in tile order: wave 0 scans the
@@ -423,9 +450,9 @@ __device__ __attribute__((always_inline)) void pair_compute_sample(const FusedPa
   float ep[PER], eq[PER];
   unpack_tile<E, PER>(raw.p, lo, a.V, ep);
   unpack_tile<E, PER>(raw.q, lo, a.V, eq);
-  const float mp = thread_max<PER>(ep), mq = thread_max<PER>(eq);
+  const float mp = thread_max<PER>(ep) * k, mq = thread_max<PER>(eq) * k;  // scaled maxima
   const float sp = thread_exp_sum<PER, true>(ep, mp, k), sq = thread_exp_sum<PER, true>(eq, mq, k);
-  const float2 lp = wave_lse(mp, sp, k), lq = wave_lse(mq, sq, k);
+  const float2 lp = wave_lse(mp, sp), lq = wave_lse(mq, sq);
   uint64_t* part1 = P.part1 + (size_t)item * P.W * 2;
   if (wave_lane() == 0) {
     st_u64(part1 + 2 * c, pack2(lp.x, lp.y));
@@ -434,10 +461,10 @@ __device__ __attribute__((always_inline)) void pair_compute_sample(const FusedPa
 
   // wave 0 waits for the whole team's partials and forms the normalisers
   if (threadIdx.x < kWave) {
-    const bool ok = wave_poll(part1, 2 * P.W, w1, nullptr, 0, nullptr);
+    const bool ok = wave_poll<SPECV_FUSED_L2_POLL != 0>(part1, 2 * P.W, w1, nullptr, 0, nullptr);
     NormMsg m{0.f, 0.f, 0.f, 0.f, 0};
     if (ok) {
-      const Norm2 n = wave_norm2(w1, P.W, k);
+      const Norm2 n = wave_norm2(w1, P.W);
       m = NormMsg{n.Mp, n.Mq, (float)(1.0 / n.Sp), (float)(1.0 / n.Sq), 1};
     }
     if (threadIdx.x == 0) msg[parity] = m;
@@ -449,8 +476,8 @@ __device__ __attribute__((always_inline)) void pair_compute_sample(const FusedPa
     if (wave_lane() == 0) st_u64(mine2, pack2i(kPoison, 0u));
     return;
   }
-  const float fp = mp == -INFINITY ? 0.f : fast_exp2((mp - m.Mp) * k) * m.invSp;
-  const float fq = mq == -INFINITY ? 0.f : fast_exp2((mq - m.Mq) * k) * m.invSq;
+  const float fp = mp == -INFINITY ? 0.f : fast_exp2(mp - m.Mp) * m.invSp;
+  const float fq = mq == -INFINITY ? 0.f : fast_exp2(mq - m.Mq) * m.invSq;
   float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
   if (fp > 0.f && fq > 0.f) {
     // sum min(ep fp, eq fq) = fq * sum min(ep (fp / fq), eq); ep <= 1, so the
@@ -491,9 +518,9 @@ __device__ __attribute__((always_inline)) void single_pass_compute(const FusedPa
       const ArgMax ab = wave_argmax(thread_argmax<E, PER>(x, lo));
       w0 = pack2i(nz_bits(ab.v), (uint32_t)ab.i);
     } else {
-      const float m = thread_max<PER>(x);
+      const float m = thread_max<PER>(x) * a.k;
       const float sm = thread_exp_sum<PER, false>(x, m, a.k);
-      const float2 l = wave_lse(m, sm, a.k);
+      const float2 l = wave_lse(m, sm);
       w0 = pack2(l.x, l.y);
     }
     w1 = pack2i(0x80000000u, 0u);  // unused second word: (-0, 0), published
@@ -529,10 +556,17 @@ __device__ __attribute__((always_inline)) void compute_loop_staged(const FusedPa
   constexpr int NS = PER / E::kVec;
   constexpr int kLoads = 2 * kWavesPerGroup * NS;
   const VerifyArgs& a = P.a;
-  const int wave = threadIdx.x / kWave, lane = wave_lane();
+  // the wave index is uniform across the wave: keep it (and everything derived
+  // from it) in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave), lane = wave_lane();
   const int c = rank * kWavesPerGroup + wave;
   const int lo = c * kWave * PER;
+  const unsigned row_bytes = (unsigned)a.V * (unsigned)sizeof(E::storage);
 
+  // Each copy is one buffer load into LDS: the resource starts at the copy's
+  // first vector and ends at the end of the row, so vectors past V read as
+  // zero (unpack_tile masks them to -inf) and all address arithmetic is
+  // scalar; lane l moves bytes [16 l, 16 l + 16).
   auto issue = [&](int item) {  // waves 1..3
     const bool pair = item < P.n_pairs;
     const int b = pair ? item / a.gamma : item - P.n_pairs;
@@ -542,9 +576,16 @@ __device__ __attribute__((always_inline)) void compute_loop_staged(const FusedPa
     const int n = pair ? kLoads : kLoads / 2;
     for (int l = wave - 1; l < n; l += kWavesPerGroup - 1) {
       const int r = l / (kWavesPerGroup * NS), w = (l / NS) % kWavesPerGroup, v = l % NS;
-      const int j0 = (rank * kWavesPerGroup + w) * kWave * PER + (v * kWave + lane) * E::kVec;
-      const E::storage* src = (r == 0 ? prow : qrow) + min(j0, a.V - E::kVec);
-      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)&stage[l * kWave], 16, 0, 0);
+      const unsigned off = (unsigned)(((rank * kWavesPerGroup + w) * kWave * PER + v * kWave * E::kVec) *
+                                      (int)sizeof(E::storage));
+      const uint64_t addr = reinterpret_cast<uint64_t>(r == 0 ? prow : qrow) + off;
+      const uint64_t uaddr = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(addr >> 32)) << 32) |
+                             (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)addr);
+      const int nrec = __builtin_amdgcn_readfirstlane((int)(off < row_bytes ? row_bytes - off : 0u));
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(uaddr), (short)0, nrec, 0x00020000);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)&stage[l * kWave], 16,
+                                               (unsigned)lane * 16u, 0, 0, 0);
     }
   };
 
@@ -577,6 +618,15 @@ __device__ __attribute__((always_inline)) void compute_loop_staged(const FusedPa
 
 // ---------------------------------------------------- finisher workgroups
 
+// The finisher's inverse-CDF search covers a group of consecutive wave tiles,
+// enough that each of its threads scans at least one whole vector.
+template <class E, int PER>
+struct SearchShape {
+  static constexpr int kGroup = (kThreads * E::kVec) / (kWave * PER) > 1 ? (kThreads * E::kVec) / (kWave * PER) : 1;
+  static constexpr int kTokens = kGroup * kWave * PER;  // tokens per search group
+  static constexpr int kPer = kTokens / kThreads;       // tokens per thread
+};
+
 // Combine W argmax partials (value, index) in tile order.
 __device__ inline ArgMax combine_argmax(const uint64_t* w, int W, int half) {
   ArgMax g{-INFINITY, 0x7fffffff};
@@ -591,7 +641,7 @@ __device__ inline ArgMax combine_argmax(const uint64_t* w, int W, int half) {
 // sample.  Publishes (accept, token) for the sequence's bonus finisher.
 template <class E, int PER, bool ARGMAX>
 __device__ void finish_pair(const FusedParams& P, int item, uint64_t* w1, uint64_t* w2) {
-  constexpr int kSearchPer = kWave * PER / kThreads;  // tokens per thread in a one-tile search
+  using S = SearchShape<E, PER>;
   __shared__ float lds_f[kMaxWaves];
   __shared__ int lds_i[kMaxWaves];
   __shared__ int tile_s, acc_s;
@@ -647,7 +697,7 @@ __device__ void finish_pair(const FusedParams& P, int item, uint64_t* w1, uint64
     clear_slots(part2, W);
     // normalisers, alpha and the residual mass (wave 0, fixed order)
     if (threadIdx.x < kWave) {
-      const Norm2 n = wave_norm2(w1, W, k);
+      const Norm2 n = wave_norm2(w1, W);
       double al = 0.0, sw = 0.0;
       for (int c = threadIdx.x; c < W; c += kWave) {
         al += (double)lo_f(w2[c]);
@@ -670,8 +720,8 @@ __device__ void finish_pair(const FusedParams& P, int item, uint64_t* w1, uint64
     if (threadIdx.x == 0) {
       double px = 0.0, qx = 0.0;
       if (x >= 0 && x < a.V) {
-        px = exp2(((double)lp - (double)Mp) * (double)k) / Sp;
-        qx = exp2(((double)lq - (double)Mq) * (double)k) / Sq;
+        px = exp2((double)lp * (double)k - (double)Mp) / Sp;
+        qx = exp2((double)lq * (double)k - (double)Mq) / Sq;
       }
       // accept iff u <= min(1, p(x) / q(x)) ([FI] Algorithm 1 step 3; [SD]
       // "The algorithm").  q(x) = 0 keeps the draft when p(x) > 0 (the ratio
@@ -692,25 +742,35 @@ __device__ void finish_pair(const FusedParams& P, int item, uint64_t* w1, uint64
     int mode = 0;
     if (!acc_i) {
       const double uf = (double)a.uniforms[(size_t)b * (G + 1) + G];
+      // search groups of S::kGroup consecutive wave tiles, in token order
+      const int ng = (W + S::kGroup - 1) / S::kGroup;
       if (sw_s > 0.0) {
         mode = 1;  // residual max(0, p_i - q_i) ([FI] eq. (2); [SD] "Exactness")
-        wave_pick_tile(W, uf * sw_s, [&](int c) { return (double)hi_f(w2[c]); }, &tile_s, &rest_s);
+        wave_pick_tile(ng, uf * sw_s, [&](int g) {
+          double m = 0.0;
+          for (int c = g * S::kGroup; c < min(W, (g + 1) * S::kGroup); ++c) m += (double)hi_f(w2[c]);
+          return m;
+        }, &tile_s, &rest_s);
       } else {
         mode = 2;  // no residual mass: sample p_i itself
-        wave_pick_tile(W, uf * Sp, [&](int c) { return p_tile_mass(w1, c, Mp, k); }, &tile_s, &rest_s);
+        wave_pick_tile(ng, uf * Sp, [&](int g) {
+          double m = 0.0;
+          for (int c = g * S::kGroup; c < min(W, (g + 1) * S::kGroup); ++c) m += p_tile_mass(w1, c, Mp);
+          return m;
+        }, &tile_s, &rest_s);
       }
     }
     int t = 0;
     if (mode) {
       const float invSp = (float)(1.0 / Sp), invSq = (float)(1.0 / Sq);
-      const int tlo = tile_s * kWave * PER;
+      const int tlo = tile_s * S::kTokens;
       if (mode == 1)
-        t = tile_search<E, kSearchPer, kThreads>(prow, qrow, tlo, a.V, rest_s, [&](float xp, float xq) {
-          return fmaxf(fast_exp2((xp - Mp) * k) * invSp - fast_exp2((xq - Mq) * k) * invSq, 0.f);
+        t = tile_search<E, S::kPer, kThreads>(prow, qrow, tlo, a.V, rest_s, [&](float xp, float xq) {
+          return fmaxf(fast_exp2(fmaf(xp, k, -Mp)) * invSp - fast_exp2(fmaf(xq, k, -Mq)) * invSq, 0.f);
         }, lds_f, lds_i);
       else
-        t = tile_search<E, kSearchPer, kThreads>(prow, nullptr, tlo, a.V, rest_s, [&](float xp, float) {
-          return fast_exp2((xp - Mp) * k);
+        t = tile_search<E, S::kPer, kThreads>(prow, nullptr, tlo, a.V, rest_s, [&](float xp, float) {
+          return fast_exp2(fmaf(xp, k, -Mp));
         }, lds_f, lds_i);
     }
     if (threadIdx.x == 0) st_u64(P.pair_res + item, pack2i((uint32_t)acc_s | kResMark, (uint32_t)t));
@@ -721,7 +781,7 @@ __device__ void finish_pair(const FusedParams& P, int item, uint64_t* w1, uint64
 // sequence's outputs once every pair result of the sequence is published.
 template <class E, int PER, bool ARGMAX>
 __device__ void finish_bonus(const FusedParams& P, int item, uint64_t* w1, uint64_t* res) {
-  constexpr int kSearchPer = kWave * PER / kThreads;
+  using S = SearchShape<E, PER>;
   __shared__ float lds_f[kMaxWaves];
   __shared__ int lds_i[kMaxWaves];
   __shared__ int tile_s;
@@ -741,7 +801,7 @@ __device__ void finish_bonus(const FusedParams& P, int item, uint64_t* w1, uint6
     t_bonus = combine_argmax(w1, W, 0).i;
   } else {
     if (threadIdx.x < kWave) {
-      const Norm2 n = wave_norm2(w1, W, k);
+      const Norm2 n = wave_norm2(w1, W);
       if (threadIdx.x == 0) {
         M_s = n.Mp;
         S_s = n.Sp;
@@ -750,9 +810,13 @@ __device__ void finish_bonus(const FusedParams& P, int item, uint64_t* w1, uint6
     __syncthreads();
     const float M = M_s;
     const double uf = (double)a.uniforms[(size_t)b * (G + 1) + G];
-    wave_pick_tile(W, uf * S_s, [&](int c) { return p_tile_mass(w1, c, M, k); }, &tile_s, &rest_s);
-    t_bonus = tile_search<E, kSearchPer, kThreads>(row, nullptr, tile_s * kWave * PER, a.V, rest_s,
-                                                   [&](float xp, float) { return fast_exp2((xp - M) * k); },
+    wave_pick_tile((W + S::kGroup - 1) / S::kGroup, uf * S_s, [&](int g) {
+      double m = 0.0;
+      for (int c = g * S::kGroup; c < min(W, (g + 1) * S::kGroup); ++c) m += p_tile_mass(w1, c, M);
+      return m;
+    }, &tile_s, &rest_s);
+    t_bonus = tile_search<E, S::kPer, kThreads>(row, nullptr, tile_s * S::kTokens, a.V, rest_s,
+                                                   [&](float xp, float) { return fast_exp2(fmaf(xp, k, -M)); },
                                                    lds_f, lds_i);
   }
   // the sequence's pair results (published by other finishers)
@@ -796,8 +860,23 @@ __global__ __launch_bounds__(kThreads, SPECV_FUSED_MIN_WAVES) void fused_kernel(
   uint64_t* fin_w2 = fin_w1 + 2 * kMaxWaveTiles;
   uint64_t* fin_res = fin_w2 + kMaxWaveTiles;
   const int ncompute = P.nteams * P.K;
-  if ((int)blockIdx.x < ncompute) {
-    const int team = blockIdx.x / P.K, rank = blockIdx.x % P.K;
+  // role of this workgroup: compute (team, rank) or finisher f
+  int team = -1, rank = 0, f = 0;
+  if (P.xcd_teams) {
+    const int x = blockIdx.x % 8, j = blockIdx.x / 8, cpx = ncompute / 8;
+    if (j < cpx) {
+      team = (j / P.K) * 8 + x;
+      rank = j % P.K;
+    } else {
+      f = (j - cpx) * 8 + x;
+    }
+  } else if ((int)blockIdx.x < ncompute) {
+    team = blockIdx.x / P.K;
+    rank = blockIdx.x % P.K;
+  } else {
+    f = blockIdx.x - ncompute;
+  }
+  if (team >= 0) {
     if constexpr (L::kStaged) {
       compute_loop_staged<PER, ARGMAX>(P, team, rank, reinterpret_cast<u32x4*>(pool), poll_buf, msg);
     } else {
@@ -818,7 +897,7 @@ __global__ __launch_bounds__(kThreads, SPECV_FUSED_MIN_WAVES) void fused_kernel(
   } else {
     // pairs precede bonus items in the item order, so a finisher never waits
     // on an item it has yet to finish itself
-    for (int item = blockIdx.x - ncompute; item < P.n_items; item += P.nfin) {
+    for (int item = f; item < P.n_items; item += P.nfin) {
       if (item < P.n_pairs)
         finish_pair<E, PER, ARGMAX>(P, item, fin_w1, fin_w2);
       else
@@ -829,7 +908,7 @@ __global__ __launch_bounds__(kThreads, SPECV_FUSED_MIN_WAVES) void fused_kernel(
 
 constexpr int kFinisherDiv = SPECV_FUSED_FIN_DIV;
 constexpr int kPer = SPECV_FUSED_PER;
-static_assert(kPer % 8 == 0 && (kWave * kPer) % kThreads == 0, "tile shape");
+static_assert(kPer % 8 == 0, "tile shape");
 
 // Workgroups per team and wave-tile slots per row for a row of V tokens.
 int groups_for(int V) {
@@ -888,6 +967,17 @@ hipError_t launch(const VerifyArgs& a, hipStream_t s) {
   // run concurrently and every wait ends.
   P.nfin = (int)std::min<long>(P.n_items, std::max<long>(1, resident / kFinisherDiv));
   P.nteams = (int)std::min<long>(P.n_items, (resident - P.nfin) / P.K);
+  if (SPECV_FUSED_XCD_TEAMS) {
+    // an equal share of teams and finishers on each of the 8 XCDs
+    const long per_xcd = resident / 8, need_x = (P.n_items + 7) / 8;
+    const long fin_x = std::min(need_x, std::max<long>(1, per_xcd / kFinisherDiv));
+    const long teams_x = std::min(need_x, (per_xcd - fin_x) / P.K);
+    if (teams_x >= 1) {
+      P.xcd_teams = 1;
+      P.nteams = (int)(8 * teams_x);
+      P.nfin = (int)(8 * fin_x);
+    }
+  }
   if (P.nteams < 1) return hipErrorNotSupported;
   kern<<<dim3(P.nteams * P.K + P.nfin), dim3(kThreads), 0, s>>>(P);
   return hipGetLastError();
