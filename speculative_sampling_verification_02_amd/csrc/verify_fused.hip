@@ -289,7 +289,11 @@ __device__ inline float thread_max(const float (&x)[PER]) {
 // FLT_MAX), which holds whenever l / T is representable at all.
 
 // sum_i exp2(l_i k - c) over four independent accumulators.  With KEEP the
-// weights replace x in place.  c == -inf (no finite logit) gives 0.
+// weights replace x in place.  c == -inf (no finite logit) gives 0 and leaves
+// x as it is: a caller skips such a thread, whose scale factor is then 0.
+// (Filling x with zeros there costs a register copy per token; a branch-free
+// form that selected the shift instead gave a wrong overlap for f32 tiles at
+// T = 1e-3 on gfx950, so the branch stays.)
 template <int PER, bool KEEP>
 __device__ inline float thread_exp_sum(float (&x)[PER], float c, float k) {
   float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
@@ -309,9 +313,6 @@ __device__ inline float thread_exp_sum(float (&x)[PER], float c, float k) {
       s2 += e2;
       s3 += e3;
     }
-  } else if (KEEP) {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) x[i] = 0.f;
   }
   return (s0 + s1) + (s2 + s3);
 }
@@ -482,6 +483,8 @@ __device__ __attribute__((always_inline)) void pair_compute_sample(const FusedPa
   if (fp > 0.f && fq > 0.f) {
     // sum min(ep fp, eq fq) = fq * sum min(ep (fp / fq), eq); ep <= 1, so the
     // clamp keeps ep * r finite
+    // an exact division: fq can be subnormal at low temperature, where the
+    // hardware reciprocal flushes to zero
     const float r = fminf(fp / fq, FLT_MAX);
 #pragma unroll
     for (int j = 0; j < PER; j += 4) {
