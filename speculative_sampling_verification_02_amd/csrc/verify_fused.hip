@@ -58,10 +58,14 @@
 namespace specv {
 namespace {
 
-// Tokens per thread per row (the wave tile is kWave times this) and the share
-// of resident workgroups that finish items (1 / SPECV_FUSED_FIN_DIV).
-#ifndef SPECV_FUSED_PER
-#define SPECV_FUSED_PER 32
+// Tokens per thread per row for each dtype (the wave tile is kWave times
+// this) and the share of resident workgroups that finish items
+// (1 / SPECV_FUSED_FIN_DIV).
+#ifndef SPECV_FUSED_PER_BF16
+#define SPECV_FUSED_PER_BF16 32
+#endif
+#ifndef SPECV_FUSED_PER_F32
+#define SPECV_FUSED_PER_F32 32
 #endif
 #ifndef SPECV_FUSED_FIN_DIV
 #define SPECV_FUSED_FIN_DIV 8
@@ -79,6 +83,11 @@ namespace {
 #endif
 #ifndef SPECV_FUSED_L2_POLL
 #define SPECV_FUSED_L2_POLL 0
+#endif
+// Keep two bf16 pair items in flight per workgroup (1): phase 1 of one runs
+// while the team exchange of the other completes.
+#ifndef SPECV_FUSED_PIPELINE
+#define SPECV_FUSED_PIPELINE 1
 #endif
 // Minimum waves per SIMD the register allocation must allow (1: no limit).
 #ifndef SPECV_FUSED_MIN_WAVES
@@ -440,28 +449,36 @@ struct NormMsg {
   int ok;
 };
 
-// Pair item, T > 0: the tile stays in registers across the team's one wait.
+// Pair item, T > 0, in three steps.  Phase 1 turns the wave tile into kept
+// weights and publishes the wave's (scaled max, sum) of both rows.
 template <class E, int PER>
-__device__ __attribute__((always_inline)) void pair_compute_sample(const FusedParams& P, int item, int c, int lo,
-                                                                   int parity, const RawPair<E, PER>& raw,
-                                                                   uint64_t* w1, NormMsg* msg) {
+__device__ __attribute__((always_inline)) void pair_phase1(const FusedParams& P, int item, int c, int lo,
+                                                           const RawPair<E, PER>& raw, float (&ep)[PER],
+                                                           float (&eq)[PER], float& mp, float& mq, float& sp) {
   const VerifyArgs& a = P.a;
   const float k = a.k;
-
-  float ep[PER], eq[PER];
   unpack_tile<E, PER>(raw.p, lo, a.V, ep);
   unpack_tile<E, PER>(raw.q, lo, a.V, eq);
-  const float mp = thread_max<PER>(ep) * k, mq = thread_max<PER>(eq) * k;  // scaled maxima
-  const float sp = thread_exp_sum<PER, true>(ep, mp, k), sq = thread_exp_sum<PER, true>(eq, mq, k);
+  mp = thread_max<PER>(ep) * k;  // scaled maxima
+  mq = thread_max<PER>(eq) * k;
+  sp = thread_exp_sum<PER, true>(ep, mp, k);
+  const float sq = thread_exp_sum<PER, true>(eq, mq, k);
   const float2 lp = wave_lse(mp, sp), lq = wave_lse(mq, sq);
   uint64_t* part1 = P.part1 + (size_t)item * P.W * 2;
   if (wave_lane() == 0) {
     st_u64(part1 + 2 * c, pack2(lp.x, lp.y));
     st_u64(part1 + 2 * c + 1, pack2(lq.x, lq.y));
   }
+}
 
-  // wave 0 waits for the whole team's partials and forms the normalisers
+// The team wait: wave 0 polls until every wave of the team has published its
+// phase-1 partials, combines them in one fixed order and hands both row
+// normalisers to the other waves through msg[parity] (one LDS-only barrier).
+// Called by the whole workgroup.
+__device__ __attribute__((always_inline)) inline NormMsg pair_wait(const FusedParams& P, int item, int parity,
+                                                                   uint64_t* w1, NormMsg* msg) {
   if (threadIdx.x < kWave) {
+    const uint64_t* part1 = P.part1 + (size_t)item * P.W * 2;
     const bool ok = wave_poll<SPECV_FUSED_L2_POLL != 0>(part1, 2 * P.W, w1, nullptr, 0, nullptr);
     NormMsg m{0.f, 0.f, 0.f, 0.f, 0};
     if (ok) {
@@ -471,7 +488,15 @@ __device__ __attribute__((always_inline)) void pair_compute_sample(const FusedPa
     if (threadIdx.x == 0) msg[parity] = m;
   }
   lds_barrier();
-  const NormMsg m = msg[parity];
+  return msg[parity];
+}
+
+// Phase 2: the wave's share of alpha = sum min(p, q) and of the residual mass
+// sum max(0, p - q) from the kept weights, published as one word.
+template <int PER>
+__device__ __attribute__((always_inline)) void pair_phase2(const FusedParams& P, int item, int c, const NormMsg& m,
+                                                           const float (&ep)[PER], const float (&eq)[PER],
+                                                           float mp, float mq, float sp) {
   uint64_t* mine2 = P.part2 + (size_t)item * P.W + c;
   if (!m.ok) {
     if (wave_lane() == 0) st_u64(mine2, pack2i(kPoison, 0u));
@@ -482,9 +507,8 @@ __device__ __attribute__((always_inline)) void pair_compute_sample(const FusedPa
   float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
   if (fp > 0.f && fq > 0.f) {
     // sum min(ep fp, eq fq) = fq * sum min(ep (fp / fq), eq); ep <= 1, so the
-    // clamp keeps ep * r finite
-    // an exact division: fq can be subnormal at low temperature, where the
-    // hardware reciprocal flushes to zero
+    // clamp keeps ep * r finite.  An exact division: fq can be subnormal at
+    // low temperature, where the hardware reciprocal flushes to zero.
     const float r = fminf(fp / fq, FLT_MAX);
 #pragma unroll
     for (int j = 0; j < PER; j += 4) {
@@ -498,6 +522,17 @@ __device__ __attribute__((always_inline)) void pair_compute_sample(const FusedPa
   const float res_t = fmaxf(sp * fp - alpha_t, 0.f);  // sum max(0, p - q) = sum p - sum min(p, q)
   const float alpha_w = wave_sum(alpha_t), res_w = wave_sum(res_t);
   if (wave_lane() == 0) st_u64(mine2, pack2(alpha_w, res_w));
+}
+
+// The three steps back to back: the tile stays in registers across the wait.
+template <class E, int PER>
+__device__ __attribute__((always_inline)) void pair_compute_sample(const FusedParams& P, int item, int c, int lo,
+                                                                   int parity, const RawPair<E, PER>& raw,
+                                                                   uint64_t* w1, NormMsg* msg) {
+  float ep[PER], eq[PER], mp, mq, sp;
+  pair_phase1<E, PER>(P, item, c, lo, raw, ep, eq, mp, mq, sp);
+  const NormMsg m = pair_wait(P, item, parity, w1, msg);
+  pair_phase2<PER>(P, item, c, m, ep, eq, mp, mq, sp);
 }
 
 // Pair item at T = 0, or a bonus item: one pass, no waiting.
@@ -597,6 +632,8 @@ __device__ __attribute__((always_inline)) void compute_loop_staged(const FusedPa
   if (wave != 0) wait_vmem();
   lds_barrier();
   int parity = 0;
+  int pend = -1;  // pipelined: the pair item whose kept weights wait in (ep, eq)
+  float ep[PER], eq[PER], mp = 0.f, mq = 0.f, sp = 0.f;
   while (item < P.n_items) {
     RawPair<E, PER> A;
 #pragma unroll
@@ -607,7 +644,39 @@ __device__ __attribute__((always_inline)) void compute_loop_staged(const FusedPa
     lds_barrier();
     const int next = item + P.nteams;
     if (wave != 0 && next < P.n_items) issue(next);
-    if (!ARGMAX && item < P.n_pairs) {
+    if constexpr (!ARGMAX && SPECV_FUSED_PIPELINE) {
+      // Two pair items in flight: phase 1 of this item runs while the team
+      // exchange of the previous one completes, and only then is the previous
+      // one finished.  (Copying the new weights into the pending set costs a
+      // register move per token but needs fewer registers than two sets that
+      // swap roles.)
+      if (item < P.n_pairs) {
+        float xp[PER], xq[PER], cp, cq, s_p;
+        pair_phase1<E, PER>(P, item, c, lo, A, xp, xq, cp, cq, s_p);
+        if (pend >= 0) {
+          const NormMsg m = pair_wait(P, pend, parity, w1, msg);
+          pair_phase2<PER>(P, pend, c, m, ep, eq, mp, mq, sp);
+          parity ^= 1;
+        }
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+          ep[j] = xp[j];
+          eq[j] = xq[j];
+        }
+        mp = cp;
+        mq = cq;
+        sp = s_p;
+        pend = item;
+      } else {
+        single_pass_compute<E, PER, ARGMAX>(P, item, c, lo, A);
+        if (pend >= 0) {
+          const NormMsg m = pair_wait(P, pend, parity, w1, msg);
+          pair_phase2<PER>(P, pend, c, m, ep, eq, mp, mq, sp);
+          parity ^= 1;
+          pend = -1;
+        }
+      }
+    } else if (!ARGMAX && item < P.n_pairs) {
       pair_compute_sample<E, PER>(P, item, c, lo, parity, A, w1, msg);
       parity ^= 1;
     } else {
@@ -617,6 +686,12 @@ __device__ __attribute__((always_inline)) void compute_loop_staged(const FusedPa
     lds_barrier();
     item = next;
   }
+  if constexpr (!ARGMAX && SPECV_FUSED_PIPELINE) {
+    if (pend >= 0) {
+      const NormMsg m = pair_wait(P, pend, parity, w1, msg);
+      pair_phase2<PER>(P, pend, c, m, ep, eq, mp, mq, sp);
+    }
+  }
 }
 
 // ---------------------------------------------------- finisher workgroups
@@ -625,7 +700,13 @@ __device__ __attribute__((always_inline)) void compute_loop_staged(const FusedPa
 // enough that each of its threads scans at least one whole vector.
 template <class E, int PER>
 struct SearchShape {
-  static constexpr int kGroup = (kThreads * E::kVec) / (kWave * PER) > 1 ? (kThreads * E::kVec) / (kWave * PER) : 1;
+  // the smallest group whose tokens split into whole vectors per thread
+  static constexpr int group_for() {
+    int g = 1;
+    while ((g * kWave * PER) % (kThreads * E::kVec) != 0) ++g;
+    return g;
+  }
+  static constexpr int kGroup = group_for();
   static constexpr int kTokens = kGroup * kWave * PER;  // tokens per search group
   static constexpr int kPer = kTokens / kThreads;       // tokens per thread
 };
@@ -910,12 +991,15 @@ __global__ __launch_bounds__(kThreads, SPECV_FUSED_MIN_WAVES) void fused_kernel(
 }
 
 constexpr int kFinisherDiv = SPECV_FUSED_FIN_DIV;
-constexpr int kPer = SPECV_FUSED_PER;
-static_assert(kPer % 8 == 0, "tile shape");
+template <class E>
+constexpr int per_of() { return std::is_same<E, BF16>::value ? SPECV_FUSED_PER_BF16 : SPECV_FUSED_PER_F32; }
+static_assert(per_of<BF16>() % 8 == 0 && per_of<F32>() % 8 == 0, "tile shape");
 
-// Workgroups per team and wave-tile slots per row for a row of V tokens.
-int groups_for(int V) {
-  const int group_tokens = kThreads * kPer;
+int per_for(int dtype) { return dtype == SPEC_BF16 ? per_of<BF16>() : per_of<F32>(); }
+
+// Workgroups per team for a row of V tokens.
+int groups_for(int V, int per) {
+  const int group_tokens = kThreads * per;
   return (V + group_tokens - 1) / group_tokens;
 }
 
@@ -926,7 +1010,8 @@ struct Layout {
 };
 
 Layout layout(int B, int gamma, int V) {
-  const size_t W = (size_t)groups_for(V) * kWavesPerGroup;
+  // the larger slot count of the two dtypes
+  const size_t W = (size_t)std::max(groups_for(V, per_of<BF16>()), groups_for(V, per_of<F32>())) * kWavesPerGroup;
   const size_t n_items = (size_t)B * (gamma + 1), n_pairs = (size_t)B * gamma;
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   Layout L{};
@@ -954,7 +1039,7 @@ hipError_t launch(const VerifyArgs& a, hipStream_t s) {
   char* ws = static_cast<char*>(a.ws);
   FusedParams P{};
   P.a = a;
-  P.K = groups_for(a.V);
+  P.K = groups_for(a.V, per_of<E>());
   P.W = P.K * kWavesPerGroup;
   P.n_pairs = a.B * a.gamma;
   P.n_items = a.B * (a.gamma + 1);
@@ -962,7 +1047,7 @@ hipError_t launch(const VerifyArgs& a, hipStream_t s) {
   P.part2 = reinterpret_cast<uint64_t*>(ws + L.off_part2);
   P.pair_res = reinterpret_cast<uint64_t*>(ws + L.off_res);
 
-  auto kern = fused_kernel<E, kPer, ARGMAX>;
+  auto kern = fused_kernel<E, per_of<E>(), ARGMAX>;
   long resident = 0;
   hipError_t e = resident_blocks(kern, &resident);
   if (e != hipSuccess) return e;
@@ -992,7 +1077,7 @@ size_t fused_workspace_bytes(int B, int gamma, int V) { return layout(B, gamma, 
 
 bool fused_supported(int B, int gamma, int V, int dtype) {
   const int vec = dtype == SPEC_BF16 ? BF16::kVec : F32::kVec;
-  return B >= 1 && V % vec == 0 && groups_for(V) * kWavesPerGroup <= kMaxWaveTiles &&
+  return B >= 1 && V % vec == 0 && groups_for(V, per_for(dtype)) * kWavesPerGroup <= kMaxWaveTiles &&
          (size_t)B * (gamma + 1) < (1u << 30);
 }
 
