@@ -91,7 +91,7 @@ namespace {
 #endif
 // Minimum waves per SIMD the register allocation must allow (1: no limit).
 #ifndef SPECV_FUSED_MIN_WAVES
-#define SPECV_FUSED_MIN_WAVES 1
+#define SPECV_FUSED_MIN_WAVES 3
 #endif
 constexpr int kThreads = 256;
 constexpr int kWavesPerGroup = kThreads / kWave;
@@ -276,16 +276,25 @@ __device__ inline int tile_token(int tile_lo, int idx) {
   return tile_lo + ((idx / KVEC) * kWave + wave_lane()) * KVEC + idx % KVEC;
 }
 
-// Thread maximum with independent max chains (three-input maxima: half an
-// instruction per token).
+// Three-input maximum as one instruction.  The compiler rebalances chains of
+// fmaxf into trees of two-input maxima, which costs about 1.4 instructions per
+// two tokens instead of one.
+__device__ inline float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// Thread maximum with two independent chains of three-input maxima: half an
+// instruction per token.
 template <int PER>
 __device__ inline float thread_max(const float (&x)[PER]) {
   static_assert(PER % 4 == 0, "PER must be a multiple of 4");
   float m0 = fmaxf(x[0], x[1]), m1 = fmaxf(x[2], x[3]);
 #pragma unroll
   for (int i = 4; i < PER; i += 4) {
-    m0 = fmaxf(m0, fmaxf(x[i], x[i + 1]));
-    m1 = fmaxf(m1, fmaxf(x[i + 2], x[i + 3]));
+    m0 = max3f(m0, x[i], x[i + 1]);
+    m1 = max3f(m1, x[i + 2], x[i + 3]);
   }
   return fmaxf(m0, m1);
 }
@@ -317,10 +326,17 @@ __device__ inline float thread_exp_sum(float (&x)[PER], float c, float k) {
         x[i + 2] = e2;
         x[i + 3] = e3;
       }
-      s0 += e0;
-      s1 += e1;
-      s2 += e2;
-      s3 += e3;
+      if (i == 0) {  // 0 + e is not foldable to e (signed zeros): start from e
+        s0 = e0;
+        s1 = e1;
+        s2 = e2;
+        s3 = e3;
+      } else {
+        s0 += e0;
+        s1 += e1;
+        s2 += e2;
+        s3 += e3;
+      }
     }
   }
   return (s0 + s1) + (s2 + s3);
@@ -454,7 +470,8 @@ struct NormMsg {
 template <class E, int PER>
 __device__ __attribute__((always_inline)) void pair_phase1(const FusedParams& P, int item, int c, int lo,
                                                            const RawPair<E, PER>& raw, float (&ep)[PER],
-                                                           float (&eq)[PER], float& mp, float& mq, float& sp) {
+                                                           float (&eq)[PER], float& mp, float& mq, float& sp,
+                                                           float& sq) {
   const VerifyArgs& a = P.a;
   const float k = a.k;
   unpack_tile<E, PER>(raw.p, lo, a.V, ep);
@@ -462,7 +479,7 @@ __device__ __attribute__((always_inline)) void pair_phase1(const FusedParams& P,
   mp = thread_max<PER>(ep) * k;  // scaled maxima
   mq = thread_max<PER>(eq) * k;
   sp = thread_exp_sum<PER, true>(ep, mp, k);
-  const float sq = thread_exp_sum<PER, true>(eq, mq, k);
+  sq = thread_exp_sum<PER, true>(eq, mq, k);
   const float2 lp = wave_lse(mp, sp), lq = wave_lse(mq, sq);
   uint64_t* part1 = P.part1 + (size_t)item * P.W * 2;
   if (wave_lane() == 0) {
@@ -493,10 +510,20 @@ __device__ __attribute__((always_inline)) inline NormMsg pair_wait(const FusedPa
 
 // Phase 2: the wave's share of alpha = sum min(p, q) and of the residual mass
 // sum max(0, p - q) from the kept weights, published as one word.
+//
+// With p = ep fp and q = eq fq (fp, fq the thread's scale factors) and
+// r = fp / fq, sum min(p, q) = fq sum min(ep r, eq), and min(a, b) =
+// (a + b - |a - b|) / 2 turns that into fq (r sp + sq - sum |ep r - eq|) / 2:
+// one fused multiply-add and one add with an absolute-value operand per token.
+// The subtraction loses a few ulps of the thread's p and q mass (absolute),
+// far below the overlap's tolerance.  r is an exact quotient (fq can be
+// subnormal at low temperature, where the hardware reciprocal flushes to
+// zero).  Above 2^64 the thread's q mass is under 2^-53 of its p mass and its
+// share of the overlap is taken as 0, which also keeps every term finite.
 template <int PER>
 __device__ __attribute__((always_inline)) void pair_phase2(const FusedParams& P, int item, int c, const NormMsg& m,
                                                            const float (&ep)[PER], const float (&eq)[PER],
-                                                           float mp, float mq, float sp) {
+                                                           float mp, float mq, float sp, float sq) {
   uint64_t* mine2 = P.part2 + (size_t)item * P.W + c;
   if (!m.ok) {
     if (wave_lane() == 0) st_u64(mine2, pack2i(kPoison, 0u));
@@ -504,21 +531,20 @@ __device__ __attribute__((always_inline)) void pair_phase2(const FusedParams& P,
   }
   const float fp = mp == -INFINITY ? 0.f : fast_exp2(mp - m.Mp) * m.invSp;
   const float fq = mq == -INFINITY ? 0.f : fast_exp2(mq - m.Mq) * m.invSq;
-  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-  if (fp > 0.f && fq > 0.f) {
-    // sum min(ep fp, eq fq) = fq * sum min(ep (fp / fq), eq); ep <= 1, so the
-    // clamp keeps ep * r finite.  An exact division: fq can be subnormal at
-    // low temperature, where the hardware reciprocal flushes to zero.
-    const float r = fminf(fp / fq, FLT_MAX);
+  float alpha_t = 0.f;
+  const float r = fp / fq;
+  if (fp > 0.f && fq > 0.f && r <= 0x1p64f) {
+    float d0 = fabsf(fmaf(ep[0], r, -eq[0])), d1 = fabsf(fmaf(ep[1], r, -eq[1]));
+    float d2 = fabsf(fmaf(ep[2], r, -eq[2])), d3 = fabsf(fmaf(ep[3], r, -eq[3]));
 #pragma unroll
-    for (int j = 0; j < PER; j += 4) {
-      a0 += fminf(ep[j] * r, eq[j]);
-      a1 += fminf(ep[j + 1] * r, eq[j + 1]);
-      a2 += fminf(ep[j + 2] * r, eq[j + 2]);
-      a3 += fminf(ep[j + 3] * r, eq[j + 3]);
+    for (int j = 4; j < PER; j += 4) {
+      d0 += fabsf(fmaf(ep[j], r, -eq[j]));
+      d1 += fabsf(fmaf(ep[j + 1], r, -eq[j + 1]));
+      d2 += fabsf(fmaf(ep[j + 2], r, -eq[j + 2]));
+      d3 += fabsf(fmaf(ep[j + 3], r, -eq[j + 3]));
     }
+    alpha_t = fmaxf(0.5f * (fmaf(r, sp, sq) - ((d0 + d1) + (d2 + d3))), 0.f) * fq;
   }
-  const float alpha_t = ((a0 + a1) + (a2 + a3)) * fq;
   const float res_t = fmaxf(sp * fp - alpha_t, 0.f);  // sum max(0, p - q) = sum p - sum min(p, q)
   const float alpha_w = wave_sum(alpha_t), res_w = wave_sum(res_t);
   if (wave_lane() == 0) st_u64(mine2, pack2(alpha_w, res_w));
@@ -529,10 +555,10 @@ template <class E, int PER>
 __device__ __attribute__((always_inline)) void pair_compute_sample(const FusedParams& P, int item, int c, int lo,
                                                                    int parity, const RawPair<E, PER>& raw,
                                                                    uint64_t* w1, NormMsg* msg) {
-  float ep[PER], eq[PER], mp, mq, sp;
-  pair_phase1<E, PER>(P, item, c, lo, raw, ep, eq, mp, mq, sp);
+  float ep[PER], eq[PER], mp, mq, sp, sq;
+  pair_phase1<E, PER>(P, item, c, lo, raw, ep, eq, mp, mq, sp, sq);
   const NormMsg m = pair_wait(P, item, parity, w1, msg);
-  pair_phase2<PER>(P, item, c, m, ep, eq, mp, mq, sp);
+  pair_phase2<PER>(P, item, c, m, ep, eq, mp, mq, sp, sq);
 }
 
 // Pair item at T = 0, or a bonus item: one pass, no waiting.
@@ -633,7 +659,7 @@ __device__ __attribute__((always_inline)) void compute_loop_staged(const FusedPa
   lds_barrier();
   int parity = 0;
   int pend = -1;  // pipelined: the pair item whose kept weights wait in (ep, eq)
-  float ep[PER], eq[PER], mp = 0.f, mq = 0.f, sp = 0.f;
+  float ep[PER], eq[PER], mp = 0.f, mq = 0.f, sp = 0.f, sq = 0.f;
   while (item < P.n_items) {
     RawPair<E, PER> A;
 #pragma unroll
@@ -651,11 +677,11 @@ __device__ __attribute__((always_inline)) void compute_loop_staged(const FusedPa
       // register move per token but needs fewer registers than two sets that
       // swap roles.)
       if (item < P.n_pairs) {
-        float xp[PER], xq[PER], cp, cq, s_p;
-        pair_phase1<E, PER>(P, item, c, lo, A, xp, xq, cp, cq, s_p);
+        float xp[PER], xq[PER], cp, cq, s_p, s_q;
+        pair_phase1<E, PER>(P, item, c, lo, A, xp, xq, cp, cq, s_p, s_q);
         if (pend >= 0) {
           const NormMsg m = pair_wait(P, pend, parity, w1, msg);
-          pair_phase2<PER>(P, pend, c, m, ep, eq, mp, mq, sp);
+          pair_phase2<PER>(P, pend, c, m, ep, eq, mp, mq, sp, sq);
           parity ^= 1;
         }
 #pragma unroll
@@ -666,12 +692,13 @@ __device__ __attribute__((always_inline)) void compute_loop_staged(const FusedPa
         mp = cp;
         mq = cq;
         sp = s_p;
+        sq = s_q;
         pend = item;
       } else {
         single_pass_compute<E, PER, ARGMAX>(P, item, c, lo, A);
         if (pend >= 0) {
           const NormMsg m = pair_wait(P, pend, parity, w1, msg);
-          pair_phase2<PER>(P, pend, c, m, ep, eq, mp, mq, sp);
+          pair_phase2<PER>(P, pend, c, m, ep, eq, mp, mq, sp, sq);
           parity ^= 1;
           pend = -1;
         }
@@ -689,7 +716,7 @@ __device__ __attribute__((always_inline)) void compute_loop_staged(const FusedPa
   if constexpr (!ARGMAX && SPECV_FUSED_PIPELINE) {
     if (pend >= 0) {
       const NormMsg m = pair_wait(P, pend, parity, w1, msg);
-      pair_phase2<PER>(P, pend, c, m, ep, eq, mp, mq, sp);
+      pair_phase2<PER>(P, pend, c, m, ep, eq, mp, mq, sp, sq);
     }
   }
 }
