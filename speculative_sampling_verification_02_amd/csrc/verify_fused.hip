@@ -89,6 +89,17 @@ namespace {
 #ifndef SPECV_FUSED_PIPELINE
 #define SPECV_FUSED_PIPELINE 1
 #endif
+// Rotate the compute waves' issue priority by item round (1) or leave every
+// wave at the default priority (0).  With three workgroups per compute unit,
+// the one dispatched first wins every tie in the instruction arbiter (the
+// oldest wave goes first), so on the hardware the teams made of the first,
+// second and third dispatched workgroups of each unit ran their items at
+// about 1 : 1.2 : 1.4 of the first's pace, and the kernel waited for the
+// slowest class.  Giving each class the top level one round in three levels
+// that out.
+#ifndef SPECV_FUSED_ROT_PRIO
+#define SPECV_FUSED_ROT_PRIO 1
+#endif
 // Minimum waves per SIMD the register allocation must allow (1: no limit).
 #ifndef SPECV_FUSED_MIN_WAVES
 #define SPECV_FUSED_MIN_WAVES 3
@@ -201,11 +212,78 @@ __device__ inline bool wave_poll(const uint64_t* a, int na, uint64_t* la, const 
   return true;
 }
 
+// The same for at most 2 kWave slots of one array: each poll reads every slot
+// at once, so it costs one memory round trip (wave_poll polls 64 slots at a
+// time, one round trip each).
+__device__ inline bool wave_poll_once(const uint64_t* a, int n, uint64_t* lds) {
+  // the lane index is made opaque here, so the per-lane offsets are formed
+  // at each wait instead of being hoisted out of the compute loop (where they
+  // would hold registers through the whole item)
+  int lane;
+  asm volatile("" : "=v"(lane) : "0"((int)(threadIdx.x & (kWave - 1))));
+  const int c0 = lane, c1 = lane + kWave;
+  const uint32_t o0 = (uint32_t)c0 * 8u, o1 = (uint32_t)c1 * 8u;
+  const char* base = reinterpret_cast<const char*>(a);
+  unsigned it = 0;
+  while (true) {
+    uint64_t v0 = pack2i(1u, 0u), v1 = pack2i(1u, 0u);
+    if (c0 < n) v0 = ld_u64(reinterpret_cast<const uint64_t*>(base + o0));
+    if (c1 < n) v1 = ld_u64(reinterpret_cast<const uint64_t*>(base + o1));
+    if (__all(published(v0) && published(v1))) {
+      if (c0 < n) lds[c0] = v0;
+      if (c1 < n) lds[c1] = v1;
+      return !__any(poisoned(v0) || poisoned(v1));
+    }
+    __builtin_amdgcn_s_sleep(1);
+    if (++it >= kSpinIters) return false;
+  }
+}
+
+// wave_poll for at most NL kWave slots: every poll reads all of them at once
+// (one memory round trip).
+template <int NL>
+__device__ inline bool wave_poll_all(const uint64_t* a, int na, uint64_t* la, const uint64_t* b, int nb,
+                                     uint64_t* lb) {
+  const int lane = threadIdx.x & (kWave - 1), n = na + nb;
+  unsigned it = 0;
+  while (true) {
+    uint64_t v[NL];
+    bool all = true, bad = false;
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+      const int c = lane + j * kWave;
+      v[j] = pack2i(1u, 0u);
+      if (c < na)
+        v[j] = ld_u64(a + c);
+      else if (c < n)
+        v[j] = ld_u64(b + (c - na));
+    }
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+      all = all && published(v[j]);
+      bad = bad || poisoned(v[j]);
+    }
+    if (__all(all)) {
+#pragma unroll
+      for (int j = 0; j < NL; ++j) {
+        const int c = lane + j * kWave;
+        if (c < na)
+          la[c] = v[j];
+        else if (c < n)
+          lb[c - na] = v[j];
+      }
+      return !__any(bad);
+    }
+    __builtin_amdgcn_s_sleep(1);
+    if (++it >= kSpinIters) return false;
+  }
+}
+
 // Whole-workgroup wait: wave 0 polls, then a barrier.  Finishers only.
 __device__ inline bool gather2(const uint64_t* a, int na, uint64_t* la, const uint64_t* b, int nb, uint64_t* lb) {
   __shared__ int ok_s;
   if (threadIdx.x < kWave) {
-    const bool ok = wave_poll(a, na, la, b, nb, lb);
+    const bool ok = na + nb <= 4 * kWave ? wave_poll_all<4>(a, na, la, b, nb, lb) : wave_poll(a, na, la, b, nb, lb);
     if (threadIdx.x == 0) ok_s = ok;
   }
   __syncthreads();
@@ -496,7 +574,8 @@ __device__ __attribute__((always_inline)) inline NormMsg pair_wait(const FusedPa
                                                                    uint64_t* w1, NormMsg* msg) {
   if (threadIdx.x < kWave) {
     const uint64_t* part1 = P.part1 + (size_t)item * P.W * 2;
-    const bool ok = wave_poll<SPECV_FUSED_L2_POLL != 0>(part1, 2 * P.W, w1, nullptr, 0, nullptr);
+    const bool ok = 2 * P.W <= 2 * kWave ? wave_poll_once(part1, 2 * P.W, w1)
+                                         : wave_poll<SPECV_FUSED_L2_POLL != 0>(part1, 2 * P.W, w1, nullptr, 0, nullptr);
     NormMsg m{0.f, 0.f, 0.f, 0.f, 0};
     if (ok) {
       const Norm2 n = wave_norm2(w1, P.W);
@@ -660,7 +739,19 @@ __device__ __attribute__((always_inline)) void compute_loop_staged(const FusedPa
   int parity = 0;
   int pend = -1;  // pipelined: the pair item whose kept weights wait in (ep, eq)
   float ep[PER], eq[PER], mp = 0.f, mq = 0.f, sp = 0.f, sq = 0.f;
+  // dispatch class of this workgroup: which third of the grid (the grid fills
+  // every compute unit once before it places a second workgroup on any)
+  const int slot_class = (int)((blockIdx.x * 3u) / gridDim.x);
+  int round = 0;
   while (item < P.n_items) {
+    if (SPECV_FUSED_ROT_PRIO) {
+      switch ((round + slot_class) % 3) {  // s_setprio takes an immediate
+        case 0: __builtin_amdgcn_s_setprio(0); break;
+        case 1: __builtin_amdgcn_s_setprio(1); break;
+        default: __builtin_amdgcn_s_setprio(2); break;
+      }
+    }
+    ++round;
     RawPair<E, PER> A;
 #pragma unroll
     for (int v = 0; v < NS; ++v) {
