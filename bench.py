@@ -1,6 +1,7 @@
 """Benchmark of the verification step on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--algo auto|multipass|fused]
+    python bench.py --workload lmhead [--steps K] [--warmup W]
 
 Workload: B=64 sequences, gamma=4 drafts, V=128256, bf16 logits, T=1.  Target
 logits are N(0, 3^2) with 8 peaked tokens per row (+8).  Draft logits are the
@@ -9,10 +10,17 @@ synthetic).  One step is one spec_verify call over the whole batch.  The inputs
 are resident in HBM; NSETS copies rotate so that the working set exceeds the
 256 MB last-level cache and every step streams from HBM.
 
+With --workload lmhead the step is instead the LM heads of both models plus
+the verification (spec_lmhead_verify): B=8, gamma=4, hidden size d=4096,
+V=128256, bf16 hidden states and weights (W_p ~ N(0, 0.02^2), W_q = W_p +
+N(0, 0.005^2)), fp32 logits.  The weights (2 x 1.05 GB) exceed the last-level
+cache, so every step streams them from HBM.
+
 Prints one JSON line (rank 0) with the throughput in verified target rows/s
 (B*(gamma+1) per step).  It also carries:
-  roofline:     algorithmic bytes of one launch / its average HIP-event
-                duration, against 8 TB/s;
+  roofline:     algorithmic bytes of one launch / its average duration
+                (one pair of HIP events on the launch stream around the
+                back-to-back timed steps), against 8 TB/s;
   cpu_baseline: the fp64 oracle (test infrastructure) timed on a bounded
                 sample of the same workload on this host.
 """
@@ -86,6 +94,31 @@ def load_traffic(algo_name: str):
     return entry.get("bytes_per_launch")
 
 
+class LoopTime:
+    def __init__(self, mean_us: float, wall_s: float):
+        self.mean = mean_us   # average launch duration on the stream, µs
+        self.wall_s = wall_s  # host wall time of the timed region, s
+
+
+def timed_loop(torch, steps: int, step) -> LoopTime:
+    """Runs `steps` steps back to back between one pair of HIP events on the
+    launch stream (torch's current stream, which every step launches on).
+    Events between the steps would each add a marker packet and several µs
+    of idle time to the stream, so the per-launch duration is the events'
+    interval over the steps: the kernels' own durations plus the (sub-µs)
+    dispatch gaps between them."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    for k in range(steps):
+        step(k)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return LoopTime(1e3 * e0.elapsed_time(e1) / steps, wall)
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -96,11 +129,14 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (for counter calibration)")
+    ap.add_argument("--workload", default="verify", choices=["verify", "lmhead"])
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the verification step shards by sequence with no communication)", file=sys.stderr)
         return 2
+    if args.workload == "lmhead":
+        return run_lmhead(args)
 
     import torch
 
@@ -126,9 +162,13 @@ def main() -> int:
         ("alpha", (B, G), torch.float32), ("p_draft", (B, G), torch.float32),
         ("q_draft", (B, G), torch.float32))} for _ in sets]
 
+    # one prepared launch per buffer set: the timed loop then spends only the
+    # C call on the host, well under the kernel's duration
+    launches = [sv.prepare_verify(t, d, tokens, uniforms, 1.0, algo=algo, workspace=ws, outputs=o)
+                for (t, d), o in zip(sets, outs)]
+
     def step(k):
-        t, d = sets[k % len(sets)]
-        sv.verify(t, d, tokens, uniforms, 1.0, algo=algo, workspace=ws, outputs=outs[k % len(sets)])
+        launches[k % len(sets)]()
 
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -141,23 +181,14 @@ def main() -> int:
         step(k)
     torch.cuda.synchronize()
 
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        starts[k].record()
-        step(k)
-        ends[k].record()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    launch_ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+    launch_us = timed_loop(torch, args.steps, step)
+    elapsed = launch_us.wall_s
 
     ms_per_step = 1e3 * elapsed / args.steps
     rows = B * (G + 1)
     n0 = outs[0]["n_accepted"].cpu().numpy()
     alg = algorithmic_bytes(n0, G, V, 2)
-    avg_launch_s = float(launch_ms.mean()) * 1e-3
+    avg_launch_s = launch_us.mean * 1e-6
     achieved = alg / avg_launch_s / 1e9
     algo_name = {sv.ALGO_AUTO: "auto", sv.ALGO_MULTIPASS: "multipass", sv.ALGO_FUSED: "fused"}[algo]
     # AUTO dispatches this workload (aligned bf16 rows, 16 tiles per row) to the
@@ -182,12 +213,85 @@ def main() -> int:
                    "algo": algo_name, "buffer_sets": len(sets)},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "launch_us_mean": 1e3 * float(launch_ms.mean()),
-                     "launch_us_median": 1e3 * float(np.median(launch_ms)),
+                     "launch_us_mean": launch_us.mean,
                      "alg_bytes": alg, "full_bytes": (2 * G + 1) * V * 2 * B},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(case)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def lmhead_step_bytes(n_accepted: np.ndarray, B: int, gamma: int, d: int, V: int) -> int:
+    """Bytes one spec_lmhead_verify call must move: both weight matrices once,
+    the hidden states, the fp32 logits written once and read back by the
+    verification (its algorithmic rows, as for spec_verify), and the small I/O."""
+    weights = 2 * d * V * 2
+    hidden = (B * (gamma + 1) + B * gamma) * d * 2
+    logits_out = B * (2 * gamma + 1) * V * 4
+    return weights + hidden + logits_out + algorithmic_bytes(n_accepted, gamma, V, 4)
+
+
+def run_lmhead(args) -> int:
+    import torch
+
+    import speculative_sampling_verification_02_amd as sv
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    case = W.config4(0, 1.0)
+    B, G, d, V = case.B, case.gamma, case.d, case.V
+    print(f"[bench] generated LM-head workload B={B} gamma={G} d={d} V={V}", file=sys.stderr, flush=True)
+
+    def to_dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    hidden, wp, wq = to_dev(case.hidden), to_dev(case.w_target), to_dev(case.w_draft)
+    tokens = torch.from_numpy(case.tokens).to(dev)
+    uniforms = torch.from_numpy(case.uniforms).to(dev)
+    ws = torch.zeros(max(1, sv.lmhead_workspace_size(B, G, d, V)), dtype=torch.uint8, device=dev)
+    out = {"target_logits": torch.empty(B, G + 1, V, dtype=torch.float32, device=dev),
+           "draft_logits": torch.empty(B, G, V, dtype=torch.float32, device=dev),
+           "n_accepted": torch.empty(B, dtype=torch.int32, device=dev),
+           "next_token": torch.empty(B, dtype=torch.int32, device=dev),
+           "alpha": torch.empty(B, G, dtype=torch.float32, device=dev),
+           "p_draft": torch.empty(B, G, dtype=torch.float32, device=dev),
+           "q_draft": torch.empty(B, G, dtype=torch.float32, device=dev)}
+
+    def step():
+        sv.lmhead_verify(hidden, wp, wq, B, G, tokens, uniforms, 1.0, workspace=ws, outputs=out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    launch_us = timed_loop(torch, args.steps, lambda k: step())
+    ms_per_step = 1e3 * launch_us.wall_s / args.steps
+    step_bytes = lmhead_step_bytes(out["n_accepted"].cpu().numpy(), B, G, d, V)
+    achieved = step_bytes / (launch_us.mean * 1e-6) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": B * (G + 1) / (ms_per_step * 1e-3),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"spec_lmhead_verify B={B} gamma={G} d={d} V={V}, bf16 hidden states "
+                               "and weights, fp32 logits, T=1",
+                   "B": B, "gamma": G, "d": d, "V": V, "temperature": 1.0},
+        # one step is one matrix-core launch for both heads plus the
+        # verification launch on its fp32 logits; the bytes and the duration
+        # are those of the whole step
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "launch_us_mean": launch_us.mean,
+                     "step_bytes": step_bytes},
+    }
     print(json.dumps(line), flush=True)
     return 0
 

@@ -161,13 +161,46 @@ def verify(target_logits, draft_logits, draft_tokens, uniforms, temperature: flo
     need = workspace_size(B, gamma, V, dt)
     if workspace is None:
         workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)
-    _check(lib.spec_verify_algo(
-        algo, _ptr(target_logits), _ptr(draft_logits), dt, _ptr(draft_tokens), _ptr(uniforms),
-        B, gamma, V, float(temperature),
-        _ptr(outputs["n_accepted"]), _ptr(outputs["next_token"]), _ptr(outputs.get("alpha")),
-        _ptr(outputs.get("p_draft")), _ptr(outputs.get("q_draft")),
-        _ptr(workspace), workspace.numel(), _stream(dev)), "spec_verify")
+    _check(lib.spec_verify_algo(*_verify_args(algo, target_logits, draft_logits, dt, draft_tokens, uniforms,
+                                              B, gamma, V, temperature, outputs, workspace, dev)),
+           "spec_verify")
     return outputs
+
+
+def _verify_args(algo, target_logits, draft_logits, dt, draft_tokens, uniforms, B, gamma, V, temperature,
+                 outputs, workspace, dev):
+    return (algo, _ptr(target_logits), _ptr(draft_logits), dt, _ptr(draft_tokens), _ptr(uniforms),
+            B, gamma, V, float(temperature),
+            _ptr(outputs["n_accepted"]), _ptr(outputs["next_token"]), _ptr(outputs.get("alpha")),
+            _ptr(outputs.get("p_draft")), _ptr(outputs.get("q_draft")),
+            _ptr(workspace), workspace.numel(), _stream(dev))
+
+
+def prepare_verify(target_logits, draft_logits, draft_tokens, uniforms, temperature: float, *,
+                   algo: int = ALGO_AUTO, workspace, outputs):
+    """Checks the arguments of verify() once and returns a callable that
+    launches that same verification again (same tensors, current stream at
+    preparation) with no per-call Python work beyond the C call, for loops
+    whose host time per step must stay well under the kernel's.  The tensors
+    must stay alive and unchanged in shape while the callable is used."""
+    verify(target_logits, draft_logits, draft_tokens, uniforms, temperature, algo=algo, workspace=workspace,
+           outputs=outputs)
+    B, g1, V = target_logits.shape
+    args = _verify_args(algo, target_logits, draft_logits, _dtype_code(target_logits), draft_tokens, uniforms,
+                        B, g1 - 1, V, temperature, outputs, workspace, target_logits.device)
+    fn = lib.spec_verify_algo
+
+    def launch():
+        status = fn(*args)
+        if status != 0:
+            _check(status, "spec_verify")
+
+    return launch
+
+
+def lmhead_workspace_size(B: int, gamma: int, d: int, V: int) -> int:
+    """Bytes of device workspace spec_lmhead_verify needs (zero on entry)."""
+    return int(lib.spec_lmhead_workspace_size(B, gamma, d, V))
 
 
 def lmhead_logits(hidden, W, out=None):
@@ -189,12 +222,13 @@ def lmhead_logits(hidden, W, out=None):
 
 
 def lmhead_verify(hidden, W_target, W_draft, B: int, gamma: int, draft_tokens, uniforms,
-                  temperature: float, hidden_draft=None, workspace=None):
+                  temperature: float, hidden_draft=None, workspace=None, outputs=None):
     """LM heads of both models over the verified positions, then the verification.
 
     hidden bf16 [B*(gamma+1), d]; W_target / W_draft bf16 [d, V]; hidden_draft
     bf16 [B*gamma, d] or None (rows 0..gamma-1 of each sequence in `hidden`).
-    Returns the verify outputs plus the fp32 target_logits and draft_logits.
+    Returns the verify outputs plus the fp32 target_logits and draft_logits
+    (in `outputs` when given: a dict of tensors of those names and shapes).
     """
     torch = _torch()
     dev = hidden.device
@@ -208,7 +242,7 @@ def lmhead_verify(hidden, W_target, W_draft, B: int, gamma: int, draft_tokens, u
     d, V = W_target.shape
     if tuple(hidden.shape) != (B * (gamma + 1), d):
         raise ValueError("hidden must be [B*(gamma+1), d]")
-    out = {
+    out = outputs if outputs is not None else {
         "target_logits": torch.empty(B, gamma + 1, V, dtype=torch.float32, device=dev),
         "draft_logits": torch.empty(B, gamma, V, dtype=torch.float32, device=dev),
         "n_accepted": torch.empty(B, dtype=torch.int32, device=dev),
@@ -217,6 +251,15 @@ def lmhead_verify(hidden, W_target, W_draft, B: int, gamma: int, draft_tokens, u
         "p_draft": torch.empty(B, gamma, dtype=torch.float32, device=dev),
         "q_draft": torch.empty(B, gamma, dtype=torch.float32, device=dev),
     }
+    if outputs is not None:
+        for name, shape, dt in (("target_logits", (B, gamma + 1, V), torch.float32),
+                                ("draft_logits", (B, gamma, V), torch.float32),
+                                ("n_accepted", (B,), torch.int32), ("next_token", (B,), torch.int32),
+                                ("alpha", (B, gamma), torch.float32), ("p_draft", (B, gamma), torch.float32),
+                                ("q_draft", (B, gamma), torch.float32)):
+            _need(out[name], name, dt, dev)
+            if tuple(out[name].shape) != shape:
+                raise ValueError(f"{name} must have shape {shape}")
     need = int(lib.spec_lmhead_workspace_size(B, gamma, d, V))
     if workspace is None:
         workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)
