@@ -43,6 +43,13 @@ METRIC = "verified logit rows/s (B*(gamma+1) x V) and % of peak HBM GB/s at V=12
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ["verify_multipass.hip", "verify_fused.hip", "common.hpp"]
+WORKLOAD_TEXT = {
+    "verify": "Gaussian rows with 8 peaked tokens, per-sequence draft noise",
+    "small1": "target N(0, 2^2), draft = target + N(0, 1)",
+    "small2": "target N(0, 3^2), draft = 0.8 target + N(0, 0.5^2)",
+    "large5": "target N(0, 4^2) with a Zipf(1.1)-ranked bias, draft noise N(0, 1.5^2), "
+              "5% confidently wrong draft rows",
+}
 
 
 def kernel_source_hash() -> str:
@@ -129,7 +136,12 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (for counter calibration)")
-    ap.add_argument("--workload", default="verify", choices=["verify", "lmhead"])
+    ap.add_argument("--workload", default="verify", choices=["verify", "lmhead", "small1", "small2", "large5"],
+                    help="verify: B=64, gamma=4, V=128256 bf16 (the headline); lmhead: LM heads + verify at "
+                         "B=8, d=4096; small1 / small2: B=1, gamma=3 / 7, V=32128 fp32; large5: B=256, "
+                         "gamma=8, V=256000 bf16")
+    ap.add_argument("--temperature", type=float, default=1.0,
+                    help="temperature of the verify workloads (0: argmax mode)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -145,18 +157,24 @@ def main() -> int:
 
     dev = torch.device("cuda:0")
     algo = {"auto": sv.ALGO_AUTO, "multipass": sv.ALGO_MULTIPASS, "fused": sv.ALGO_FUSED}[args.algo]
-    case = W.config3(0, 1.0)
+    T = float(args.temperature)
+    case = {"verify": W.config3, "small1": W.config1, "small2": W.config2, "large5": W.config5}[args.workload](0, T)
     B, G, V = case.B, case.gamma, case.V
-    print(f"[bench] generated B={B} gamma={G} V={V} bf16", file=sys.stderr, flush=True)
+    bf16 = case.dtype == "bf16"
+    elem = 2 if bf16 else 4
+    print(f"[bench] generated B={B} gamma={G} V={V} {case.dtype}", file=sys.stderr, flush=True)
 
     def to_dev(a):
-        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        if bf16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
     base = (to_dev(case.target), to_dev(case.draft))
     sets = [base] + [(base[0].clone(), base[1].clone()) for _ in range(args.sets - 1)]
     tokens = torch.from_numpy(case.tokens).to(dev)
     uniforms = torch.from_numpy(case.uniforms).to(dev)
-    ws = torch.zeros(sv.workspace_size(B, G, V, sv.SPEC_BF16), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(sv.workspace_size(B, G, V, sv.SPEC_BF16 if bf16 else sv.SPEC_F32), dtype=torch.uint8,
+                     device=dev)
     outs = [{k: torch.empty(s, dtype=dt, device=dev) for k, s, dt in (
         ("n_accepted", (B,), torch.int32), ("next_token", (B,), torch.int32),
         ("alpha", (B, G), torch.float32), ("p_draft", (B, G), torch.float32),
@@ -164,7 +182,7 @@ def main() -> int:
 
     # one prepared launch per buffer set: the timed loop then spends only the
     # C call on the host, well under the kernel's duration
-    launches = [sv.prepare_verify(t, d, tokens, uniforms, 1.0, algo=algo, workspace=ws, outputs=o)
+    launches = [sv.prepare_verify(t, d, tokens, uniforms, T, algo=algo, workspace=ws, outputs=o)
                 for (t, d), o in zip(sets, outs)]
 
     def step(k):
@@ -187,13 +205,15 @@ def main() -> int:
     ms_per_step = 1e3 * elapsed / args.steps
     rows = B * (G + 1)
     n0 = outs[0]["n_accepted"].cpu().numpy()
-    alg = algorithmic_bytes(n0, G, V, 2)
+    alg = algorithmic_bytes(n0, G, V, elem)
     avg_launch_s = launch_us.mean * 1e-6
     achieved = alg / avg_launch_s / 1e9
     algo_name = {sv.ALGO_AUTO: "auto", sv.ALGO_MULTIPASS: "multipass", sv.ALGO_FUSED: "fused"}[algo]
-    # AUTO dispatches this workload (aligned bf16 rows, 16 tiles per row) to the
-    # fused kernel, whose counters the traffic record holds
-    traffic = load_traffic("fused" if algo_name == "auto" else algo_name)
+    # AUTO dispatches the headline workload (aligned bf16 rows, 16 workgroups
+    # per row) to the fused kernel, whose counters the traffic record holds
+    traffic = None
+    if args.workload == "verify" and T == 1.0:
+        traffic = load_traffic("fused" if algo_name == "auto" else algo_name)
     line = {
         "metric": METRIC,
         "value": rows / (ms_per_step * 1e-3),
@@ -207,16 +227,16 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": f"spec_verify B={B} gamma={G} V={V} bf16 logits T=1, Gaussian rows "
-                               "with 8 peaked tokens, per-sequence draft noise",
-                   "B": B, "gamma": G, "V": V, "logits": "bf16", "temperature": 1.0,
+        "config": {"workload": f"spec_verify B={B} gamma={G} V={V} {case.dtype} logits T={T:g}, "
+                               + WORKLOAD_TEXT[args.workload],
+                   "B": B, "gamma": G, "V": V, "logits": case.dtype, "temperature": T,
                    "algo": algo_name, "buffer_sets": len(sets)},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "launch_us_mean": launch_us.mean,
-                     "alg_bytes": alg, "full_bytes": (2 * G + 1) * V * 2 * B},
+                     "alg_bytes": alg, "full_bytes": (2 * G + 1) * V * elem * B},
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.workload == "verify":
         line["cpu_baseline"] = cpu_baseline(case)
     print(json.dumps(line), flush=True)
     return 0
