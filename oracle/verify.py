@@ -33,6 +33,21 @@ Readings taken where the pages are silent (each is listed in the design notes):
   * alpha is reported for every draft position, whatever n is.
   * p/q uses IEEE semantics: q(x) = 0 < p(x) gives +inf (accept); 0/0 gives NaN,
     and any comparison with NaN is false (reject).
+
+Two extensions, both off by default:
+  * Lenience l in (0, 1] ([FI] "The acceptance rate is the overlap of p and q",
+    the paragraph on the lenience factor of Appendix A.5): q(x) is multiplied by
+    l before the comparison, so x is kept when u <= min(1, p(x) / (l q(x))).  The
+    page does not give the residual under l; the reading taken here builds it
+    from the same scaled comparison, max(0, p - l q).  With that residual no
+    token is emitted more than 1/l times as often as under p (the bound the page
+    states), and l = 1 is the exact method.
+  * Per-sequence draft counts gamma_b <= gamma (a dynamic lookahead, [DB]
+    "Dynamic lookahead"): sequence b's data sit in positions 0..gamma_b of the
+    padded arrays (drafts 0..gamma_b-1, target rows 0..gamma_b, accept uniforms
+    0..gamma_b-1, final-sample uniform u[b][gamma_b]); positions past gamma_b are
+    padding, never read, and report alpha = p(x) = q(x) = NaN.  gamma_b = 0 is a
+    plain decoding step: the token is sampled from p_0.
 """
 
 from __future__ import annotations
@@ -94,10 +109,10 @@ def total_variation(p: np.ndarray, q: np.ndarray) -> np.ndarray:
 
 # ------------------------------------------------------------------ step 3
 
-def ratio_test(p_x: np.ndarray, q_x: np.ndarray, u: np.ndarray):
-    """Accept iff u <= min(1, p(x)/q(x)).  Returns (accept, min(1, ratio))."""
+def ratio_test(p_x: np.ndarray, q_x: np.ndarray, u: np.ndarray, lenience: float = 1.0):
+    """Accept iff u <= min(1, p(x) / (l q(x))).  Returns (accept, min(1, ratio))."""
     with np.errstate(divide="ignore", invalid="ignore"):
-        ratio = p_x / q_x
+        ratio = p_x / (lenience * q_x)
     capped = np.minimum(1.0, ratio)          # NaN propagates, so 0/0 rejects
     return u <= capped, capped
 
@@ -113,9 +128,9 @@ def accepted_prefix(accept: np.ndarray) -> np.ndarray:
 
 # ------------------------------------------------------------------ step 4
 
-def residual_weights(p_row: np.ndarray, q_row: np.ndarray) -> np.ndarray:
-    """max(0, p - q), not yet normalised."""
-    return np.maximum(0.0, p_row - q_row)
+def residual_weights(p_row: np.ndarray, q_row: np.ndarray, lenience: float = 1.0) -> np.ndarray:
+    """max(0, p - l q), not yet normalised (l = 1: the exact residual)."""
+    return np.maximum(0.0, p_row - lenience * q_row)
 
 
 # ------------------------------------------------------------------ step 5
@@ -154,22 +169,31 @@ class Result:
     weights: np.ndarray | None  # float64 [B, V] normalised sampling row, if requested
 
 
-def _verify_block(target, draft, tokens, u, temperature, dtype, keep_weights):
+def _verify_block(target, draft, tokens, u, temperature, dtype, keep_weights, lenience=1.0, gseq=None):
     tl = widen(target, dtype)            # [b, gamma+1, V]
     dl = widen(draft, dtype)             # [b, gamma, V]
     nb, g1, V = tl.shape
     gamma = g1 - 1
     rows = np.arange(nb)
     tokens = np.asarray(tokens, dtype=np.int64).reshape(nb, gamma)
+    # per-sequence draft counts; a position i >= gamma_b is padding
+    gb = np.full(nb, gamma, dtype=np.int64) if gseq is None else np.asarray(gseq, dtype=np.int64)
+    live = np.arange(gamma)[None, :] < gb[:, None]                     # [b, gamma]
+    tok = np.where(live, tokens, 0)                                      # padding is never looked up
+    u_final = u[rows, gb]
+    if gseq is not None:
+        # padding rows take no part: zero them so nothing of theirs can leak in
+        tl = np.where((np.arange(g1)[None, :] <= gb[:, None])[..., None], tl, 0.0)
+        dl = np.where(live[..., None], dl, 0.0)
 
     if temperature == 0.0:
         a = argmax_first(tl)             # target argmax per position
         d = argmax_first(dl)             # draft argmax per position
-        alpha = (a[:, :gamma] == d).astype(np.float64)
-        p_x = (tokens == a[:, :gamma]).astype(np.float64)
-        q_x = (tokens == d).astype(np.float64)
-        accept = tokens == a[:, :gamma]
-        n = accepted_prefix(accept)
+        alpha = np.where(live, (a[:, :gamma] == d).astype(np.float64), np.nan)
+        p_x = np.where(live, (tok == a[:, :gamma]).astype(np.float64), np.nan)
+        q_x = np.where(live, (tok == d).astype(np.float64), np.nan)
+        accept = (tok == a[:, :gamma]) & live
+        n = accepted_prefix(accept)      # at most gamma_b: the first padding position stops it
         t = a[rows, n]
         weights = None
         if keep_weights:
@@ -180,39 +204,45 @@ def _verify_block(target, draft, tokens, u, temperature, dtype, keep_weights):
 
     p = softmax(tl, temperature)         # [b, gamma+1, V]
     q = softmax(dl, temperature)         # [b, gamma, V]
-    alpha = overlap(p[:, :gamma], q)
-    tv = total_variation(p[:, :gamma], q)
-    p_x = np.take_along_axis(p[:, :gamma], tokens[..., None], axis=-1)[..., 0]
-    q_x = np.take_along_axis(q, tokens[..., None], axis=-1)[..., 0]
-    accept, capped = ratio_test(p_x, q_x, u[:, :gamma])
-    n = accepted_prefix(accept)
+    alpha = np.where(live, overlap(p[:, :gamma], q), np.nan)
+    tv = np.where(live, total_variation(p[:, :gamma], q), np.nan)
+    p_x = np.take_along_axis(p[:, :gamma], tok[..., None], axis=-1)[..., 0]
+    q_x = np.take_along_axis(q, tok[..., None], axis=-1)[..., 0]
+    accept, capped = ratio_test(p_x, q_x, u[:, :gamma], lenience)
+    accept &= live
+    n = accepted_prefix(accept)          # at most gamma_b: the first padding position stops it
+    p_x = np.where(live, p_x, np.nan)
+    q_x = np.where(live, q_x, np.nan)
 
-    evaluated = np.arange(gamma)[None, :] <= n[:, None]
+    evaluated = (np.arange(gamma)[None, :] <= n[:, None]) & live
     with np.errstate(invalid="ignore"):
         near = np.abs(u[:, :gamma] - capped) < U_BAND
     u_band = (near & evaluated).any(axis=-1) if gamma else np.zeros(nb, bool)
 
-    residual = n < gamma
-    w = p[rows, n].copy()                          # bonus row p_gamma when n == gamma
+    residual = n < gb
+    w = p[rows, n].copy()                          # bonus row p_{gamma_b} when n == gamma_b
     if residual.any():
         idx = np.nonzero(residual)[0]
-        res = residual_weights(p[idx, n[idx]], q[idx, n[idx]])
+        res = residual_weights(p[idx, n[idx]], q[idx, n[idx]], lenience)
         mass = res.sum(axis=-1)
         ok = mass > 0.0                            # zero mass: keep p_n
         w[idx[ok]] = res[ok] / mass[ok][:, None]
     w /= w.sum(axis=-1, keepdims=True)
-    t, cdf = inverse_cdf(w, u[:, gamma].astype(np.float64))
-    margin = np.abs(cdf - u[:, gamma:gamma + 1]).min(axis=-1)
+    t, cdf = inverse_cdf(w, u_final.astype(np.float64))
+    margin = np.abs(cdf - u_final[:, None]).min(axis=-1)
     return Result(n, t, alpha, tv, p_x, q_x, u_band, margin, residual,
                   w if keep_weights else None)
 
 
 def verify(target, draft, tokens, uniforms, temperature: float, dtype: str,
-           keep_weights: bool = False, block_elems: int = 1 << 25) -> Result:
+           keep_weights: bool = False, block_elems: int = 1 << 25, lenience: float = 1.0,
+           gamma_seq=None) -> Result:
     """Run the verification step for every sequence of the batch.
 
     target [B, gamma+1, V], draft [B, gamma, V] (float32, or uint16 bf16 bits),
     tokens int [B, gamma], uniforms float32 [B, gamma+1] in (0, 1).
+    lenience l in (0, 1] and gamma_seq int [B] with 0 <= gamma_b <= gamma are the
+    two extensions described in the module notes.
     Sequences are independent, so they are processed in blocks to bound memory.
     """
     target = np.asarray(target)
@@ -223,12 +253,19 @@ def verify(target, draft, tokens, uniforms, temperature: float, dtype: str,
         raise ValueError("draft must be [B, gamma, V]")
     if temperature < 0.0 or not np.isfinite(temperature):
         raise ValueError("temperature must be finite and >= 0")
+    if not (0.0 < lenience <= 1.0):
+        raise ValueError("lenience must be in (0, 1]")
+    if gamma_seq is not None:
+        gamma_seq = np.asarray(gamma_seq, dtype=np.int64).reshape(B)
+        if (gamma_seq < 0).any() or (gamma_seq > gamma).any():
+            raise ValueError("every gamma_b must lie in [0, gamma]")
     u = np.asarray(uniforms, dtype=np.float32).astype(np.float64).reshape(B, g1)
     tokens = np.asarray(tokens).reshape(B, gamma)
     per_seq = max(1, (2 * gamma + 1) * V)
     step = max(1, block_elems // per_seq)
     parts = [_verify_block(target[s:s + step], draft[s:s + step], tokens[s:s + step],
-                           u[s:s + step], temperature, dtype, keep_weights)
+                           u[s:s + step], temperature, dtype, keep_weights, lenience,
+                           None if gamma_seq is None else gamma_seq[s:s + step])
              for s in range(0, B, step)]
     if not parts:
         z = np.zeros(0)
@@ -241,9 +278,11 @@ def verify(target, draft, tokens, uniforms, temperature: float, dtype: str,
                   cat("residual"), cat("weights") if keep_weights else None)
 
 
-def verify_case(case, keep_weights: bool = False, seqs=None) -> Result:
+def verify_case(case, keep_weights: bool = False, seqs=None, lenience: float = 1.0, gamma_seq=None) -> Result:
     """verify() on a workloads.VerifyCase, optionally on a subset of sequences."""
     if seqs is not None:
         case = case.subset(seqs)
+        if gamma_seq is not None:
+            gamma_seq = np.asarray(gamma_seq)[np.asarray(seqs)]
     return verify(case.target, case.draft, case.tokens, case.uniforms,
-                  case.temperature, case.dtype, keep_weights)
+                  case.temperature, case.dtype, keep_weights, lenience=lenience, gamma_seq=gamma_seq)

@@ -276,9 +276,9 @@ def test_planted_mistakes_are_caught(mutant, monkeypatch):
     orig = {k: getattr(ov, k) for k in ("residual_weights", "ratio_test", "accepted_prefix",
                                          "overlap", "inverse_cdf", "softmax", "argmax_first")}
     if mutant == "residual_sign":
-        monkeypatch.setattr(ov, "residual_weights", lambda p, q: np.maximum(0.0, q - p))
+        monkeypatch.setattr(ov, "residual_weights", lambda p, q, l=1.0: np.maximum(0.0, l * q - p))
     elif mutant == "ratio_inverted":
-        monkeypatch.setattr(ov, "ratio_test", lambda px, qx, u: orig["ratio_test"](qx, px, u))
+        monkeypatch.setattr(ov, "ratio_test", lambda px, qx, u, l=1.0: orig["ratio_test"](qx, px, u, l))
     elif mutant == "prefix_off_by_one":
         monkeypatch.setattr(ov, "accepted_prefix",
                             lambda a: np.minimum(orig["accepted_prefix"](a) + 1, a.shape[-1]))
