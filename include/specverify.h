@@ -141,6 +141,44 @@ int spec_verify_algo(int algo,
                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * spec_verify_ex -- spec_verify_algo with two optional extensions of the step.
+ * With lenience == 1 and gamma_seq == NULL it is spec_verify_algo exactly.
+ *
+ *   lenience   l in (0, 1] ([FI] "The acceptance rate is the overlap of p and q",
+ *              the lenience factor): draft i is kept when
+ *              u_i <= min(1, p_i(x_i) / (l q_i(x_i))), and after the first
+ *              rejection n the token is drawn from max(0, p_n - l q_n) (the page
+ *              does not give the residual under l; this one is built from the
+ *              same scaled comparison, and no token is then emitted more than
+ *              1/l times as often as under p).  The output is exact only for
+ *              l = 1.  alpha stays sum_x min(p_i, q_i).  Argmax mode (T == 0)
+ *              is unaffected.  A value outside (0, 1] (or NaN) is SPEC_EINVAL.
+ *   gamma_seq  NULL, or a device int32 [B]: gamma_b, the number of drafts of
+ *              sequence b, for a batch of sequences with different draft counts
+ *              ([LH] "A longer draft is not always faster": a draft may stop
+ *              early) padded to gamma.  Sequence b's data sit in positions
+ *              0..gamma_b of the padded arrays: draft rows and tokens
+ *              0..gamma_b-1, target rows 0..gamma_b (row gamma_b is its
+ *              bonus row), accept uniforms 0..gamma_b-1 and the final-sample
+ *              uniform u[b][gamma_b].  Positions past gamma_b are padding: never
+ *              read, and alpha / p_draft / q_draft there are set to NaN.
+ *              n_accepted[b] <= gamma_b.  gamma_b = 0 is a plain decoding step
+ *              (the token is drawn from target row 0).  The values are read on
+ *              the device, so they are not checked here: a value below 0 or
+ *              above gamma is taken as 0 or gamma.
+ * All other arguments, the workspace and the return values are as for
+ * spec_verify / spec_verify_algo.
+ */
+int spec_verify_ex(int algo,
+                   const void* target_logits, const void* draft_logits, int dtype,
+                   const int32_t* draft_tokens, const float* uniforms,
+                   int B, int gamma, int V, float temperature,
+                   float lenience, const int32_t* gamma_seq,
+                   int32_t* n_accepted, int32_t* next_token, float* alpha,
+                   float* p_draft, float* q_draft,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * spec_lmhead_logits -- the target pass's final matrix product for the positions
  * being verified ([FI] "Decoding waits on memory, not arithmetic": every weight
  * is read once per pass).

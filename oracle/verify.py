@@ -42,8 +42,8 @@ Two extensions, both off by default:
     from the same scaled comparison, max(0, p - l q).  With that residual no
     token is emitted more than 1/l times as often as under p (the bound the page
     states), and l = 1 is the exact method.
-  * Per-sequence draft counts gamma_b <= gamma (a dynamic lookahead, [DB]
-    "Dynamic lookahead"): sequence b's data sit in positions 0..gamma_b of the
+  * Per-sequence draft counts gamma_b <= gamma (a dynamic lookahead, [LH] "A
+    longer draft is not always faster"): sequence b's data sit in positions 0..gamma_b of the
     padded arrays (drafts 0..gamma_b-1, target rows 0..gamma_b, accept uniforms
     0..gamma_b-1, final-sample uniform u[b][gamma_b]); positions past gamma_b are
     padding, never read, and report alpha = p(x) = q(x) = NaN.  gamma_b = 0 is a

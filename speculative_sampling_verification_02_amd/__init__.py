@@ -37,6 +37,10 @@ SIGNATURES = {
                                   _c_int, _c_int, _c_int, _c_float,
                                   _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                   _c_void_p, _c_size_t, _c_void_p]),
+    "spec_verify_ex": (_c_int, [_c_int, _c_void_p, _c_void_p, _c_int, _c_void_p, _c_void_p,
+                                _c_int, _c_int, _c_int, _c_float, _c_float, _c_void_p,
+                                _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                _c_void_p, _c_size_t, _c_void_p]),
     "spec_lmhead_logits": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_void_p, _c_void_p]),
     "spec_lmhead_workspace_size": (_c_size_t, [_c_int, _c_int, _c_int, _c_int]),
     "spec_lmhead_verify": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p,
@@ -119,7 +123,7 @@ def workspace_size(B: int, gamma: int, V: int, dtype: int = SPEC_BF16) -> int:
 
 
 def verify(target_logits, draft_logits, draft_tokens, uniforms, temperature: float, *,
-           algo: int = ALGO_AUTO, workspace=None, outputs=None):
+           algo: int = ALGO_AUTO, workspace=None, outputs=None, lenience: float = 1.0, gamma_seq=None):
     """One verification step on the current stream.
 
     target_logits [B, gamma+1, V] and draft_logits [B, gamma, V] (float32 or
@@ -134,6 +138,11 @@ def verify(target_logits, draft_logits, draft_tokens, uniforms, temperature: flo
     allocated for this call.  n_accepted = -1 marks a sequence whose result
     was lost because the device was shared (see include/specverify.h); the
     workspace must then be zeroed again.
+
+    lenience (l in (0, 1]) and gamma_seq (int32 [B] on the same GPU, each
+    gamma_b in [0, gamma]) are the extensions of spec_verify_ex: q scaled by l
+    in the accept test and the residual, and per-sequence draft counts in the
+    padded layout (positions past gamma_b report NaN).
     """
     torch = _torch()
     dev = target_logits.device
@@ -149,6 +158,10 @@ def verify(target_logits, draft_logits, draft_tokens, uniforms, temperature: flo
     _need(draft_logits, "draft_logits", device=dev)
     _need(draft_tokens, "draft_tokens", torch.int32, dev)
     _need(uniforms, "uniforms", torch.float32, dev)
+    if gamma_seq is not None:
+        _need(gamma_seq, "gamma_seq", torch.int32, dev)
+        if tuple(gamma_seq.shape) != (B,):
+            raise ValueError(f"gamma_seq must be [{B}]")
     dt = _dtype_code(target_logits)
     if outputs is None:
         outputs = {
@@ -161,34 +174,35 @@ def verify(target_logits, draft_logits, draft_tokens, uniforms, temperature: flo
     need = workspace_size(B, gamma, V, dt)
     if workspace is None:
         workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)
-    _check(lib.spec_verify_algo(*_verify_args(algo, target_logits, draft_logits, dt, draft_tokens, uniforms,
-                                              B, gamma, V, temperature, outputs, workspace, dev)),
+    _check(lib.spec_verify_ex(*_verify_args(algo, target_logits, draft_logits, dt, draft_tokens, uniforms,
+                                            B, gamma, V, temperature, lenience, gamma_seq, outputs,
+                                            workspace, dev)),
            "spec_verify")
     return outputs
 
 
 def _verify_args(algo, target_logits, draft_logits, dt, draft_tokens, uniforms, B, gamma, V, temperature,
-                 outputs, workspace, dev):
+                 lenience, gamma_seq, outputs, workspace, dev):
     return (algo, _ptr(target_logits), _ptr(draft_logits), dt, _ptr(draft_tokens), _ptr(uniforms),
-            B, gamma, V, float(temperature),
+            B, gamma, V, float(temperature), float(lenience), _ptr(gamma_seq),
             _ptr(outputs["n_accepted"]), _ptr(outputs["next_token"]), _ptr(outputs.get("alpha")),
             _ptr(outputs.get("p_draft")), _ptr(outputs.get("q_draft")),
             _ptr(workspace), workspace.numel(), _stream(dev))
 
 
 def prepare_verify(target_logits, draft_logits, draft_tokens, uniforms, temperature: float, *,
-                   algo: int = ALGO_AUTO, workspace, outputs):
+                   algo: int = ALGO_AUTO, workspace, outputs, lenience: float = 1.0, gamma_seq=None):
     """Checks the arguments of verify() once and returns a callable that
     launches that same verification again (same tensors, current stream at
     preparation) with no per-call Python work beyond the C call, for loops
     whose host time per step must stay well under the kernel's.  The tensors
     must stay alive and unchanged in shape while the callable is used."""
     verify(target_logits, draft_logits, draft_tokens, uniforms, temperature, algo=algo, workspace=workspace,
-           outputs=outputs)
+           outputs=outputs, lenience=lenience, gamma_seq=gamma_seq)
     B, g1, V = target_logits.shape
     args = _verify_args(algo, target_logits, draft_logits, _dtype_code(target_logits), draft_tokens, uniforms,
-                        B, g1 - 1, V, temperature, outputs, workspace, target_logits.device)
-    fn = lib.spec_verify_algo
+                        B, g1 - 1, V, temperature, lenience, gamma_seq, outputs, workspace, target_logits.device)
+    fn = lib.spec_verify_ex
 
     def launch():
         status = fn(*args)

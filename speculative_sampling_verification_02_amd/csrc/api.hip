@@ -57,15 +57,16 @@ size_t spec_verify_workspace_size(int B, int gamma, int V, int dtype) {
                                         specv::multipass_workspace_bytes(B, gamma, V)));
 }
 
-int spec_verify_algo(int algo, const void* target_logits, const void* draft_logits, int dtype,
-                     const int32_t* draft_tokens, const float* uniforms, int B, int gamma, int V,
-                     float temperature, int32_t* n_accepted, int32_t* next_token, float* alpha,
-                     float* p_draft, float* q_draft, void* workspace, size_t workspace_bytes,
-                     void* stream) {
+int spec_verify_ex(int algo, const void* target_logits, const void* draft_logits, int dtype,
+                   const int32_t* draft_tokens, const float* uniforms, int B, int gamma, int V,
+                   float temperature, float lenience, const int32_t* gamma_seq, int32_t* n_accepted,
+                   int32_t* next_token, float* alpha, float* p_draft, float* q_draft, void* workspace,
+                   size_t workspace_bytes, void* stream) {
   if (algo != SPEC_ALGO_AUTO && algo != SPEC_ALGO_MULTIPASS && algo != SPEC_ALGO_FUSED)
     return SPEC_EUNSUPPORTED;
   if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_EUNSUPPORTED;
   if (!valid_shape(B, gamma, V) || !valid_temperature(temperature)) return SPEC_EINVAL;
+  if (!(lenience > 0.f && lenience <= 1.f)) return SPEC_EINVAL;  // also rejects NaN
   if (B == 0) return SPEC_OK;
   if (!target_logits || !uniforms || !n_accepted || !next_token) return SPEC_EINVAL;
   if (gamma > 0 && (!draft_logits || !draft_tokens)) return SPEC_EINVAL;
@@ -90,6 +91,8 @@ int spec_verify_algo(int algo, const void* target_logits, const void* draft_logi
   a.q_draft = gamma > 0 ? q_draft : nullptr;
   a.ws = workspace;
   a.ws_bytes = workspace_bytes;
+  a.lenience = lenience;
+  a.gamma_seq = gamma > 0 ? gamma_seq : nullptr;
   hipStream_t s = static_cast<hipStream_t>(stream);
 
   if (algo == SPEC_ALGO_FUSED) return map_hip(specv::fused_launch(a, s));
@@ -99,6 +102,16 @@ int spec_verify_algo(int algo, const void* target_logits, const void* draft_logi
     if (e != hipErrorNotSupported) return map_hip(e);
   }
   return map_hip(specv::multipass_launch(a, s));
+}
+
+int spec_verify_algo(int algo, const void* target_logits, const void* draft_logits, int dtype,
+                     const int32_t* draft_tokens, const float* uniforms, int B, int gamma, int V,
+                     float temperature, int32_t* n_accepted, int32_t* next_token, float* alpha,
+                     float* p_draft, float* q_draft, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  return spec_verify_ex(algo, target_logits, draft_logits, dtype, draft_tokens, uniforms, B, gamma, V,
+                        temperature, 1.f, nullptr, n_accepted, next_token, alpha, p_draft, q_draft,
+                        workspace, workspace_bytes, stream);
 }
 
 int spec_verify(const void* target_logits, const void* draft_logits, int dtype,

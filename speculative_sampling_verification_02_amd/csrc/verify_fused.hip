@@ -525,15 +525,31 @@ struct RawPair {
   RawTile<E, PER> p, q;
 };
 
-template <class E, int PER>
+// A pair item past its sequence's draft count (a padding position): nothing
+// is read, computed or published for it.  Only the extended kernels (EXT:
+// lenience below 1 or per-sequence draft counts) look; the others run the
+// exact, fully padded step with none of this code.
+template <bool EXT>
+__device__ inline bool empty_item(const FusedParams& P, int item) {
+  if constexpr (!EXT) return false;
+  return P.a.gamma_seq && item < P.n_pairs && item % P.a.gamma >= seq_gamma(P.a, item / P.a.gamma);
+}
+template <bool EXT>
+__device__ inline int seq_gamma_of(const VerifyArgs& a, int b) {
+  if constexpr (!EXT) return a.gamma;
+  return seq_gamma(a, b);
+}
+
+template <class E, int PER, bool EXT>
 __device__ __attribute__((always_inline)) void issue_item(const FusedParams& P, int item, int lo, RawPair<E, PER>& r) {
   const VerifyArgs& a = P.a;
   const bool pair = item < P.n_pairs;
   const int b = pair ? item / a.gamma : item - P.n_pairs;
-  const int i = pair ? item % a.gamma : a.gamma;
+  const int i = pair ? item % a.gamma : seq_gamma_of<EXT>(a, b);  // a bonus item reads row gamma_b
   load_raw<E, PER>(trow<E>(a, b, i), lo, a.V, r.p);
   if (pair) load_raw<E, PER>(drow<E>(a, b, i), lo, a.V, r.q);
 }
+
 
 // Row normalisers handed from wave 0 to the other waves, double-buffered by
 // item parity: a buffer is rewritten two items later, after every wave has
@@ -599,7 +615,7 @@ __device__ __attribute__((always_inline)) inline NormMsg pair_wait(const FusedPa
 // subnormal at low temperature, where the hardware reciprocal flushes to
 // zero).  Above 2^64 the thread's q mass is under 2^-53 of its p mass and its
 // share of the overlap is taken as 0, which also keeps every term finite.
-template <int PER>
+template <int PER, bool EXT>
 __device__ __attribute__((always_inline)) void pair_phase2(const FusedParams& P, int item, int c, const NormMsg& m,
                                                            const float (&ep)[PER], const float (&eq)[PER],
                                                            float mp, float mq, float sp, float sq) {
@@ -610,9 +626,8 @@ __device__ __attribute__((always_inline)) void pair_phase2(const FusedParams& P,
   }
   const float fp = mp == -INFINITY ? 0.f : fast_exp2(mp - m.Mp) * m.invSp;
   const float fq = mq == -INFINITY ? 0.f : fast_exp2(mq - m.Mq) * m.invSq;
-  float alpha_t = 0.f;
-  const float r = fp / fq;
-  if (fp > 0.f && fq > 0.f && r <= 0x1p64f) {
+  // sum_x min(ep r, eq) over the thread's tokens, by the |a - b| form
+  auto overlap = [&](float r) {
     float d0 = fabsf(fmaf(ep[0], r, -eq[0])), d1 = fabsf(fmaf(ep[1], r, -eq[1]));
     float d2 = fabsf(fmaf(ep[2], r, -eq[2])), d3 = fabsf(fmaf(ep[3], r, -eq[3]));
 #pragma unroll
@@ -622,22 +637,37 @@ __device__ __attribute__((always_inline)) void pair_phase2(const FusedParams& P,
       d2 += fabsf(fmaf(ep[j + 2], r, -eq[j + 2]));
       d3 += fabsf(fmaf(ep[j + 3], r, -eq[j + 3]));
     }
-    alpha_t = fmaxf(0.5f * (fmaf(r, sp, sq) - ((d0 + d1) + (d2 + d3))), 0.f) * fq;
+    return fmaxf(0.5f * (fmaf(r, sp, sq) - ((d0 + d1) + (d2 + d3))), 0.f);
+  };
+  float alpha_t = 0.f, lmin_t = 0.f;
+  const float r = fp / fq;
+  if (fp > 0.f && fq > 0.f && r <= 0x1p64f) alpha_t = overlap(r) * fq;
+  // The residual sum max(0, p - l q) = sum p - sum min(p, l q); with l = 1
+  // the second sum is alpha.  For l < 1 (only in the extended kernels, so the
+  // exact path carries no code for it) it is the same overlap with q scaled
+  // by l (ratio r / l).
+  lmin_t = alpha_t;
+  if constexpr (EXT) {
+    const float l = P.a.lenience;
+    if (l != 1.f) {
+      const float rl = r / l;
+      lmin_t = fp > 0.f && fq > 0.f && rl <= 0x1p64f ? overlap(rl) * (l * fq) : 0.f;
+    }
   }
-  const float res_t = fmaxf(sp * fp - alpha_t, 0.f);  // sum max(0, p - q) = sum p - sum min(p, q)
+  const float res_t = fmaxf(sp * fp - lmin_t, 0.f);
   const float alpha_w = wave_sum(alpha_t), res_w = wave_sum(res_t);
   if (wave_lane() == 0) st_u64(mine2, pack2(alpha_w, res_w));
 }
 
 // The three steps back to back: the tile stays in registers across the wait.
-template <class E, int PER>
+template <class E, int PER, bool EXT>
 __device__ __attribute__((always_inline)) void pair_compute_sample(const FusedParams& P, int item, int c, int lo,
                                                                    int parity, const RawPair<E, PER>& raw,
                                                                    uint64_t* w1, NormMsg* msg) {
   float ep[PER], eq[PER], mp, mq, sp, sq;
   pair_phase1<E, PER>(P, item, c, lo, raw, ep, eq, mp, mq, sp, sq);
   const NormMsg m = pair_wait(P, item, parity, w1, msg);
-  pair_phase2<PER>(P, item, c, m, ep, eq, mp, mq, sp, sq);
+  pair_phase2<PER, EXT>(P, item, c, m, ep, eq, mp, mq, sp, sq);
 }
 
 // Pair item at T = 0, or a bonus item: one pass, no waiting.
@@ -692,7 +722,7 @@ __device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 template <int PER>
 constexpr int stage_vectors() { return 2 * kWavesPerGroup * (PER / BF16::kVec) * kWave; }
 
-template <int PER, bool ARGMAX>
+template <int PER, bool ARGMAX, bool EXT>
 __device__ __attribute__((always_inline)) void compute_loop_staged(const FusedParams& P, int team, int rank,
                                                                    u32x4* stage, uint64_t* w1, NormMsg* msg) {
   using E = BF16;
@@ -713,7 +743,8 @@ __device__ __attribute__((always_inline)) void compute_loop_staged(const FusedPa
   auto issue = [&](int item) {  // waves 1..3
     const bool pair = item < P.n_pairs;
     const int b = pair ? item / a.gamma : item - P.n_pairs;
-    const int i = pair ? item % a.gamma : a.gamma;
+    // a bonus item reads row gamma_b (padding items are never issued)
+    const int i = pair ? item % a.gamma : seq_gamma_of<EXT>(a, b);
     const E::storage* prow = trow<E>(a, b, i);
     const E::storage* qrow = pair ? drow<E>(a, b, i) : prow;
     const int n = pair ? kLoads : kLoads / 2;
@@ -733,7 +764,7 @@ __device__ __attribute__((always_inline)) void compute_loop_staged(const FusedPa
   };
 
   int item = team;
-  if (wave != 0 && item < P.n_items) issue(item);
+  if (wave != 0 && item < P.n_items && !empty_item<EXT>(P, item)) issue(item);
   if (wave != 0) wait_vmem();
   lds_barrier();
   int parity = 0;
@@ -760,19 +791,21 @@ __device__ __attribute__((always_inline)) void compute_loop_staged(const FusedPa
     }
     lds_barrier();
     const int next = item + P.nteams;
-    if (wave != 0 && next < P.n_items) issue(next);
+    if (wave != 0 && next < P.n_items && !empty_item<EXT>(P, next)) issue(next);
     if constexpr (!ARGMAX && SPECV_FUSED_PIPELINE) {
       // Two pair items in flight: phase 1 of this item runs while the team
       // exchange of the previous one completes, and only then is the previous
       // one finished.  (Copying the new weights into the pending set costs a
       // register move per token but needs fewer registers than two sets that
-      // swap roles.)
-      if (item < P.n_pairs) {
+      // swap roles.)  A padding item does nothing: the pending item stays
+      // pending until the next pair or bonus item, or the end.
+      if (empty_item<EXT>(P, item)) {
+      } else if (item < P.n_pairs) {
         float xp[PER], xq[PER], cp, cq, s_p, s_q;
         pair_phase1<E, PER>(P, item, c, lo, A, xp, xq, cp, cq, s_p, s_q);
         if (pend >= 0) {
           const NormMsg m = pair_wait(P, pend, parity, w1, msg);
-          pair_phase2<PER>(P, pend, c, m, ep, eq, mp, mq, sp, sq);
+          pair_phase2<PER, EXT>(P, pend, c, m, ep, eq, mp, mq, sp, sq);
           parity ^= 1;
         }
 #pragma unroll
@@ -789,13 +822,14 @@ __device__ __attribute__((always_inline)) void compute_loop_staged(const FusedPa
         single_pass_compute<E, PER, ARGMAX>(P, item, c, lo, A);
         if (pend >= 0) {
           const NormMsg m = pair_wait(P, pend, parity, w1, msg);
-          pair_phase2<PER>(P, pend, c, m, ep, eq, mp, mq, sp, sq);
+          pair_phase2<PER, EXT>(P, pend, c, m, ep, eq, mp, mq, sp, sq);
           parity ^= 1;
           pend = -1;
         }
       }
+    } else if (empty_item<EXT>(P, item)) {
     } else if (!ARGMAX && item < P.n_pairs) {
-      pair_compute_sample<E, PER>(P, item, c, lo, parity, A, w1, msg);
+      pair_compute_sample<E, PER, EXT>(P, item, c, lo, parity, A, w1, msg);
       parity ^= 1;
     } else {
       single_pass_compute<E, PER, ARGMAX>(P, item, c, lo, A);
@@ -807,7 +841,7 @@ __device__ __attribute__((always_inline)) void compute_loop_staged(const FusedPa
   if constexpr (!ARGMAX && SPECV_FUSED_PIPELINE) {
     if (pend >= 0) {
       const NormMsg m = pair_wait(P, pend, parity, w1, msg);
-      pair_phase2<PER>(P, pend, c, m, ep, eq, mp, mq, sp, sq);
+      pair_phase2<PER, EXT>(P, pend, c, m, ep, eq, mp, mq, sp, sq);
     }
   }
 }
@@ -841,7 +875,7 @@ __device__ inline ArgMax combine_argmax(const uint64_t* w, int W, int half) {
 
 // Pair item: alpha, the ratio test and, after a rejection, the residual
 // sample.  Publishes (accept, token) for the sequence's bonus finisher.
-template <class E, int PER, bool ARGMAX>
+template <class E, int PER, bool ARGMAX, bool EXT>
 __device__ void finish_pair(const FusedParams& P, int item, uint64_t* w1, uint64_t* w2) {
   using S = SearchShape<E, PER>;
   __shared__ float lds_f[kMaxWaves];
@@ -859,6 +893,18 @@ __device__ void finish_pair(const FusedParams& P, int item, uint64_t* w1, uint64
   const size_t o = (size_t)b * G + i;
   uint64_t* part1 = P.part1 + (size_t)item * W * 2;
   uint64_t* part2 = P.part2 + (size_t)item * W;
+  const int gb = seq_gamma_of<EXT>(a, b);
+  if (i >= gb) {
+    // a padding position: no draft to test; its outputs say so with NaN, and
+    // the bonus finisher does not wait for it
+    if (threadIdx.x == 0) {
+      const float nan = __uint_as_float(0x7fc00000u);
+      if (a.alpha) a.alpha[o] = nan;
+      if (a.p_draft) a.p_draft[o] = nan;
+      if (a.q_draft) a.q_draft[o] = nan;
+    }
+    return;
+  }
 
   if constexpr (ARGMAX) {
     if (!gather(part1, 2 * W, w1)) {
@@ -928,9 +974,11 @@ __device__ void finish_pair(const FusedParams& P, int item, uint64_t* w1, uint64
       // accept iff u <= min(1, p(x) / q(x)) ([FI] Algorithm 1 step 3; [SD]
       // "The algorithm").  q(x) = 0 keeps the draft when p(x) > 0 (the ratio
       // is +inf) and rejects it when p(x) = 0 (0/0).
+      // With lenience l the comparison is against p(x) / (l q(x)) ([FI]
+      // "The acceptance rate is the overlap of p and q", lenience factor).
       const double u = (double)a.uniforms[(size_t)b * (G + 1) + i];
       if (qx > 0.0) {
-        const double ratio = px / qx;
+        const double ratio = px / ((double)a.lenience * qx);
         acc_s = (ratio >= 1.0) || (u <= ratio);
       } else {
         acc_s = px > 0.0;
@@ -943,11 +991,11 @@ __device__ void finish_pair(const FusedParams& P, int item, uint64_t* w1, uint64
     const int acc_i = acc_s;
     int mode = 0;
     if (!acc_i) {
-      const double uf = (double)a.uniforms[(size_t)b * (G + 1) + G];
+      const double uf = (double)a.uniforms[(size_t)b * (G + 1) + gb];  // the final sample's uniform
       // search groups of S::kGroup consecutive wave tiles, in token order
       const int ng = (W + S::kGroup - 1) / S::kGroup;
       if (sw_s > 0.0) {
-        mode = 1;  // residual max(0, p_i - q_i) ([FI] eq. (2); [SD] "Exactness")
+        mode = 1;  // residual max(0, p_i - l q_i) ([FI] eq. (2); [SD] "Exactness"; l = 1 there)
         wave_pick_tile(ng, uf * sw_s, [&](int g) {
           double m = 0.0;
           for (int c = g * S::kGroup; c < min(W, (g + 1) * S::kGroup); ++c) m += (double)hi_f(w2[c]);
@@ -964,7 +1012,7 @@ __device__ void finish_pair(const FusedParams& P, int item, uint64_t* w1, uint64
     }
     int t = 0;
     if (mode) {
-      const float invSp = (float)(1.0 / Sp), invSq = (float)(1.0 / Sq);
+      const float invSp = (float)(1.0 / Sp), invSq = (float)((double)a.lenience / Sq);  // l / S_q
       const int tlo = tile_s * S::kTokens;
       if (mode == 1)
         t = tile_search<E, S::kPer, kThreads>(prow, qrow, tlo, a.V, rest_s, [&](float xp, float xq) {
@@ -981,7 +1029,7 @@ __device__ void finish_pair(const FusedParams& P, int item, uint64_t* w1, uint64
 
 // Bonus item: the token from p_gamma ([FI] Algorithm 1 step 4), then the
 // sequence's outputs once every pair result of the sequence is published.
-template <class E, int PER, bool ARGMAX>
+template <class E, int PER, bool ARGMAX, bool EXT>
 __device__ void finish_bonus(const FusedParams& P, int item, uint64_t* w1, uint64_t* res) {
   using S = SearchShape<E, PER>;
   __shared__ float lds_f[kMaxWaves];
@@ -993,7 +1041,8 @@ __device__ void finish_bonus(const FusedParams& P, int item, uint64_t* w1, uint6
   const int G = a.gamma, W = P.W;
   const int b = item - P.n_pairs;
   const float k = a.k;
-  const auto* row = trow<E>(a, b, G);
+  const int gb = seq_gamma_of<EXT>(a, b);
+  const auto* row = trow<E>(a, b, gb);  // the bonus row follows the sequence's last draft
   uint64_t* part1 = P.part1 + (size_t)item * W * 2;
   const bool ok1 = gather(part1, 2 * W, w1);
   if (ok1) clear_slots(part1, 2 * W);
@@ -1011,7 +1060,7 @@ __device__ void finish_bonus(const FusedParams& P, int item, uint64_t* w1, uint6
     }
     __syncthreads();
     const float M = M_s;
-    const double uf = (double)a.uniforms[(size_t)b * (G + 1) + G];
+    const double uf = (double)a.uniforms[(size_t)b * (G + 1) + gb];
     wave_pick_tile((W + S::kGroup - 1) / S::kGroup, uf * S_s, [&](int g) {
       double m = 0.0;
       for (int c = g * S::kGroup; c < min(W, (g + 1) * S::kGroup); ++c) m += p_tile_mass(w1, c, M);
@@ -1022,14 +1071,14 @@ __device__ void finish_bonus(const FusedParams& P, int item, uint64_t* w1, uint6
                                                    lds_f, lds_i);
   }
   // the sequence's pair results (published by other finishers)
-  const bool ok2 = gather(P.pair_res + (size_t)b * G, G, res);
-  if (ok2) clear_slots(P.pair_res + (size_t)b * G, G);
+  const bool ok2 = gather(P.pair_res + (size_t)b * G, gb, res);
+  if (ok2) clear_slots(P.pair_res + (size_t)b * G, gb);
   if (threadIdx.x == 0) {
     if (ok1 && ok2) {
       int n = 0;
-      while (n < G && ((uint32_t)res[n] & 1u) != 0u) ++n;
+      while (n < gb && ((uint32_t)res[n] & 1u) != 0u) ++n;
       a.n_out[b] = n;
-      a.t_out[b] = n < G ? (int)(uint32_t)(res[n] >> 32) : t_bonus;
+      a.t_out[b] = n < gb ? (int)(uint32_t)(res[n] >> 32) : t_bonus;
     } else {
       a.n_out[b] = -1;  // a wait gave up (the device was shared): no result
       a.t_out[b] = -1;
@@ -1052,7 +1101,7 @@ struct Pool {
   static constexpr int kBytes = kABytes + 2 * kMaxWaveTiles * 8 + 2 * (int)sizeof(NormMsg);
 };
 
-template <class E, int PER, bool ARGMAX>
+template <class E, int PER, bool ARGMAX, bool EXT>
 __global__ __launch_bounds__(kThreads, SPECV_FUSED_MIN_WAVES) void fused_kernel(FusedParams P) {
   using L = Pool<E, PER>;
   __shared__ __align__(16) unsigned char pool[L::kBytes];
@@ -1080,16 +1129,17 @@ __global__ __launch_bounds__(kThreads, SPECV_FUSED_MIN_WAVES) void fused_kernel(
   }
   if (team >= 0) {
     if constexpr (L::kStaged) {
-      compute_loop_staged<PER, ARGMAX>(P, team, rank, reinterpret_cast<u32x4*>(pool), poll_buf, msg);
+      compute_loop_staged<PER, ARGMAX, EXT>(P, team, rank, reinterpret_cast<u32x4*>(pool), poll_buf, msg);
     } else {
       const int c = rank * kWavesPerGroup + (int)threadIdx.x / kWave;  // this wave's tile
       const int lo = c * kWave * PER;
       int parity = 0;
       for (int item = team; item < P.n_items; item += P.nteams) {
+        if (empty_item<EXT>(P, item)) continue;
         RawPair<E, PER> A;
-        issue_item<E, PER>(P, item, lo, A);
+        issue_item<E, PER, EXT>(P, item, lo, A);
         if (!ARGMAX && item < P.n_pairs) {
-          pair_compute_sample<E, PER>(P, item, c, lo, parity, A, poll_buf, msg);
+          pair_compute_sample<E, PER, EXT>(P, item, c, lo, parity, A, poll_buf, msg);
           parity ^= 1;
         } else {
           single_pass_compute<E, PER, ARGMAX>(P, item, c, lo, A);
@@ -1101,9 +1151,9 @@ __global__ __launch_bounds__(kThreads, SPECV_FUSED_MIN_WAVES) void fused_kernel(
     // on an item it has yet to finish itself
     for (int item = f; item < P.n_items; item += P.nfin) {
       if (item < P.n_pairs)
-        finish_pair<E, PER, ARGMAX>(P, item, fin_w1, fin_w2);
+        finish_pair<E, PER, ARGMAX, EXT>(P, item, fin_w1, fin_w2);
       else
-        finish_bonus<E, PER, ARGMAX>(P, item, fin_w1, fin_res);
+        finish_bonus<E, PER, ARGMAX, EXT>(P, item, fin_w1, fin_res);
     }
   }
 }
@@ -1151,7 +1201,7 @@ hipError_t resident_blocks(Kern kern, long* out) {
   return e;
 }
 
-template <class E, bool ARGMAX>
+template <class E, bool ARGMAX, bool EXT = false>
 hipError_t launch(const VerifyArgs& a, hipStream_t s) {
   const Layout L = layout(a.B, a.gamma, a.V);
   char* ws = static_cast<char*>(a.ws);
@@ -1165,7 +1215,7 @@ hipError_t launch(const VerifyArgs& a, hipStream_t s) {
   P.part2 = reinterpret_cast<uint64_t*>(ws + L.off_part2);
   P.pair_res = reinterpret_cast<uint64_t*>(ws + L.off_res);
 
-  auto kern = fused_kernel<E, per_of<E>(), ARGMAX>;
+  auto kern = fused_kernel<E, per_of<E>(), ARGMAX, EXT>;
   long resident = 0;
   hipError_t e = resident_blocks(kern, &resident);
   if (e != hipSuccess) return e;
@@ -1203,8 +1253,15 @@ hipError_t fused_launch(const VerifyArgs& a, hipStream_t s) {
   if (!fused_supported(a.B, a.gamma, a.V, a.dtype)) return hipErrorNotSupported;
   if ((uintptr_t)a.target % 16 != 0 || (a.gamma > 0 && (uintptr_t)a.draft % 16 != 0)) return hipErrorNotSupported;
   const bool argmax = a.temperature == 0.f;
-  if (a.dtype == SPEC_BF16) return argmax ? launch<BF16, true>(a, s) : launch<BF16, false>(a, s);
-  return argmax ? launch<F32, true>(a, s) : launch<F32, false>(a, s);
+  // The extended kernels take lenience below 1 and per-sequence draft counts;
+  // lenience does not change argmax mode.
+  const bool ext = a.gamma_seq != nullptr || (!argmax && a.lenience != 1.f);
+  if (a.dtype == SPEC_BF16) {
+    if (argmax) return ext ? launch<BF16, true, true>(a, s) : launch<BF16, true>(a, s);
+    return ext ? launch<BF16, false, true>(a, s) : launch<BF16, false>(a, s);
+  }
+  if (argmax) return ext ? launch<F32, true, true>(a, s) : launch<F32, true>(a, s);
+  return ext ? launch<F32, false, true>(a, s) : launch<F32, false>(a, s);
 }
 
 }  // namespace specv

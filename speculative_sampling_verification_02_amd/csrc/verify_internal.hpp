@@ -24,7 +24,16 @@ struct VerifyArgs {
   float* q_draft;          // may be null
   void* ws;
   size_t ws_bytes;
+  float lenience;              // l in (0, 1]; 1 = exact speculative sampling
+  const int32_t* gamma_seq;    // [B] per-sequence draft counts, or null (all gamma)
 };
+
+// Draft count of sequence b: gamma_seq[b] clamped into [0, gamma], or gamma.
+__device__ inline int seq_gamma(const VerifyArgs& a, int b) {
+  if (!a.gamma_seq) return a.gamma;
+  const int g = a.gamma_seq[b];
+  return g < 0 ? 0 : (g > a.gamma ? a.gamma : g);
+}
 
 // ---- multi-pass path
 size_t multipass_workspace_bytes(int B, int gamma, int V);

@@ -104,6 +104,14 @@ __global__ __launch_bounds__(kThreads) void row_stats_kernel(VerifyArgs a, float
   const int c = blockIdx.x % nch;
   const int lo = c * kChunk, hi = min(a.V, lo + kChunk);
   const auto* r = row_ptr<E>(a, row);
+  if (a.gamma_seq) {
+    // rows past a sequence's draft count are padding: never read
+    const size_t nt = (size_t)a.B * (a.gamma + 1);
+    const bool target = row < nt;
+    const int b = target ? (int)(row / (a.gamma + 1)) : (int)((row - nt) / a.gamma);
+    const int i = target ? (int)(row % (a.gamma + 1)) : (int)((row - nt) % a.gamma);
+    if (i > seq_gamma(a, b) - (target ? 0 : 1)) return;
+  }
 
   if constexpr (VEC) {
     ChunkRegs<E> ch;
@@ -179,7 +187,9 @@ __global__ __launch_bounds__(kThreads) void pair_overlap_kernel(VerifyArgs a, co
   const int pair = blockIdx.x / nch;  // b * gamma + i
   const int c = blockIdx.x % nch;
   const int b = pair / a.gamma, i = pair % a.gamma;
+  if (i >= seq_gamma(a, b)) return;  // a padding position
   const size_t rp = target_row(b, i, a.gamma), rq = draft_row(b, i, a.gamma, a.B);
+  const float l = a.lenience;  // the residual is max(0, p - l q)
   const float k = a.k;
   const int lo = c * kChunk, hi = min(a.V, lo + kChunk);
   const auto* p_row = row_ptr<E>(a, rp);
@@ -206,7 +216,7 @@ __global__ __launch_bounds__(kThreads) void pair_overlap_kernel(VerifyArgs a, co
     for (int t = 0; t < ChunkRegs<E>::kPer; ++t) {
       const float p = prob(cp.x[t], np.M, np.invS, k), q = prob(cq.x[t], nq.M, nq.invS, k);
       mn[t & 1] += fminf(p, q);
-      rs[t & 1] += fmaxf(p - q, 0.f);
+      rs[t & 1] += fmaxf(p - l * q, 0.f);
     }
     acc_min = mn[0] + mn[1];
     acc_res = rs[0] + rs[1];
@@ -214,7 +224,7 @@ __global__ __launch_bounds__(kThreads) void pair_overlap_kernel(VerifyArgs a, co
     for (int j = lo + threadIdx.x; j < hi; j += kThreads) {
       const float p = prob(E::at(p_row, j), np.M, np.invS, k), q = prob(E::at(q_row, j), nq.M, nq.invS, k);
       acc_min += fminf(p, q);
-      acc_res += fmaxf(p - q, 0.f);
+      acc_res += fmaxf(p - l * q, 0.f);
     }
   }
   const float2 r = block_sum2(acc_min, acc_res, lds_f);
@@ -247,28 +257,37 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(VerifyArgs a, float2* 
   __shared__ double prefix_s;
   __shared__ int n_s, chunk_s;
   __shared__ float theta_s;
-  const int b = blockIdx.x, G = a.gamma, nch = num_chunks(a.V);
+  // G is the padded draft count (the row stride), Gb this sequence's own
+  const int b = blockIdx.x, G = a.gamma, nch = num_chunks(a.V), Gb = seq_gamma(a, b);
   const float k = a.k;
   const int tid = threadIdx.x;
   const float* u = a.uniforms + (size_t)b * (G + 1);
+  if (tid >= Gb && tid < G) {
+    // padding positions report NaN
+    const float nan = __uint_as_float(0x7fc00000u);
+    const size_t o = (size_t)b * G + tid;
+    if (a.alpha) a.alpha[o] = nan;
+    if (a.p_draft) a.p_draft[o] = nan;
+    if (a.q_draft) a.q_draft[o] = nan;
+  }
 
   if (a.temperature == 0.f) {
     // ---- argmax mode: combine each row's chunk argmaxes
     __shared__ int amax_t[SPEC_MAX_GAMMA + 1], amax_d[SPEC_MAX_GAMMA];
-    if (tid <= G) {
+    if (tid <= Gb) {
       const float2* st = stats + target_row(b, tid, G) * nch;
       ArgMax best{-INFINITY, 0x7fffffff};
       for (int c = 0; c < nch; ++c) best = argmax_better(best, ArgMax{st[c].x, __float_as_int(st[c].y)});
       amax_t[tid] = best.i;
     }
-    if (tid < G) {
+    if (tid < Gb) {
       const float2* st = stats + draft_row(b, tid, G, a.B) * nch;
       ArgMax best{-INFINITY, 0x7fffffff};
       for (int c = 0; c < nch; ++c) best = argmax_better(best, ArgMax{st[c].x, __float_as_int(st[c].y)});
       amax_d[tid] = best.i;
     }
     __syncthreads();
-    if (tid < G) {
+    if (tid < Gb) {
       const int x = a.tokens[(size_t)b * G + tid];
       const size_t o = (size_t)b * G + tid;
       accept_s[tid] = (x == amax_t[tid]);
@@ -280,7 +299,7 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(VerifyArgs a, float2* 
     clear_sequence_stats(a, stats, pair_stats, b, nch);
     if (tid == 0) {
       int n = 0;
-      while (n < G && accept_s[n]) ++n;
+      while (n < Gb && accept_s[n]) ++n;
       a.n_out[b] = n;
       a.t_out[b] = amax_t[n];
     }
@@ -290,7 +309,7 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(VerifyArgs a, float2* 
   // ---- ratio tests ([FI] Algorithm 1 step 3; [SD] "The algorithm"), in fp64.
   // Wave w handles draft positions w, w + 4, ...; lane 0 does the test.
   const int wid = tid / kWave, lane = tid & (kWave - 1), nw = kThreads / kWave;
-  for (int i = wid; i < G; i += nw) {
+  for (int i = wid; i < Gb; i += nw) {
     const size_t rp = target_row(b, i, G), rq = draft_row(b, i, G, a.B);
     const RowNorm np = row_norm(stats, rp, nch, k), nq = row_norm(stats, rq, nch, k);
     const size_t o = (size_t)b * G + i;
@@ -306,8 +325,9 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(VerifyArgs a, float2* 
       }
       // q(x) = 0 keeps the draft when p(x) > 0 (ratio +inf) and rejects it
       // when p(x) = 0 (0/0)
+      // with lenience l the comparison is against p(x) / (l q(x))
       if (qx > 0.0) {
-        const double ratio = px / qx;
+        const double ratio = px / ((double)a.lenience * qx);
         accept_s[i] = (ratio >= 1.0) || ((double)u[i] <= ratio);
       } else {
         accept_s[i] = px > 0.0;
@@ -320,20 +340,20 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(VerifyArgs a, float2* 
   __syncthreads();
   if (tid == 0) {
     int n = 0;
-    while (n < G && accept_s[n]) ++n;
+    while (n < Gb && accept_s[n]) ++n;
     n_s = n;
   }
   __syncthreads();
   const int n = n_s;
 
   // ---- the sampled row's chunk masses, in chunk order: the residual
-  // max(0, p_n - q_n) ([FI] eq. (2); [SD] "Exactness") when a draft was
-  // rejected, else p_gamma (the bonus token).  A residual with no mass
+  // max(0, p_n - l q_n) ([FI] eq. (2); [SD] "Exactness"; l = 1 there) when a
+  // draft was rejected, else p_{gamma_b} (the bonus token).  A residual with no mass
   // (impossible in exact arithmetic after a rejection) falls back to p_n.
-  const float2* res_st = n < G ? pair_stats + ((size_t)b * G + n) * nch : nullptr;
+  const float2* res_st = n < Gb ? pair_stats + ((size_t)b * G + n) * nch : nullptr;
   const float2* row_st = stats + target_row(b, n, G) * nch;
   __shared__ RowNorm norm_s[2];
-  if (wid < 2 && (wid == 0 || n < G)) {
+  if (wid < 2 && (wid == 0 || n < Gb)) {
     const RowNorm nr = row_norm(stats, wid == 0 ? target_row(b, n, G) : draft_row(b, n, G, a.B), nch, k);
     if (lane == 0) norm_s[wid] = nr;
   }
@@ -351,7 +371,7 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(VerifyArgs a, float2* 
   };
   part = 0.0;
   for (int c = tid; c < nch; c += kThreads) part += (double)mass(c);
-  const double theta = (double)u[G] * block_sum(part, lds_d);
+  const double theta = (double)u[Gb] * block_sum(part, lds_d);  // the final sample's uniform
 
   // ---- locate the chunk holding theta: stage up to kThreads masses in LDS
   // with one parallel load, then scan them in order on one thread.
@@ -395,7 +415,8 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(VerifyArgs a, float2* 
   if (residual) {
     const RowNorm nq = norm_s[1];
     const auto* q_row = row_ptr<E>(a, draft_row(b, n, G, a.B));
-    auto w = [&](float xp, float xq) { return fmaxf(prob(xp, np.M, np.invS, k) - prob(xq, nq.M, nq.invS, k), 0.f); };
+    const float l = a.lenience;
+    auto w = [&](float xp, float xq) { return fmaxf(prob(xp, np.M, np.invS, k) - l * prob(xq, nq.M, nq.invS, k), 0.f); };
     if constexpr (VEC)
       t = tile_search<E, kChunk / kThreads, kThreads>(p_row, q_row, lo, a.V, theta_s, w, lds_f, lds_i);
     else

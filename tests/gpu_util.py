@@ -28,13 +28,16 @@ def case_tensors(case, dev):
     )
 
 
-def run_case(case, algo, tensors=None, dev=None):
+def run_case(case, algo, tensors=None, dev=None, lenience: float = 1.0, gamma_seq=None, workspace=None):
+    """gamma_seq: numpy int [B] (per-sequence draft counts) or None."""
     import torch
     import speculative_sampling_verification_02_amd as sv
     dev = dev or device()
     t = tensors or case_tensors(case, dev)
+    gs = None if gamma_seq is None else torch.from_numpy(np.ascontiguousarray(gamma_seq, dtype=np.int32)).to(dev)
     try:
-        out = sv.verify(t["target"], t["draft"], t["tokens"], t["uniforms"], case.temperature, algo=algo)
+        out = sv.verify(t["target"], t["draft"], t["tokens"], t["uniforms"], case.temperature, algo=algo,
+                        lenience=lenience, gamma_seq=gs, workspace=workspace)
     except sv.SpecVerifyError as e:
         if e.status == sv.SPEC_EUNSUPPORTED and algo == sv.ALGO_FUSED:
             import pytest

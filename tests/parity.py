@@ -12,6 +12,7 @@ The bar:
     must still be a valid draw: positive weight, with u inside its CDF interval
     widened by CDF_EPS.
   * alpha, p_draft and q_draft agree within 1e-5 absolute.
+  * With per-sequence draft counts, the padding positions are NaN on both sides.
 
 CDF_EPS comes from the GPU's fp32 arithmetic.  Each weight carries a few ulps
 from exp2 and the 1/S scaling (relative ~1e-6 at exponent arguments near 30).
@@ -52,23 +53,26 @@ def _cdf_interval(w: np.ndarray, t: int):
     return lo, c[t]
 
 
-def check(case, gpu: dict, seqs=None, where: str = "") -> Report:
-    """Compare GPU outputs (numpy dict, full batch) with the oracle on `seqs`."""
+def check(case, gpu: dict, seqs=None, where: str = "", lenience: float = 1.0, gamma_seq=None) -> Report:
+    """Compare GPU outputs (numpy dict, full batch) with the oracle on `seqs`.
+
+    lenience and gamma_seq (numpy int [B]) are passed to the oracle unchanged."""
     if seqs is None:
         seqs = np.arange(case.B)
     seqs = np.asarray(seqs)
-    res = ov.verify_case(case, keep_weights=case.temperature > 0, seqs=seqs)
+    res = ov.verify_case(case, keep_weights=case.temperature > 0, seqs=seqs, lenience=lenience,
+                         gamma_seq=gamma_seq)
     g = {k: np.asarray(v)[seqs] for k, v in gpu.items()}
     rep = Report(rows=len(seqs))
     G = case.gamma
+    gb = np.full(len(seqs), G) if gamma_seq is None else np.asarray(gamma_seq)[seqs]
 
     if case.temperature == 0.0:
         assert np.array_equal(g["n_accepted"], res.n_accepted), where
         assert np.array_equal(g["next_token"], res.next_token), where
         if G:
-            assert np.array_equal(g["alpha"], res.alpha.astype(np.float32)), where
-            assert np.array_equal(g["p_draft"], res.p_draft.astype(np.float32)), where
-            assert np.array_equal(g["q_draft"], res.q_draft.astype(np.float32)), where
+            for key, ref in (("alpha", res.alpha), ("p_draft", res.p_draft), ("q_draft", res.q_draft)):
+                assert np.array_equal(g[key], ref.astype(np.float32), equal_nan=True), f"{where}: {key}"
         return rep
 
     band = res.u_band
@@ -88,12 +92,14 @@ def check(case, gpu: dict, seqs=None, where: str = "") -> Report:
                               f"{seqs[r]} (margin {res.cdf_margin[r]:.3g})")
         w = res.weights[r]
         lo, hi = _cdf_interval(w, t_gpu)
-        u = float(case.uniforms[seqs[r], G])
+        u = float(case.uniforms[seqs[r], gb[r]])
         assert w[t_gpu] > 0 and lo - CDF_EPS <= u < hi + CDF_EPS, f"{where}: invalid token in row {seqs[r]}"
         rep.token_mismatch_valid += 1
 
     if G:
         for key, ref in (("alpha", res.alpha), ("p_draft", res.p_draft), ("q_draft", res.q_draft)):
-            err = np.abs(g[key].astype(np.float64) - ref)
+            pad = np.isnan(ref)
+            assert np.array_equal(np.isnan(g[key]), pad), f"{where}: {key} padding positions differ"
+            err = np.abs(g[key].astype(np.float64) - ref)[~pad]
             assert np.all(err <= PROB_TOL), f"{where}: {key} max error {err.max():.3g}"
     return rep
