@@ -61,12 +61,13 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(n_accepted: np.ndarray, gamma: int, V: int, elem: int) -> int:
-    """Bytes the method must read per call: the 2*gamma draft/target rows of every
+def algorithmic_bytes(n_accepted: np.ndarray, gamma: int, V: int, elem: int, gamma_seq=None) -> int:
+    """Bytes the method must read per call: the 2*gamma_b draft/target rows of every
     sequence (all overlaps are reported), the bonus row only where every draft was
     kept, plus tokens, uniforms and outputs."""
     B = len(n_accepted)
-    rows = 2 * gamma * B + int((n_accepted == gamma).sum())
+    gb = np.full(B, gamma) if gamma_seq is None else np.asarray(gamma_seq)
+    rows = 2 * int(gb.sum()) + int((n_accepted == gb).sum())
     small = 4 * B * gamma + 4 * B * (gamma + 1) + 4 * B * (2 + 3 * gamma)
     return rows * V * elem + small
 
@@ -142,6 +143,9 @@ def main() -> int:
                          "gamma=8, V=256000 bf16")
     ap.add_argument("--temperature", type=float, default=1.0,
                     help="temperature of the verify workloads (0: argmax mode)")
+    ap.add_argument("--lenience", type=float, default=1.0, help="lenience factor l in (0, 1] (spec_verify_ex)")
+    ap.add_argument("--ragged", action="store_true",
+                    help="per-sequence draft counts gamma_b ~ U{1..gamma} (seeded; spec_verify_ex)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -175,6 +179,8 @@ def main() -> int:
     uniforms = torch.from_numpy(case.uniforms).to(dev)
     ws = torch.zeros(sv.workspace_size(B, G, V, sv.SPEC_BF16 if bf16 else sv.SPEC_F32), dtype=torch.uint8,
                      device=dev)
+    gseq_np = np.random.default_rng([0, 0x6A]).integers(1, G + 1, size=B) if args.ragged else None
+    gseq = None if gseq_np is None else torch.from_numpy(gseq_np.astype(np.int32)).to(dev)
     outs = [{k: torch.empty(s, dtype=dt, device=dev) for k, s, dt in (
         ("n_accepted", (B,), torch.int32), ("next_token", (B,), torch.int32),
         ("alpha", (B, G), torch.float32), ("p_draft", (B, G), torch.float32),
@@ -182,7 +188,8 @@ def main() -> int:
 
     # one prepared launch per buffer set: the timed loop then spends only the
     # C call on the host, well under the kernel's duration
-    launches = [sv.prepare_verify(t, d, tokens, uniforms, T, algo=algo, workspace=ws, outputs=o)
+    launches = [sv.prepare_verify(t, d, tokens, uniforms, T, algo=algo, workspace=ws, outputs=o,
+                                  lenience=args.lenience, gamma_seq=gseq)
                 for (t, d), o in zip(sets, outs)]
 
     def step(k):
@@ -205,14 +212,14 @@ def main() -> int:
     ms_per_step = 1e3 * elapsed / args.steps
     rows = B * (G + 1)
     n0 = outs[0]["n_accepted"].cpu().numpy()
-    alg = algorithmic_bytes(n0, G, V, elem)
+    alg = algorithmic_bytes(n0, G, V, elem, gseq_np)
     avg_launch_s = launch_us.mean * 1e-6
     achieved = alg / avg_launch_s / 1e9
     algo_name = {sv.ALGO_AUTO: "auto", sv.ALGO_MULTIPASS: "multipass", sv.ALGO_FUSED: "fused"}[algo]
     # AUTO dispatches the headline workload (aligned bf16 rows, 16 workgroups
     # per row) to the fused kernel, whose counters the traffic record holds
     traffic = None
-    if args.workload == "verify" and T == 1.0:
+    if args.workload == "verify" and T == 1.0 and args.lenience == 1.0 and not args.ragged:
         traffic = load_traffic("fused" if algo_name == "auto" else algo_name)
     line = {
         "metric": METRIC,
@@ -230,13 +237,14 @@ def main() -> int:
         "config": {"workload": f"spec_verify B={B} gamma={G} V={V} {case.dtype} logits T={T:g}, "
                                + WORKLOAD_TEXT[args.workload],
                    "B": B, "gamma": G, "V": V, "logits": case.dtype, "temperature": T,
-                   "algo": algo_name, "buffer_sets": len(sets)},
+                   "algo": algo_name, "buffer_sets": len(sets), "lenience": args.lenience,
+                   "gamma_seq": None if gseq_np is None else "U{1..gamma}, mean %.2f" % gseq_np.mean()},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "launch_us_mean": launch_us.mean,
                      "alg_bytes": alg, "full_bytes": (2 * G + 1) * V * elem * B},
     }
-    if not args.no_cpu_baseline and args.workload == "verify":
+    if not args.no_cpu_baseline and args.workload == "verify" and args.lenience == 1.0 and not args.ragged:
         line["cpu_baseline"] = cpu_baseline(case)
     print(json.dumps(line), flush=True)
     return 0

@@ -195,20 +195,23 @@ def prepare_verify(target_logits, draft_logits, draft_tokens, uniforms, temperat
     """Checks the arguments of verify() once and returns a callable that
     launches that same verification again (same tensors, current stream at
     preparation) with no per-call Python work beyond the C call, for loops
-    whose host time per step must stay well under the kernel's.  The tensors
-    must stay alive and unchanged in shape while the callable is used."""
+    whose host time per step must stay well under the kernel's.  The callable
+    holds references to every tensor it launches on, so they stay allocated
+    while it lives; their shapes and contents are the caller's to keep."""
     verify(target_logits, draft_logits, draft_tokens, uniforms, temperature, algo=algo, workspace=workspace,
            outputs=outputs, lenience=lenience, gamma_seq=gamma_seq)
     B, g1, V = target_logits.shape
     args = _verify_args(algo, target_logits, draft_logits, _dtype_code(target_logits), draft_tokens, uniforms,
                         B, g1 - 1, V, temperature, lenience, gamma_seq, outputs, workspace, target_logits.device)
     fn = lib.spec_verify_ex
+    keep = (target_logits, draft_logits, draft_tokens, uniforms, gamma_seq, workspace, dict(outputs))
 
     def launch():
         status = fn(*args)
         if status != 0:
             _check(status, "spec_verify")
 
+    launch.tensors = keep  # the device buffers behind the raw pointers in args
     return launch
 
 
