@@ -56,6 +56,8 @@ import dataclasses
 
 import numpy as np
 
+from oracle import adjust
+
 # |u_i - min(1, p_i(x_i)/q_i(x_i))| below this marks a decision that fp32 on the
 # GPU and fp64 here may take differently.
 U_BAND = 1e-6
@@ -167,9 +169,11 @@ class Result:
     cdf_margin: np.ndarray      # float64 [B]: min_j |u_gamma - cdf_j| of the sampled row
     residual: np.ndarray        # bool [B]: sampled from a residual (else bonus / argmax)
     weights: np.ndarray | None  # float64 [B, V] normalised sampling row, if requested
+    filter_margin: np.ndarray | None = None  # float64 [B]: smallest top-p margin of the sequence's rows
 
 
-def _verify_block(target, draft, tokens, u, temperature, dtype, keep_weights, lenience=1.0, gseq=None):
+def _verify_block(target, draft, tokens, u, temperature, dtype, keep_weights, lenience=1.0, gseq=None,
+                  top_k=0, top_p=1.0):
     tl = widen(target, dtype)            # [b, gamma+1, V]
     dl = widen(draft, dtype)             # [b, gamma, V]
     nb, g1, V = tl.shape
@@ -185,6 +189,13 @@ def _verify_block(target, draft, tokens, u, temperature, dtype, keep_weights, le
         # padding rows take no part: zero them so nothing of theirs can leak in
         tl = np.where((np.arange(g1)[None, :] <= gb[:, None])[..., None], tl, 0.0)
         dl = np.where(live[..., None], dl, 0.0)
+    fmargin = np.full(nb, np.inf)
+    if temperature > 0.0 and ((0 < top_k < V) or top_p < 1.0):
+        # top-k / top-p adjust p and q the same way before anything else
+        tau_t, mg_t = adjust.thresholds(tl, temperature, top_k, top_p)
+        tau_d, mg_d = adjust.thresholds(dl, temperature, top_k, top_p)
+        tl, dl = adjust.apply(tl, tau_t), adjust.apply(dl, tau_d)
+        fmargin = np.minimum(mg_t.min(axis=-1), mg_d.min(axis=-1) if gamma else np.inf)
 
     if temperature == 0.0:
         a = argmax_first(tl)             # target argmax per position
@@ -200,7 +211,7 @@ def _verify_block(target, draft, tokens, u, temperature, dtype, keep_weights, le
             weights = np.zeros((nb, V))
             weights[rows, t] = 1.0
         return Result(n, t, alpha, 1.0 - alpha, p_x, q_x, np.zeros(nb, bool),
-                      np.full(nb, np.inf), np.zeros(nb, bool), weights)
+                      np.full(nb, np.inf), np.zeros(nb, bool), weights, fmargin)
 
     p = softmax(tl, temperature)         # [b, gamma+1, V]
     q = softmax(dl, temperature)         # [b, gamma, V]
@@ -231,18 +242,19 @@ def _verify_block(target, draft, tokens, u, temperature, dtype, keep_weights, le
     t, cdf = inverse_cdf(w, u_final.astype(np.float64))
     margin = np.abs(cdf - u_final[:, None]).min(axis=-1)
     return Result(n, t, alpha, tv, p_x, q_x, u_band, margin, residual,
-                  w if keep_weights else None)
+                  w if keep_weights else None, fmargin)
 
 
 def verify(target, draft, tokens, uniforms, temperature: float, dtype: str,
            keep_weights: bool = False, block_elems: int = 1 << 25, lenience: float = 1.0,
-           gamma_seq=None) -> Result:
+           gamma_seq=None, top_k: int = 0, top_p: float = 1.0) -> Result:
     """Run the verification step for every sequence of the batch.
 
     target [B, gamma+1, V], draft [B, gamma, V] (float32, or uint16 bf16 bits),
     tokens int [B, gamma], uniforms float32 [B, gamma+1] in (0, 1).
     lenience l in (0, 1] and gamma_seq int [B] with 0 <= gamma_b <= gamma are the
-    two extensions described in the module notes.
+    two extensions described in the module notes; top_k and top_p adjust every
+    row first (oracle/adjust.py; top_k <= 0 and top_p >= 1 disable them).
     Sequences are independent, so they are processed in blocks to bound memory.
     """
     target = np.asarray(target)
@@ -255,6 +267,8 @@ def verify(target, draft, tokens, uniforms, temperature: float, dtype: str,
         raise ValueError("temperature must be finite and >= 0")
     if not (0.0 < lenience <= 1.0):
         raise ValueError("lenience must be in (0, 1]")
+    if not (top_p > 0.0):
+        raise ValueError("top_p must be > 0")
     if gamma_seq is not None:
         gamma_seq = np.asarray(gamma_seq, dtype=np.int64).reshape(B)
         if (gamma_seq < 0).any() or (gamma_seq > gamma).any():
@@ -265,7 +279,7 @@ def verify(target, draft, tokens, uniforms, temperature: float, dtype: str,
     step = max(1, block_elems // per_seq)
     parts = [_verify_block(target[s:s + step], draft[s:s + step], tokens[s:s + step],
                            u[s:s + step], temperature, dtype, keep_weights, lenience,
-                           None if gamma_seq is None else gamma_seq[s:s + step])
+                           None if gamma_seq is None else gamma_seq[s:s + step], top_k, top_p)
              for s in range(0, B, step)]
     if not parts:
         z = np.zeros(0)
@@ -275,14 +289,16 @@ def verify(target, draft, tokens, uniforms, temperature: float, dtype: str,
     cat = lambda f: np.concatenate([getattr(r, f) for r in parts])  # noqa: E731
     return Result(cat("n_accepted"), cat("next_token"), cat("alpha"), cat("tv"),
                   cat("p_draft"), cat("q_draft"), cat("u_band"), cat("cdf_margin"),
-                  cat("residual"), cat("weights") if keep_weights else None)
+                  cat("residual"), cat("weights") if keep_weights else None, cat("filter_margin"))
 
 
-def verify_case(case, keep_weights: bool = False, seqs=None, lenience: float = 1.0, gamma_seq=None) -> Result:
+def verify_case(case, keep_weights: bool = False, seqs=None, lenience: float = 1.0, gamma_seq=None,
+                top_k: int = 0, top_p: float = 1.0) -> Result:
     """verify() on a workloads.VerifyCase, optionally on a subset of sequences."""
     if seqs is not None:
         case = case.subset(seqs)
         if gamma_seq is not None:
             gamma_seq = np.asarray(gamma_seq)[np.asarray(seqs)]
     return verify(case.target, case.draft, case.tokens, case.uniforms,
-                  case.temperature, case.dtype, keep_weights, lenience=lenience, gamma_seq=gamma_seq)
+                  case.temperature, case.dtype, keep_weights, lenience=lenience, gamma_seq=gamma_seq,
+                  top_k=top_k, top_p=top_p)

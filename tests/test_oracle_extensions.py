@@ -256,10 +256,10 @@ def test_planted_mistakes_in_the_extensions_are_caught(mutant, monkeypatch):
         check = lambda: test_lenient_exact_enumeration("W100", F(1, 2))  # noqa: E731
     else:
         # the bonus row of a ragged sequence taken from the padded position gamma
-        def block(target, draft, tokens, u, T, dtype, keep, lenience=1.0, gseq=None):
-            r = orig_block(target, draft, tokens, u, T, dtype, keep, lenience, gseq)
+        def block(target, draft, tokens, u, T, dtype, keep, lenience=1.0, gseq=None, *rest):
+            r = orig_block(target, draft, tokens, u, T, dtype, keep, lenience, gseq, *rest)
             if gseq is not None:
-                full = orig_block(target, draft, tokens, u, T, dtype, keep, lenience, None)
+                full = orig_block(target, draft, tokens, u, T, dtype, keep, lenience, None, *rest)
                 allk = r.n_accepted == np.asarray(gseq)
                 r.next_token = np.where(allk, full.next_token, r.next_token)
             return r
