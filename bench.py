@@ -61,13 +61,15 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(n_accepted: np.ndarray, gamma: int, V: int, elem: int, gamma_seq=None) -> int:
+def algorithmic_bytes(n_accepted: np.ndarray, gamma: int, V: int, elem: int, gamma_seq=None,
+                      filtered: bool = False) -> int:
     """Bytes the method must read per call: the 2*gamma_b draft/target rows of every
     sequence (all overlaps are reported), the bonus row only where every draft was
-    kept, plus tokens, uniforms and outputs."""
+    kept (always, with top-k / top-p: every row's threshold needs the whole row),
+    plus tokens, uniforms and outputs."""
     B = len(n_accepted)
     gb = np.full(B, gamma) if gamma_seq is None else np.asarray(gamma_seq)
-    rows = 2 * int(gb.sum()) + int((n_accepted == gb).sum())
+    rows = 2 * int(gb.sum()) + (B if filtered else int((n_accepted == gb).sum()))
     small = 4 * B * gamma + 4 * B * (gamma + 1) + 4 * B * (2 + 3 * gamma)
     return rows * V * elem + small
 
@@ -146,6 +148,8 @@ def main() -> int:
     ap.add_argument("--lenience", type=float, default=1.0, help="lenience factor l in (0, 1] (spec_verify_ex)")
     ap.add_argument("--ragged", action="store_true",
                     help="per-sequence draft counts gamma_b ~ U{1..gamma} (seeded; spec_verify_ex)")
+    ap.add_argument("--top-k", type=int, default=0, help="top-k filter of p and q (0: off; spec_verify_ex)")
+    ap.add_argument("--top-p", type=float, default=1.0, help="top-p filter of p and q (1: off; spec_verify_ex)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -189,7 +193,7 @@ def main() -> int:
     # one prepared launch per buffer set: the timed loop then spends only the
     # C call on the host, well under the kernel's duration
     launches = [sv.prepare_verify(t, d, tokens, uniforms, T, algo=algo, workspace=ws, outputs=o,
-                                  lenience=args.lenience, gamma_seq=gseq)
+                                  lenience=args.lenience, gamma_seq=gseq, top_k=args.top_k, top_p=args.top_p)
                 for (t, d), o in zip(sets, outs)]
 
     def step(k):
@@ -212,14 +216,16 @@ def main() -> int:
     ms_per_step = 1e3 * elapsed / args.steps
     rows = B * (G + 1)
     n0 = outs[0]["n_accepted"].cpu().numpy()
-    alg = algorithmic_bytes(n0, G, V, elem, gseq_np)
+    filtered = T > 0 and (0 < args.top_k < V or args.top_p < 1.0)
+    default_path = args.lenience == 1.0 and not args.ragged and not filtered
+    alg = algorithmic_bytes(n0, G, V, elem, gseq_np, filtered)
     avg_launch_s = launch_us.mean * 1e-6
     achieved = alg / avg_launch_s / 1e9
     algo_name = {sv.ALGO_AUTO: "auto", sv.ALGO_MULTIPASS: "multipass", sv.ALGO_FUSED: "fused"}[algo]
     # AUTO dispatches the headline workload (aligned bf16 rows, 16 workgroups
     # per row) to the fused kernel, whose counters the traffic record holds
     traffic = None
-    if args.workload == "verify" and T == 1.0 and args.lenience == 1.0 and not args.ragged:
+    if args.workload == "verify" and T == 1.0 and default_path:
         traffic = load_traffic("fused" if algo_name == "auto" else algo_name)
     line = {
         "metric": METRIC,
@@ -238,13 +244,14 @@ def main() -> int:
                                + WORKLOAD_TEXT[args.workload],
                    "B": B, "gamma": G, "V": V, "logits": case.dtype, "temperature": T,
                    "algo": algo_name, "buffer_sets": len(sets), "lenience": args.lenience,
-                   "gamma_seq": None if gseq_np is None else "U{1..gamma}, mean %.2f" % gseq_np.mean()},
+                   "gamma_seq": None if gseq_np is None else "U{1..gamma}, mean %.2f" % gseq_np.mean(),
+                   "top_k": args.top_k, "top_p": args.top_p},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "launch_us_mean": launch_us.mean,
                      "alg_bytes": alg, "full_bytes": (2 * G + 1) * V * elem * B},
     }
-    if not args.no_cpu_baseline and args.workload == "verify" and args.lenience == 1.0 and not args.ragged:
+    if not args.no_cpu_baseline and args.workload == "verify" and default_path:
         line["cpu_baseline"] = cpu_baseline(case)
     print(json.dumps(line), flush=True)
     return 0

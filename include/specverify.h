@@ -90,7 +90,9 @@ size_t spec_verify_workspace_size(int B, int gamma, int V, int dtype);
  *     (the first token whose cumulative weight exceeds u * total).  The weights
  *     are max(0, p_n - q_n) when n < gamma (the residual, [FI] "Speculative
  *     sampling: the accept/reject rule", eq. (2)), and p_gamma when every draft
- *     was kept (the bonus token).
+ *     was kept (the bonus token).  A residual whose mass is at most 2^-20 (the
+ *     fp32 rounding noise of p_n - q_n when the two rows agree) is taken as
+ *     empty, and next_token is drawn from p_n itself.
  *   T == 0 is argmax mode: p_i and q_i are one-hot at the row argmax, with ties
  *     going to the lowest index.  A draft is kept iff it equals the target
  *     argmax.  next_token is the target argmax at position n.  alpha is 1 where
@@ -141,8 +143,27 @@ int spec_verify_algo(int algo,
                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * spec_verify_ex -- spec_verify_algo with two optional extensions of the step.
- * With lenience == 1 and gamma_seq == NULL it is spec_verify_algo exactly.
+ * spec_verify_ex -- spec_verify_algo with optional extensions of the step.
+ * With top_k == 0, top_p == 1, lenience == 1 and gamma_seq == NULL it is
+ * spec_verify_algo exactly.
+ *
+ *   top_k, top_p  top-k and nucleus filtering of both models' rows before the
+ *              step ([FI] "The loop: draft, verify in one pass, keep a prefix":
+ *              the method runs on p and q as the sampling method adjusted them;
+ *              [NZ] "5. Sampling and evaluation": the same settings for both).
+ *              After the temperature, top-k keeps every token whose logit is at
+ *              least the row's k-th largest (ties kept); then top-p keeps, of
+ *              those, the smallest set of whole tie groups, most likely first,
+ *              that holds at least top_p of their probability mass.  Every other
+ *              token has probability 0, in alpha, the ratio tests and the
+ *              samples.  top_k <= 0 or >= V, and top_p >= 1, disable a filter;
+ *              top_p must be > 0 (else SPEC_EINVAL).  In argmax mode (T == 0)
+ *              the filters change nothing and are skipped.  Filtering runs on
+ *              the fused path only: SPEC_ALGO_MULTIPASS, or a shape the fused
+ *              path declines, gives SPEC_EUNSUPPORTED.  A filtered call launches
+ *              a threshold kernel (one workgroup per row, a radix select over
+ *              the logits' bit keys), the verification, and a fill kernel that
+ *              leaves the workspace zero.
  *
  *   lenience   l in (0, 1] ([FI] "The acceptance rate is the overlap of p and q",
  *              the lenience factor): draft i is kept when
@@ -173,7 +194,7 @@ int spec_verify_ex(int algo,
                    const void* target_logits, const void* draft_logits, int dtype,
                    const int32_t* draft_tokens, const float* uniforms,
                    int B, int gamma, int V, float temperature,
-                   float lenience, const int32_t* gamma_seq,
+                   int top_k, float top_p, float lenience, const int32_t* gamma_seq,
                    int32_t* n_accepted, int32_t* next_token, float* alpha,
                    float* p_draft, float* q_draft,
                    void* workspace, size_t workspace_bytes, void* stream);

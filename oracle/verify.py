@@ -26,8 +26,11 @@ draft rows q_0..q_{gamma-1}, drafted tokens x_0..x_{gamma-1}):
 Readings taken where the pages are silent (each is listed in the design notes):
   * u_gamma is a fresh uniform for the final sample; the rejecting u_n is not reused.
   * `sample()` is the inverse CDF with a strict ">" in token-index order.
-  * A zero-mass residual (impossible in exact arithmetic after a rejection) falls
-    back to p_n.
+  * A residual with no mass falls back to p_n.  In exact arithmetic that needs
+    p_n = q_n (then only a draft outside the support, 0/0, is rejected); the
+    GPU computes p and q in fp32, where rows that agree leave a residual of
+    rounding noise, so a mass at most RESIDUAL_FLOOR = 2^-20 (of p_n's total)
+    counts as none on both sides.
   * Argmax ties go to the lowest token index; alpha in argmax mode is the
     indicator that the two argmaxes agree.
   * alpha is reported for every draft position, whatever n is.
@@ -61,6 +64,10 @@ from oracle import adjust
 # |u_i - min(1, p_i(x_i)/q_i(x_i))| below this marks a decision that fp32 on the
 # GPU and fp64 here may take differently.
 U_BAND = 1e-6
+
+# A residual max(0, p - l q) with at most this mass is taken as empty (reading
+# above): the token is then drawn from p_n.
+RESIDUAL_FLOOR = 2.0 ** -20
 
 
 # ------------------------------------------------------------------ step 0
@@ -170,6 +177,7 @@ class Result:
     residual: np.ndarray        # bool [B]: sampled from a residual (else bonus / argmax)
     weights: np.ndarray | None  # float64 [B, V] normalised sampling row, if requested
     filter_margin: np.ndarray | None = None  # float64 [B]: smallest top-p margin of the sequence's rows
+    res_mass: np.ndarray | None = None  # float64 [B]: mass of the residual after a rejection, else NaN
 
 
 def _verify_block(target, draft, tokens, u, temperature, dtype, keep_weights, lenience=1.0, gseq=None,
@@ -211,7 +219,7 @@ def _verify_block(target, draft, tokens, u, temperature, dtype, keep_weights, le
             weights = np.zeros((nb, V))
             weights[rows, t] = 1.0
         return Result(n, t, alpha, 1.0 - alpha, p_x, q_x, np.zeros(nb, bool),
-                      np.full(nb, np.inf), np.zeros(nb, bool), weights, fmargin)
+                      np.full(nb, np.inf), np.zeros(nb, bool), weights, fmargin, np.full(nb, np.nan))
 
     p = softmax(tl, temperature)         # [b, gamma+1, V]
     q = softmax(dl, temperature)         # [b, gamma, V]
@@ -232,17 +240,19 @@ def _verify_block(target, draft, tokens, u, temperature, dtype, keep_weights, le
 
     residual = n < gb
     w = p[rows, n].copy()                          # bonus row p_{gamma_b} when n == gamma_b
+    res_mass = np.full(nb, np.nan)
     if residual.any():
         idx = np.nonzero(residual)[0]
         res = residual_weights(p[idx, n[idx]], q[idx, n[idx]], lenience)
         mass = res.sum(axis=-1)
-        ok = mass > 0.0                            # zero mass: keep p_n
+        res_mass[idx] = mass
+        ok = mass > RESIDUAL_FLOOR                 # no mass: keep p_n
         w[idx[ok]] = res[ok] / mass[ok][:, None]
     w /= w.sum(axis=-1, keepdims=True)
     t, cdf = inverse_cdf(w, u_final.astype(np.float64))
     margin = np.abs(cdf - u_final[:, None]).min(axis=-1)
     return Result(n, t, alpha, tv, p_x, q_x, u_band, margin, residual,
-                  w if keep_weights else None, fmargin)
+                  w if keep_weights else None, fmargin, res_mass)
 
 
 def verify(target, draft, tokens, uniforms, temperature: float, dtype: str,
@@ -285,11 +295,12 @@ def verify(target, draft, tokens, uniforms, temperature: float, dtype: str,
         z = np.zeros(0)
         return Result(z.astype(np.int64), z.astype(np.int64), np.zeros((0, gamma)),
                       np.zeros((0, gamma)), np.zeros((0, gamma)), np.zeros((0, gamma)),
-                      z.astype(bool), z, z.astype(bool), None)
+                      z.astype(bool), z, z.astype(bool), None, z, z)
     cat = lambda f: np.concatenate([getattr(r, f) for r in parts])  # noqa: E731
     return Result(cat("n_accepted"), cat("next_token"), cat("alpha"), cat("tv"),
                   cat("p_draft"), cat("q_draft"), cat("u_band"), cat("cdf_margin"),
-                  cat("residual"), cat("weights") if keep_weights else None, cat("filter_margin"))
+                  cat("residual"), cat("weights") if keep_weights else None, cat("filter_margin"),
+                  cat("res_mass"))
 
 
 def verify_case(case, keep_weights: bool = False, seqs=None, lenience: float = 1.0, gamma_seq=None,

@@ -38,7 +38,7 @@ SIGNATURES = {
                                   _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                   _c_void_p, _c_size_t, _c_void_p]),
     "spec_verify_ex": (_c_int, [_c_int, _c_void_p, _c_void_p, _c_int, _c_void_p, _c_void_p,
-                                _c_int, _c_int, _c_int, _c_float, _c_float, _c_void_p,
+                                _c_int, _c_int, _c_int, _c_float, _c_int, _c_float, _c_float, _c_void_p,
                                 _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                 _c_void_p, _c_size_t, _c_void_p]),
     "spec_lmhead_logits": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_void_p, _c_void_p]),
@@ -123,7 +123,8 @@ def workspace_size(B: int, gamma: int, V: int, dtype: int = SPEC_BF16) -> int:
 
 
 def verify(target_logits, draft_logits, draft_tokens, uniforms, temperature: float, *,
-           algo: int = ALGO_AUTO, workspace=None, outputs=None, lenience: float = 1.0, gamma_seq=None):
+           algo: int = ALGO_AUTO, workspace=None, outputs=None, lenience: float = 1.0, gamma_seq=None,
+           top_k: int = 0, top_p: float = 1.0):
     """One verification step on the current stream.
 
     target_logits [B, gamma+1, V] and draft_logits [B, gamma, V] (float32 or
@@ -139,9 +140,10 @@ def verify(target_logits, draft_logits, draft_tokens, uniforms, temperature: flo
     was lost because the device was shared (see include/specverify.h); the
     workspace must then be zeroed again.
 
-    lenience (l in (0, 1]) and gamma_seq (int32 [B] on the same GPU, each
-    gamma_b in [0, gamma]) are the extensions of spec_verify_ex: q scaled by l
-    in the accept test and the residual, and per-sequence draft counts in the
+    top_k / top_p (filters of both models' rows), lenience (l in (0, 1]) and
+    gamma_seq (int32 [B] on the same GPU, each gamma_b in [0, gamma]) are the
+    extensions of spec_verify_ex: the adjusted distributions, q scaled by l in
+    the accept test and the residual, and per-sequence draft counts in the
     padded layout (positions past gamma_b report NaN).
     """
     torch = _torch()
@@ -175,23 +177,24 @@ def verify(target_logits, draft_logits, draft_tokens, uniforms, temperature: flo
     if workspace is None:
         workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)
     _check(lib.spec_verify_ex(*_verify_args(algo, target_logits, draft_logits, dt, draft_tokens, uniforms,
-                                            B, gamma, V, temperature, lenience, gamma_seq, outputs,
-                                            workspace, dev)),
+                                            B, gamma, V, temperature, top_k, top_p, lenience, gamma_seq,
+                                            outputs, workspace, dev)),
            "spec_verify")
     return outputs
 
 
 def _verify_args(algo, target_logits, draft_logits, dt, draft_tokens, uniforms, B, gamma, V, temperature,
-                 lenience, gamma_seq, outputs, workspace, dev):
+                 top_k, top_p, lenience, gamma_seq, outputs, workspace, dev):
     return (algo, _ptr(target_logits), _ptr(draft_logits), dt, _ptr(draft_tokens), _ptr(uniforms),
-            B, gamma, V, float(temperature), float(lenience), _ptr(gamma_seq),
+            B, gamma, V, float(temperature), int(top_k), float(top_p), float(lenience), _ptr(gamma_seq),
             _ptr(outputs["n_accepted"]), _ptr(outputs["next_token"]), _ptr(outputs.get("alpha")),
             _ptr(outputs.get("p_draft")), _ptr(outputs.get("q_draft")),
             _ptr(workspace), workspace.numel(), _stream(dev))
 
 
 def prepare_verify(target_logits, draft_logits, draft_tokens, uniforms, temperature: float, *,
-                   algo: int = ALGO_AUTO, workspace, outputs, lenience: float = 1.0, gamma_seq=None):
+                   algo: int = ALGO_AUTO, workspace, outputs, lenience: float = 1.0, gamma_seq=None,
+                   top_k: int = 0, top_p: float = 1.0):
     """Checks the arguments of verify() once and returns a callable that
     launches that same verification again (same tensors, current stream at
     preparation) with no per-call Python work beyond the C call, for loops
@@ -199,10 +202,11 @@ def prepare_verify(target_logits, draft_logits, draft_tokens, uniforms, temperat
     holds references to every tensor it launches on, so they stay allocated
     while it lives; their shapes and contents are the caller's to keep."""
     verify(target_logits, draft_logits, draft_tokens, uniforms, temperature, algo=algo, workspace=workspace,
-           outputs=outputs, lenience=lenience, gamma_seq=gamma_seq)
+           outputs=outputs, lenience=lenience, gamma_seq=gamma_seq, top_k=top_k, top_p=top_p)
     B, g1, V = target_logits.shape
     args = _verify_args(algo, target_logits, draft_logits, _dtype_code(target_logits), draft_tokens, uniforms,
-                        B, g1 - 1, V, temperature, lenience, gamma_seq, outputs, workspace, target_logits.device)
+                        B, g1 - 1, V, temperature, top_k, top_p, lenience, gamma_seq, outputs, workspace,
+                        target_logits.device)
     fn = lib.spec_verify_ex
     keep = (target_logits, draft_logits, draft_tokens, uniforms, gamma_seq, workspace, dict(outputs))
 

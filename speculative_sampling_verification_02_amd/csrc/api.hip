@@ -51,15 +51,23 @@ const char* spec_status_string(int status) {
 
 // Both paths start their scratch at the workspace's base and both leave all
 // of it zero when they complete (the fused path needs zero slots on entry).
+// The top-k / top-p keep thresholds (one float per row) follow, and are
+// zeroed again after the verification that reads them.
+static size_t paths_bytes(int B, int gamma, int V) {
+  const size_t b = std::max(specv::fused_workspace_bytes(B, gamma, V), specv::multipass_workspace_bytes(B, gamma, V));
+  return (std::max<size_t>(b, 256) + 255) & ~(size_t)255;
+}
+
 size_t spec_verify_workspace_size(int B, int gamma, int V, int dtype) {
   if (!valid_shape(B, gamma, V) || (dtype != SPEC_F32 && dtype != SPEC_BF16)) return 0;
-  return std::max<size_t>(256, std::max(specv::fused_workspace_bytes(B, gamma, V),
-                                        specv::multipass_workspace_bytes(B, gamma, V)));
+  const size_t thr = ((size_t)B * (2 * gamma + 1) * sizeof(float) + 255) & ~(size_t)255;
+  return paths_bytes(B, gamma, V) + thr;
 }
 
 int spec_verify_ex(int algo, const void* target_logits, const void* draft_logits, int dtype,
                    const int32_t* draft_tokens, const float* uniforms, int B, int gamma, int V,
-                   float temperature, float lenience, const int32_t* gamma_seq, int32_t* n_accepted,
+                   float temperature, int top_k, float top_p, float lenience, const int32_t* gamma_seq,
+                   int32_t* n_accepted,
                    int32_t* next_token, float* alpha, float* p_draft, float* q_draft, void* workspace,
                    size_t workspace_bytes, void* stream) {
   if (algo != SPEC_ALGO_AUTO && algo != SPEC_ALGO_MULTIPASS && algo != SPEC_ALGO_FUSED)
@@ -67,6 +75,7 @@ int spec_verify_ex(int algo, const void* target_logits, const void* draft_logits
   if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_EUNSUPPORTED;
   if (!valid_shape(B, gamma, V) || !valid_temperature(temperature)) return SPEC_EINVAL;
   if (!(lenience > 0.f && lenience <= 1.f)) return SPEC_EINVAL;  // also rejects NaN
+  if (!(top_p > 0.f)) return SPEC_EINVAL;                          // also rejects NaN
   if (B == 0) return SPEC_OK;
   if (!target_logits || !uniforms || !n_accepted || !next_token) return SPEC_EINVAL;
   if (gamma > 0 && (!draft_logits || !draft_tokens)) return SPEC_EINVAL;
@@ -95,6 +104,22 @@ int spec_verify_ex(int algo, const void* target_logits, const void* draft_logits
   a.gamma_seq = gamma > 0 ? gamma_seq : nullptr;
   hipStream_t s = static_cast<hipStream_t>(stream);
 
+  // Top-k / top-p (T > 0 only: they leave the argmax unchanged) need the
+  // fused path: thresholds first, then the verification that reads them, then
+  // the thresholds are zeroed again.
+  const bool filtered = temperature > 0.f && ((top_k > 0 && top_k < V) || top_p < 1.f);
+  if (filtered) {
+    if (algo == SPEC_ALGO_MULTIPASS || !specv::fused_supported(B, gamma, V, dtype)) return SPEC_EUNSUPPORTED;
+    float* thr = reinterpret_cast<float*>(static_cast<char*>(workspace) + paths_bytes(B, gamma, V));
+    const int rows = B * (2 * gamma + 1);
+    hipError_t e = specv::filter_thresholds(a, top_k, top_p, thr, s);
+    if (e != hipSuccess) return map_hip(e);
+    a.thr = thr;
+    e = specv::fused_launch(a, s);
+    const hipError_t ec = specv::filter_clear(thr, rows, s);
+    if (e != hipSuccess) return map_hip(e);
+    return map_hip(ec);
+  }
   if (algo == SPEC_ALGO_FUSED) return map_hip(specv::fused_launch(a, s));
   if (algo == SPEC_ALGO_AUTO && specv::fused_supported(B, gamma, V, dtype)) {
     // the fused path declines unaligned rows and teams that cannot be resident
@@ -110,7 +135,7 @@ int spec_verify_algo(int algo, const void* target_logits, const void* draft_logi
                      float* p_draft, float* q_draft, void* workspace, size_t workspace_bytes,
                      void* stream) {
   return spec_verify_ex(algo, target_logits, draft_logits, dtype, draft_tokens, uniforms, B, gamma, V,
-                        temperature, 1.f, nullptr, n_accepted, next_token, alpha, p_draft, q_draft,
+                        temperature, 0, 1.f, 1.f, nullptr, n_accepted, next_token, alpha, p_draft, q_draft,
                         workspace, workspace_bytes, stream);
 }
 

@@ -11,6 +11,14 @@ namespace specv {
 
 constexpr int kWave = 64;
 
+// A residual max(0, p - l q) whose mass (in units of p's total) is at most
+// this is taken as having no mass, and the token is drawn from p itself.  Each
+// token's residual carries up to an ulp of its p and q (2^-24 relative), so a
+// p and q that agree to fp32 leave a residual of rounding noise that sums to
+// at most a few 2^-24; 2^-20 stays above that, and a rejection whose true
+// residual mass is below it has probability under 2^-20.
+constexpr double kResidualFloor = 0x1p-20;
+
 // 16 bytes as four 32-bit words (a native clang vector, so it can be used
 // with the nontemporal load builtin).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));

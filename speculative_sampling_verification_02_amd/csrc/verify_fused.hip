@@ -559,9 +559,17 @@ struct NormMsg {
   int ok;
 };
 
+// Top-k / top-p filtering (extended kernels): a logit below its row's keep
+// threshold becomes -inf, i.e. probability 0.
+template <int PER>
+__device__ inline void mask_below(float (&x)[PER], float t) {
+#pragma unroll
+  for (int j = 0; j < PER; ++j) x[j] = x[j] >= t ? x[j] : -INFINITY;
+}
+
 // Pair item, T > 0, in three steps.  Phase 1 turns the wave tile into kept
 // weights and publishes the wave's (scaled max, sum) of both rows.
-template <class E, int PER>
+template <class E, int PER, bool EXT>
 __device__ __attribute__((always_inline)) void pair_phase1(const FusedParams& P, int item, int c, int lo,
                                                            const RawPair<E, PER>& raw, float (&ep)[PER],
                                                            float (&eq)[PER], float& mp, float& mq, float& sp,
@@ -570,6 +578,13 @@ __device__ __attribute__((always_inline)) void pair_phase1(const FusedParams& P,
   const float k = a.k;
   unpack_tile<E, PER>(raw.p, lo, a.V, ep);
   unpack_tile<E, PER>(raw.q, lo, a.V, eq);
+  if constexpr (EXT) {
+    if (a.thr) {
+      const int b = item / a.gamma, i = item % a.gamma;
+      mask_below<PER>(ep, thr_target(a, b, i));
+      mask_below<PER>(eq, thr_draft(a, b, i));
+    }
+  }
   mp = thread_max<PER>(ep) * k;  // scaled maxima
   mq = thread_max<PER>(eq) * k;
   sp = thread_exp_sum<PER, true>(ep, mp, k);
@@ -665,13 +680,13 @@ __device__ __attribute__((always_inline)) void pair_compute_sample(const FusedPa
                                                                    int parity, const RawPair<E, PER>& raw,
                                                                    uint64_t* w1, NormMsg* msg) {
   float ep[PER], eq[PER], mp, mq, sp, sq;
-  pair_phase1<E, PER>(P, item, c, lo, raw, ep, eq, mp, mq, sp, sq);
+  pair_phase1<E, PER, EXT>(P, item, c, lo, raw, ep, eq, mp, mq, sp, sq);
   const NormMsg m = pair_wait(P, item, parity, w1, msg);
   pair_phase2<PER, EXT>(P, item, c, m, ep, eq, mp, mq, sp, sq);
 }
 
 // Pair item at T = 0, or a bonus item: one pass, no waiting.
-template <class E, int PER, bool ARGMAX>
+template <class E, int PER, bool ARGMAX, bool EXT>
 __device__ __attribute__((always_inline)) void single_pass_compute(const FusedParams& P, int item, int c, int lo,
                                                                    const RawPair<E, PER>& raw) {
   const VerifyArgs& a = P.a;
@@ -691,6 +706,12 @@ __device__ __attribute__((always_inline)) void single_pass_compute(const FusedPa
       const ArgMax ab = wave_argmax(thread_argmax<E, PER>(x, lo));
       w0 = pack2i(nz_bits(ab.v), (uint32_t)ab.i);
     } else {
+      if constexpr (EXT) {
+        if (a.thr) {  // the bonus row is target row gamma_b
+          const int b = item - P.n_pairs;
+          mask_below<PER>(x, thr_target(a, b, seq_gamma_of<EXT>(a, b)));
+        }
+      }
       const float m = thread_max<PER>(x) * a.k;
       const float sm = thread_exp_sum<PER, false>(x, m, a.k);
       const float2 l = wave_lse(m, sm);
@@ -802,7 +823,7 @@ __device__ __attribute__((always_inline)) void compute_loop_staged(const FusedPa
       if (empty_item<EXT>(P, item)) {
       } else if (item < P.n_pairs) {
         float xp[PER], xq[PER], cp, cq, s_p, s_q;
-        pair_phase1<E, PER>(P, item, c, lo, A, xp, xq, cp, cq, s_p, s_q);
+        pair_phase1<E, PER, EXT>(P, item, c, lo, A, xp, xq, cp, cq, s_p, s_q);
         if (pend >= 0) {
           const NormMsg m = pair_wait(P, pend, parity, w1, msg);
           pair_phase2<PER, EXT>(P, pend, c, m, ep, eq, mp, mq, sp, sq);
@@ -819,7 +840,7 @@ __device__ __attribute__((always_inline)) void compute_loop_staged(const FusedPa
         sq = s_q;
         pend = item;
       } else {
-        single_pass_compute<E, PER, ARGMAX>(P, item, c, lo, A);
+        single_pass_compute<E, PER, ARGMAX, EXT>(P, item, c, lo, A);
         if (pend >= 0) {
           const NormMsg m = pair_wait(P, pend, parity, w1, msg);
           pair_phase2<PER, EXT>(P, pend, c, m, ep, eq, mp, mq, sp, sq);
@@ -832,7 +853,7 @@ __device__ __attribute__((always_inline)) void compute_loop_staged(const FusedPa
       pair_compute_sample<E, PER, EXT>(P, item, c, lo, parity, A, w1, msg);
       parity ^= 1;
     } else {
-      single_pass_compute<E, PER, ARGMAX>(P, item, c, lo, A);
+      single_pass_compute<E, PER, ARGMAX, EXT>(P, item, c, lo, A);
     }
     if (wave != 0) wait_vmem();
     lds_barrier();
@@ -932,6 +953,10 @@ __device__ void finish_pair(const FusedParams& P, int item, uint64_t* w1, uint64
       if (x >= 0 && x < a.V) {
         lp = E::at(prow, x);
         lq = E::at(qrow, x);
+        if (EXT && a.thr) {  // a filtered-out token has probability 0
+          if (lp < thr_target(a, b, i)) lp = -INFINITY;
+          if (lq < thr_draft(a, b, i)) lq = -INFINITY;
+        }
       }
     }
     // part2 is published after part1 by every wave; polling both in one pass
@@ -990,11 +1015,18 @@ __device__ void finish_pair(const FusedParams& P, int item, uint64_t* w1, uint64
     __syncthreads();
     const int acc_i = acc_s;
     int mode = 0;
+    const double uf = (double)a.uniforms[(size_t)b * (G + 1) + gb];  // the final sample's uniform
+    // search groups of S::kGroup consecutive wave tiles, in token order
+    const int ng = (W + S::kGroup - 1) / S::kGroup;
+    auto pick_p_tile = [&]() {
+      wave_pick_tile(ng, uf * Sp, [&](int g) {
+        double m = 0.0;
+        for (int c = g * S::kGroup; c < min(W, (g + 1) * S::kGroup); ++c) m += p_tile_mass(w1, c, Mp);
+        return m;
+      }, &tile_s, &rest_s);
+    };
     if (!acc_i) {
-      const double uf = (double)a.uniforms[(size_t)b * (G + 1) + gb];  // the final sample's uniform
-      // search groups of S::kGroup consecutive wave tiles, in token order
-      const int ng = (W + S::kGroup - 1) / S::kGroup;
-      if (sw_s > 0.0) {
+      if (sw_s > kResidualFloor) {
         mode = 1;  // residual max(0, p_i - l q_i) ([FI] eq. (2); [SD] "Exactness"; l = 1 there)
         wave_pick_tile(ng, uf * sw_s, [&](int g) {
           double m = 0.0;
@@ -1002,25 +1034,37 @@ __device__ void finish_pair(const FusedParams& P, int item, uint64_t* w1, uint64
           return m;
         }, &tile_s, &rest_s);
       } else {
-        mode = 2;  // no residual mass: sample p_i itself
-        wave_pick_tile(ng, uf * Sp, [&](int g) {
-          double m = 0.0;
-          for (int c = g * S::kGroup; c < min(W, (g + 1) * S::kGroup); ++c) m += p_tile_mass(w1, c, Mp);
-          return m;
-        }, &tile_s, &rest_s);
+        mode = 2;  // no residual mass (at most kResidualFloor): sample p_i itself
+        pick_p_tile();
       }
     }
     int t = 0;
     if (mode) {
       const float invSp = (float)(1.0 / Sp), invSq = (float)((double)a.lenience / Sq);  // l / S_q
-      const int tlo = tile_s * S::kTokens;
-      if (mode == 1)
-        t = tile_search<E, S::kPer, kThreads>(prow, qrow, tlo, a.V, rest_s, [&](float xp, float xq) {
-          return fmaxf(fast_exp2(fmaf(xp, k, -Mp)) * invSp - fast_exp2(fmaf(xq, k, -Mq)) * invSq, 0.f);
+      // keep thresholds of the two rows (-inf: nothing filtered)
+      const float tp = EXT && a.thr ? thr_target(a, b, i) : -INFINITY;
+      const float tq = EXT && a.thr ? thr_draft(a, b, i) : -INFINITY;
+      if (mode == 1) {
+        t = tile_search<E, S::kPer, kThreads>(prow, qrow, tile_s * S::kTokens, a.V, rest_s,
+                                              [&](float xp, float xq) {
+          const float wp = xp >= tp ? fast_exp2(fmaf(xp, k, -Mp)) : 0.f;
+          const float wq = xq >= tq ? fast_exp2(fmaf(xq, k, -Mq)) : 0.f;
+          // both products rounded (no fused multiply-add), so equal p and q
+          // give exactly 0
+          return fmaxf(__fmul_rn(wp, invSp) - __fmul_rn(wq, invSq), 0.f);
         }, lds_f, lds_i);
-      else
-        t = tile_search<E, S::kPer, kThreads>(prow, nullptr, tlo, a.V, rest_s, [&](float xp, float) {
-          return fast_exp2(fmaf(xp, k, -Mp));
+        // No token of the picked tile has a positive residual: p_i and q_i
+        // agree to fp32 there, and the tile's positive sum came from rounding.
+        // That is the residual without mass: sample p_i itself.
+        if (t < 0) {
+          mode = 2;
+          pick_p_tile();
+        }
+      }
+      if (mode == 2)
+        t = tile_search<E, S::kPer, kThreads>(prow, nullptr, tile_s * S::kTokens, a.V, rest_s,
+                                              [&](float xp, float) {
+          return xp >= tp ? fast_exp2(fmaf(xp, k, -Mp)) : 0.f;
         }, lds_f, lds_i);
     }
     if (threadIdx.x == 0) st_u64(P.pair_res + item, pack2i((uint32_t)acc_s | kResMark, (uint32_t)t));
@@ -1060,6 +1104,7 @@ __device__ void finish_bonus(const FusedParams& P, int item, uint64_t* w1, uint6
     }
     __syncthreads();
     const float M = M_s;
+    const float tb = EXT && a.thr ? thr_target(a, b, gb) : -INFINITY;  // the bonus row's keep threshold
     const double uf = (double)a.uniforms[(size_t)b * (G + 1) + gb];
     wave_pick_tile((W + S::kGroup - 1) / S::kGroup, uf * S_s, [&](int g) {
       double m = 0.0;
@@ -1067,7 +1112,9 @@ __device__ void finish_bonus(const FusedParams& P, int item, uint64_t* w1, uint6
       return m;
     }, &tile_s, &rest_s);
     t_bonus = tile_search<E, S::kPer, kThreads>(row, nullptr, tile_s * S::kTokens, a.V, rest_s,
-                                                   [&](float xp, float) { return fast_exp2(fmaf(xp, k, -M)); },
+                                                   [&](float xp, float) {
+                                                     return xp >= tb ? fast_exp2(fmaf(xp, k, -M)) : 0.f;
+                                                   },
                                                    lds_f, lds_i);
   }
   // the sequence's pair results (published by other finishers)
@@ -1142,7 +1189,7 @@ __global__ __launch_bounds__(kThreads, SPECV_FUSED_MIN_WAVES) void fused_kernel(
           pair_compute_sample<E, PER, EXT>(P, item, c, lo, parity, A, poll_buf, msg);
           parity ^= 1;
         } else {
-          single_pass_compute<E, PER, ARGMAX>(P, item, c, lo, A);
+          single_pass_compute<E, PER, ARGMAX, EXT>(P, item, c, lo, A);
         }
       }
     }
@@ -1253,9 +1300,10 @@ hipError_t fused_launch(const VerifyArgs& a, hipStream_t s) {
   if (!fused_supported(a.B, a.gamma, a.V, a.dtype)) return hipErrorNotSupported;
   if ((uintptr_t)a.target % 16 != 0 || (a.gamma > 0 && (uintptr_t)a.draft % 16 != 0)) return hipErrorNotSupported;
   const bool argmax = a.temperature == 0.f;
-  // The extended kernels take lenience below 1 and per-sequence draft counts;
-  // lenience does not change argmax mode.
-  const bool ext = a.gamma_seq != nullptr || (!argmax && a.lenience != 1.f);
+  // The extended kernels take lenience below 1, per-sequence draft counts and
+  // top-k / top-p thresholds; lenience and the filters do not change argmax
+  // mode.
+  const bool ext = a.gamma_seq != nullptr || (!argmax && (a.lenience != 1.f || a.thr != nullptr));
   if (a.dtype == SPEC_BF16) {
     if (argmax) return ext ? launch<BF16, true, true>(a, s) : launch<BF16, true>(a, s);
     return ext ? launch<BF16, false, true>(a, s) : launch<BF16, false>(a, s);

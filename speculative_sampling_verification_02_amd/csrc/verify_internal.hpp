@@ -26,7 +26,17 @@ struct VerifyArgs {
   size_t ws_bytes;
   float lenience;              // l in (0, 1]; 1 = exact speculative sampling
   const int32_t* gamma_seq;    // [B] per-sequence draft counts, or null (all gamma)
+  const float* thr;            // top-k / top-p keep thresholds per row, or null:
+                               // [B(gamma+1)] target rows, then [B gamma] draft rows
 };
+
+// A logit below its row's keep threshold counts as -inf (probability 0).
+__device__ inline float thr_target(const VerifyArgs& a, int b, int i) {
+  return a.thr[(size_t)b * (a.gamma + 1) + i];
+}
+__device__ inline float thr_draft(const VerifyArgs& a, int b, int i) {
+  return a.thr[(size_t)a.B * (a.gamma + 1) + (size_t)b * a.gamma + i];
+}
 
 // Draft count of sequence b: gamma_seq[b] clamped into [0, gamma], or gamma.
 __device__ inline int seq_gamma(const VerifyArgs& a, int b) {
@@ -46,6 +56,11 @@ size_t fused_workspace_bytes(int B, int gamma, int V);
 // Returns hipErrorNotSupported when the shape does not fit the fused design.
 hipError_t fused_launch(const VerifyArgs& a, hipStream_t stream);
 bool fused_supported(int B, int gamma, int V, int dtype);
+
+// ---- top-k / top-p keep thresholds (filter.hip): one float per row into thr,
+// and a fill kernel that zeroes them again after the verification
+hipError_t filter_thresholds(const VerifyArgs& a, int top_k, float top_p, float* thr, hipStream_t stream);
+hipError_t filter_clear(float* thr, int rows, hipStream_t stream);
 
 // ---- LM head
 // One head of the product: out[m][v] = sum_k hidden[r(m)][k] W[k][v] for

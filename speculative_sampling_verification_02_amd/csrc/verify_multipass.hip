@@ -348,8 +348,9 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(VerifyArgs a, float2* 
 
   // ---- the sampled row's chunk masses, in chunk order: the residual
   // max(0, p_n - l q_n) ([FI] eq. (2); [SD] "Exactness"; l = 1 there) when a
-  // draft was rejected, else p_{gamma_b} (the bonus token).  A residual with no mass
-  // (impossible in exact arithmetic after a rejection) falls back to p_n.
+  // draft was rejected, else p_{gamma_b} (the bonus token).  A residual with no
+  // mass (at most kResidualFloor, the fp32 rounding of a p_n equal to q_n)
+  // falls back to p_n.
   const float2* res_st = n < Gb ? pair_stats + ((size_t)b * G + n) * nch : nullptr;
   const float2* row_st = stats + target_row(b, n, G) * nch;
   __shared__ RowNorm norm_s[2];
@@ -362,72 +363,82 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(VerifyArgs a, float2* 
   double part = 0.0;
   if (res_st)
     for (int c = tid; c < nch; c += kThreads) part += (double)res_st[c].y;
-  const bool residual = res_st && block_sum(part, lds_d) > 0.0;
+  bool residual = res_st && block_sum(part, lds_d) > kResidualFloor;
   // chunk c's mass: R_c for the residual, S_c rescaled to the row maximum for p_n
   auto mass = [&](int c) -> float {
     if (residual) return res_st[c].y;
     const float2 v = row_st[c];
     return v.x == -INFINITY ? 0.f : v.y * fast_exp2((v.x - np.M) * k);
   };
-  part = 0.0;
-  for (int c = tid; c < nch; c += kThreads) part += (double)mass(c);
-  const double theta = (double)u[Gb] * block_sum(part, lds_d);  // the final sample's uniform
+  const auto* p_row = row_ptr<E>(a, target_row(b, n, G));
+  int t;
+  for (;;) {
+    part = 0.0;
+    for (int c = tid; c < nch; c += kThreads) part += (double)mass(c);
+    const double theta = (double)u[Gb] * block_sum(part, lds_d);  // the final sample's uniform
 
-  // ---- locate the chunk holding theta: stage up to kThreads masses in LDS
-  // with one parallel load, then scan them in order on one thread.
-  if (tid == 0) {
-    prefix_s = 0.0;
-    chunk_s = -1;
-  }
-  int last = 0;
-  for (int base = 0; base < nch; base += kThreads) {
-    const int c = base + tid;
-    mass_s[tid] = c < nch ? mass(c) : 0.f;
-    __syncthreads();
-    if (tid == 0 && chunk_s < 0) {
-      double P = prefix_s;
-      for (int j = 0; j < kThreads && base + j < nch; ++j) {
-        const double w = (double)mass_s[j];
-        if (w > 0.0) {
-          last = base + j;
-          if (P + w > theta) {
-            chunk_s = base + j;
-            break;
+    // ---- locate the chunk holding theta: stage up to kThreads masses in LDS
+    // with one parallel load, then scan them in order on one thread.
+    if (tid == 0) {
+      prefix_s = 0.0;
+      chunk_s = -1;
+    }
+    int last = 0;
+    for (int base = 0; base < nch; base += kThreads) {
+      const int c = base + tid;
+      mass_s[tid] = c < nch ? mass(c) : 0.f;
+      __syncthreads();
+      if (tid == 0 && chunk_s < 0) {
+        double P = prefix_s;
+        for (int j = 0; j < kThreads && base + j < nch; ++j) {
+          const double w = (double)mass_s[j];
+          if (w > 0.0) {
+            last = base + j;
+            if (P + w > theta) {
+              chunk_s = base + j;
+              break;
+            }
           }
+          P += w;
         }
-        P += w;
+        prefix_s = P;
       }
-      prefix_s = P;
+      __syncthreads();
+      if (chunk_s >= 0) break;
+    }
+    if (tid == 0) {
+      if (chunk_s < 0) chunk_s = last;  // rounding guard: theta past every chunk
+      theta_s = (float)(theta - prefix_s);
     }
     __syncthreads();
-    if (chunk_s >= 0) break;
-  }
-  if (tid == 0) {
-    if (chunk_s < 0) chunk_s = last;  // rounding guard: theta past every chunk
-    theta_s = (float)(theta - prefix_s);
+
+    const int c = chunk_s, lo = c * kChunk, hi = min(a.V, lo + kChunk);
+    if (residual) {
+      const RowNorm nq = norm_s[1];
+      const auto* q_row = row_ptr<E>(a, draft_row(b, n, G, a.B));
+      const float l = a.lenience;
+      auto w = [&](float xp, float xq) { return fmaxf(prob(xp, np.M, np.invS, k) - l * prob(xq, nq.M, nq.invS, k), 0.f); };
+      if constexpr (VEC)
+        t = tile_search<E, kChunk / kThreads, kThreads>(p_row, q_row, lo, a.V, theta_s, w, lds_f, lds_i);
+      else
+        t = range_search<E, false, kThreads>(p_row, q_row, lo, hi, theta_s, w, lds_f, lds_i);
+    } else {
+      auto w = [&](float xp, float) { return fast_exp2((xp - np.M) * k); };
+      if constexpr (VEC)
+        t = tile_search<E, kChunk / kThreads, kThreads>(p_row, nullptr, lo, a.V, theta_s, w, lds_f, lds_i);
+      else
+        t = range_search<E, false, kThreads>(p_row, nullptr, lo, hi, theta_s, w, lds_f, lds_i);
+    }
+    // No token of the picked chunk has a positive residual: p_n and q_n agree
+    // to fp32 there and the positive chunk sum came from rounding.  That is the
+    // residual without mass: sample p_n itself (t is the same in every thread).
+    if (!(residual && t < 0)) break;
+    residual = false;
+    __syncthreads();
   }
   __syncthreads();
   clear_sequence_stats(a, stats, pair_stats, b, nch);  // no statistic is read after this
 
-  const int c = chunk_s, lo = c * kChunk, hi = min(a.V, lo + kChunk);
-  const auto* p_row = row_ptr<E>(a, target_row(b, n, G));
-  int t;
-  if (residual) {
-    const RowNorm nq = norm_s[1];
-    const auto* q_row = row_ptr<E>(a, draft_row(b, n, G, a.B));
-    const float l = a.lenience;
-    auto w = [&](float xp, float xq) { return fmaxf(prob(xp, np.M, np.invS, k) - l * prob(xq, nq.M, nq.invS, k), 0.f); };
-    if constexpr (VEC)
-      t = tile_search<E, kChunk / kThreads, kThreads>(p_row, q_row, lo, a.V, theta_s, w, lds_f, lds_i);
-    else
-      t = range_search<E, false, kThreads>(p_row, q_row, lo, hi, theta_s, w, lds_f, lds_i);
-  } else {
-    auto w = [&](float xp, float) { return fast_exp2((xp - np.M) * k); };
-    if constexpr (VEC)
-      t = tile_search<E, kChunk / kThreads, kThreads>(p_row, nullptr, lo, a.V, theta_s, w, lds_f, lds_i);
-    else
-      t = range_search<E, false, kThreads>(p_row, nullptr, lo, hi, theta_s, w, lds_f, lds_i);
-  }
   if (tid == 0) {
     a.n_out[b] = n;
     a.t_out[b] = t;

@@ -28,7 +28,8 @@ def case_tensors(case, dev):
     )
 
 
-def run_case(case, algo, tensors=None, dev=None, lenience: float = 1.0, gamma_seq=None, workspace=None):
+def run_case(case, algo, tensors=None, dev=None, lenience: float = 1.0, gamma_seq=None, workspace=None,
+             top_k: int = 0, top_p: float = 1.0):
     """gamma_seq: numpy int [B] (per-sequence draft counts) or None."""
     import torch
     import speculative_sampling_verification_02_amd as sv
@@ -37,7 +38,7 @@ def run_case(case, algo, tensors=None, dev=None, lenience: float = 1.0, gamma_se
     gs = None if gamma_seq is None else torch.from_numpy(np.ascontiguousarray(gamma_seq, dtype=np.int32)).to(dev)
     try:
         out = sv.verify(t["target"], t["draft"], t["tokens"], t["uniforms"], case.temperature, algo=algo,
-                        lenience=lenience, gamma_seq=gs, workspace=workspace)
+                        lenience=lenience, gamma_seq=gs, workspace=workspace, top_k=top_k, top_p=top_p)
     except sv.SpecVerifyError as e:
         if e.status == sv.SPEC_EUNSUPPORTED and algo == sv.ALGO_FUSED:
             import pytest

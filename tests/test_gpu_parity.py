@@ -148,6 +148,21 @@ def test_identical_draft_accepts_everything(dev, algo):
 
 
 @pytest.mark.parametrize("algo", list(ALGOS))
+def test_rejection_with_zero_residual_samples_p(dev, algo):
+    """Identical p and q rows at T = 0.02 with each draft at its row's minimum:
+    p(x) = q(x) = 0 even in fp64 (the exponent is below -1074), so 0/0 rejects
+    at position 0, the residual max(0, p - q) has no mass, and the token is
+    drawn from p_0 itself."""
+    case = W.gaussian_case(8, 3, 20000, "f32", 0.02, seed=6, target_std=2.5)
+    draft = case.target[:, :3].copy()
+    tokens = draft.argmin(-1).astype(np.int32)
+    case = W.VerifyCase("zero-residual", case.target, draft, "f32", tokens, case.uniforms, 0.02)
+    gpu = gpu_util.run_case(case, ALGOS[algo], dev=dev)
+    assert np.all(gpu["n_accepted"] == 0)
+    parity.check(case, gpu, where="zero residual")
+
+
+@pytest.mark.parametrize("algo", list(ALGOS))
 def test_argmax_ties_lowest_index(dev, algo):
     rng = np.random.default_rng(4)
     B, G, V = 8, 3, 20000

@@ -3,8 +3,10 @@ on adjusted distributions.
 
   * top-k against torch's library top-k on the CPU (every value at least the k-th
     largest, ties included);
-  * top-p against a brute-force statement of the definition over tiny rows: the
-    largest probability threshold pi whose set {p >= pi} holds at least top_p;
+  * top-p against a brute-force statement of the definition over tiny rows, in
+    fp64: the largest probability threshold pi whose set {p >= pi} holds at
+    least top_p (rows whose decision lies within the fp32 weights' rounding of
+    a boundary are exempt from the equality, not from the mass checks);
   * top-p after top-k renormalises over the top-k survivors;
   * the sampler then emits the adjusted target distribution ([FI] "The loop":
     the method treats the adjusted p and q as its distributions), checked by
@@ -63,15 +65,15 @@ def test_topp_matches_brute_force_definition(top_p, T):
     for r in _rows(rng, 30, 40, levels=3):
         tau, margin = adjust.topp_threshold(r, T, top_p)
         want = brute_topp(r, T, top_p, np.ones_like(r, bool))
-        if margin > 1e-9:                        # not exactly on a tie-group boundary
+        if margin > 1e-6:                        # not within the fp32 decision's rounding of a boundary
             assert tau == want
         kept = r >= tau
         p = np.exp((r - r.max()) / T)
         p /= p.sum()
-        assert p[kept].sum() >= top_p - 1e-12
+        assert p[kept].sum() >= top_p - 1e-6
         # minimal: dropping the smallest kept tie group falls below top_p
         lowest = r[kept].min()
-        assert p[kept & (r > lowest)].sum() < top_p + 1e-12
+        assert p[kept & (r > lowest)].sum() < top_p + 1e-6
 
 
 @pytest.mark.parametrize("k,top_p", [(5, 0.6), (12, 0.3), (3, 0.95)])

@@ -189,3 +189,24 @@ def test_inverse_cdf_strict_boundary_and_guard():
     # rounding guard: u above every cumulative value -> last positive-weight token
     w = np.array([[0.25, 0.25, 0.25, 0.0]])
     assert ov.inverse_cdf(w, np.array([0.9]))[0][0] == 2
+
+
+# ------------------------------------------------------- residual floor
+
+@pytest.mark.parametrize("delta,expect", [(2.0 ** -16, 0), (2.0 ** -21, 1), (2.0 ** -8, 0)])
+def test_residual_mass_floor(delta, expect):
+    """Two tokens: target logits (delta, 0), draft logits (0, 0), so p(0) =
+    1/(1 + e^-delta), about 1/2 + delta/4, and q = (1/2, 1/2).  Draft x = 1 has
+    ratio 1 - 2 (p(0) - 1/2), below the largest uniform 1 - 2^-24, so it is
+    rejected.  The residual max(0, p - q) sits on token 0 with mass about
+    delta/4.  Above the 2^-20 floor (delta = 2^-16, 2^-8) the token is 0 whatever
+    u is; below it (delta = 2^-21, mass about 2^-23) the token is drawn from p
+    itself, so u = 0.9 > p(0) gives token 1."""
+    target = np.array([[[delta, 0.0], [0.0, 0.0]]], np.float32)
+    draft = np.zeros((1, 1, 2), np.float32)
+    u = np.array([[1.0 - 2.0 ** -24, 0.9]], np.float32)
+    res = ov.verify(target, draft, np.array([[1]]), u, 1.0, "f32")
+    assert res.n_accepted[0] == 0
+    mass = 1.0 / (1.0 + np.exp(-np.float64(np.float32(delta)))) - 0.5
+    np.testing.assert_allclose(res.res_mass[0], mass, rtol=1e-9)
+    assert res.next_token[0] == expect
