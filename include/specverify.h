@@ -161,9 +161,9 @@ int spec_verify_algo(int algo,
  *              the filters change nothing and are skipped.  Filtering runs on
  *              the fused path only: SPEC_ALGO_MULTIPASS, or a shape the fused
  *              path declines, gives SPEC_EUNSUPPORTED.  A filtered call launches
- *              a threshold kernel (one workgroup per row, a radix select over
- *              the logits' bit keys), the verification, and a fill kernel that
- *              leaves the workspace zero.
+ *              the threshold kernel of spec_filter_thresholds (into the
+ *              workspace), the verification, and a fill kernel that leaves the
+ *              workspace zero.
  *
  *   lenience   l in (0, 1] ([FI] "The acceptance rate is the overlap of p and q",
  *              the lenience factor): draft i is kept when
@@ -198,6 +198,29 @@ int spec_verify_ex(int algo,
                    int32_t* n_accepted, int32_t* next_token, float* alpha,
                    float* p_draft, float* q_draft,
                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * spec_filter_thresholds -- the per-row keep thresholds of top-k / top-p, as
+ * spec_verify_ex applies them ([FI] "The loop: draft, verify in one pass, keep
+ * a prefix"; [NZ] "5. Sampling and evaluation"), for callers that mask or
+ * sample rows themselves.
+ *   target_logits [B][gamma+1][V], draft_logits [B][gamma][V] (NULL when
+ *   gamma == 0), dtype SPEC_F32 or SPEC_BF16, both 16-byte aligned with V *
+ *   element size a multiple of 16.  temperature > 0 and finite (the top-p mass
+ *   is that of softmax(logit / T)); top_k and top_p as for spec_verify_ex.
+ *   thresholds  device float32 [B*(gamma+1) + B*gamma] out: first the target
+ *               rows in order (b, i), then the draft rows.  Row r keeps the
+ *               tokens whose logit is >= thresholds[r]; the value is one of the
+ *               row's logits, or -inf when the row keeps everything (no filter
+ *               active, or fewer finite logits than top_k).
+ *   Ties are kept.  Masses are fp32 exp2((logit - max) log2(e) / T), summed in
+ *   fp64 and 2^-40 fixed point; a nucleus boundary within about 2^-23 of
+ *   top_p times the total may fall on either side of that tie group.
+ *   Returns SPEC_EINVAL for a bad shape, alignment, temperature or top_p.
+ */
+int spec_filter_thresholds(const void* target_logits, const void* draft_logits, int dtype,
+                           int B, int gamma, int V, float temperature, int top_k, float top_p,
+                           float* thresholds, void* stream);
 
 /*
  * spec_lmhead_logits -- the target pass's final matrix product for the positions

@@ -41,6 +41,8 @@ SIGNATURES = {
                                 _c_int, _c_int, _c_int, _c_float, _c_int, _c_float, _c_float, _c_void_p,
                                 _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                 _c_void_p, _c_size_t, _c_void_p]),
+    "spec_filter_thresholds": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_int, _c_float,
+                                        _c_int, _c_float, _c_void_p, _c_void_p]),
     "spec_lmhead_logits": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_void_p, _c_void_p]),
     "spec_lmhead_workspace_size": (_c_size_t, [_c_int, _c_int, _c_int, _c_int]),
     "spec_lmhead_verify": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p,
@@ -181,6 +183,28 @@ def verify(target_logits, draft_logits, draft_tokens, uniforms, temperature: flo
                                             outputs, workspace, dev)),
            "spec_verify")
     return outputs
+
+
+def filter_thresholds(target_logits, draft_logits, temperature: float, top_k: int = 0, top_p: float = 1.0):
+    """Per-row keep thresholds of top-k / top-p (spec_filter_thresholds).
+
+    target_logits [B, gamma+1, V] and draft_logits [B, gamma, V] (float32 or
+    bfloat16) on one GPU; temperature > 0.  Returns float32 GPU tensors
+    (target [B, gamma+1], draft [B, gamma]): a row keeps the tokens whose logit
+    is >= its threshold (-inf: the whole row)."""
+    torch = _torch()
+    dev = target_logits.device
+    _need(target_logits, "target_logits")
+    B, g1, V = target_logits.shape
+    gamma = g1 - 1
+    if tuple(draft_logits.shape) != (B, gamma, V) or draft_logits.dtype != target_logits.dtype:
+        raise ValueError("draft_logits must be [B, gamma, V] with the target's dtype")
+    _need(draft_logits, "draft_logits", device=dev)
+    thr = torch.empty(B * g1 + B * gamma, dtype=torch.float32, device=dev)
+    _check(lib.spec_filter_thresholds(_ptr(target_logits), _ptr(draft_logits) if gamma else None,
+                                      _dtype_code(target_logits), B, gamma, V, float(temperature), int(top_k),
+                                      float(top_p), _ptr(thr), _stream(dev)), "spec_filter_thresholds")
+    return thr[:B * g1].view(B, g1), thr[B * g1:].view(B, gamma)
 
 
 def _verify_args(algo, target_logits, draft_logits, dt, draft_tokens, uniforms, B, gamma, V, temperature,

@@ -160,6 +160,27 @@ int spec_lmhead_logits(const void* hidden, const void* W, int M, int d, int V, f
   return map_hip(specv::lmhead_launch(&job, 1, d, V, static_cast<hipStream_t>(stream)));
 }
 
+int spec_filter_thresholds(const void* target_logits, const void* draft_logits, int dtype, int B, int gamma,
+                           int V, float temperature, int top_k, float top_p, float* thresholds, void* stream) {
+  if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_EUNSUPPORTED;
+  if (!valid_shape(B, gamma, V) || !valid_temperature(temperature) || !(temperature > 0.f)) return SPEC_EINVAL;
+  if (!(top_p > 0.f)) return SPEC_EINVAL;  // also rejects NaN
+  if (B == 0) return SPEC_OK;
+  if (!target_logits || !thresholds || (gamma > 0 && !draft_logits)) return SPEC_EINVAL;
+  const size_t row_bytes = (size_t)V * (dtype == SPEC_BF16 ? 2 : 4);
+  if (row_bytes % 16 || !aligned16(target_logits) || (gamma > 0 && !aligned16(draft_logits))) return SPEC_EINVAL;
+  VerifyArgs a{};
+  a.target = target_logits;
+  a.draft = draft_logits;
+  a.dtype = dtype;
+  a.B = B;
+  a.gamma = gamma;
+  a.V = V;
+  a.temperature = temperature;
+  a.k = kLog2e / temperature;
+  return map_hip(specv::filter_thresholds(a, top_k, top_p, thresholds, static_cast<hipStream_t>(stream)));
+}
+
 size_t spec_lmhead_workspace_size(int B, int gamma, int d, int V) {
   if (!specv::lmhead_shape_ok(d, V)) return 0;
   return spec_verify_workspace_size(B, gamma, V, SPEC_F32);

@@ -12,14 +12,28 @@
 // and the row keeps logit >= max(tau_k, tau_p).  The verification kernels then
 // read a dropped logit as -inf.
 //
-// One workgroup per row finds each threshold by a radix select over the
-// logits' order-preserving bit keys, 8 bits per pass from the top: per pass,
-// a histogram of the next byte of the keys that share the bytes already
-// chosen (counts for top-k, softmax mass for top-p), then a scan from the top
-// bin picks the byte.  bf16 keys are 16 bits (2 passes per filter), fp32 keys
-// 32 bits (4 passes).  Mass is accumulated in 64-bit fixed point (2^-40 of the
-// row maximum's weight), so the sums, and therefore the thresholds, do not
-// depend on the order of the atomic additions.
+// One workgroup of 1024 threads per row, with the row held in registers (one
+// read from memory).  Every pass over the row is a few instructions per token:
+//   1. row maximum and finite minimum;
+//   2. a 16-bin histogram over [min, max] (linear in the logit): counts for
+//      top-k, fp64 softmax mass for top-p.  Each lane owns its own column of
+//      bins in LDS, so the additions never contend;
+//   3. the bin where the running count (mass) from the top reaches k (top_p
+//      of the total) is copied to an LDS list (wave-aggregated appends);
+//   4. the exact threshold is found inside that list by a radix select over
+//      the candidates' order-preserving 32-bit keys (mass in 2^-40 fixed
+//      point, so sums do not depend on the order of the atomic additions).
+// A crossing bin too large for the list is refined once (16 finer bins inside
+// it).  With top-k active and its survivors fitting the list, top-p runs on
+// the copied survivors alone and the row needs no full exponential pass.
+// Rows that still do not fit, rows longer than the register capacity and rows
+// whose finite logits are all equal take a radix select over the whole row
+// from memory instead (8 bits per pass).
+//
+// Masses are exp2((l - m) log2(e) / T) in fp32 (m the row maximum).  The
+// histogram adds them in fp64 (each lane in its own fixed order), the lists in
+// 2^-40 fixed point; against the exact sum of the same fp32 weights the two
+// differ by under 2^-41 per token, far below the fp32 exponential's own ulp.
 
 #include <hip/hip_runtime.h>
 
@@ -32,8 +46,12 @@
 namespace specv {
 namespace {
 
-constexpr int kFThreads = 512;
+constexpr int kFT = 1024;        // threads per row
+constexpr int kFNV = 16;         // 16-byte vectors per thread held in registers
+constexpr int kNB = 16;          // bins per histogram level (one wave reduces one bin)
+constexpr int kCap = 32768;      // candidates the LDS list holds
 constexpr double kMassScale = 1099511627776.0;  // 2^40
+static_assert(kFT / kWave == kNB, "one wave per bin in the reductions");
 
 struct FilterArgs {
   const void* target;  // [B][gamma+1][V]
@@ -44,6 +62,27 @@ struct FilterArgs {
   int top_k;           // active when 0 < top_k < V
   float top_p;         // active when top_p < 1
   float* thr;          // [rows] out: keep threshold (-inf: keep all)
+};
+
+struct FilterLds {
+  union {
+    uint32_t cnt[kNB][kFT];  // per-lane count bins
+    double mass[kNB][kFT];   // per-lane mass bins
+    float cand[kCap];        // candidate logits
+  } big;
+  uint32_t cnt256[256];
+  unsigned long long m256[256];
+  uint32_t pcnt[2][256];              // the candidate picks' bins, double-buffered
+  unsigned long long pmass[2][256];
+  double bin_val[kNB];
+  float redf[2 * kMaxWaves];
+  uint32_t ncand;
+  int pick_b;
+  double pick_before;
+  uint32_t prefix_s, need_s;
+  uint32_t kmin_s, kmax_s;
+  unsigned long long above_s;
+  double target_s;
 };
 
 // Order-preserving unsigned key of a finite or -inf logit (-0 as +0), in the
@@ -65,24 +104,61 @@ __device__ inline float value_of(uint32_t key) {
   return __uint_as_float(u);
 }
 
+__device__ inline unsigned long long fixed_mass(float w) {
+  return (unsigned long long)((double)w * kMassScale + 0.5);
+}
+
+// One wave scans 256 bin values from bin 255 down to 0 and finds the first
+// bin b at which (sum of the bins above b) + bin b >= need.  Returns b (-1
+// when the total falls short) and *before = the sum above b, the same in
+// every lane.  Values are exact integers (counts, or fixed-point masses below
+// 2^53) or fp64 sums; the scan adds them in one fixed order.
+template <class F>
+__device__ inline int wave_pick_desc(F binval, double need, double* before_out) {
+  const int lane = threadIdx.x;
+  double c[4], s = 0.0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    c[i] = binval(255 - 4 * lane - i);
+    s += c[i];
+  }
+  const double incl = wave_inclusive_scan(s);
+  double acc = __shfl_up(incl, 1);
+  if (lane == 0) acc = 0.0;
+  int found = -1;
+  double before = 0.0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (found < 0 && acc + c[i] >= need) {
+      found = 255 - 4 * lane - i;
+      before = acc;
+    }
+    acc += c[i];
+  }
+  const unsigned long long hit = __ballot(found >= 0);
+  if (!hit) {
+    *before_out = 0.0;
+    return -1;
+  }
+  const int leader = __ffsll((long long)hit) - 1;
+  *before_out = lane_d(before, leader);
+  return __builtin_amdgcn_readlane(found, leader);
+}
+
+// ---------------------------------------------------------------- fallback
+// Radix select over the whole row read from memory, 8 bits per pass: top-k by
+// counts, then top-p by 2^-40 fixed-point mass.  Exact for any row; slower,
+// since every pass re-reads the row and bins contend.
 template <class E>
-__global__ __launch_bounds__(kFThreads) void row_threshold_kernel(FilterArgs f) {
+__device__ __attribute__((always_inline)) inline float radix_threshold(const typename E::storage* row,
+                                                                       const FilterArgs f, FilterLds& L) {
   constexpr int KB = std::is_same<E, BF16>::value ? 16 : 32;
   constexpr int kPasses = KB / 8;
-  __shared__ uint32_t cnt[256];
-  __shared__ unsigned long long msum[256];
-  __shared__ float red_f[kFThreads / kWave];
-  __shared__ uint32_t prefix_s, need_s;
-  __shared__ unsigned long long above_s;
-  __shared__ double target_s;
   const int tid = threadIdx.x;
-  const int r = blockIdx.x;
-  const auto* row = r < f.nt ? static_cast<const typename E::storage*>(f.target) + (size_t)r * f.V
-                             : static_cast<const typename E::storage*>(f.draft) + (size_t)(r - f.nt) * f.V;
   auto for_each = [&](auto fn) {
-    for (int j0 = tid * E::kVec; j0 < f.V; j0 += kFThreads * E::kVec) {
+    for (int j0 = tid * E::kVec; j0 < f.V; j0 += kFT * E::kVec) {
       float t[E::kVec];
-      E::unpack(load_stream(row + j0), t);
+      E::unpack(load_cached(row + j0), t);
 #pragma unroll
       for (int e = 0; e < E::kVec; ++e) fn(t[e]);
     }
@@ -90,91 +166,480 @@ __global__ __launch_bounds__(kFThreads) void row_threshold_kernel(FilterArgs f) 
   const bool use_k = f.top_k > 0 && f.top_k < f.V;
   const bool use_p = f.top_p < 1.f;
 
-  // ---- top-k: the key of the k-th largest logit
   uint32_t tau_k = 0;  // the smallest key: keep all
   if (use_k) {
+    __syncthreads();
     if (tid == 0) {
-      prefix_s = 0;
-      need_s = (uint32_t)f.top_k;  // rank from the top among the keys that share the prefix
+      L.prefix_s = 0;
+      L.need_s = (uint32_t)f.top_k;  // rank from the top among the keys that share the prefix
     }
     for (int pass = 0; pass < kPasses; ++pass) {
       const int shift = KB - 8 * (pass + 1);
       const uint32_t mask = pass == 0 ? 0u : (~0u << (shift + 8)) & (KB == 32 ? ~0u : 0xffffu);
-      for (int b = tid; b < 256; b += kFThreads) cnt[b] = 0;
+      for (int b = tid; b < 256; b += kFT) L.cnt256[b] = 0;
       __syncthreads();
-      const uint32_t prefix = prefix_s;
+      const uint32_t prefix = L.prefix_s;
       for_each([&](float x) {
         const uint32_t key = key_of<KB>(x);
-        if ((key & mask) == prefix) atomicAdd(&cnt[(key >> shift) & 0xffu], 1u);
+        if ((key & mask) == prefix) atomicAdd(&L.cnt256[(key >> shift) & 0xffu], 1u);
       });
       __syncthreads();
       if (tid == 0) {
-        const uint32_t need = need_s;
+        const uint32_t need = L.need_s;
         uint32_t acc = 0;
         for (int b = 255; b >= 0; --b) {
-          if (acc + cnt[b] >= need) {
-            need_s = need - acc;
-            prefix_s = prefix | ((uint32_t)b << shift);
+          if (acc + L.cnt256[b] >= need) {
+            L.need_s = need - acc;
+            L.prefix_s = prefix | ((uint32_t)b << shift);
             break;
           }
-          acc += cnt[b];
+          acc += L.cnt256[b];
         }
       }
       __syncthreads();
     }
-    tau_k = prefix_s;
+    tau_k = L.prefix_s;
   }
 
-  // ---- top-p: the largest key whose upper set holds top_p of the survivors' mass
   uint32_t tau_p = 0;
   if (use_p) {
     // the row maximum, for weights exp2((l - m) k) in (0, 1]
     float m = -INFINITY;
     for_each([&](float x) { m = fmaxf(m, x); });
-    m = wave_max(m);
-    if ((tid & (kWave - 1)) == 0) red_f[tid / kWave] = m;
+    m = block_max(m, L.redf);
     __syncthreads();
-    m = red_f[0];
-    for (int w = 1; w < kFThreads / kWave; ++w) m = fmaxf(m, red_f[w]);
     if (tid == 0) {
-      prefix_s = 0;
-      above_s = 0;
+      L.prefix_s = 0;
+      L.above_s = 0;
     }
     for (int pass = 0; pass < kPasses; ++pass) {
       const int shift = KB - 8 * (pass + 1);
       const uint32_t mask = pass == 0 ? 0u : (~0u << (shift + 8)) & (KB == 32 ? ~0u : 0xffffu);
-      for (int b = tid; b < 256; b += kFThreads) msum[b] = 0;
+      for (int b = tid; b < 256; b += kFT) L.m256[b] = 0;
       __syncthreads();
-      const uint32_t prefix = prefix_s;
+      const uint32_t prefix = L.prefix_s;
       for_each([&](float x) {
         const uint32_t key = key_of<KB>(x);
-        if (key >= tau_k && (key & mask) == prefix && x != -INFINITY) {
-          const float w = __builtin_amdgcn_exp2f((x - m) * f.k);
-          atomicAdd(&msum[(key >> shift) & 0xffu], (unsigned long long)((double)w * kMassScale + 0.5));
-        }
+        if (key >= tau_k && (key & mask) == prefix && x != -INFINITY)
+          atomicAdd(&L.m256[(key >> shift) & 0xffu], fixed_mass(__builtin_amdgcn_exp2f((x - m) * f.k)));
       });
       __syncthreads();
       if (tid == 0) {
         if (pass == 0) {
           unsigned long long total = 0;
-          for (int b = 0; b < 256; ++b) total += msum[b];
-          target_s = (double)f.top_p * (double)total;
+          for (int b = 0; b < 256; ++b) total += L.m256[b];
+          L.target_s = (double)f.top_p * (double)total;
         }
-        unsigned long long acc = above_s;
+        unsigned long long acc = L.above_s;
         for (int b = 255; b >= 0; --b) {
-          if ((double)(acc + msum[b]) >= target_s) {
-            above_s = acc;
-            prefix_s = prefix | ((uint32_t)b << shift);
+          if ((double)(acc + L.m256[b]) >= L.target_s) {
+            L.above_s = acc;
+            L.prefix_s = prefix | ((uint32_t)b << shift);
             break;
           }
-          acc += msum[b];
+          acc += L.m256[b];
         }
       }
       __syncthreads();
     }
-    tau_p = prefix_s;
+    tau_p = L.prefix_s;
   }
-  if (tid == 0) f.thr[r] = (use_k || use_p) ? value_of<KB>(max(tau_k, tau_p)) : -INFINITY;
+  return (use_k || use_p) ? value_of<KB>(max(tau_k, tau_p)) : -INFINITY;
+}
+
+// ------------------------------------------------------------- fast path
+
+template <class E>
+__global__ __launch_bounds__(kFT) void row_threshold_kernel(FilterArgs f) {
+  constexpr int KV = E::kVec;
+  __shared__ FilterLds L;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+  const int r = blockIdx.x;
+  const auto* row = r < f.nt ? static_cast<const typename E::storage*>(f.target) + (size_t)r * f.V
+                             : static_cast<const typename E::storage*>(f.draft) + (size_t)(r - f.nt) * f.V;
+  const int V = f.V;
+  const bool use_k = f.top_k > 0 && f.top_k < V;
+  const bool use_p = f.top_p < 1.f;
+  if (!use_k && !use_p) {
+    if (tid == 0) f.thr[r] = -INFINITY;
+    return;
+  }
+  // rows longer than the registers hold take the radix select from memory
+  bool fallback = V > kFT * kFNV * KV;
+
+  // the row, in registers: vector v of thread t holds tokens (v kFT + t) KV ..
+  u32x4 raw[kFNV];
+#pragma unroll
+  for (int v = 0; v < kFNV; ++v) {
+    const int j0 = (v * kFT + tid) * KV;
+    raw[v] = !fallback && j0 < V ? load_cached(row + j0) : u32x4{0u, 0u, 0u, 0u};
+  }
+  auto each = [&](auto fn) {
+#pragma unroll
+    for (int v = 0; v < kFNV; ++v) {
+      if ((v * kFT + tid) * KV < V) {
+        // a copy of the words that is opaque to the compiler, so every pass
+        // unpacks afresh instead of keeping up to 128 unpacked values live
+        u32x4 w = raw[v];
+        asm volatile("" : "+v"(w.x), "+v"(w.y), "+v"(w.z), "+v"(w.w));
+        float t[KV];
+        E::unpack(w, t);
+#pragma unroll
+        for (int e = 0; e < KV; ++e) fn(t[e]);
+      }
+    }
+  };
+
+  // ---- 1. row maximum; each thread's own maximum is kept for the top-k pivot
+  float tmax = -INFINITY;
+  if (!fallback) each([&](float x) { tmax = fmaxf(tmax, x); });
+  float mx = -INFINITY;
+  if (!fallback) {
+    mx = block_max(tmax, L.redf);
+    fallback = mx == -INFINITY;  // no finite logit
+  }
+  const float k = f.k;
+  // Histogram bins are two octaves of softmax weight wide: t(x) ~ (m - x) k / 2,
+  // bin = clamp(t, 0, 15) truncated (bin 15 also takes the tail and -inf).
+  // A second level splits one bin j into 16: bin = clamp(16 (t - j), 0, 15).
+  const float c = 0.5f * k, mc = mx * c;
+  auto binof = [](float t) { return (int)__builtin_amdgcn_fmed3f(t, 0.f, 15.f); };
+  int lv_j = 0;  // the bin a second level refines
+
+  // One pass over the row.  Values in range are those >= lo and, at level 1,
+  // those of level-0 bin lv_j; `b` is the bin at the pass's level.
+  //   kind 0: per-lane count histogram, reduced to L.bin_val[16]
+  //   kind 1: per-lane fp64 mass histogram, reduced to L.bin_val[16]
+  //   kind 2: copy the values in range whose bin is jsel to the candidate
+  //           list; returns how many there were
+  //   kind 3: copy every value >= lo (no bins); returns how many there were
+  // The per-lane additions are branchless (out of range adds 0).
+  auto run_pass = [&](auto level_c, auto kind_c, float lo, int jsel) -> uint32_t {
+    constexpr int LEVEL = decltype(level_c)::value;
+    constexpr int kind = decltype(kind_c)::value;
+    auto locate = [&](float x, int* b) -> bool {
+      const float t = fmaf(x, -c, mc);
+      const int b0 = binof(t);
+      if constexpr (LEVEL == 0) {
+        *b = b0;
+        return x >= lo;
+      } else {
+        *b = binof(fmaf(t, 16.f, -16.f * (float)lv_j));
+        return b0 == lv_j && x >= lo;
+      }
+    };
+    __syncthreads();  // the LDS region may still hold a candidate list or bins
+    if constexpr (kind == 0) {
+#pragma unroll
+      for (int b = 0; b < kNB; ++b) L.big.cnt[b][tid] = 0u;
+      each([&](float x) {
+        int b;
+        const bool in = locate(x, &b);
+        __hip_atomic_fetch_add(&L.big.cnt[b][tid], (uint32_t)in, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      });
+    } else if constexpr (kind == 1) {
+#pragma unroll
+      for (int b = 0; b < kNB; ++b) L.big.mass[b][tid] = 0.0;
+      each([&](float x) {
+        int b;
+        const bool in = locate(x, &b);
+        const float w = in ? __builtin_amdgcn_exp2f((x - mx) * k) : 0.f;
+        __hip_atomic_fetch_add(&L.big.mass[b][tid], (double)w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      });
+    } else {
+      static_assert(kind == 2 || kind == 3, "pass kinds 0-3");
+      if (tid == 0) L.ncand = 0;
+      __syncthreads();
+      // per 16-byte vector: a lane's candidates as a bit mask; a wave with
+      // none skips the vector, else one prefix scan and one LDS atomic place
+      // the wave's candidates in the list
+#pragma unroll
+      for (int v = 0; v < kFNV; ++v) {
+        const bool valid = (v * kFT + tid) * KV < V;
+        u32x4 w = raw[v];
+        asm volatile("" : "+v"(w.x), "+v"(w.y), "+v"(w.z), "+v"(w.w));
+        float t[KV];
+        E::unpack(w, t);
+        uint32_t mask = 0;
+#pragma unroll
+        for (int e = 0; e < KV; ++e) {
+          bool in;
+          if constexpr (kind == 3) {
+            in = t[e] >= lo;
+          } else {
+            int b;
+            in = locate(t[e], &b) && b == jsel;
+          }
+          mask |= (uint32_t)(valid && in) << e;
+        }
+        if (__ballot(mask != 0u) == 0ull) continue;
+        const uint32_t cnt = (uint32_t)__popc(mask);
+        const uint32_t incl = (uint32_t)wave_inclusive_scan((float)cnt);  // exact: at most 512
+        const uint32_t total = (uint32_t)__shfl((int)incl, kWave - 1);
+        uint32_t base = 0;
+        if (lane == 0) base = atomicAdd(&L.ncand, total);
+        uint32_t pos = (uint32_t)__shfl((int)base, 0) + incl - cnt;
+#pragma unroll
+        for (int e = 0; e < KV; ++e) {
+          if ((mask >> e) & 1u) {
+            if (pos < (uint32_t)kCap) L.big.cand[pos] = t[e];
+            ++pos;
+          }
+        }
+      }
+    }
+    __syncthreads();
+    if constexpr (kind >= 2) return L.ncand;
+    // wave w sums bin w over all lanes in one fixed order
+    double s = 0.0;
+    if constexpr (kind == 0) {
+#pragma unroll
+      for (int i = 0; i < kFT / kWave; ++i) s += (double)L.big.cnt[wid][lane + i * kWave];
+    } else {
+#pragma unroll
+      for (int i = 0; i < kFT / kWave; ++i) s += L.big.mass[wid][lane + i * kWave];
+    }
+    s = wave_sum(s);
+    if (lane == 0) L.bin_val[wid] = s;
+    __syncthreads();
+    return 0u;
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  // first bin from the top whose running sum (from `base`) reaches need:
+  // returns the bin (-1 if none) and the running sum above it
+  auto crossing = [&](double base, double need, double* above) {
+    double acc = base;
+    for (int b = 0; b < kNB; ++b) {
+      if (acc + L.bin_val[b] >= need) {
+        *above = acc;
+        return b;
+      }
+      acc += L.bin_val[b];
+    }
+    *above = acc;
+    return -1;
+  };
+  // Radix pick over the listed values >= lo: the largest key K (returned as
+  // its value) with base + W(listed keys >= K) >= need, W a count (MASS
+  // false) or the 2^-40 fixed-point softmax mass (MASS true).  need < 0 (mass
+  // only) means top_p of the listed values' own total, with base 0.  The
+  // 8-bit digits are taken over the keys' actual range [kmin, kmax], so the
+  // first pass already spreads a narrow list over many bins (few colliding
+  // LDS atomics) and a list of close values needs few passes.  Keys are the
+  // 16 significant bits for bf16 rows (the list holds widened bf16 values).
+  auto pick = [&](auto mass_c, uint32_t n, float lo, double base, double need) -> float {
+    constexpr bool MASS = decltype(mass_c)::value;
+    constexpr int KB = std::is_same<E, BF16>::value ? 16 : 32;
+    // key range of the listed values >= lo
+    if (tid == 0) {
+      L.kmin_s = 0xffffffffu;
+      L.kmax_s = 0u;
+    }
+    __syncthreads();
+    uint32_t kmn = 0xffffffffu, kmx = 0u;
+    for (uint32_t i = tid; i < n; i += kFT) {
+      const float x = L.big.cand[i];
+      if (x >= lo) {
+        const uint32_t key = key_of<KB>(x);
+        kmn = min(kmn, key);
+        kmx = max(kmx, key);
+      }
+    }
+#pragma unroll
+    for (int off = kWave / 2; off >= 1; off >>= 1) {
+      kmn = min(kmn, (uint32_t)__shfl_xor((int)kmn, off));
+      kmx = max(kmx, (uint32_t)__shfl_xor((int)kmx, off));
+    }
+    if (lane == 0) {
+      atomicMin(&L.kmin_s, kmn);
+      atomicMax(&L.kmax_s, kmx);
+    }
+    __syncthreads();
+    const uint32_t kmin = L.kmin_s, span = L.kmax_s - L.kmin_s;
+    const int nbits = span ? 32 - __clz((int)span) : 0;
+    uint32_t prefix = 0;  // chosen high bits of (key - kmin)
+    // each pass picks bits [shift, hi) of (key - kmin), hi falling from nbits
+    // to 0; a span of one key still takes one pass (the mass total).  The
+    // bins are double-buffered: a pass clears the next pass's set, so it
+    // needs only the barrier after its additions and the one after the pick.
+    if (tid < 256) {
+      if constexpr (MASS) L.pmass[0][tid] = 0ull;
+      else L.pcnt[0][tid] = 0u;
+    }
+    __syncthreads();
+    int hi = nbits, buf = 0;
+    do {
+      const int shift = hi > 8 ? hi - 8 : 0;
+      const uint32_t hi_mask = hi >= 32 ? 0u : ~0u << hi;
+      const uint32_t dmask = (1u << (hi - shift)) - 1u;
+      if (tid < 256) {
+        if constexpr (MASS) L.pmass[buf ^ 1][tid] = 0ull;
+        else L.pcnt[buf ^ 1][tid] = 0u;
+      }
+      for (uint32_t i = tid; i < n; i += kFT) {
+        const float x = L.big.cand[i];
+        const uint32_t d = key_of<KB>(x) - kmin;
+        if (x >= lo && (d & hi_mask) == prefix) {
+          if constexpr (MASS)
+            atomicAdd(&L.pmass[buf][(d >> shift) & dmask], fixed_mass(__builtin_amdgcn_exp2f((x - mx) * k)));
+          else
+            atomicAdd(&L.pcnt[buf][(d >> shift) & dmask], 1u);
+        }
+      }
+      __syncthreads();
+      auto binv = [&](int b) -> double {
+        if constexpr (MASS) return (double)L.pmass[buf][b] / kMassScale;
+        else return (double)L.pcnt[buf][b];
+      };
+      if (wid == 0) {
+        if constexpr (MASS) {
+          if (need < 0.0) {  // top_p of the listed total (wave 0 only needs it)
+            double s = 0.0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s += (double)L.pmass[buf][lane * 4 + i];
+            need = (double)f.top_p * (wave_sum(s) / kMassScale);
+            base = 0.0;
+          }
+        }
+        double before;
+        int b = wave_pick_desc(binv, need - base, &before);
+        if (b < 0) {
+          // the list's total fell short of need by rounding (the fixed-point
+          // list against the histogram's fp64 sum): keep all of this prefix
+          b = 0;
+          before = 0.0;
+          for (int q = 255; q >= 0; --q) {
+            if (binv(q) > 0.0) {
+              b = q;
+              break;
+            }
+          }
+          for (int q = 255; q > b; --q) before += binv(q);
+        }
+        if (lane == 0) {
+          L.pick_b = b;
+          L.pick_before = before;
+        }
+      }
+      __syncthreads();  // every read of this pass's bins is done
+      base += L.pick_before;
+      prefix |= (uint32_t)L.pick_b << shift;
+      hi = shift;
+      buf ^= 1;
+    } while (hi > 0);
+    return value_of<KB>(kmin + prefix);
+  };
+  using BF = std::integral_constant<bool, false>;
+  using BT = std::integral_constant<bool, true>;
+  // the rank-th largest listed value >= lo (ties counted)
+  auto select_kth = [&](uint32_t n, uint32_t rank, float lo) { return pick(BF{}, n, lo, 0.0, (double)rank); };
+  // the nucleus threshold of the listed values >= lo: base + mass(>= tau) >=
+  // target (target < 0: top_p of their own total)
+  auto nucleus = [&](uint32_t n, double base, double target, float lo) { return pick(BT{}, n, lo, base, target); };
+
+  // ---- 2-4. the filters, as a sequence of passes; each (level, kind) of
+  // run_pass has one call site, so its unrolled body is instantiated once
+  enum { K_PIVOT, K_HIST0, K_COPY0, K_HIST1, K_COPY1, P_START, P_SURV, P_HIST0, P_COPY0, P_HIST1, P_COPY1, DONE };
+  float tau_k = -INFINITY, tau_p = -INFINITY, pivot = -INFINITY;
+  bool survivors_listed = false;  // the list holds every value >= tau_k
+  double above = 0.0, target = 0.0;
+  uint32_t n = 0;
+  int j = 0;
+  int state = fallback ? DONE : !use_k ? P_START : f.top_k <= kFT ? K_PIVOT : K_HIST0;
+  while (state != DONE) {
+    if (state == P_START) {
+      if (!use_p) {
+        state = DONE;
+      } else if (survivors_listed) {  // the nucleus of the listed survivors: no pass
+        tau_p = nucleus(n, 0.0, -1.0, tau_k);
+        state = DONE;
+      } else {
+        state = use_k && above + (double)n <= (double)kCap ? P_SURV : P_HIST0;
+      }
+      continue;
+    }
+    if (state == K_PIVOT) {
+      // The k-th largest thread maximum is a lower bound of tau_k (k threads
+      // each hold a value at least that large); the values at or above it
+      // are usually few, and the exact k-th largest is among them.
+      __syncthreads();
+      L.big.cand[tid] = tmax;
+      __syncthreads();
+      pivot = select_kth(kFT, (uint32_t)f.top_k, -INFINITY);
+    }
+    const bool lv1 = state == K_HIST1 || state == K_COPY1 || state == P_HIST1 || state == P_COPY1;
+    const int kind = (state == K_HIST0 || state == K_HIST1) ? 0
+                     : (state == P_HIST0 || state == P_HIST1) ? 1
+                     : (state == K_PIVOT || state == P_SURV) ? 3 : 2;
+    const float lo = state == K_PIVOT ? pivot : state > P_START ? tau_k : -INFINITY;
+    uint32_t got;
+    if (kind == 3)
+      got = run_pass(I0{}, I3{}, lo, 0);
+    else if (!lv1)
+      got = kind == 0 ? run_pass(I0{}, I0{}, lo, j)
+            : kind == 1 ? run_pass(I0{}, I1{}, lo, j) : run_pass(I0{}, I2{}, lo, j);
+    else
+      got = kind == 0 ? run_pass(I1{}, I0{}, lo, j)
+            : kind == 1 ? run_pass(I1{}, I1{}, lo, j) : run_pass(I1{}, I2{}, lo, j);
+    double ab = 0.0;
+    switch (state) {
+      case K_PIVOT:
+        n = got;
+        if (n <= (uint32_t)kCap) {
+          tau_k = select_kth(n, (uint32_t)f.top_k, -INFINITY);
+          survivors_listed = true;
+          state = P_START;
+        } else {
+          state = K_HIST0;
+        }
+        break;
+      case K_HIST0:  // found: all V values are counted (-inf in bin 15) and k < V
+        j = crossing(0.0, (double)f.top_k, &above);
+        state = K_COPY0;
+        break;
+      case P_HIST0: {
+        double total = 0.0;
+        for (int b = 0; b < kNB; ++b) total += L.bin_val[b];
+        target = (double)f.top_p * total;
+        j = crossing(0.0, target, &above);  // found: the running sum ends at total > target
+        state = P_COPY0;
+        break;
+      }
+      case K_HIST1:
+      case P_HIST1:
+        j = crossing(above, state == K_HIST1 ? (double)f.top_k : target, &ab);
+        above = ab;
+        state = j < 0 ? DONE : state == K_HIST1 ? K_COPY1 : P_COPY1;
+        fallback = j < 0;
+        break;
+      default:  // a list was copied
+        n = got;
+        if (n > (uint32_t)kCap) {
+          if (state == K_COPY0 || state == P_COPY0) {  // refine the crossing bin once
+            lv_j = j;
+            state = state == K_COPY0 ? K_HIST1 : P_HIST1;
+          } else {
+            fallback = true;
+            state = DONE;
+          }
+        } else if (state == K_COPY0 || state == K_COPY1) {
+          tau_k = select_kth(n, (uint32_t)((double)f.top_k - above), -INFINITY);
+          state = P_START;
+        } else if (state == P_SURV) {
+          tau_p = nucleus(n, 0.0, -1.0, tau_k);
+          state = DONE;
+        } else {
+          tau_p = nucleus(n, above, target, -INFINITY);
+          state = DONE;
+        }
+        break;
+    }
+  }
+  const float t = fallback ? radix_threshold<E>(row, f, L) : fmaxf(tau_k, tau_p);
+  if (tid == 0) f.thr[r] = t;
 }
 
 __global__ void fill_zero_kernel(float* p, int n) {
@@ -189,9 +654,9 @@ hipError_t filter_thresholds(const VerifyArgs& a, int top_k, float top_p, float*
   const int rows = a.B * (2 * a.gamma + 1);
   if (rows == 0) return hipSuccess;
   if (a.dtype == SPEC_BF16)
-    row_threshold_kernel<BF16><<<dim3(rows), dim3(kFThreads), 0, s>>>(f);
+    row_threshold_kernel<BF16><<<dim3(rows), dim3(kFT), 0, s>>>(f);
   else
-    row_threshold_kernel<F32><<<dim3(rows), dim3(kFThreads), 0, s>>>(f);
+    row_threshold_kernel<F32><<<dim3(rows), dim3(kFT), 0, s>>>(f);
   return hipGetLastError();
 }
 

@@ -19,7 +19,8 @@ def _declared_functions():
 
 def test_header_declares_the_entry_points():
     names = _declared_functions()
-    for want in ("spec_verify", "spec_verify_algo", "spec_verify_workspace_size",
+    for want in ("spec_verify", "spec_verify_algo", "spec_verify_ex", "spec_filter_thresholds",
+                 "spec_verify_workspace_size",
                  "spec_lmhead_logits", "spec_lmhead_verify", "spec_lmhead_workspace_size",
                  "spec_status_string"):
         assert want in names
@@ -87,3 +88,19 @@ def test_lmhead_argument_errors():
     assert lib.spec_lmhead_logits(FAKE, FAKE, 4, 60, 64, FAKE, None) == -1
     assert lib.spec_lmhead_logits(FAKE, FAKE, 4, 64, 63, FAKE, None) == -1
     assert lib.spec_lmhead_logits(None, FAKE, 4, 64, 64, FAKE, None) == -1
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=0.0), -1), (dict(T=float("nan")), -1), (dict(top_p=0.0), -1), (dict(top_p=float("nan")), -1),
+    (dict(B=-1), -1), (dict(V=0), -1), (dict(dtype=5), -2), (dict(target=None), -1), (dict(thr=None), -1),
+    (dict(draft=None), -1), (dict(V=102), -1), (dict(target=ctypes.c_void_p(0x1008)), -1),
+])
+def test_filter_threshold_argument_errors(kw, status):
+    """Shape, dtype, temperature, top_p, pointers and 16-byte row alignment are
+    checked on the host; V = 102 fp32 rows are 408 bytes, not a multiple of 16."""
+    import speculative_sampling_verification_02_amd as sv
+    args = dict(target=FAKE, draft=FAKE, dtype=0, B=2, gamma=3, V=100, T=1.0, top_k=5, top_p=0.9,
+                thr=FAKE, stream=None)
+    args.update(kw)
+    assert sv.lib.spec_filter_thresholds(*args.values()) == status
+    assert sv.lib.spec_filter_thresholds(None, None, 0, 0, 3, 100, 1.0, 5, 0.9, None, None) == 0
