@@ -540,6 +540,42 @@ __device__ inline int seq_gamma_of(const VerifyArgs& a, int b) {
   return seq_gamma(a, b);
 }
 
+// With per-sequence draft counts the teams and finishers walk the live items
+// only, densely: the pairs (b, i) with i < gamma_b, by b then i, then the B
+// bonus items (pairs first, so a finisher never waits on an item it has yet
+// to finish itself).  Every item keeps its own slots.  live_item maps a dense
+// index (the same in every lane) to its item by a wave scan over gamma_b; it
+// is called by whole waves.  Without draft counts both are the identity.
+template <bool EXT>
+__device__ inline int live_count(const FusedParams& P) {
+  if constexpr (!EXT) return P.n_items;
+  const VerifyArgs& a = P.a;
+  if (!a.gamma_seq) return P.n_items;
+  float s = 0.f;  // exact: at most 32 per sequence
+  for (int b = wave_lane(); b < a.B; b += kWave) s += (float)seq_gamma(a, b);
+  return (int)wave_sum(s) + a.B;
+}
+template <bool EXT>
+__device__ inline int live_item(const FusedParams& P, int d) {
+  if constexpr (!EXT) return d;
+  const VerifyArgs& a = P.a;
+  if (!a.gamma_seq) return d;
+  const int lane = wave_lane();
+  int acc = 0;  // live pairs of the sequences before this chunk of 64
+  for (int b0 = 0; b0 < a.B; b0 += kWave) {
+    const int g = b0 + lane < a.B ? seq_gamma(a, b0 + lane) : 0;
+    const int incl = (int)wave_inclusive_scan((float)g);  // exact: at most 2048
+    const int total = __builtin_amdgcn_readlane(incl, kWave - 1);
+    if (d < acc + total) {
+      // the sequences wholly before d form a prefix of the lanes
+      const int l = __popcll(__ballot(acc + incl <= d));
+      return (b0 + l) * a.gamma + (d - acc - __builtin_amdgcn_readlane(incl - g, l));
+    }
+    acc += total;
+  }
+  return P.n_pairs + (d - acc);  // a bonus item
+}
+
 template <class E, int PER, bool EXT>
 __device__ __attribute__((always_inline)) void issue_item(const FusedParams& P, int item, int lo, RawPair<E, PER>& r) {
   const VerifyArgs& a = P.a;
@@ -784,7 +820,9 @@ __device__ __attribute__((always_inline)) void compute_loop_staged(const FusedPa
     }
   };
 
-  int item = team;
+  const int n_live = live_count<EXT>(P);
+  int d = team;  // dense index over the live items
+  int item = d < n_live ? live_item<EXT>(P, d) : P.n_items;
   if (wave != 0 && item < P.n_items && !empty_item<EXT>(P, item)) issue(item);
   if (wave != 0) wait_vmem();
   lds_barrier();
@@ -811,7 +849,8 @@ __device__ __attribute__((always_inline)) void compute_loop_staged(const FusedPa
       A.q.v[v] = stage[((kWavesPerGroup + wave) * NS + v) * kWave + lane];
     }
     lds_barrier();
-    const int next = item + P.nteams;
+    const int next_d = d + P.nteams;
+    const int next = next_d < n_live ? live_item<EXT>(P, next_d) : P.n_items;
     if (wave != 0 && next < P.n_items && !empty_item<EXT>(P, next)) issue(next);
     if constexpr (!ARGMAX && SPECV_FUSED_PIPELINE) {
       // Two pair items in flight: phase 1 of this item runs while the team
@@ -858,6 +897,7 @@ __device__ __attribute__((always_inline)) void compute_loop_staged(const FusedPa
     if (wave != 0) wait_vmem();
     lds_barrier();
     item = next;
+    d = next_d;
   }
   if constexpr (!ARGMAX && SPECV_FUSED_PIPELINE) {
     if (pend >= 0) {
@@ -1117,6 +1157,16 @@ __device__ void finish_bonus(const FusedParams& P, int item, uint64_t* w1, uint6
                                                    },
                                                    lds_f, lds_i);
   }
+  if constexpr (EXT) {
+    // the padding positions (never scheduled as items): NaN outputs
+    const float nan = __uint_as_float(0x7fc00000u);
+    for (int i = gb + (int)threadIdx.x; i < G; i += (int)blockDim.x) {
+      const size_t o = (size_t)b * G + i;
+      if (a.alpha) a.alpha[o] = nan;
+      if (a.p_draft) a.p_draft[o] = nan;
+      if (a.q_draft) a.q_draft[o] = nan;
+    }
+  }
   // the sequence's pair results (published by other finishers)
   const bool ok2 = gather(P.pair_res + (size_t)b * G, gb, res);
   if (ok2) clear_slots(P.pair_res + (size_t)b * G, gb);
@@ -1181,7 +1231,9 @@ __global__ __launch_bounds__(kThreads, SPECV_FUSED_MIN_WAVES) void fused_kernel(
       const int c = rank * kWavesPerGroup + (int)threadIdx.x / kWave;  // this wave's tile
       const int lo = c * kWave * PER;
       int parity = 0;
-      for (int item = team; item < P.n_items; item += P.nteams) {
+      const int n_live = live_count<EXT>(P);
+      for (int d = team; d < n_live; d += P.nteams) {
+        const int item = live_item<EXT>(P, d);
         if (empty_item<EXT>(P, item)) continue;
         RawPair<E, PER> A;
         issue_item<E, PER, EXT>(P, item, lo, A);
@@ -1196,7 +1248,9 @@ __global__ __launch_bounds__(kThreads, SPECV_FUSED_MIN_WAVES) void fused_kernel(
   } else {
     // pairs precede bonus items in the item order, so a finisher never waits
     // on an item it has yet to finish itself
-    for (int item = f; item < P.n_items; item += P.nfin) {
+    const int n_live = live_count<EXT>(P);
+    for (int d = f; d < n_live; d += P.nfin) {
+      const int item = live_item<EXT>(P, d);
       if (item < P.n_pairs)
         finish_pair<E, PER, ARGMAX, EXT>(P, item, fin_w1, fin_w2);
       else
