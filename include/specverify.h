@@ -162,8 +162,8 @@ int spec_verify_algo(int algo,
  *              the fused path only: SPEC_ALGO_MULTIPASS, or a shape the fused
  *              path declines, gives SPEC_EUNSUPPORTED.  A filtered call launches
  *              the threshold kernel of spec_filter_thresholds (into the
- *              workspace), the verification, and a fill kernel that leaves the
- *              workspace zero.
+ *              workspace), then the verification, whose finishers zero each
+ *              threshold after its last read (the workspace is left zero).
  *
  *   lenience   l in (0, 1] ([FI] "The acceptance rate is the overlap of p and q",
  *              the lenience factor): draft i is kept when

@@ -105,20 +105,16 @@ int spec_verify_ex(int algo, const void* target_logits, const void* draft_logits
   hipStream_t s = static_cast<hipStream_t>(stream);
 
   // Top-k / top-p (T > 0 only: they leave the argmax unchanged) need the
-  // fused path: thresholds first, then the verification that reads them, then
-  // the thresholds are zeroed again.
+  // fused path: thresholds first, then the verification that reads them (its
+  // finishers zero each threshold after its last read).
   const bool filtered = temperature > 0.f && ((top_k > 0 && top_k < V) || top_p < 1.f);
   if (filtered) {
     if (algo == SPEC_ALGO_MULTIPASS || !specv::fused_supported(B, gamma, V, dtype)) return SPEC_EUNSUPPORTED;
     float* thr = reinterpret_cast<float*>(static_cast<char*>(workspace) + paths_bytes(B, gamma, V));
-    const int rows = B * (2 * gamma + 1);
-    hipError_t e = specv::filter_thresholds(a, top_k, top_p, thr, s);
+    const hipError_t e = specv::filter_thresholds(a, top_k, top_p, thr, s);
     if (e != hipSuccess) return map_hip(e);
     a.thr = thr;
-    e = specv::fused_launch(a, s);
-    const hipError_t ec = specv::filter_clear(thr, rows, s);
-    if (e != hipSuccess) return map_hip(e);
-    return map_hip(ec);
+    return map_hip(specv::fused_launch(a, s));
   }
   if (algo == SPEC_ALGO_FUSED) return map_hip(specv::fused_launch(a, s));
   if (algo == SPEC_ALGO_AUTO && specv::fused_supported(B, gamma, V, dtype)) {

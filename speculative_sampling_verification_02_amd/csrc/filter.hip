@@ -642,11 +642,6 @@ __global__ __launch_bounds__(kFT) void row_threshold_kernel(FilterArgs f) {
   if (tid == 0) f.thr[r] = t;
 }
 
-__global__ void fill_zero_kernel(float* p, int n) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0.f;
-}
-
 }  // namespace
 
 hipError_t filter_thresholds(const VerifyArgs& a, int top_k, float top_p, float* thr, hipStream_t s) {
@@ -657,12 +652,6 @@ hipError_t filter_thresholds(const VerifyArgs& a, int top_k, float top_p, float*
     row_threshold_kernel<BF16><<<dim3(rows), dim3(kFT), 0, s>>>(f);
   else
     row_threshold_kernel<F32><<<dim3(rows), dim3(kFT), 0, s>>>(f);
-  return hipGetLastError();
-}
-
-hipError_t filter_clear(float* thr, int rows, hipStream_t s) {
-  if (rows == 0) return hipSuccess;
-  fill_zero_kernel<<<dim3((rows + 255) / 256), dim3(256), 0, s>>>(thr, rows);
   return hipGetLastError();
 }
 

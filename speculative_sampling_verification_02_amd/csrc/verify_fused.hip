@@ -1107,7 +1107,18 @@ __device__ void finish_pair(const FusedParams& P, int item, uint64_t* w1, uint64
           return xp >= tp ? fast_exp2(fmaf(xp, k, -Mp)) : 0.f;
         }, lds_f, lds_i);
     }
-    if (threadIdx.x == 0) st_u64(P.pair_res + item, pack2i((uint32_t)acc_s | kResMark, (uint32_t)t));
+    if (threadIdx.x == 0) {
+      st_u64(P.pair_res + item, pack2i((uint32_t)acc_s | kResMark, (uint32_t)t));
+      if constexpr (EXT) {
+        // this finisher is the last reader of the pair's two keep thresholds
+        // (the compute workgroups read them before publishing): zero them, so
+        // the workspace is left zero
+        if (a.thr) {
+          a.thr[(size_t)b * (G + 1) + i] = 0.f;
+          a.thr[(size_t)a.B * (G + 1) + o] = 0.f;
+        }
+      }
+    }
   }
 }
 
@@ -1170,6 +1181,15 @@ __device__ void finish_bonus(const FusedParams& P, int item, uint64_t* w1, uint6
   // the sequence's pair results (published by other finishers)
   const bool ok2 = gather(P.pair_res + (size_t)b * G, gb, res);
   if (ok2) clear_slots(P.pair_res + (size_t)b * G, gb);
+  if constexpr (EXT) {
+    // the last reader of the bonus row's keep threshold; the padding rows'
+    // thresholds are never read: zero them all
+    if (a.thr && ok1) {
+      for (int i = gb + (int)threadIdx.x; i <= G; i += (int)blockDim.x) a.thr[(size_t)b * (G + 1) + i] = 0.f;
+      for (int i = gb + (int)threadIdx.x; i < G; i += (int)blockDim.x)
+        a.thr[(size_t)a.B * (G + 1) + (size_t)b * G + i] = 0.f;
+    }
+  }
   if (threadIdx.x == 0) {
     if (ok1 && ok2) {
       int n = 0;

@@ -26,8 +26,9 @@ struct VerifyArgs {
   size_t ws_bytes;
   float lenience;              // l in (0, 1]; 1 = exact speculative sampling
   const int32_t* gamma_seq;    // [B] per-sequence draft counts, or null (all gamma)
-  const float* thr;            // top-k / top-p keep thresholds per row, or null:
-                               // [B(gamma+1)] target rows, then [B gamma] draft rows
+  float* thr;                  // top-k / top-p keep thresholds per row, or null:
+                               // [B(gamma+1)] target rows, then [B gamma] draft rows;
+                               // each is zeroed by its last reader in the fused kernel
 };
 
 // A logit below its row's keep threshold counts as -inf (probability 0).
@@ -60,7 +61,6 @@ bool fused_supported(int B, int gamma, int V, int dtype);
 // ---- top-k / top-p keep thresholds (filter.hip): one float per row into thr,
 // and a fill kernel that zeroes them again after the verification
 hipError_t filter_thresholds(const VerifyArgs& a, int top_k, float top_p, float* thr, hipStream_t stream);
-hipError_t filter_clear(float* thr, int rows, hipStream_t stream);
 
 // ---- LM head
 // One head of the product: out[m][v] = sum_k hidden[r(m)][k] W[k][v] for
