@@ -129,6 +129,29 @@ def timed_loop(torch, steps: int, step) -> LoopTime:
     return LoopTime(1e3 * e0.elapsed_time(e1) / steps, wall)
 
 
+def stream_read_rate(torch, sv, dev, nbytes: int = 1 << 30, reps: int = 20) -> float:
+    """GB/s of a plain streaming read (spec_stream_read) of a 1 GiB buffer, four
+    times the last-level cache: the HBM read rate this device sustains, for
+    context beside the 8 TB/s peak."""
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    # two 256-thread workgroups per compute unit: the fastest shape of a sweep
+    # of 256..16384 workgroups on the MI355X (7.1 TB/s; more workgroups read
+    # more scattered pages at once and fall back to 5.7-6.2 TB/s)
+    blocks = 2 * 256
+    sink = torch.empty(blocks, dtype=torch.int32, device=dev)
+    for _ in range(3):
+        sv.stream_read(buf, sink, blocks)
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        sv.stream_read(buf, sink, blocks)
+    e.record()
+    e.synchronize()
+    gbs = nbytes * reps / (s.elapsed_time(e) * 1e-3) / 1e9
+    del buf, sink
+    return gbs
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -212,6 +235,7 @@ def main() -> int:
 
     launch_us = timed_loop(torch, args.steps, step)
     elapsed = launch_us.wall_s
+    stream_gbs = stream_read_rate(torch, sv, dev)
 
     ms_per_step = 1e3 * elapsed / args.steps
     rows = B * (G + 1)
@@ -249,7 +273,8 @@ def main() -> int:
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "launch_us_mean": launch_us.mean,
-                     "alg_bytes": alg, "full_bytes": (2 * G + 1) * V * elem * B},
+                     "alg_bytes": alg, "full_bytes": (2 * G + 1) * V * elem * B,
+                     "stream_read_GBps": stream_gbs, "frac_of_stream_read": achieved / stream_gbs},
     }
     if not args.no_cpu_baseline and args.workload == "verify" and default_path:
         line["cpu_baseline"] = cpu_baseline(case)

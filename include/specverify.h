@@ -262,6 +262,18 @@ int spec_lmhead_verify(const void* hidden, const void* hidden_draft,
                        float* p_draft, float* q_draft,
                        void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * spec_stream_read -- a plain streaming read of a device buffer, for the HBM
+ * read rate the device sustains (the context the verification's bandwidth
+ * is judged against; not part of the method).
+ *   buffer  device pointer, 16-byte aligned; bytes a multiple of 16 (read once)
+ *   sink    device uint32 [blocks] out: the XOR of each workgroup's words (it
+ *           keeps the reads from being dropped; the values mean nothing)
+ *   blocks  workgroups of 256 threads (a few per compute unit fill the device)
+ * Returns SPEC_EINVAL for a null pointer, misalignment or blocks < 1.
+ */
+int spec_stream_read(const void* buffer, size_t bytes, uint32_t* sink, int blocks, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -44,6 +44,7 @@ SIGNATURES = {
     "spec_filter_thresholds": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_int, _c_float,
                                         _c_int, _c_float, _c_void_p, _c_void_p]),
     "spec_lmhead_logits": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_void_p, _c_void_p]),
+    "spec_stream_read": (_c_int, [_c_void_p, _c_size_t, _c_void_p, _c_int, _c_void_p]),
     "spec_lmhead_workspace_size": (_c_size_t, [_c_int, _c_int, _c_int, _c_int]),
     "spec_lmhead_verify": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                     _c_int, _c_int, _c_int, _c_int,
@@ -205,6 +206,18 @@ def filter_thresholds(target_logits, draft_logits, temperature: float, top_k: in
                                       _dtype_code(target_logits), B, gamma, V, float(temperature), int(top_k),
                                       float(top_p), _ptr(thr), _stream(dev)), "spec_filter_thresholds")
     return thr[:B * g1].view(B, g1), thr[B * g1:].view(B, gamma)
+
+
+def stream_read(buffer, sink, blocks: int):
+    """One plain streaming read of `buffer` (a 16-byte aligned GPU tensor) on
+    the current stream; `sink` is a GPU int32 tensor of at least `blocks`."""
+    _need(buffer, "buffer")
+    _need(sink, "sink", device=buffer.device)
+    if sink.numel() * sink.element_size() < 4 * int(blocks):
+        raise ValueError("sink must hold one 32-bit word per workgroup")
+    nbytes = buffer.numel() * buffer.element_size()
+    _check(lib.spec_stream_read(_ptr(buffer), nbytes, _ptr(sink), int(blocks), _stream(buffer.device)),
+           "spec_stream_read")
 
 
 def _verify_args(algo, target_logits, draft_logits, dt, draft_tokens, uniforms, B, gamma, V, temperature,

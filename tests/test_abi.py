@@ -104,3 +104,14 @@ def test_filter_threshold_argument_errors(kw, status):
     args.update(kw)
     assert sv.lib.spec_filter_thresholds(*args.values()) == status
     assert sv.lib.spec_filter_thresholds(None, None, 0, 0, 3, 100, 1.0, 5, 0.9, None, None) == 0
+
+
+def test_stream_read_argument_errors():
+    import speculative_sampling_verification_02_amd as sv
+    lib = sv.lib
+    assert lib.spec_stream_read(None, 64, FAKE, 8, None) == -1
+    assert lib.spec_stream_read(FAKE, 64, None, 8, None) == -1
+    assert lib.spec_stream_read(FAKE, 60, FAKE, 8, None) == -1
+    assert lib.spec_stream_read(ctypes.c_void_p(0x1004), 64, FAKE, 8, None) == -1
+    assert lib.spec_stream_read(FAKE, 64, FAKE, 0, None) == -1
+    assert lib.spec_stream_read(FAKE, 0, FAKE, 8, None) == 0

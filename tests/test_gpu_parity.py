@@ -265,3 +265,17 @@ def test_workspace_reused_across_shapes_and_paths(dev, T):
             parity.check(case, got, where=f"ws reuse rep{rep} case{j} algo{algo}")
             assert (got["n_accepted"] >= 0).all()
             assert int(ws.count_nonzero()) == 0, f"algo {algo} left the workspace dirty"
+
+
+def test_stream_read_reads_every_word(dev):
+    """The XOR of the per-workgroup results is the XOR of every 32-bit word."""
+    import torch
+    import speculative_sampling_verification_02_amd as sv
+    rng = np.random.default_rng(9)
+    words = rng.integers(0, 2 ** 32, size=(1 << 20) + 4, dtype=np.uint64).astype(np.uint32)
+    buf = torch.from_numpy(words.view(np.int32)).to(dev)
+    for blocks in (1, 7, 2048):
+        sink = torch.zeros(blocks, dtype=torch.int32, device=dev)
+        sv.stream_read(buf, sink, blocks)
+        got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+        assert got == np.bitwise_xor.reduce(words), blocks
