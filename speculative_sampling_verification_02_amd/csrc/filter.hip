@@ -14,21 +14,25 @@
 //
 // One workgroup of 1024 threads per row, with the row held in registers (one
 // read from memory).  Every pass over the row is a few instructions per token:
-//   1. row maximum and finite minimum;
-//   2. a 16-bin histogram over [min, max] (linear in the logit): counts for
-//      top-k, fp64 softmax mass for top-p.  Each lane owns its own column of
-//      bins in LDS, so the additions never contend;
-//   3. the bin where the running count (mass) from the top reaches k (top_p
-//      of the total) is copied to an LDS list (wave-aggregated appends);
-//   4. the exact threshold is found inside that list by a radix select over
-//      the candidates' order-preserving 32-bit keys (mass in 2^-40 fixed
-//      point, so sums do not depend on the order of the atomic additions).
-// A crossing bin too large for the list is refined once (16 finer bins inside
-// it).  With top-k active and its survivors fitting the list, top-p runs on
-// the copied survivors alone and the row needs no full exponential pass.
-// Rows that still do not fit, rows longer than the register capacity and rows
-// whose finite logits are all equal take a radix select over the whole row
-// from memory instead (8 bits per pass).
+//   1. the row maximum (each thread keeps its own maximum too);
+//   2. top-k with k <= 1024: a lower bound of tau_k from the thread maxima
+//      (each wave's ceil(k/16)-th largest, the smallest of the 16), and the
+//      values at or above it copied to an LDS list;
+//   3. otherwise, and for top-p, a 16-bin histogram in octaves of softmax
+//      weight below the maximum: counts for top-k, fp64 masses for top-p.
+//      Each lane owns its own column of bins in LDS, so the additions never
+//      contend.  The bin where the running count (mass) from the top reaches
+//      k (top_p of the total) is copied to the list;
+//   4. the exact threshold is picked inside the list by 8-bit radix passes
+//      over the listed keys' range (counts, or masses in 2^-40 fixed point,
+//      so sums do not depend on the order of the atomic additions).
+// The list is kept in per-thread columns: each thread appends its own
+// candidates, with no scan or atomic.  A crossing bin too large for the list
+// is refined once (16 finer bins inside it).  With top-k active and its
+// survivors listed, top-p runs on the list alone and the row needs no
+// exponential pass.  Rows that still do not fit, rows longer than the
+// registers hold and rows with no finite logit take a radix select over the
+// whole row from memory instead (8 bits per pass).
 //
 // Masses are exp2((l - m) log2(e) / T) in fp32 (m the row maximum).  The
 // histogram adds them in fp64 (each lane in its own fixed order), the lists in
@@ -49,7 +53,8 @@ namespace {
 constexpr int kFT = 1024;        // threads per row
 constexpr int kFNV = 16;         // 16-byte vectors per thread held in registers
 constexpr int kNB = 16;          // bins per histogram level (one wave reduces one bin)
-constexpr int kCap = 32768;      // candidates the LDS list holds
+constexpr int kCap = 32768;      // slots of the LDS candidate list
+constexpr int kCol = kCap / 1024 - 1;  // candidates a thread may list (its column has one spare slot)
 constexpr double kMassScale = 1099511627776.0;  // 2^40
 static_assert(kFT / kWave == kNB, "one wave per bin in the reductions");
 
@@ -68,7 +73,7 @@ struct FilterLds {
   union {
     uint32_t cnt[kNB][kFT];  // per-lane count bins
     double mass[kNB][kFT];   // per-lane mass bins
-    float cand[kCap];        // candidate logits
+    float cand[kCap];        // candidate logits: slot s of thread t at s * kFT + t
   } big;
   uint32_t cnt256[256];
   unsigned long long m256[256];
@@ -304,7 +309,8 @@ __global__ __launch_bounds__(kFT) void row_threshold_kernel(FilterArgs f) {
   // A second level splits one bin j into 16: bin = clamp(16 (t - j), 0, 15).
   const float c = 0.5f * k, mc = mx * c;
   auto binof = [](float t) { return (int)__builtin_amdgcn_fmed3f(t, 0.f, 15.f); };
-  int lv_j = 0;  // the bin a second level refines
+  int lv_j = 0;     // the bin a second level refines
+  uint32_t my_n = 0;  // values this thread has in the candidate list
 
   // One pass over the row.  Values in range are those >= lo and, at level 1,
   // those of level-0 bin lv_j; `b` is the bin at the pass's level.
@@ -348,45 +354,27 @@ __global__ __launch_bounds__(kFT) void row_threshold_kernel(FilterArgs f) {
       });
     } else {
       static_assert(kind == 2 || kind == 3, "pass kinds 0-3");
-      if (tid == 0) L.ncand = 0;
-      __syncthreads();
-      // per 16-byte vector: a lane's candidates as a bit mask; a wave with
-      // none skips the vector, else one prefix scan and one LDS atomic place
-      // the wave's candidates in the list
-#pragma unroll
-      for (int v = 0; v < kFNV; ++v) {
-        const bool valid = (v * kFT + tid) * KV < V;
-        u32x4 w = raw[v];
-        asm volatile("" : "+v"(w.x), "+v"(w.y), "+v"(w.z), "+v"(w.w));
-        float t[KV];
-        E::unpack(w, t);
-        uint32_t mask = 0;
-#pragma unroll
-        for (int e = 0; e < KV; ++e) {
-          bool in;
-          if constexpr (kind == 3) {
-            in = t[e] >= lo;
-          } else {
-            int b;
-            in = locate(t[e], &b) && b == jsel;
-          }
-          mask |= (uint32_t)(valid && in) << e;
+      // Each thread lists its own candidates in its column of the list (slot
+      // s of thread t at s * kFT + t: no bank conflicts, no scan, no atomic).
+      // The write is branchless: every value goes to the next free slot, and
+      // only a candidate advances it (the column's spare slot takes the
+      // writes past the last usable one).  A thread with more than kCol
+      // candidates makes the list overflow.
+      uint32_t cnt = 0;
+      each([&](float x) {
+        bool in;
+        if constexpr (kind == 3) {
+          in = x >= lo;
+        } else {
+          int b;
+          in = locate(x, &b) && b == jsel;
         }
-        if (__ballot(mask != 0u) == 0ull) continue;
-        const uint32_t cnt = (uint32_t)__popc(mask);
-        const uint32_t incl = (uint32_t)wave_inclusive_scan((float)cnt);  // exact: at most 512
-        const uint32_t total = (uint32_t)__shfl((int)incl, kWave - 1);
-        uint32_t base = 0;
-        if (lane == 0) base = atomicAdd(&L.ncand, total);
-        uint32_t pos = (uint32_t)__shfl((int)base, 0) + incl - cnt;
-#pragma unroll
-        for (int e = 0; e < KV; ++e) {
-          if ((mask >> e) & 1u) {
-            if (pos < (uint32_t)kCap) L.big.cand[pos] = t[e];
-            ++pos;
-          }
-        }
-      }
+        L.big.cand[min(cnt, (uint32_t)kCol) * kFT + tid] = x;
+        cnt += (uint32_t)in;
+      });
+      my_n = min(cnt, (uint32_t)kCol);
+      const float2 r = block_sum2((float)cnt, cnt > (uint32_t)kCol ? 1.f : 0.f, L.redf);  // exact: <= 2^17
+      if (tid == 0) L.ncand = r.y > 0.f ? (uint32_t)kCap + 1u : (uint32_t)r.x;
     }
     __syncthreads();
     if constexpr (kind >= 2) return L.ncand;
@@ -430,7 +418,7 @@ __global__ __launch_bounds__(kFT) void row_threshold_kernel(FilterArgs f) {
   // first pass already spreads a narrow list over many bins (few colliding
   // LDS atomics) and a list of close values needs few passes.  Keys are the
   // 16 significant bits for bf16 rows (the list holds widened bf16 values).
-  auto pick = [&](auto mass_c, uint32_t n, float lo, double base, double need) -> float {
+  auto pick = [&](auto mass_c, float lo, double base, double need) -> float {
     constexpr bool MASS = decltype(mass_c)::value;
     constexpr int KB = std::is_same<E, BF16>::value ? 16 : 32;
     // key range of the listed values >= lo
@@ -440,8 +428,8 @@ __global__ __launch_bounds__(kFT) void row_threshold_kernel(FilterArgs f) {
     }
     __syncthreads();
     uint32_t kmn = 0xffffffffu, kmx = 0u;
-    for (uint32_t i = tid; i < n; i += kFT) {
-      const float x = L.big.cand[i];
+    for (uint32_t q = 0; q < my_n; ++q) {  // this thread's column of the list
+      const float x = L.big.cand[q * kFT + tid];
       if (x >= lo) {
         const uint32_t key = key_of<KB>(x);
         kmn = min(kmn, key);
@@ -479,8 +467,8 @@ __global__ __launch_bounds__(kFT) void row_threshold_kernel(FilterArgs f) {
         if constexpr (MASS) L.pmass[buf ^ 1][tid] = 0ull;
         else L.pcnt[buf ^ 1][tid] = 0u;
       }
-      for (uint32_t i = tid; i < n; i += kFT) {
-        const float x = L.big.cand[i];
+      for (uint32_t q = 0; q < my_n; ++q) {
+        const float x = L.big.cand[q * kFT + tid];
         const uint32_t d = key_of<KB>(x) - kmin;
         if (x >= lo && (d & hi_mask) == prefix) {
           if constexpr (MASS)
@@ -535,10 +523,10 @@ __global__ __launch_bounds__(kFT) void row_threshold_kernel(FilterArgs f) {
   using BF = std::integral_constant<bool, false>;
   using BT = std::integral_constant<bool, true>;
   // the rank-th largest listed value >= lo (ties counted)
-  auto select_kth = [&](uint32_t n, uint32_t rank, float lo) { return pick(BF{}, n, lo, 0.0, (double)rank); };
+  auto select_kth = [&](uint32_t rank, float lo) { return pick(BF{}, lo, 0.0, (double)rank); };
   // the nucleus threshold of the listed values >= lo: base + mass(>= tau) >=
   // target (target < 0: top_p of their own total)
-  auto nucleus = [&](uint32_t n, double base, double target, float lo) { return pick(BT{}, n, lo, base, target); };
+  auto nucleus = [&](double base, double target, float lo) { return pick(BT{}, lo, base, target); };
 
   // ---- 2-4. the filters, as a sequence of passes; each (level, kind) of
   // run_pass has one call site, so its unrolled body is instantiated once
@@ -554,7 +542,7 @@ __global__ __launch_bounds__(kFT) void row_threshold_kernel(FilterArgs f) {
       if (!use_p) {
         state = DONE;
       } else if (survivors_listed) {  // the nucleus of the listed survivors: no pass
-        tau_p = nucleus(n, 0.0, -1.0, tau_k);
+        tau_p = nucleus(0.0, -1.0, tau_k);
         state = DONE;
       } else {
         state = use_k && above + (double)n <= (double)kCap ? P_SURV : P_HIST0;
@@ -562,13 +550,20 @@ __global__ __launch_bounds__(kFT) void row_threshold_kernel(FilterArgs f) {
       continue;
     }
     if (state == K_PIVOT) {
-      // The k-th largest thread maximum is a lower bound of tau_k (k threads
-      // each hold a value at least that large); the values at or above it
-      // are usually few, and the exact k-th largest is among them.
-      __syncthreads();
-      L.big.cand[tid] = tmax;
-      __syncthreads();
-      pivot = select_kth(kFT, (uint32_t)f.top_k, -INFINITY);
+      // A lower bound of tau_k with few values above it: each wave finds the
+      // m-th largest of its 64 thread maxima (m = ceil(k / 16), by m rounds
+      // of a wave maximum that knocks out one holder), and the pivot is the
+      // smallest of the 16.  Every wave then holds m maxima >= pivot, and
+      // each maximum is a value of the row: at least 16 m >= k values are
+      // >= pivot, so tau_k >= pivot and the exact k-th largest is among them.
+      const int m = (f.top_k + kNB - 1) / kNB;
+      float v = tmax, mth = -INFINITY;
+      for (int r = 0; r < m; ++r) {
+        mth = wave_max(v);
+        const unsigned long long hit = __ballot(v == mth);
+        if (lane == __ffsll((long long)hit) - 1) v = -INFINITY;
+      }
+      pivot = -block_max(-mth, L.redf);
     }
     const bool lv1 = state == K_HIST1 || state == K_COPY1 || state == P_HIST1 || state == P_COPY1;
     const int kind = (state == K_HIST0 || state == K_HIST1) ? 0
@@ -589,7 +584,7 @@ __global__ __launch_bounds__(kFT) void row_threshold_kernel(FilterArgs f) {
       case K_PIVOT:
         n = got;
         if (n <= (uint32_t)kCap) {
-          tau_k = select_kth(n, (uint32_t)f.top_k, -INFINITY);
+          tau_k = select_kth((uint32_t)f.top_k, -INFINITY);
           survivors_listed = true;
           state = P_START;
         } else {
@@ -626,13 +621,13 @@ __global__ __launch_bounds__(kFT) void row_threshold_kernel(FilterArgs f) {
             state = DONE;
           }
         } else if (state == K_COPY0 || state == K_COPY1) {
-          tau_k = select_kth(n, (uint32_t)((double)f.top_k - above), -INFINITY);
+          tau_k = select_kth((uint32_t)((double)f.top_k - above), -INFINITY);
           state = P_START;
         } else if (state == P_SURV) {
-          tau_p = nucleus(n, 0.0, -1.0, tau_k);
+          tau_p = nucleus(0.0, -1.0, tau_k);
           state = DONE;
         } else {
-          tau_p = nucleus(n, above, target, -INFINITY);
+          tau_p = nucleus(above, target, -INFINITY);
           state = DONE;
         }
         break;
