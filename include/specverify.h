@@ -158,12 +158,11 @@ int spec_verify_algo(int algo,
  *              token has probability 0, in alpha, the ratio tests and the
  *              samples.  top_k <= 0 or >= V, and top_p >= 1, disable a filter;
  *              top_p must be > 0 (else SPEC_EINVAL).  In argmax mode (T == 0)
- *              the filters change nothing and are skipped.  Filtering runs on
- *              the fused path only: SPEC_ALGO_MULTIPASS, or a shape the fused
- *              path declines, gives SPEC_EUNSUPPORTED.  A filtered call launches
- *              the threshold kernel of spec_filter_thresholds (into the
- *              workspace), then the verification, whose finishers zero each
- *              threshold after its last read (the workspace is left zero).
+ *              the filters change nothing and are skipped.  Both paths take
+ *              filters, for any shape.  A filtered call launches the
+ *              threshold kernel of spec_filter_thresholds (into the
+ *              workspace), then the verification, whose last reader of each
+ *              threshold zeroes it (the workspace is left zero).
  *
  *   lenience   l in (0, 1] ([FI] "The acceptance rate is the overlap of p and q",
  *              the lenience factor): draft i is kept when
@@ -205,9 +204,10 @@ int spec_verify_ex(int algo,
  * a prefix"; [NZ] "5. Sampling and evaluation"), for callers that mask or
  * sample rows themselves.
  *   target_logits [B][gamma+1][V], draft_logits [B][gamma][V] (NULL when
- *   gamma == 0), dtype SPEC_F32 or SPEC_BF16, both 16-byte aligned with V *
- *   element size a multiple of 16.  temperature > 0 and finite (the top-p mass
- *   is that of softmax(logit / T)); top_k and top_p as for spec_verify_ex.
+ *   gamma == 0), dtype SPEC_F32 or SPEC_BF16, any V and alignment (16-byte
+ *   aligned rows of whole 16-byte vectors take vector loads, other rows
+ *   element loads).  temperature > 0 and finite (the top-p mass is that of
+ *   softmax(logit / T)); top_k and top_p as for spec_verify_ex.
  *   thresholds  device float32 [B*(gamma+1) + B*gamma] out: first the target
  *               rows in order (b, i), then the draft rows.  Row r keeps the
  *               tokens whose logit is >= thresholds[r]; the value is one of the
@@ -216,7 +216,7 @@ int spec_verify_ex(int algo,
  *   Ties are kept.  Masses are fp32 exp2((logit - max) log2(e) / T), summed in
  *   fp64 and 2^-40 fixed point; a nucleus boundary within about 2^-23 of
  *   top_p times the total may fall on either side of that tie group.
- *   Returns SPEC_EINVAL for a bad shape, alignment, temperature or top_p.
+ *   Returns SPEC_EINVAL for a bad shape, temperature or top_p.
  */
 int spec_filter_thresholds(const void* target_logits, const void* draft_logits, int dtype,
                            int B, int gamma, int V, float temperature, int top_k, float top_p,

@@ -104,17 +104,15 @@ int spec_verify_ex(int algo, const void* target_logits, const void* draft_logits
   a.gamma_seq = gamma > 0 ? gamma_seq : nullptr;
   hipStream_t s = static_cast<hipStream_t>(stream);
 
-  // Top-k / top-p (T > 0 only: they leave the argmax unchanged) need the
-  // fused path: thresholds first, then the verification that reads them (its
-  // finishers zero each threshold after its last read).
+  // Top-k / top-p (T > 0 only: they leave the argmax unchanged): the keep
+  // thresholds first, then the verification that reads them (on either path
+  // the last reader of each threshold zeroes it).
   const bool filtered = temperature > 0.f && ((top_k > 0 && top_k < V) || top_p < 1.f);
   if (filtered) {
-    if (algo == SPEC_ALGO_MULTIPASS || !specv::fused_supported(B, gamma, V, dtype)) return SPEC_EUNSUPPORTED;
     float* thr = reinterpret_cast<float*>(static_cast<char*>(workspace) + paths_bytes(B, gamma, V));
     const hipError_t e = specv::filter_thresholds(a, top_k, top_p, thr, s);
     if (e != hipSuccess) return map_hip(e);
     a.thr = thr;
-    return map_hip(specv::fused_launch(a, s));
   }
   if (algo == SPEC_ALGO_FUSED) return map_hip(specv::fused_launch(a, s));
   if (algo == SPEC_ALGO_AUTO && specv::fused_supported(B, gamma, V, dtype)) {
@@ -163,8 +161,6 @@ int spec_filter_thresholds(const void* target_logits, const void* draft_logits, 
   if (!(top_p > 0.f)) return SPEC_EINVAL;  // also rejects NaN
   if (B == 0) return SPEC_OK;
   if (!target_logits || !thresholds || (gamma > 0 && !draft_logits)) return SPEC_EINVAL;
-  const size_t row_bytes = (size_t)V * (dtype == SPEC_BF16 ? 2 : 4);
-  if (row_bytes % 16 || !aligned16(target_logits) || (gamma > 0 && !aligned16(draft_logits))) return SPEC_EINVAL;
   VerifyArgs a{};
   a.target = target_logits;
   a.draft = draft_logits;

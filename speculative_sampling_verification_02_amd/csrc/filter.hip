@@ -109,6 +109,26 @@ __device__ inline float value_of(uint32_t key) {
   return __uint_as_float(u);
 }
 
+// Elements j0 .. j0 + kVec - 1 of a row that may not be 16-byte aligned, in
+// the layout of one 16-byte vector of E (elements at or past V read as 0; the
+// callers skip them).
+template <class E>
+__device__ inline u32x4 load_vec_scalar(const typename E::storage* row, int j0, int V) {
+  uint32_t w[4];
+  if constexpr (std::is_same<E, BF16>::value) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t lo = j0 + 2 * k < V ? (uint32_t)row[j0 + 2 * k] : 0u;
+      const uint32_t hi = j0 + 2 * k + 1 < V ? (uint32_t)row[j0 + 2 * k + 1] : 0u;
+      w[k] = lo | (hi << 16);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) w[k] = j0 + k < V ? __float_as_uint(row[j0 + k]) : 0u;
+  }
+  return u32x4{w[0], w[1], w[2], w[3]};
+}
+
 __device__ inline unsigned long long fixed_mass(float w) {
   return (unsigned long long)((double)w * kMassScale + 0.5);
 }
@@ -154,7 +174,7 @@ __device__ inline int wave_pick_desc(F binval, double need, double* before_out) 
 // Radix select over the whole row read from memory, 8 bits per pass: top-k by
 // counts, then top-p by 2^-40 fixed-point mass.  Exact for any row; slower,
 // since every pass re-reads the row and bins contend.
-template <class E>
+template <class E, bool ALIGNED>
 __device__ __attribute__((always_inline)) inline float radix_threshold(const typename E::storage* row,
                                                                        const FilterArgs f, FilterLds& L) {
   constexpr int KB = std::is_same<E, BF16>::value ? 16 : 32;
@@ -163,9 +183,10 @@ __device__ __attribute__((always_inline)) inline float radix_threshold(const typ
   auto for_each = [&](auto fn) {
     for (int j0 = tid * E::kVec; j0 < f.V; j0 += kFT * E::kVec) {
       float t[E::kVec];
-      E::unpack(load_cached(row + j0), t);
+      E::unpack(ALIGNED ? load_cached(row + j0) : load_vec_scalar<E>(row, j0, f.V), t);
 #pragma unroll
-      for (int e = 0; e < E::kVec; ++e) fn(t[e]);
+      for (int e = 0; e < E::kVec; ++e)
+        if (ALIGNED || j0 + e < f.V) fn(t[e]);
     }
   };
   const bool use_k = f.top_k > 0 && f.top_k < f.V;
@@ -254,7 +275,9 @@ __device__ __attribute__((always_inline)) inline float radix_threshold(const typ
 
 // ------------------------------------------------------------- fast path
 
-template <class E>
+// ALIGNED: 16-byte aligned rows of whole vectors (V a multiple of the vector
+// width); otherwise elements are loaded one by one and checked against V.
+template <class E, bool ALIGNED>
 __global__ __launch_bounds__(kFT) void row_threshold_kernel(FilterArgs f) {
   constexpr int KV = E::kVec;
   __shared__ FilterLds L;
@@ -277,12 +300,15 @@ __global__ __launch_bounds__(kFT) void row_threshold_kernel(FilterArgs f) {
 #pragma unroll
   for (int v = 0; v < kFNV; ++v) {
     const int j0 = (v * kFT + tid) * KV;
-    raw[v] = !fallback && j0 < V ? load_cached(row + j0) : u32x4{0u, 0u, 0u, 0u};
+    raw[v] = fallback || j0 >= V ? u32x4{0u, 0u, 0u, 0u}
+             : ALIGNED          ? load_cached(row + j0)
+                                : load_vec_scalar<E>(row, j0, V);
   }
   auto each = [&](auto fn) {
 #pragma unroll
     for (int v = 0; v < kFNV; ++v) {
-      if ((v * kFT + tid) * KV < V) {
+      const int j0 = (v * kFT + tid) * KV;
+      if (j0 < V) {
         // a copy of the words that is opaque to the compiler, so every pass
         // unpacks afresh instead of keeping up to 128 unpacked values live
         u32x4 w = raw[v];
@@ -290,7 +316,8 @@ __global__ __launch_bounds__(kFT) void row_threshold_kernel(FilterArgs f) {
         float t[KV];
         E::unpack(w, t);
 #pragma unroll
-        for (int e = 0; e < KV; ++e) fn(t[e]);
+        for (int e = 0; e < KV; ++e)
+          if (ALIGNED || j0 + e < V) fn(t[e]);
       }
     }
   };
@@ -633,7 +660,7 @@ __global__ __launch_bounds__(kFT) void row_threshold_kernel(FilterArgs f) {
         break;
     }
   }
-  const float t = fallback ? radix_threshold<E>(row, f, L) : fmaxf(tau_k, tau_p);
+  const float t = fallback ? radix_threshold<E, ALIGNED>(row, f, L) : fmaxf(tau_k, tau_p);
   if (tid == 0) f.thr[r] = t;
 }
 
@@ -643,10 +670,21 @@ hipError_t filter_thresholds(const VerifyArgs& a, int top_k, float top_p, float*
   FilterArgs f{a.target, a.draft, a.B * (a.gamma + 1), a.V, a.k, top_k, top_p, thr};
   const int rows = a.B * (2 * a.gamma + 1);
   if (rows == 0) return hipSuccess;
-  if (a.dtype == SPEC_BF16)
-    row_threshold_kernel<BF16><<<dim3(rows), dim3(kFT), 0, s>>>(f);
-  else
-    row_threshold_kernel<F32><<<dim3(rows), dim3(kFT), 0, s>>>(f);
+  const size_t row_bytes = (size_t)a.V * (a.dtype == SPEC_BF16 ? 2 : 4);
+  const bool aligned = row_bytes % 16 == 0 && (uintptr_t)a.target % 16 == 0 &&
+                       (a.gamma == 0 || (uintptr_t)a.draft % 16 == 0);
+  const dim3 grid(rows), block(kFT);
+  if (a.dtype == SPEC_BF16) {
+    if (aligned)
+      row_threshold_kernel<BF16, true><<<grid, block, 0, s>>>(f);
+    else
+      row_threshold_kernel<BF16, false><<<grid, block, 0, s>>>(f);
+  } else {
+    if (aligned)
+      row_threshold_kernel<F32, true><<<grid, block, 0, s>>>(f);
+    else
+      row_threshold_kernel<F32, false><<<grid, block, 0, s>>>(f);
+  }
   return hipGetLastError();
 }
 

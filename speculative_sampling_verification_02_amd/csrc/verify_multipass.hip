@@ -49,6 +49,11 @@ __device__ inline const typename E::storage* row_ptr(const VerifyArgs& a, size_t
   return static_cast<const typename E::storage*>(a.draft) + (row - nt) * (size_t)a.V;
 }
 
+// Top-k / top-p: a logit below its row's keep threshold counts as -inf
+// (probability 0); without thresholds every logit is kept.
+__device__ inline float row_thr(const VerifyArgs& a, size_t row) { return a.thr ? a.thr[row] : -INFINITY; }
+__device__ inline float keep(float x, float th) { return x >= th ? x : -INFINITY; }
+
 // A row's normaliser: maximum, 1/S in fp32 and S in fp64.
 struct RowNorm {
   float M;
@@ -123,6 +128,11 @@ __global__ __launch_bounds__(kThreads) void row_stats_kernel(VerifyArgs a, float
       best = block_argmax(best, lds_f, lds_i);
       if (threadIdx.x == 0) stats[blockIdx.x] = make_float2(best.v, __int_as_float(best.i));
     } else {
+      if (a.thr) {
+        const float th = a.thr[row];
+#pragma unroll
+        for (int t = 0; t < ChunkRegs<E>::kPer; ++t) ch.x[t] = keep(ch.x[t], th);
+      }
       // four independent chains keep the dependency chains short
       float m0 = -INFINITY, m1 = -INFINITY, m2 = -INFINITY, m3 = -INFINITY;
 #pragma unroll
@@ -154,12 +164,13 @@ __global__ __launch_bounds__(kThreads) void row_stats_kernel(VerifyArgs a, float
       best = block_argmax(best, lds_f, lds_i);
       if (threadIdx.x == 0) stats[blockIdx.x] = make_float2(best.v, __int_as_float(best.i));
     } else {
+      const float th = row_thr(a, row);
       float m = -INFINITY;
-      for (int j = lo + threadIdx.x; j < hi; j += kThreads) m = fmaxf(m, E::at(r, j));
+      for (int j = lo + threadIdx.x; j < hi; j += kThreads) m = fmaxf(m, keep(E::at(r, j), th));
       const float M = block_max(m, lds_f);
       float s = 0.f;
       if (M != -INFINITY)
-        for (int j = lo + threadIdx.x; j < hi; j += kThreads) s += fast_exp2((E::at(r, j) - M) * a.k);
+        for (int j = lo + threadIdx.x; j < hi; j += kThreads) s += fast_exp2((keep(E::at(r, j), th) - M) * a.k);
       s = block_sum(s, lds_f);
       if (threadIdx.x == 0) stats[blockIdx.x] = make_float2(M, s);
     }
@@ -191,6 +202,7 @@ __global__ __launch_bounds__(kThreads) void pair_overlap_kernel(VerifyArgs a, co
   const size_t rp = target_row(b, i, a.gamma), rq = draft_row(b, i, a.gamma, a.B);
   const float l = a.lenience;  // the residual is max(0, p - l q)
   const float k = a.k;
+  const float thp = row_thr(a, rp), thq = row_thr(a, rq);
   const int lo = c * kChunk, hi = min(a.V, lo + kChunk);
   const auto* p_row = row_ptr<E>(a, rp);
   const auto* q_row = row_ptr<E>(a, rq);
@@ -214,7 +226,7 @@ __global__ __launch_bounds__(kThreads) void pair_overlap_kernel(VerifyArgs a, co
     float mn[2] = {0.f, 0.f}, rs[2] = {0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < ChunkRegs<E>::kPer; ++t) {
-      const float p = prob(cp.x[t], np.M, np.invS, k), q = prob(cq.x[t], nq.M, nq.invS, k);
+      const float p = prob(keep(cp.x[t], thp), np.M, np.invS, k), q = prob(keep(cq.x[t], thq), nq.M, nq.invS, k);
       mn[t & 1] += fminf(p, q);
       rs[t & 1] += fmaxf(p - l * q, 0.f);
     }
@@ -222,7 +234,8 @@ __global__ __launch_bounds__(kThreads) void pair_overlap_kernel(VerifyArgs a, co
     acc_res = rs[0] + rs[1];
   } else {
     for (int j = lo + threadIdx.x; j < hi; j += kThreads) {
-      const float p = prob(E::at(p_row, j), np.M, np.invS, k), q = prob(E::at(q_row, j), nq.M, nq.invS, k);
+      const float p = prob(keep(E::at(p_row, j), thp), np.M, np.invS, k);
+      const float q = prob(keep(E::at(q_row, j), thq), nq.M, nq.invS, k);
       acc_min += fminf(p, q);
       acc_res += fmaxf(p - l * q, 0.f);
     }
@@ -320,8 +333,8 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(VerifyArgs a, float2* 
       const int x = a.tokens[o];
       double px = 0.0, qx = 0.0;
       if (x >= 0 && x < a.V) {
-        px = exp2(((double)E::at(row_ptr<E>(a, rp), x) - (double)np.M) * (double)k) / np.S;
-        qx = exp2(((double)E::at(row_ptr<E>(a, rq), x) - (double)nq.M) * (double)k) / nq.S;
+        px = exp2(((double)keep(E::at(row_ptr<E>(a, rp), x), row_thr(a, rp)) - (double)np.M) * (double)k) / np.S;
+        qx = exp2(((double)keep(E::at(row_ptr<E>(a, rq), x), row_thr(a, rq)) - (double)nq.M) * (double)k) / nq.S;
       }
       // q(x) = 0 keeps the draft when p(x) > 0 (ratio +inf) and rejects it
       // when p(x) = 0 (0/0)
@@ -413,17 +426,21 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(VerifyArgs a, float2* 
     __syncthreads();
 
     const int c = chunk_s, lo = c * kChunk, hi = min(a.V, lo + kChunk);
+    const float thp = row_thr(a, target_row(b, n, G));
     if (residual) {
       const RowNorm nq = norm_s[1];
       const auto* q_row = row_ptr<E>(a, draft_row(b, n, G, a.B));
       const float l = a.lenience;
-      auto w = [&](float xp, float xq) { return fmaxf(prob(xp, np.M, np.invS, k) - l * prob(xq, nq.M, nq.invS, k), 0.f); };
+      const float thq = row_thr(a, draft_row(b, n, G, a.B));
+      auto w = [&](float xp, float xq) {
+        return fmaxf(prob(keep(xp, thp), np.M, np.invS, k) - l * prob(keep(xq, thq), nq.M, nq.invS, k), 0.f);
+      };
       if constexpr (VEC)
         t = tile_search<E, kChunk / kThreads, kThreads>(p_row, q_row, lo, a.V, theta_s, w, lds_f, lds_i);
       else
         t = range_search<E, false, kThreads>(p_row, q_row, lo, hi, theta_s, w, lds_f, lds_i);
     } else {
-      auto w = [&](float xp, float) { return fast_exp2((xp - np.M) * k); };
+      auto w = [&](float xp, float) { return fast_exp2((keep(xp, thp) - np.M) * k); };
       if constexpr (VEC)
         t = tile_search<E, kChunk / kThreads, kThreads>(p_row, nullptr, lo, a.V, theta_s, w, lds_f, lds_i);
       else
@@ -438,6 +455,12 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(VerifyArgs a, float2* 
   }
   __syncthreads();
   clear_sequence_stats(a, stats, pair_stats, b, nch);  // no statistic is read after this
+  if (a.thr) {
+    // every kernel before this one has read the sequence's keep thresholds
+    // and this one is done with them: zero them (the workspace is left zero)
+    for (int r = tid; r < 2 * G + 1; r += kThreads)
+      a.thr[r <= G ? target_row(b, r, G) : draft_row(b, r - G - 1, G, a.B)] = 0.f;
+  }
 
   if (tid == 0) {
     a.n_out[b] = n;

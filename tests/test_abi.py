@@ -93,11 +93,11 @@ def test_lmhead_argument_errors():
 @pytest.mark.parametrize("kw,status", [
     (dict(T=0.0), -1), (dict(T=float("nan")), -1), (dict(top_p=0.0), -1), (dict(top_p=float("nan")), -1),
     (dict(B=-1), -1), (dict(V=0), -1), (dict(dtype=5), -2), (dict(target=None), -1), (dict(thr=None), -1),
-    (dict(draft=None), -1), (dict(V=102), -1), (dict(target=ctypes.c_void_p(0x1008)), -1),
+    (dict(draft=None), -1),
 ])
 def test_filter_threshold_argument_errors(kw, status):
-    """Shape, dtype, temperature, top_p, pointers and 16-byte row alignment are
-    checked on the host; V = 102 fp32 rows are 408 bytes, not a multiple of 16."""
+    """Shape, dtype, temperature, top_p and pointers are checked on the host
+    (any row length and alignment is accepted)."""
     import speculative_sampling_verification_02_amd as sv
     args = dict(target=FAKE, draft=FAKE, dtype=0, B=2, gamma=3, V=100, T=1.0, top_k=5, top_p=0.9,
                 thr=FAKE, stream=None)

@@ -112,26 +112,28 @@ def test_bad_lenience_is_rejected(dev):
 
 # ------------------------------------------------------------ top-k / top-p
 
+@pytest.mark.parametrize("algo", list(ALGOS))
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("k,p", [(50, 1.0), (0, 0.9), (200, 0.8), (1, 1.0), (3000, 0.5), (0, 0.2)])
-def test_topk_topp(dev, dt, k, p):
+def test_topk_topp(dev, dt, k, p, algo):
     case = W.gaussian_case(8, 4, 20008, dt, 1.0, seed=47, target_std=2.5, draft_noise=1.0)
-    _banner(f"filter {dt} top_k={k} top_p={p}")
-    gpu = gpu_util.run_case(case, ALGOS["fused"], dev=dev, top_k=k, top_p=p)
+    _banner(f"filter {dt} top_k={k} top_p={p} {algo}")
+    gpu = gpu_util.run_case(case, ALGOS[algo], dev=dev, top_k=k, top_p=p)
     rep = parity.check(case, gpu, where=f"filter {dt} k{k} p{p}", top_k=k, top_p=p)
     _banner(f"  {rep}")
     assert rep.rows >= case.B - 2  # at most two rows near a nucleus boundary
 
 
+@pytest.mark.parametrize("algo", list(ALGOS))
 @pytest.mark.parametrize("T", [1.0, 0.5])
-def test_full_size_filtered_with_every_extension(dev, T):
+def test_full_size_filtered_with_every_extension(dev, T, algo):
     """The B=64, gamma=4, V=128256 bf16 workload (many bf16 ties) with top-k 64,
     top-p 0.9, lenience 0.7 and random per-sequence draft counts at once."""
     rng = np.random.default_rng(48)
     case = W.config3(3, T)
     g = _gseq(rng, case.B, case.gamma)
     _banner(f"full size filtered T={T}")
-    gpu = gpu_util.run_case(case, ALGOS["fused"], dev=dev, top_k=64, top_p=0.9, lenience=0.7, gamma_seq=g)
+    gpu = gpu_util.run_case(case, ALGOS[algo], dev=dev, top_k=64, top_p=0.9, lenience=0.7, gamma_seq=g)
     rep = parity.check(case, gpu, where=f"cfg3 filtered T{T}", top_k=64, top_p=0.9, lenience=0.7, gamma_seq=g)
     _banner(f"  {rep}")
     assert rep.rows >= case.B - 3
@@ -151,13 +153,31 @@ def test_filters_leave_argmax_mode_alone_and_workspace_zero(dev):
     assert int(ws.count_nonzero()) == 0
 
 
-def test_filters_need_the_fused_path(dev):
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_filters_on_unaligned_rows(dev, dt):
+    """V = 50257 (an odd vocabulary): the rows are not 16-byte aligned, so the
+    fused path declines, the default algorithm runs the multipass path and the
+    thresholds take element loads; every extension at once, workspace left
+    zero."""
+    import torch
+    import speculative_sampling_verification_02_amd as sv
+    rng = np.random.default_rng(51)
+    case = W.gaussian_case(6, 3, 50257, dt, 1.0, seed=51, target_std=2.5)
+    g = _gseq(rng, case.B, case.gamma)
+    ws = torch.zeros(sv.workspace_size(case.B, case.gamma, case.V, sv.SPEC_BF16 if dt == "bf16" else sv.SPEC_F32),
+                     dtype=torch.uint8, device=dev)
+    _banner(f"unaligned {dt} filters")
+    gpu = gpu_util.run_case(case, 0, dev=dev, top_k=100, top_p=0.8, lenience=0.8, gamma_seq=g, workspace=ws)
+    rep = parity.check(case, gpu, where=f"unaligned {dt}", top_k=100, top_p=0.8, lenience=0.8, gamma_seq=g)
+    _banner(f"  {rep}")
+    assert rep.rows >= case.B - 2
+    assert int(ws.count_nonzero()) == 0
+
+
+def test_bad_top_p_is_rejected(dev):
     import speculative_sampling_verification_02_amd as sv
     case = W.gaussian_case(2, 2, 1024, "f32", 1.0, seed=50)
     t = gpu_util.case_tensors(case, dev)
-    with pytest.raises(sv.SpecVerifyError) as e:
-        sv.verify(t["target"], t["draft"], t["tokens"], t["uniforms"], 1.0, algo=ALGOS["multipass"], top_k=4)
-    assert e.value.status == sv.SPEC_EUNSUPPORTED
     with pytest.raises(sv.SpecVerifyError) as e:
         sv.verify(t["target"], t["draft"], t["tokens"], t["uniforms"], 1.0, top_p=0.0)
     assert e.value.status == sv.SPEC_EINVAL

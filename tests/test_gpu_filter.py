@@ -115,6 +115,15 @@ def test_refinement_overflow_takes_the_row_radix_select(dev):
     _check(dev, x[:, :2], x[:, :1], "bf16", 1000.0, 0, 0.6, "overflow top-p")
 
 
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_unaligned_rows(dev, dt):
+    """V = 50257: rows that are not 16-byte aligned take element loads."""
+    case = W.gaussian_case(3, 2, 50257, "f32", 1.0, seed=78, target_std=3.0)
+    t, d = (case.target, case.draft) if dt == "f32" else (_bf16(case.target), _bf16(case.draft))
+    for k, p in ((40, 1.0), (0, 0.9), (300, 0.7)):
+        _check(dev, t, d, dt, 1.0, k, p, f"unaligned {dt}")
+
+
 def test_rows_longer_than_the_registers(dev):
     """fp32 rows of 70000 tokens exceed the 65536 the registers hold."""
     case = W.gaussian_case(2, 2, 70000, "f32", 1.0, seed=74, target_std=2.0)
