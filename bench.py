@@ -171,6 +171,9 @@ def main() -> int:
     ap.add_argument("--lenience", type=float, default=1.0, help="lenience factor l in (0, 1] (spec_verify_ex)")
     ap.add_argument("--ragged", action="store_true",
                     help="per-sequence draft counts gamma_b ~ U{1..gamma} (seeded; spec_verify_ex)")
+    ap.add_argument("--vocab", type=int, default=0,
+                    help="the verify workload's recipe at another vocabulary size (e.g. 50257, whose rows are "
+                         "not 16-byte aligned and take the multipass path)")
     ap.add_argument("--top-k", type=int, default=0, help="top-k filter of p and q (0: off; spec_verify_ex)")
     ap.add_argument("--top-p", type=float, default=1.0, help="top-p filter of p and q (1: off; spec_verify_ex)")
     args = ap.parse_args()
@@ -189,7 +192,10 @@ def main() -> int:
     dev = torch.device("cuda:0")
     algo = {"auto": sv.ALGO_AUTO, "multipass": sv.ALGO_MULTIPASS, "fused": sv.ALGO_FUSED}[args.algo]
     T = float(args.temperature)
-    case = {"verify": W.config3, "small1": W.config1, "small2": W.config2, "large5": W.config5}[args.workload](0, T)
+    if args.vocab and args.workload == "verify":
+        case = W.config3(0, T, V=args.vocab)
+    else:
+        case = {"verify": W.config3, "small1": W.config1, "small2": W.config2, "large5": W.config5}[args.workload](0, T)
     B, G, V = case.B, case.gamma, case.V
     bf16 = case.dtype == "bf16"
     elem = 2 if bf16 else 4
@@ -249,7 +255,7 @@ def main() -> int:
     # AUTO dispatches the headline workload (aligned bf16 rows, 16 workgroups
     # per row) to the fused kernel, whose counters the traffic record holds
     traffic = None
-    if args.workload == "verify" and T == 1.0 and default_path:
+    if args.workload == "verify" and T == 1.0 and default_path and not args.vocab:
         traffic = load_traffic("fused" if algo_name == "auto" else algo_name)
     line = {
         "metric": METRIC,
@@ -276,7 +282,7 @@ def main() -> int:
                      "alg_bytes": alg, "full_bytes": (2 * G + 1) * V * elem * B,
                      "stream_read_GBps": stream_gbs, "frac_of_stream_read": achieved / stream_gbs},
     }
-    if not args.no_cpu_baseline and args.workload == "verify" and default_path:
+    if not args.no_cpu_baseline and args.workload == "verify" and default_path and not args.vocab:
         line["cpu_baseline"] = cpu_baseline(case)
     print(json.dumps(line), flush=True)
     return 0
