@@ -590,9 +590,9 @@ __device__ __attribute__((always_inline)) void issue_item(const FusedParams& P, 
 // Row normalisers handed from wave 0 to the other waves, double-buffered by
 // item parity: a buffer is rewritten two items later, after every wave has
 // passed the barrier of the item in between.
-struct NormMsg {
+struct __align__(16) NormMsg {
   float Mp, Mq, invSp, invSq;
-  int ok;
+  int ok, pad0, pad1, pad2;
 };
 
 // Top-k / top-p filtering (extended kernels): a logit below its row's keep
@@ -633,6 +633,30 @@ __device__ __attribute__((always_inline)) void pair_phase1(const FusedParams& P,
   }
 }
 
+// Barrier, then every wave reads *m from LDS.  Written in assembly so that
+// the compiler adds no wait for this wave's outstanding buffer loads into
+// LDS: the compiler cannot tell that they target the stage, not *m, and a
+// wait for them here would hold every wave until the next item's tiles have
+// arrived.  The barrier follows the completion of this wave's own LDS writes
+// (lgkmcnt(0)), so the writer's message is visible after it; the loads into
+// the stage are ordered by the explicit vmcnt wait before the stage is read.
+__device__ __attribute__((always_inline)) inline NormMsg lds_exchange_msg(const NormMsg* m) {
+  const uint32_t addr =
+      (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) NormMsg*)m);
+  float4 v;
+  int ok;
+  asm volatile(
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_barrier\n\t"
+      "ds_read_b128 %0, %2\n\t"
+      "ds_read_b32 %1, %2 offset:16\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v), "=&v"(ok)
+      : "v"(addr)
+      : "memory");
+  return NormMsg{v.x, v.y, v.z, v.w, ok, 0, 0, 0};
+}
+
 // The team wait: wave 0 polls until every wave of the team has published its
 // phase-1 partials, combines them in one fixed order and hands both row
 // normalisers to the other waves through msg[parity] (one LDS-only barrier).
@@ -643,15 +667,14 @@ __device__ __attribute__((always_inline)) inline NormMsg pair_wait(const FusedPa
     const uint64_t* part1 = P.part1 + (size_t)item * P.W * 2;
     const bool ok = 2 * P.W <= 2 * kWave ? wave_poll_once(part1, 2 * P.W, w1)
                                          : wave_poll<SPECV_FUSED_L2_POLL != 0>(part1, 2 * P.W, w1, nullptr, 0, nullptr);
-    NormMsg m{0.f, 0.f, 0.f, 0.f, 0};
+    NormMsg m{0.f, 0.f, 0.f, 0.f, 0, 0, 0, 0};
     if (ok) {
       const Norm2 n = wave_norm2(w1, P.W);
-      m = NormMsg{n.Mp, n.Mq, (float)(1.0 / n.Sp), (float)(1.0 / n.Sq), 1};
+      m = NormMsg{n.Mp, n.Mq, (float)(1.0 / n.Sp), (float)(1.0 / n.Sq), 1, 0, 0, 0};
     }
     if (threadIdx.x == 0) msg[parity] = m;
   }
-  lds_barrier();
-  return msg[parity];
+  return lds_exchange_msg(msg + parity);
 }
 
 // Phase 2: the wave's share of alpha = sum min(p, q) and of the residual mass
@@ -797,6 +820,10 @@ __device__ __attribute__((always_inline)) void compute_loop_staged(const FusedPa
   // first vector and ends at the end of the row, so vectors past V read as
   // zero (unpack_tile masks them to -inf) and all address arithmetic is
   // scalar; lane l moves bytes [16 l, 16 l + 16).
+  constexpr int kCopyBytes = kWave * 16;                  // one copy: 16 bytes per lane
+  constexpr int kRowLoads = kWavesPerGroup * NS;          // copies per row tile of the workgroup
+  static_assert(NS * E::kVec == PER && (kRowLoads & (kRowLoads - 1)) == 0, "stage copy shape");
+  const unsigned tile_bytes = (unsigned)(rank * kWavesPerGroup * kWave * PER * (int)sizeof(E::storage));
   auto issue = [&](int item) {  // waves 1..3
     const bool pair = item < P.n_pairs;
     const int b = pair ? item / a.gamma : item - P.n_pairs;
@@ -805,14 +832,15 @@ __device__ __attribute__((always_inline)) void compute_loop_staged(const FusedPa
     const E::storage* prow = trow<E>(a, b, i);
     const E::storage* qrow = pair ? drow<E>(a, b, i) : prow;
     const int n = pair ? kLoads : kLoads / 2;
+    // Copy l moves the (l mod kRowLoads)-th KiB of this workgroup's tile of
+    // row l / kRowLoads (the four wave tiles are adjacent, vector s of wave w
+    // being KiB w * NS + s) into KiB l of the stage.
     for (int l = wave - 1; l < n; l += kWavesPerGroup - 1) {
-      const int r = l / (kWavesPerGroup * NS), w = (l / NS) % kWavesPerGroup, v = l % NS;
-      const unsigned off = (unsigned)(((rank * kWavesPerGroup + w) * kWave * PER + v * kWave * E::kVec) *
-                                      (int)sizeof(E::storage));
-      const uint64_t addr = reinterpret_cast<uint64_t>(r == 0 ? prow : qrow) + off;
+      const unsigned off = tile_bytes + (unsigned)(l & (kRowLoads - 1)) * kCopyBytes;
+      const uint64_t addr = reinterpret_cast<uint64_t>(l < kRowLoads ? prow : qrow) + off;
       const uint64_t uaddr = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(addr >> 32)) << 32) |
                              (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)addr);
-      const int nrec = __builtin_amdgcn_readfirstlane((int)(off < row_bytes ? row_bytes - off : 0u));
+      const int nrec = __builtin_amdgcn_readfirstlane((int)(row_bytes - min(off, row_bytes)));
       const __amdgpu_buffer_rsrc_t rs =
           __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(uaddr), (short)0, nrec, 0x00020000);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)&stage[l * kWave], 16,
