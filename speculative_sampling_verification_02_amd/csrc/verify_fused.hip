@@ -840,7 +840,9 @@ __device__ __attribute__((always_inline)) void compute_loop_staged(const FusedPa
       const uint64_t addr = reinterpret_cast<uint64_t>(l < kRowLoads ? prow : qrow) + off;
       const uint64_t uaddr = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(addr >> 32)) << 32) |
                              (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)addr);
-      const int nrec = __builtin_amdgcn_readfirstlane((int)(row_bytes - min(off, row_bytes)));
+      // bytes from the copy's first vector to the row's end (rows are shorter
+      // than 2^31 bytes); a signed max stays a scalar instruction
+      const int nrec = max((int)row_bytes - (int)off, 0);
       const __amdgpu_buffer_rsrc_t rs =
           __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(uaddr), (short)0, nrec, 0x00020000);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)&stage[l * kWave], 16,
@@ -1167,10 +1169,19 @@ __device__ void finish_bonus(const FusedParams& P, int item, uint64_t* w1, uint6
   const int gb = seq_gamma_of<EXT>(a, b);
   const auto* row = trow<E>(a, b, gb);  // the bonus row follows the sequence's last draft
   uint64_t* part1 = P.part1 + (size_t)item * W * 2;
-  const bool ok1 = gather(part1, 2 * W, w1);
-  if (ok1) clear_slots(part1, 2 * W);
+  // The row's partials and the sequence's pair results (published by other
+  // finishers, usually long before) in one wait.  The bonus token is drawn
+  // only when every draft was kept.
+  uint64_t* pres = P.pair_res + (size_t)b * G;
+  const bool ok1 = gather2(part1, 2 * W, w1, pres, gb, res);
+  if (ok1) {
+    clear_slots(part1, 2 * W);
+    clear_slots(pres, gb);
+  }
+  int n_acc = 0;
+  while (n_acc < gb && ((uint32_t)res[n_acc] & 1u) != 0u) ++n_acc;
   int t_bonus = -1;
-  if (!ok1) {
+  if (!ok1 || n_acc < gb) {
   } else if constexpr (ARGMAX) {
     t_bonus = combine_argmax(w1, W, 0).i;
   } else {
@@ -1206,9 +1217,6 @@ __device__ void finish_bonus(const FusedParams& P, int item, uint64_t* w1, uint6
       if (a.q_draft) a.q_draft[o] = nan;
     }
   }
-  // the sequence's pair results (published by other finishers)
-  const bool ok2 = gather(P.pair_res + (size_t)b * G, gb, res);
-  if (ok2) clear_slots(P.pair_res + (size_t)b * G, gb);
   if constexpr (EXT) {
     // the last reader of the bonus row's keep threshold; the padding rows'
     // thresholds are never read: zero them all
@@ -1219,11 +1227,9 @@ __device__ void finish_bonus(const FusedParams& P, int item, uint64_t* w1, uint6
     }
   }
   if (threadIdx.x == 0) {
-    if (ok1 && ok2) {
-      int n = 0;
-      while (n < gb && ((uint32_t)res[n] & 1u) != 0u) ++n;
-      a.n_out[b] = n;
-      a.t_out[b] = n < gb ? (int)(uint32_t)(res[n] >> 32) : t_bonus;
+    if (ok1) {
+      a.n_out[b] = n_acc;
+      a.t_out[b] = n_acc < gb ? (int)(uint32_t)(res[n_acc] >> 32) : t_bonus;
     } else {
       a.n_out[b] = -1;  // a wait gave up (the device was shared): no result
       a.t_out[b] = -1;
