@@ -1243,9 +1243,14 @@ __device__ void finish_bonus(const FusedParams& P, int item, uint64_t* w1, uint6
 // the finisher's copies of an item's slots on a finisher (a workgroup is one
 // or the other); the compute workgroup's poll buffer and normaliser messages
 // follow it.
-template <class E, int PER>
+template <class E, int PER, bool ARGMAX>
 struct Pool {
-  static constexpr bool kStaged = std::is_same<E, BF16>::value && SPECV_FUSED_STAGE;
+  // Only the bf16 T > 0 kernel stages.  In argmax mode each wave loads its own
+  // tiles when their item comes up: with no team exchange to hide and little
+  // arithmetic per token, the three workgroups of a compute unit cover each
+  // other's load latency, and that measured faster than the stage (36.9 vs
+  // 41.8 us on the B=64 workload); at T > 0 the stage wins (42.5 vs 51.0 us).
+  static constexpr bool kStaged = std::is_same<E, BF16>::value && SPECV_FUSED_STAGE && !ARGMAX;
   static constexpr int kFinBytes = (3 * kMaxWaveTiles + SPEC_MAX_GAMMA) * 8;
   static constexpr int kStageBytes = kStaged ? stage_vectors<PER>() * 16 : 0;
   static constexpr int kABytes = kStageBytes > kFinBytes ? kStageBytes : kFinBytes;
@@ -1254,7 +1259,7 @@ struct Pool {
 
 template <class E, int PER, bool ARGMAX, bool EXT>
 __global__ __launch_bounds__(kThreads, SPECV_FUSED_MIN_WAVES) void fused_kernel(FusedParams P) {
-  using L = Pool<E, PER>;
+  using L = Pool<E, PER, ARGMAX>;
   __shared__ __align__(16) unsigned char pool[L::kBytes];
   uint64_t* poll_buf = reinterpret_cast<uint64_t*>(pool + L::kABytes);
   NormMsg* msg = reinterpret_cast<NormMsg*>(pool + L::kABytes + 2 * kMaxWaveTiles * 8);
