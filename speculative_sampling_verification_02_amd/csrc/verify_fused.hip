@@ -75,20 +75,6 @@ namespace {
 #ifndef SPECV_FUSED_STAGE
 #define SPECV_FUSED_STAGE 1
 #endif
-// Place each compute team's workgroups on one XCD (workgroups are dispatched
-// to the 8 XCDs round-robin by index), and poll a team's partials through that
-// XCD's L2 before falling back to device-scope polls.
-#ifndef SPECV_FUSED_XCD_TEAMS
-#define SPECV_FUSED_XCD_TEAMS 0
-#endif
-#ifndef SPECV_FUSED_L2_POLL
-#define SPECV_FUSED_L2_POLL 0
-#endif
-// Keep two bf16 pair items in flight per workgroup (1): phase 1 of one runs
-// while the team exchange of the other completes.
-#ifndef SPECV_FUSED_PIPELINE
-#define SPECV_FUSED_PIPELINE 1
-#endif
 // Rotate the compute waves' issue priority by item round (1) or leave every
 // wave at the default priority (0).  With three workgroups per compute unit,
 // the one dispatched first wins every tie in the instruction arbiter (the
@@ -126,7 +112,6 @@ struct FusedParams {
   int n_items;    // B * (gamma + 1): pairs, then one bonus item per sequence
   int nteams;     // compute teams
   int nfin;       // finisher workgroups
-  int xcd_teams;  // nonzero: team t lives on XCD t % 8 (grid = 8 * per-XCD share)
   uint64_t* part1;     // [n_items][W][2]  (max, sum) of p and q, or argmax (value, index)
   uint64_t* part2;     // [n_pairs][W]     (overlap share, residual mass share)
   uint64_t* pair_res;  // [n_pairs]        (accept flag | kResMark, sampled token)
@@ -162,15 +147,6 @@ __device__ inline void st_u64(uint64_t* p, uint64_t v) {
 __device__ inline uint64_t ld_u64(const uint64_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// 64-bit load through this XCD's L2 (sc0: bypasses only the CU's L1).  It sees
-// every store made through the same L2; a store from another XCD may stay
-// invisible to it, so a poll built on it falls back to ld_u64.
-__device__ inline uint64_t ld_u64_l2(const uint64_t* base, int idx) {
-  const __amdgpu_buffer_rsrc_t r =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint64_t*>(base), (short)0, 0x7fffffff, 0x00020000);
-  return __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(r, idx * 8, 0, 1));
-}
-constexpr unsigned kL2Polls = 64;
 
 // Workgroup barrier for LDS data only: the fences order LDS accesses, so the
 // barrier waits for this wave's LDS operations but not for its outstanding
@@ -185,7 +161,6 @@ __device__ inline void lds_barrier() {
 // copies them to lds[0..n).  Returns true, uniformly over the wave, if all
 // arrived and none is poisoned.  Gives up after kSpinIters polls, so the
 // kernel always terminates.  Called by all lanes of one wave.
-template <bool L2FIRST = false>
 __device__ inline bool wave_poll(const uint64_t* a, int na, uint64_t* la, const uint64_t* b, int nb,
                                  uint64_t* lb) {
   const int lane = threadIdx.x & (kWave - 1), n = na + nb;
@@ -195,7 +170,7 @@ __device__ inline bool wave_poll(const uint64_t* a, int na, uint64_t* la, const 
     while (true) {
       uint64_t v = pack2i(1u, 0u);
       if (c < na) {
-        v = (L2FIRST && it < kL2Polls) ? ld_u64_l2(a, c) : ld_u64(a + c);
+        v = ld_u64(a + c);
         la[c] = v;
       } else if (c < n) {
         v = ld_u64(b + (c - na));
@@ -666,7 +641,7 @@ __device__ __attribute__((always_inline)) inline NormMsg pair_wait(const FusedPa
   if (threadIdx.x < kWave) {
     const uint64_t* part1 = P.part1 + (size_t)item * P.W * 2;
     const bool ok = 2 * P.W <= 2 * kWave ? wave_poll_once(part1, 2 * P.W, w1)
-                                         : wave_poll<SPECV_FUSED_L2_POLL != 0>(part1, 2 * P.W, w1, nullptr, 0, nullptr);
+                                         : wave_poll(part1, 2 * P.W, w1, nullptr, 0, nullptr);
     NormMsg m{0.f, 0.f, 0.f, 0.f, 0, 0, 0, 0};
     if (ok) {
       const Norm2 n = wave_norm2(w1, P.W);
@@ -806,6 +781,7 @@ template <int PER, bool ARGMAX, bool EXT>
 __device__ __attribute__((always_inline)) void compute_loop_staged(const FusedParams& P, int team, int rank,
                                                                    u32x4* stage, uint64_t* w1, NormMsg* msg) {
   using E = BF16;
+  static_assert(!ARGMAX, "the argmax kernel loads without the stage");
   constexpr int NS = PER / E::kVec;
   constexpr int kLoads = 2 * kWavesPerGroup * NS;
   const VerifyArgs& a = P.a;
@@ -882,7 +858,7 @@ __device__ __attribute__((always_inline)) void compute_loop_staged(const FusedPa
     const int next_d = d + P.nteams;
     const int next = next_d < n_live ? live_item<EXT>(P, next_d) : P.n_items;
     if (wave != 0 && next < P.n_items && !empty_item<EXT>(P, next)) issue(next);
-    if constexpr (!ARGMAX && SPECV_FUSED_PIPELINE) {
+    {
       // Two pair items in flight: phase 1 of this item runs while the team
       // exchange of the previous one completes, and only then is the previous
       // one finished.  (Copying the new weights into the pending set costs a
@@ -917,23 +893,15 @@ __device__ __attribute__((always_inline)) void compute_loop_staged(const FusedPa
           pend = -1;
         }
       }
-    } else if (empty_item<EXT>(P, item)) {
-    } else if (!ARGMAX && item < P.n_pairs) {
-      pair_compute_sample<E, PER, EXT>(P, item, c, lo, parity, A, w1, msg);
-      parity ^= 1;
-    } else {
-      single_pass_compute<E, PER, ARGMAX, EXT>(P, item, c, lo, A);
     }
     if (wave != 0) wait_vmem();
     lds_barrier();
     item = next;
     d = next_d;
   }
-  if constexpr (!ARGMAX && SPECV_FUSED_PIPELINE) {
-    if (pend >= 0) {
-      const NormMsg m = pair_wait(P, pend, parity, w1, msg);
-      pair_phase2<PER, EXT>(P, pend, c, m, ep, eq, mp, mq, sp, sq);
-    }
+  if (pend >= 0) {
+    const NormMsg m = pair_wait(P, pend, parity, w1, msg);
+    pair_phase2<PER, EXT>(P, pend, c, m, ep, eq, mp, mq, sp, sq);
   }
 }
 
@@ -1269,15 +1237,7 @@ __global__ __launch_bounds__(kThreads, SPECV_FUSED_MIN_WAVES) void fused_kernel(
   const int ncompute = P.nteams * P.K;
   // role of this workgroup: compute (team, rank) or finisher f
   int team = -1, rank = 0, f = 0;
-  if (P.xcd_teams) {
-    const int x = blockIdx.x % 8, j = blockIdx.x / 8, cpx = ncompute / 8;
-    if (j < cpx) {
-      team = (j / P.K) * 8 + x;
-      rank = j % P.K;
-    } else {
-      f = (j - cpx) * 8 + x;
-    }
-  } else if ((int)blockIdx.x < ncompute) {
+  if ((int)blockIdx.x < ncompute) {
     team = blockIdx.x / P.K;
     rank = blockIdx.x % P.K;
   } else {
@@ -1383,17 +1343,6 @@ hipError_t launch(const VerifyArgs& a, hipStream_t s) {
   // run concurrently and every wait ends.
   P.nfin = (int)std::min<long>(P.n_items, std::max<long>(1, resident / kFinisherDiv));
   P.nteams = (int)std::min<long>(P.n_items, (resident - P.nfin) / P.K);
-  if (SPECV_FUSED_XCD_TEAMS) {
-    // an equal share of teams and finishers on each of the 8 XCDs
-    const long per_xcd = resident / 8, need_x = (P.n_items + 7) / 8;
-    const long fin_x = std::min(need_x, std::max<long>(1, per_xcd / kFinisherDiv));
-    const long teams_x = std::min(need_x, (per_xcd - fin_x) / P.K);
-    if (teams_x >= 1) {
-      P.xcd_teams = 1;
-      P.nteams = (int)(8 * teams_x);
-      P.nfin = (int)(8 * fin_x);
-    }
-  }
   if (P.nteams < 1) return hipErrorNotSupported;
   kern<<<dim3(P.nteams * P.K + P.nfin), dim3(kThreads), 0, s>>>(P);
   return hipGetLastError();
