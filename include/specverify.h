@@ -213,6 +213,14 @@ int spec_verify_ex(int algo,
  *               tokens whose logit is >= thresholds[r]; the value is one of the
  *               row's logits, or -inf when the row keeps everything (no filter
  *               active, or fewer finite logits than top_k).
+ *   workspace   NULL, or device scratch of at least
+ *               spec_filter_workspace_size() bytes, all-zero on entry and
+ *               all-zero on return of the queued work.  With a workspace, a
+ *               top-k of at most 64 first lists each 8192-token chunk's
+ *               candidates (the values at or above a pivot the chunk has k
+ *               values above) and selects from their union, without holding
+ *               the row; the thresholds are the same either way.  A smaller
+ *               non-NULL workspace is SPEC_ENOSPACE.
  *   Ties are kept.  Masses are fp32 exp2((logit - max) log2(e) / T), summed in
  *   fp64 and 2^-40 fixed point; a nucleus boundary within about 2^-23 of
  *   top_p times the total may fall on either side of that tie group.
@@ -220,7 +228,10 @@ int spec_verify_ex(int algo,
  */
 int spec_filter_thresholds(const void* target_logits, const void* draft_logits, int dtype,
                            int B, int gamma, int V, float temperature, int top_k, float top_p,
-                           float* thresholds, void* stream);
+                           float* thresholds, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of the optional spec_filter_thresholds() workspace; 0 for a bad shape. */
+size_t spec_filter_workspace_size(int B, int gamma, int V);
 
 /*
  * spec_lmhead_logits -- the target pass's final matrix product for the positions

@@ -42,7 +42,8 @@ SIGNATURES = {
                                 _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                 _c_void_p, _c_size_t, _c_void_p]),
     "spec_filter_thresholds": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_int, _c_float,
-                                        _c_int, _c_float, _c_void_p, _c_void_p]),
+                                        _c_int, _c_float, _c_void_p, _c_void_p, _c_size_t, _c_void_p]),
+    "spec_filter_workspace_size": (_c_size_t, [_c_int, _c_int, _c_int]),
     "spec_lmhead_logits": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_void_p, _c_void_p]),
     "spec_stream_read": (_c_int, [_c_void_p, _c_size_t, _c_void_p, _c_int, _c_void_p]),
     "spec_lmhead_workspace_size": (_c_size_t, [_c_int, _c_int, _c_int, _c_int]),
@@ -186,13 +187,21 @@ def verify(target_logits, draft_logits, draft_tokens, uniforms, temperature: flo
     return outputs
 
 
-def filter_thresholds(target_logits, draft_logits, temperature: float, top_k: int = 0, top_p: float = 1.0):
+def filter_workspace_size(B: int, gamma: int, V: int) -> int:
+    """Bytes of the optional filter_thresholds workspace (spec_filter_workspace_size)."""
+    return int(lib.spec_filter_workspace_size(int(B), int(gamma), int(V)))
+
+
+def filter_thresholds(target_logits, draft_logits, temperature: float, top_k: int = 0, top_p: float = 1.0,
+                      workspace=None):
     """Per-row keep thresholds of top-k / top-p (spec_filter_thresholds).
 
     target_logits [B, gamma+1, V] and draft_logits [B, gamma, V] (float32 or
-    bfloat16) on one GPU; temperature > 0.  Returns float32 GPU tensors
-    (target [B, gamma+1], draft [B, gamma]): a row keeps the tokens whose logit
-    is >= its threshold (-inf: the whole row)."""
+    bfloat16) on one GPU; temperature > 0.  workspace: None, or a zeroed uint8
+    GPU tensor of at least filter_workspace_size(B, gamma, V) bytes (left
+    zeroed), which lets a top-k of at most 64 select from chunk candidate lists.
+    Returns float32 GPU tensors (target [B, gamma+1], draft [B, gamma]): a row
+    keeps the tokens whose logit is >= its threshold (-inf: the whole row)."""
     torch = _torch()
     dev = target_logits.device
     _need(target_logits, "target_logits")
@@ -202,9 +211,13 @@ def filter_thresholds(target_logits, draft_logits, temperature: float, top_k: in
         raise ValueError("draft_logits must be [B, gamma, V] with the target's dtype")
     _need(draft_logits, "draft_logits", device=dev)
     thr = torch.empty(B * g1 + B * gamma, dtype=torch.float32, device=dev)
+    ws, ws_bytes = None, 0
+    if workspace is not None:
+        _need(workspace, "workspace", device=dev)
+        ws, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
     _check(lib.spec_filter_thresholds(_ptr(target_logits), _ptr(draft_logits) if gamma else None,
                                       _dtype_code(target_logits), B, gamma, V, float(temperature), int(top_k),
-                                      float(top_p), _ptr(thr), _stream(dev)), "spec_filter_thresholds")
+                                      float(top_p), _ptr(thr), ws, ws_bytes, _stream(dev)), "spec_filter_thresholds")
     return thr[:B * g1].view(B, g1), thr[B * g1:].view(B, gamma)
 
 

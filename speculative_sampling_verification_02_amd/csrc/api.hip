@@ -52,16 +52,25 @@ const char* spec_status_string(int status) {
 // Both paths start their scratch at the workspace's base and both leave all
 // of it zero when they complete (the fused path needs zero slots on entry).
 // The top-k / top-p keep thresholds (one float per row) follow, and are
-// zeroed again after the verification that reads them.
+// zeroed again after the verification that reads them; then the threshold
+// kernel's chunk lists, which it leaves zero.
 static size_t paths_bytes(int B, int gamma, int V) {
   const size_t b = std::max(specv::fused_workspace_bytes(B, gamma, V), specv::multipass_workspace_bytes(B, gamma, V));
   return (std::max<size_t>(b, 256) + 255) & ~(size_t)255;
 }
 
+static size_t thr_bytes(int B, int gamma) {
+  return ((size_t)B * (2 * gamma + 1) * sizeof(float) + 255) & ~(size_t)255;
+}
+
 size_t spec_verify_workspace_size(int B, int gamma, int V, int dtype) {
   if (!valid_shape(B, gamma, V) || (dtype != SPEC_F32 && dtype != SPEC_BF16)) return 0;
-  const size_t thr = ((size_t)B * (2 * gamma + 1) * sizeof(float) + 255) & ~(size_t)255;
-  return paths_bytes(B, gamma, V) + thr;
+  return paths_bytes(B, gamma, V) + thr_bytes(B, gamma) + specv::filter_list_bytes(B, gamma, V);
+}
+
+size_t spec_filter_workspace_size(int B, int gamma, int V) {
+  if (!valid_shape(B, gamma, V)) return 0;
+  return specv::filter_list_bytes(B, gamma, V);
 }
 
 int spec_verify_ex(int algo, const void* target_logits, const void* draft_logits, int dtype,
@@ -109,8 +118,9 @@ int spec_verify_ex(int algo, const void* target_logits, const void* draft_logits
   // the last reader of each threshold zeroes it).
   const bool filtered = temperature > 0.f && ((top_k > 0 && top_k < V) || top_p < 1.f);
   if (filtered) {
-    float* thr = reinterpret_cast<float*>(static_cast<char*>(workspace) + paths_bytes(B, gamma, V));
-    const hipError_t e = specv::filter_thresholds(a, top_k, top_p, thr, s);
+    char* base = static_cast<char*>(workspace) + paths_bytes(B, gamma, V);
+    float* thr = reinterpret_cast<float*>(base);
+    const hipError_t e = specv::filter_thresholds(a, top_k, top_p, thr, base + thr_bytes(B, gamma), s);
     if (e != hipSuccess) return map_hip(e);
     a.thr = thr;
   }
@@ -155,12 +165,14 @@ int spec_lmhead_logits(const void* hidden, const void* W, int M, int d, int V, f
 }
 
 int spec_filter_thresholds(const void* target_logits, const void* draft_logits, int dtype, int B, int gamma,
-                           int V, float temperature, int top_k, float top_p, float* thresholds, void* stream) {
+                           int V, float temperature, int top_k, float top_p, float* thresholds, void* workspace,
+                           size_t workspace_bytes, void* stream) {
   if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_EUNSUPPORTED;
   if (!valid_shape(B, gamma, V) || !valid_temperature(temperature) || !(temperature > 0.f)) return SPEC_EINVAL;
   if (!(top_p > 0.f)) return SPEC_EINVAL;  // also rejects NaN
   if (B == 0) return SPEC_OK;
   if (!target_logits || !thresholds || (gamma > 0 && !draft_logits)) return SPEC_EINVAL;
+  if (workspace && workspace_bytes < spec_filter_workspace_size(B, gamma, V)) return SPEC_ENOSPACE;
   VerifyArgs a{};
   a.target = target_logits;
   a.draft = draft_logits;
@@ -170,7 +182,7 @@ int spec_filter_thresholds(const void* target_logits, const void* draft_logits, 
   a.V = V;
   a.temperature = temperature;
   a.k = kLog2e / temperature;
-  return map_hip(specv::filter_thresholds(a, top_k, top_p, thresholds, static_cast<hipStream_t>(stream)));
+  return map_hip(specv::filter_thresholds(a, top_k, top_p, thresholds, workspace, static_cast<hipStream_t>(stream)));
 }
 
 size_t spec_lmhead_workspace_size(int B, int gamma, int d, int V) {

@@ -41,6 +41,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "common.hpp"
@@ -67,7 +68,22 @@ struct FilterArgs {
   int top_k;           // active when 0 < top_k < V
   float top_p;         // active when top_p < 1
   float* thr;          // [rows] out: keep threshold (-inf: keep all)
+  // chunk candidate lists (nullptr: the row kernel works from the row alone)
+  int nch;             // chunks of kLChunk tokens per row
+  uint32_t* lcount;    // [rows][nch] listed values, kListCap + 1 on overflow
+  float* lvals;        // [rows][nch][kListCap]
 };
+
+// Chunk candidate lists for top-k with k <= kListK.  A streaming kernel lists,
+// for every chunk of kLChunk tokens of a row, the values at or above a pivot
+// the chunk has at least k values at or above; the union over the row's chunks
+// then holds every value >= the row's k-th largest (a chunk whose pivot were
+// above it would hold k larger values), so the exact selection runs on the
+// union instead of the row.
+constexpr int kListK = 64;
+constexpr int kListCap = 256;
+constexpr int kLT = 256;           // threads of the list kernel
+constexpr int kLChunk = kLT * 32;  // tokens per chunk
 
 struct FilterLds {
   union {
@@ -88,6 +104,8 @@ struct FilterLds {
   uint32_t kmin_s, kmax_s;
   unsigned long long above_s;
   double target_s;
+  uint32_t lpre[257];  // exclusive prefix of the row's chunk list counts
+  uint32_t lovf;
 };
 
 // Order-preserving unsigned key of a finite or -inf logit (-0 as +0), in the
@@ -174,6 +192,97 @@ __device__ inline int wave_pick_desc(F binval, double need, double* before_out) 
 // Radix select over the whole row read from memory, 8 bits per pass: top-k by
 // counts, then top-p by 2^-40 fixed-point mass.  Exact for any row; slower,
 // since every pass re-reads the row and bins contend.
+// One chunk of one row per workgroup: thread t holds vectors v = 0 .. NV-1 of
+// the chunk at tokens lo + (v kLT + t) kVec.  The pivot is the smallest over
+// the 4 waves of each wave's m-th largest thread maximum, m = ceil(k / 4): a
+// wave then has m maxima at or above it, each a value of the chunk, so the
+// chunk has at least 4 m >= k values >= pivot (a chunk with fewer than k
+// values gets pivot -inf and lists them all).  The values >= pivot are listed
+// in thread order, or the count is marked as overflowed (kListCap + 1).
+template <class E, bool ALIGNED>
+__global__ __launch_bounds__(kLT) void chunk_list_kernel(FilterArgs f) {
+  constexpr int KV = E::kVec;
+  constexpr int NV = kLChunk / kLT / KV;
+  constexpr int NW = kLT / kWave;
+  __shared__ float wm[NW];
+  __shared__ uint32_t wsum[NW];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+  const int V = f.V;
+  auto row_of = [&](int r) {
+    return r < f.nt ? static_cast<const typename E::storage*>(f.target) + (size_t)r * V
+                    : static_cast<const typename E::storage*>(f.draft) + (size_t)(r - f.nt) * V;
+  };
+  // chunk w = r nch + ch of the rows (one per workgroup)
+  const int w = blockIdx.x, lo = (w % f.nch) * kLChunk;
+  const auto* row = row_of(w / f.nch);
+  u32x4 cur[NV];
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const int j0 = lo + (v * kLT + tid) * KV;
+    cur[v] = j0 >= V ? u32x4{0u, 0u, 0u, 0u} : ALIGNED ? load_stream(row + j0) : load_vec_scalar<E>(row, j0, V);
+  }
+  {
+    float x[NV * KV];
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const int j0 = lo + (v * kLT + tid) * KV;
+      float t[KV];
+      E::unpack(cur[v], t);
+#pragma unroll
+      for (int e = 0; e < KV; ++e) x[v * KV + e] = j0 + e < V ? t[e] : -INFINITY;
+    }
+    // element i of this thread lies in the row (the last chunk may end early)
+    auto in_row = [&](int i) { return lo + ((i / KV) * kLT + tid) * KV + i % KV < V; };
+    float tm = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < NV * KV; ++i) tm = fmaxf(tm, x[i]);
+    // the wave's thread maxima in descending order across the lanes (bitonic)
+    float srt = tm;
+#pragma unroll
+    for (int k2 = 2; k2 <= kWave; k2 <<= 1) {
+#pragma unroll
+      for (int j = k2 >> 1; j > 0; j >>= 1) {
+        const float o = __shfl_xor(srt, j);
+        srt = (((lane & k2) == 0) == ((lane & j) == 0)) ? fmaxf(srt, o) : fminf(srt, o);
+      }
+    }
+    const int m = (f.top_k + NW - 1) / NW;  // <= kListK / 4 <= kWave
+    const float mth = __shfl(srt, m - 1);
+    if (lane == 0) wm[wid] = mth;
+    __syncthreads();
+    float pivot = wm[0];
+#pragma unroll
+    for (int q = 1; q < NW; ++q) pivot = fminf(pivot, wm[q]);
+    uint32_t c = 0;
+#pragma unroll
+    for (int i = 0; i < NV * KV; ++i) c += in_row(i) && x[i] >= pivot ? 1u : 0u;
+    // offsets: inclusive scan within the wave, then the waves' totals
+    uint32_t incl = c;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const uint32_t o = (uint32_t)__shfl_up((int)incl, off);
+      if (lane >= off) incl += o;
+    }
+    if (lane == kWave - 1) wsum[wid] = incl;
+    __syncthreads();
+    uint32_t base = 0, total = 0;
+#pragma unroll
+    for (int q = 0; q < NW; ++q) {
+      base += q < wid ? wsum[q] : 0u;
+      total += wsum[q];
+    }
+    if (tid == 0) f.lcount[w] = total <= (uint32_t)kListCap ? total : (uint32_t)kListCap + 1u;
+    if (total <= (uint32_t)kListCap) {
+      uint32_t o = base + incl - c;
+      float* out = f.lvals + (size_t)w * kListCap;
+#pragma unroll
+      for (int i = 0; i < NV * KV; ++i) {
+        if (in_row(i) && x[i] >= pivot) out[o++] = x[i];
+      }
+    }
+  }
+}
+
 template <class E, bool ALIGNED>
 __device__ __attribute__((always_inline)) inline float radix_threshold(const typename E::storage* row,
                                                                        const FilterArgs f, FilterLds& L) {
@@ -292,15 +401,53 @@ __global__ __launch_bounds__(kFT) void row_threshold_kernel(FilterArgs f) {
     if (tid == 0) f.thr[r] = -INFINITY;
     return;
   }
+  // Top-k with k <= kListK after the chunk list kernel: the candidate list is
+  // the union of the row's chunk lists (value i in slot i / kFT of thread
+  // i % kFT), and the row is not read.  Every list entry and count read here is
+  // set back to zero.  A chunk that overflowed its list, or a union larger than
+  // the LDS list, sends the row down the path below.
+  bool listed = false;
+  uint32_t my_list = 0;
+  float lmax = -INFINITY;
+  if (f.lcount != nullptr && use_k && f.top_k <= kListK) {
+    const size_t s0 = (size_t)r * f.nch;
+    if (tid == 0) {
+      uint32_t acc = 0, ovf = 0;
+      for (int c = 0; c < f.nch; ++c) {
+        L.lpre[c] = acc;
+        const uint32_t n = f.lcount[s0 + c];
+        ovf |= n > (uint32_t)kListCap ? 1u : 0u;
+        acc += min(n, (uint32_t)kListCap);
+      }
+      L.lpre[f.nch] = acc;
+      L.lovf = ovf;
+    }
+    __syncthreads();
+    const uint32_t total = L.lpre[f.nch];
+    listed = L.lovf == 0u && total <= (uint32_t)kCap;
+    if (tid < f.nch) f.lcount[s0 + tid] = 0u;
+    int c = 0;
+    for (uint32_t i = tid, q = 0; i < total; i += kFT, ++q) {
+      while (L.lpre[c + 1] <= i) ++c;  // the chunk of entry i (i grows, so c only advances)
+      float* src = f.lvals + (s0 + c) * kListCap + (i - L.lpre[c]);
+      const float x = *src;
+      *src = 0.f;
+      if (listed) {
+        L.big.cand[q * kFT + tid] = x;
+        lmax = fmaxf(lmax, x);
+        ++my_list;
+      }
+    }
+  }
   // rows longer than the registers hold take the radix select from memory
-  bool fallback = V > kFT * kFNV * KV;
+  bool fallback = !listed && V > kFT * kFNV * KV;
 
   // the row, in registers: vector v of thread t holds tokens (v kFT + t) KV ..
   u32x4 raw[kFNV];
 #pragma unroll
   for (int v = 0; v < kFNV; ++v) {
     const int j0 = (v * kFT + tid) * KV;
-    raw[v] = fallback || j0 >= V ? u32x4{0u, 0u, 0u, 0u}
+    raw[v] = listed || fallback || j0 >= V ? u32x4{0u, 0u, 0u, 0u}
              : ALIGNED          ? load_cached(row + j0)
                                 : load_vec_scalar<E>(row, j0, V);
   }
@@ -324,10 +471,10 @@ __global__ __launch_bounds__(kFT) void row_threshold_kernel(FilterArgs f) {
 
   // ---- 1. row maximum; each thread's own maximum is kept for the top-k pivot
   float tmax = -INFINITY;
-  if (!fallback) each([&](float x) { tmax = fmaxf(tmax, x); });
+  if (!fallback && !listed) each([&](float x) { tmax = fmaxf(tmax, x); });
   float mx = -INFINITY;
   if (!fallback) {
-    mx = block_max(tmax, L.redf);
+    mx = block_max(listed ? lmax : tmax, L.redf);  // the row maximum is always listed
     fallback = mx == -INFINITY;  // no finite logit
   }
   const float k = f.k;
@@ -337,7 +484,7 @@ __global__ __launch_bounds__(kFT) void row_threshold_kernel(FilterArgs f) {
   const float c = 0.5f * k, mc = mx * c;
   auto binof = [](float t) { return (int)__builtin_amdgcn_fmed3f(t, 0.f, 15.f); };
   int lv_j = 0;     // the bin a second level refines
-  uint32_t my_n = 0;  // values this thread has in the candidate list
+  uint32_t my_n = listed ? my_list : 0u;  // values this thread has in the candidate list
 
   // One pass over the row.  Values in range are those >= lo and, at level 1,
   // those of level-0 bin lv_j; `b` is the bin at the pass's level.
@@ -564,6 +711,11 @@ __global__ __launch_bounds__(kFT) void row_threshold_kernel(FilterArgs f) {
   uint32_t n = 0;
   int j = 0;
   int state = fallback ? DONE : !use_k ? P_START : f.top_k <= kFT ? K_PIVOT : K_HIST0;
+  if (listed && !fallback) {  // the union holds every value >= tau_k
+    tau_k = select_kth((uint32_t)f.top_k, -INFINITY);
+    survivors_listed = true;
+    state = P_START;
+  }
   while (state != DONE) {
     if (state == P_START) {
       if (!use_p) {
@@ -666,13 +818,43 @@ __global__ __launch_bounds__(kFT) void row_threshold_kernel(FilterArgs f) {
 
 }  // namespace
 
-hipError_t filter_thresholds(const VerifyArgs& a, int top_k, float top_p, float* thr, hipStream_t s) {
-  FilterArgs f{a.target, a.draft, a.B * (a.gamma + 1), a.V, a.k, top_k, top_p, thr};
+size_t filter_list_bytes(int B, int gamma, int V) {
+  const size_t rows = (size_t)B * (2 * gamma + 1), nch = ((size_t)V + kLChunk - 1) / kLChunk;
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  return up(rows * nch * sizeof(uint32_t)) + up(rows * nch * kListCap * sizeof(float));
+}
+
+hipError_t filter_thresholds(const VerifyArgs& a, int top_k, float top_p, float* thr, void* lists, hipStream_t s) {
+  FilterArgs f{a.target, a.draft, a.B * (a.gamma + 1), a.V, a.k, top_k, top_p, thr, 0, nullptr, nullptr};
   const int rows = a.B * (2 * a.gamma + 1);
   if (rows == 0) return hipSuccess;
   const size_t row_bytes = (size_t)a.V * (a.dtype == SPEC_BF16 ? 2 : 4);
   const bool aligned = row_bytes % 16 == 0 && (uintptr_t)a.target % 16 == 0 &&
                        (a.gamma == 0 || (uintptr_t)a.draft % 16 == 0);
+  // chunk lists for a small top-k (the lists region is zero on entry and is
+  // left zero by the row kernel)
+  // (rows of more than 256 chunks keep to the row path: the row kernel holds
+  // at most 256 chunk offsets)
+  if (lists != nullptr && top_k > 0 && top_k <= kListK && top_k < a.V && (a.V + kLChunk - 1) / kLChunk <= 256) {
+    f.nch = (a.V + kLChunk - 1) / kLChunk;
+    f.lcount = static_cast<uint32_t*>(lists);
+    f.lvals = reinterpret_cast<float*>(static_cast<char*>(lists) +
+                                       ((rows * (size_t)f.nch * sizeof(uint32_t) + 255) & ~(size_t)255));
+    const dim3 lgrid((unsigned)(rows * f.nch)), lblock(kLT);
+    if (a.dtype == SPEC_BF16) {
+      if (aligned)
+        chunk_list_kernel<BF16, true><<<lgrid, lblock, 0, s>>>(f);
+      else
+        chunk_list_kernel<BF16, false><<<lgrid, lblock, 0, s>>>(f);
+    } else {
+      if (aligned)
+        chunk_list_kernel<F32, true><<<lgrid, lblock, 0, s>>>(f);
+      else
+        chunk_list_kernel<F32, false><<<lgrid, lblock, 0, s>>>(f);
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const dim3 grid(rows), block(kFT);
   if (a.dtype == SPEC_BF16) {
     if (aligned)

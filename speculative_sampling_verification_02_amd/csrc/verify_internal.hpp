@@ -60,7 +60,11 @@ bool fused_supported(int B, int gamma, int V, int dtype);
 
 // ---- top-k / top-p keep thresholds (filter.hip): one float per row into thr,
 // and a fill kernel that zeroes them again after the verification
-hipError_t filter_thresholds(const VerifyArgs& a, int top_k, float top_p, float* thr, hipStream_t stream);
+// Workspace of the chunk candidate lists for a top-k of at most 64 (zero on
+// entry, left zero).
+size_t filter_list_bytes(int B, int gamma, int V);
+hipError_t filter_thresholds(const VerifyArgs& a, int top_k, float top_p, float* thr, void* lists,
+                             hipStream_t stream);
 
 // ---- LM head
 // One head of the product: out[m][v] = sum_k hidden[r(m)][k] W[k][v] for

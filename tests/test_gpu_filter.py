@@ -8,6 +8,10 @@ those rows are counted and may be at most a fifth of a case's rows.  (Untied
 fp32 logits put about 1/V of the mass in each tie group, so a few percent of
 rows fall in that band by chance.)
 
+Every case also runs with the chunk-list workspace, where a top-k of at most
+64 selects from the chunks' candidate lists (rows of ties overflow the lists
+and take the row path).
+
 The cases reach every path of the threshold kernel: the register-resident
 histogram and candidate list, the survivors-only nucleus after top-k, one
 refinement level of a crossing bin too large for the list, the whole-row radix
@@ -37,7 +41,11 @@ def _banner(msg):
 
 
 def _check(dev, target, draft, dtype, T, k, p, where):
-    """target [B, G+1, V], draft [B, G, V] as float32 (bf16: already bf16-exact)."""
+    """target [B, G+1, V], draft [B, G, V] as float32 (bf16: already bf16-exact).
+    Runs without and with the chunk-list workspace (a top-k of at most 64 then
+    selects from chunk candidate lists); both must give the same thresholds,
+    checked against the oracle, and the workspace must come back zeroed."""
+    import torch
     import speculative_sampling_verification_02_amd as sv
     B, g1, V = target.shape
     if dtype == "bf16":
@@ -48,6 +56,11 @@ def _check(dev, target, draft, dtype, T, k, p, where):
     _banner(f"{where}: B={B} gamma={g1 - 1} V={V} {dtype} T={T} top_k={k} top_p={p}")
     gt, gd = sv.filter_thresholds(tt, dd, T, k, p)
     got = np.concatenate([gt.cpu().numpy().ravel(), gd.cpu().numpy().ravel()])
+    ws = torch.zeros(sv.filter_workspace_size(B, g1 - 1, V), dtype=torch.uint8, device=dev)
+    lt, ld = sv.filter_thresholds(tt, dd, T, k, p, workspace=ws)
+    got_l = np.concatenate([lt.cpu().numpy().ravel(), ld.cpu().numpy().ravel()])
+    np.testing.assert_array_equal(got_l, got, err_msg=f"{where}: list path differs")
+    assert int(torch.count_nonzero(ws)) == 0, f"{where}: workspace not left zeroed"
     rows = np.concatenate([target.reshape(-1, V), draft.reshape(-1, V)]).astype(np.float64)
     tau, margin = adjust.thresholds(rows, T, k, p)
     ok = margin >= parity.FILTER_EPS
@@ -127,7 +140,8 @@ def test_unaligned_rows(dev, dt):
 def test_rows_longer_than_the_registers(dev):
     """fp32 rows of 70000 tokens exceed the 65536 the registers hold."""
     case = W.gaussian_case(2, 2, 70000, "f32", 1.0, seed=74, target_std=2.0)
-    for k, p in ((100, 1.0), (0, 0.9), (100, 0.9)):
+    # (30, .): the chunk lists decide these rows without holding them
+    for k, p in ((100, 1.0), (0, 0.9), (100, 0.9), (30, 1.0), (30, 0.9)):
         _check(dev, case.target, case.draft, "f32", 1.0, k, p, "long f32")
 
 
