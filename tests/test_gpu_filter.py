@@ -171,3 +171,35 @@ def test_no_active_filter_keeps_every_row(dev):
     for k, p in ((0, 1.0), (256, 1.0), (-3, 1.5)):
         gt, gd = sv.filter_thresholds(tt, dd, 1.0, k, p)
         assert np.all(np.isneginf(gt.cpu().numpy())) and np.all(np.isneginf(gd.cpu().numpy()))
+
+
+@pytest.mark.parametrize("k", [1, 4, 63, 64, 65])
+def test_list_path_boundaries(dev, k):
+    """top-k at and around the largest k the chunk lists take (64), on the
+    B=64 workload's row recipe (2 sequences), with and without top-p."""
+    case = W.config3(9, 1.0, B=2)
+    t = W.bf16_bits_to_f32(case.target)
+    d = W.bf16_bits_to_f32(case.draft)
+    for p in (1.0, 0.8):
+        _check(dev, t, d, "bf16", 1.0, k, p, f"list k={k}")
+
+
+def test_list_path_with_one_overflowing_chunk(dev):
+    """Rows whose second 8192-token chunk is one repeated value next to rows
+    whose lists all fit.  Every value of such a chunk is at or above its pivot,
+    so its list overflows and the row takes the row path; the other rows take
+    the lists, in the same launch."""
+    rng = np.random.default_rng(79)
+    V = 40000
+    x = rng.standard_normal((3, 3, V)).astype(np.float32) * 2.0
+    x[0, 1, 8192:16384] = 7.5            # above the rest of the row: the top-k is one tie group
+    x[1, 0, 8192:16384] = -1.0           # inside the body of the row
+    x = _bf16(x)
+    for k, p in ((10, 1.0), (50, 0.9), (64, 1.0)):
+        _check(dev, x, x[:, :2].copy(), "bf16", 1.0, k, p, f"overflow chunk k={k}")
+
+
+def test_list_path_unaligned_f32(dev):
+    case = W.gaussian_case(2, 2, 20011, "f32", 1.0, seed=80, target_std=3.0)
+    for k, p in ((7, 1.0), (40, 0.7)):
+        _check(dev, case.target, case.draft, "f32", 1.0, k, p, f"unaligned f32 k={k}")
