@@ -221,64 +221,62 @@ __global__ __launch_bounds__(kLT) void chunk_list_kernel(FilterArgs f) {
     const int j0 = lo + (v * kLT + tid) * KV;
     cur[v] = j0 >= V ? u32x4{0u, 0u, 0u, 0u} : ALIGNED ? load_stream(row + j0) : load_vec_scalar<E>(row, j0, V);
   }
-  {
-    float x[NV * KV];
+  float x[NV * KV];
 #pragma unroll
-    for (int v = 0; v < NV; ++v) {
-      const int j0 = lo + (v * kLT + tid) * KV;
-      float t[KV];
-      E::unpack(cur[v], t);
+  for (int v = 0; v < NV; ++v) {
+    const int j0 = lo + (v * kLT + tid) * KV;
+    float t[KV];
+    E::unpack(cur[v], t);
 #pragma unroll
-      for (int e = 0; e < KV; ++e) x[v * KV + e] = j0 + e < V ? t[e] : -INFINITY;
+    for (int e = 0; e < KV; ++e) x[v * KV + e] = j0 + e < V ? t[e] : -INFINITY;
+  }
+  // element i of this thread lies in the row (the last chunk may end early)
+  auto in_row = [&](int i) { return lo + ((i / KV) * kLT + tid) * KV + i % KV < V; };
+  float tm = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < NV * KV; ++i) tm = fmaxf(tm, x[i]);
+  // the wave's thread maxima in descending order across the lanes (bitonic)
+  float srt = tm;
+#pragma unroll
+  for (int k2 = 2; k2 <= kWave; k2 <<= 1) {
+#pragma unroll
+    for (int j = k2 >> 1; j > 0; j >>= 1) {
+      const float o = __shfl_xor(srt, j);
+      srt = (((lane & k2) == 0) == ((lane & j) == 0)) ? fmaxf(srt, o) : fminf(srt, o);
     }
-    // element i of this thread lies in the row (the last chunk may end early)
-    auto in_row = [&](int i) { return lo + ((i / KV) * kLT + tid) * KV + i % KV < V; };
-    float tm = -INFINITY;
+  }
+  const int m = (f.top_k + NW - 1) / NW;  // <= kListK / 4 <= kWave
+  const float mth = __shfl(srt, m - 1);
+  if (lane == 0) wm[wid] = mth;
+  __syncthreads();
+  float pivot = wm[0];
 #pragma unroll
-    for (int i = 0; i < NV * KV; ++i) tm = fmaxf(tm, x[i]);
-    // the wave's thread maxima in descending order across the lanes (bitonic)
-    float srt = tm;
+  for (int q = 1; q < NW; ++q) pivot = fminf(pivot, wm[q]);
+  uint32_t c = 0;
 #pragma unroll
-    for (int k2 = 2; k2 <= kWave; k2 <<= 1) {
+  for (int i = 0; i < NV * KV; ++i) c += in_row(i) && x[i] >= pivot ? 1u : 0u;
+  // offsets: inclusive scan within the wave, then the waves' totals
+  uint32_t incl = c;
 #pragma unroll
-      for (int j = k2 >> 1; j > 0; j >>= 1) {
-        const float o = __shfl_xor(srt, j);
-        srt = (((lane & k2) == 0) == ((lane & j) == 0)) ? fmaxf(srt, o) : fminf(srt, o);
-      }
-    }
-    const int m = (f.top_k + NW - 1) / NW;  // <= kListK / 4 <= kWave
-    const float mth = __shfl(srt, m - 1);
-    if (lane == 0) wm[wid] = mth;
-    __syncthreads();
-    float pivot = wm[0];
+  for (int off = 1; off < kWave; off <<= 1) {
+    const uint32_t o = (uint32_t)__shfl_up((int)incl, off);
+    if (lane >= off) incl += o;
+  }
+  if (lane == kWave - 1) wsum[wid] = incl;
+  __syncthreads();
+  uint32_t base = 0, total = 0;
 #pragma unroll
-    for (int q = 1; q < NW; ++q) pivot = fminf(pivot, wm[q]);
-    uint32_t c = 0;
+  for (int q = 0; q < NW; ++q) {
+    base += q < wid ? wsum[q] : 0u;
+    total += wsum[q];
+  }
+  if (tid == 0) f.lcount[w] = total <= (uint32_t)kListCap ? total : (uint32_t)kListCap + 1u;
+  if (total <= (uint32_t)kListCap) {
+    uint32_t o = base + incl - c;
+    float* out = f.lvals + (size_t)w * kListCap;
 #pragma unroll
-    for (int i = 0; i < NV * KV; ++i) c += in_row(i) && x[i] >= pivot ? 1u : 0u;
-    // offsets: inclusive scan within the wave, then the waves' totals
-    uint32_t incl = c;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      const uint32_t o = (uint32_t)__shfl_up((int)incl, off);
-      if (lane >= off) incl += o;
-    }
-    if (lane == kWave - 1) wsum[wid] = incl;
-    __syncthreads();
-    uint32_t base = 0, total = 0;
-#pragma unroll
-    for (int q = 0; q < NW; ++q) {
-      base += q < wid ? wsum[q] : 0u;
-      total += wsum[q];
-    }
-    if (tid == 0) f.lcount[w] = total <= (uint32_t)kListCap ? total : (uint32_t)kListCap + 1u;
-    if (total <= (uint32_t)kListCap) {
-      uint32_t o = base + incl - c;
-      float* out = f.lvals + (size_t)w * kListCap;
-#pragma unroll
-      for (int i = 0; i < NV * KV; ++i) {
-        if (in_row(i) && x[i] >= pivot) out[o++] = x[i];
-      }
+    for (int i = 0; i < NV * KV; ++i) {
+      if (in_row(i) && x[i] >= pivot) out[o++] = x[i];
     }
   }
 }
