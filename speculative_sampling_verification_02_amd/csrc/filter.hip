@@ -72,6 +72,7 @@ struct FilterArgs {
   int nch;             // chunks of kLChunk tokens per row
   uint32_t* lcount;    // [rows][nch] listed values, kListCap + 1 on overflow
   float* lvals;        // [rows][nch][kListCap]
+  int marked_only;     // row kernel: only rows whose threshold holds kMarkedBits
 };
 
 // Chunk candidate lists for top-k with k <= kListK.  A streaming kernel lists,
@@ -81,6 +82,9 @@ struct FilterArgs {
 // above it would hold k larger values), so the exact selection runs on the
 // union instead of the row.
 constexpr int kListK = 64;
+// threshold word of a row the list-fed kernel leaves to the row kernel (a NaN
+// pattern; a threshold is a logit or -inf)
+constexpr uint32_t kMarkedBits = 0x7fc0beefu;
 constexpr int kListCap = 256;
 constexpr int kLT = 256;           // threads of the list kernel
 constexpr int kLChunk = kLT * 32;  // tokens per chunk
@@ -104,8 +108,6 @@ struct FilterLds {
   uint32_t kmin_s, kmax_s;
   unsigned long long above_s;
   double target_s;
-  uint32_t lpre[257];  // exclusive prefix of the row's chunk list counts
-  uint32_t lovf;
 };
 
 // Order-preserving unsigned key of a finite or -inf logit (-0 as +0), in the
@@ -384,6 +386,187 @@ __device__ __attribute__((always_inline)) inline float radix_threshold(const typ
 
 // ALIGNED: 16-byte aligned rows of whole vectors (V a multiple of the vector
 // width); otherwise elements are loaded one by one and checked against V.
+// The radix pick of the threshold kernels (see the row kernel): over the
+// listed values >= lo, slot q of thread t at cand[q NT + t], my_n of them in
+// this thread's column.  Called by all NT threads of the workgroup.
+template <class E, int NT, bool MASS, class LdsT>
+__device__ __attribute__((always_inline)) inline float list_pick(LdsT& L, const float* cand, uint32_t my_n, float lo,
+                                                               double base, double need, float mx, float k,
+                                                               float top_p) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+  constexpr int KB = std::is_same<E, BF16>::value ? 16 : 32;
+  // key range of the listed values >= lo
+  if (tid == 0) {
+    L.kmin_s = 0xffffffffu;
+    L.kmax_s = 0u;
+  }
+  __syncthreads();
+  uint32_t kmn = 0xffffffffu, kmx = 0u;
+  for (uint32_t q = 0; q < my_n; ++q) {  // this thread's column of the list
+    const float x = cand[q * NT + tid];
+    if (x >= lo) {
+      const uint32_t key = key_of<KB>(x);
+      kmn = min(kmn, key);
+      kmx = max(kmx, key);
+    }
+  }
+#pragma unroll
+  for (int off = kWave / 2; off >= 1; off >>= 1) {
+    kmn = min(kmn, (uint32_t)__shfl_xor((int)kmn, off));
+    kmx = max(kmx, (uint32_t)__shfl_xor((int)kmx, off));
+  }
+  if (lane == 0) {
+    atomicMin(&L.kmin_s, kmn);
+    atomicMax(&L.kmax_s, kmx);
+  }
+  __syncthreads();
+  const uint32_t kmin = L.kmin_s, span = L.kmax_s - L.kmin_s;
+  const int nbits = span ? 32 - __clz((int)span) : 0;
+  uint32_t prefix = 0;  // chosen high bits of (key - kmin)
+  // each pass picks bits [shift, hi) of (key - kmin), hi falling from nbits
+  // to 0; a span of one key still takes one pass (the mass total).  The
+  // bins are double-buffered: a pass clears the next pass's set, so it
+  // needs only the barrier after its additions and the one after the pick.
+  if (tid < 256) {
+    if constexpr (MASS) L.pmass[0][tid] = 0ull;
+    else L.pcnt[0][tid] = 0u;
+  }
+  __syncthreads();
+  int hi = nbits, buf = 0;
+  do {
+    const int shift = hi > 8 ? hi - 8 : 0;
+    const uint32_t hi_mask = hi >= 32 ? 0u : ~0u << hi;
+    const uint32_t dmask = (1u << (hi - shift)) - 1u;
+    if (tid < 256) {
+      if constexpr (MASS) L.pmass[buf ^ 1][tid] = 0ull;
+      else L.pcnt[buf ^ 1][tid] = 0u;
+    }
+    for (uint32_t q = 0; q < my_n; ++q) {
+      const float x = cand[q * NT + tid];
+      const uint32_t d = key_of<KB>(x) - kmin;
+      if (x >= lo && (d & hi_mask) == prefix) {
+        if constexpr (MASS)
+          atomicAdd(&L.pmass[buf][(d >> shift) & dmask], fixed_mass(__builtin_amdgcn_exp2f((x - mx) * k)));
+        else
+          atomicAdd(&L.pcnt[buf][(d >> shift) & dmask], 1u);
+      }
+    }
+    __syncthreads();
+    auto binv = [&](int b) -> double {
+      if constexpr (MASS) return (double)L.pmass[buf][b] / kMassScale;
+      else return (double)L.pcnt[buf][b];
+    };
+    if (wid == 0) {
+      if constexpr (MASS) {
+        if (need < 0.0) {  // top_p of the listed total (wave 0 only needs it)
+          double s = 0.0;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) s += (double)L.pmass[buf][lane * 4 + i];
+          need = (double)top_p * (wave_sum(s) / kMassScale);
+          base = 0.0;
+        }
+      }
+      double before;
+      int b = wave_pick_desc(binv, need - base, &before);
+      if (b < 0) {
+        // the list's total fell short of need by rounding (the fixed-point
+        // list against the histogram's fp64 sum): keep all of this prefix
+        b = 0;
+        before = 0.0;
+        for (int q = 255; q >= 0; --q) {
+          if (binv(q) > 0.0) {
+            b = q;
+            break;
+          }
+        }
+        for (int q = 255; q > b; --q) before += binv(q);
+      }
+      if (lane == 0) {
+        L.pick_b = b;
+        L.pick_before = before;
+      }
+    }
+    __syncthreads();  // every read of this pass's bins is done
+    base += L.pick_before;
+    prefix |= (uint32_t)L.pick_b << shift;
+    hi = shift;
+    buf ^= 1;
+  } while (hi > 0);
+  return value_of<KB>(kmin + prefix);
+}
+
+// The thresholds of the rows whose chunk lists all fit, from the lists alone
+// (one 256-thread workgroup per row, about 40 KB of LDS, so every row of a
+// batch is resident at once).  The union of a row's lists, value i in slot
+// i / kLTT of thread i % kLTT, holds every value >= the row's k-th largest,
+// and with it the row maximum: the exact k-th largest and, with top-p, the
+// nucleus of the survivors are the row kernel's own picks on the union, so
+// the thresholds are those of the row path.  Every list entry and count is set
+// back to zero.  A row with an overflowed chunk, more listed values than the
+// LDS holds, or no finite value gets kMarkedBits for the row kernel.
+constexpr int kLTT = 256;
+constexpr int kListSlots = 8192;
+struct ListLds {
+  float cand[kListSlots];
+  uint32_t pcnt[2][256];
+  unsigned long long pmass[2][256];
+  float redf[2 * kMaxWaves];
+  uint32_t kmin_s, kmax_s;
+  int pick_b;
+  double pick_before;
+  uint32_t lpre[257];  // exclusive prefix of the row's chunk list counts
+  uint32_t lovf;
+};
+
+template <class E>
+__global__ __launch_bounds__(kLTT) void list_threshold_kernel(FilterArgs f) {
+  __shared__ ListLds L;
+  const int tid = threadIdx.x, r = blockIdx.x;
+  const size_t s0 = (size_t)r * f.nch;
+  if (tid == 0) {
+    uint32_t acc = 0, ovf = 0;
+    for (int c = 0; c < f.nch; ++c) {
+      L.lpre[c] = acc;
+      const uint32_t n = f.lcount[s0 + c];
+      ovf |= n > (uint32_t)kListCap ? 1u : 0u;
+      acc += min(n, (uint32_t)kListCap);
+    }
+    L.lpre[f.nch] = acc;
+    L.lovf = ovf;
+  }
+  __syncthreads();
+  const uint32_t total = L.lpre[f.nch];
+  const bool listed = L.lovf == 0u && total <= (uint32_t)kListSlots;
+  if (tid < f.nch) f.lcount[s0 + tid] = 0u;
+  uint32_t my_n = 0;
+  float lmax = -INFINITY;
+  int c = 0;
+  for (uint32_t i = tid, q = 0; i < total; i += kLTT, ++q) {
+    while (L.lpre[c + 1] <= i) ++c;  // the chunk of entry i (i grows, so c only advances)
+    float* src = f.lvals + (s0 + c) * kListCap + (i - L.lpre[c]);
+    const float x = *src;
+    *src = 0.f;
+    if (listed) {
+      L.cand[q * kLTT + tid] = x;
+      lmax = fmaxf(lmax, x);
+      ++my_n;
+    }
+  }
+  if (!listed) {
+    if (tid == 0) f.thr[r] = __uint_as_float(kMarkedBits);
+    return;
+  }
+  const float mx = block_max(lmax, L.redf);  // the row maximum
+  if (mx == -INFINITY) {
+    if (tid == 0) f.thr[r] = __uint_as_float(kMarkedBits);
+    return;
+  }
+  const float tau_k = list_pick<E, kLTT, false>(L, L.cand, my_n, -INFINITY, 0.0, (double)f.top_k, mx, f.k, f.top_p);
+  float tau_p = -INFINITY;
+  if (f.top_p < 1.f) tau_p = list_pick<E, kLTT, true>(L, L.cand, my_n, tau_k, 0.0, -1.0, mx, f.k, f.top_p);
+  if (tid == 0) f.thr[r] = fmaxf(tau_k, tau_p);
+}
+
 template <class E, bool ALIGNED>
 __global__ __launch_bounds__(kFT) void row_threshold_kernel(FilterArgs f) {
   constexpr int KV = E::kVec;
@@ -399,53 +582,17 @@ __global__ __launch_bounds__(kFT) void row_threshold_kernel(FilterArgs f) {
     if (tid == 0) f.thr[r] = -INFINITY;
     return;
   }
-  // Top-k with k <= kListK after the chunk list kernel: the candidate list is
-  // the union of the row's chunk lists (value i in slot i / kFT of thread
-  // i % kFT), and the row is not read.  Every list entry and count read here is
-  // set back to zero.  A chunk that overflowed its list, or a union larger than
-  // the LDS list, sends the row down the path below.
-  bool listed = false;
-  uint32_t my_list = 0;
-  float lmax = -INFINITY;
-  if (f.lcount != nullptr && use_k && f.top_k <= kListK) {
-    const size_t s0 = (size_t)r * f.nch;
-    if (tid == 0) {
-      uint32_t acc = 0, ovf = 0;
-      for (int c = 0; c < f.nch; ++c) {
-        L.lpre[c] = acc;
-        const uint32_t n = f.lcount[s0 + c];
-        ovf |= n > (uint32_t)kListCap ? 1u : 0u;
-        acc += min(n, (uint32_t)kListCap);
-      }
-      L.lpre[f.nch] = acc;
-      L.lovf = ovf;
-    }
-    __syncthreads();
-    const uint32_t total = L.lpre[f.nch];
-    listed = L.lovf == 0u && total <= (uint32_t)kCap;
-    if (tid < f.nch) f.lcount[s0 + tid] = 0u;
-    int c = 0;
-    for (uint32_t i = tid, q = 0; i < total; i += kFT, ++q) {
-      while (L.lpre[c + 1] <= i) ++c;  // the chunk of entry i (i grows, so c only advances)
-      float* src = f.lvals + (s0 + c) * kListCap + (i - L.lpre[c]);
-      const float x = *src;
-      *src = 0.f;
-      if (listed) {
-        L.big.cand[q * kFT + tid] = x;
-        lmax = fmaxf(lmax, x);
-        ++my_list;
-      }
-    }
-  }
+  // after the list-fed kernel: only the rows it marked
+  if (f.marked_only && __float_as_uint(f.thr[r]) != kMarkedBits) return;
   // rows longer than the registers hold take the radix select from memory
-  bool fallback = !listed && V > kFT * kFNV * KV;
+  bool fallback = V > kFT * kFNV * KV;
 
   // the row, in registers: vector v of thread t holds tokens (v kFT + t) KV ..
   u32x4 raw[kFNV];
 #pragma unroll
   for (int v = 0; v < kFNV; ++v) {
     const int j0 = (v * kFT + tid) * KV;
-    raw[v] = listed || fallback || j0 >= V ? u32x4{0u, 0u, 0u, 0u}
+    raw[v] = fallback || j0 >= V ? u32x4{0u, 0u, 0u, 0u}
              : ALIGNED          ? load_cached(row + j0)
                                 : load_vec_scalar<E>(row, j0, V);
   }
@@ -469,10 +616,10 @@ __global__ __launch_bounds__(kFT) void row_threshold_kernel(FilterArgs f) {
 
   // ---- 1. row maximum; each thread's own maximum is kept for the top-k pivot
   float tmax = -INFINITY;
-  if (!fallback && !listed) each([&](float x) { tmax = fmaxf(tmax, x); });
+  if (!fallback) each([&](float x) { tmax = fmaxf(tmax, x); });
   float mx = -INFINITY;
   if (!fallback) {
-    mx = block_max(listed ? lmax : tmax, L.redf);  // the row maximum is always listed
+    mx = block_max(tmax, L.redf);
     fallback = mx == -INFINITY;  // no finite logit
   }
   const float k = f.k;
@@ -482,7 +629,7 @@ __global__ __launch_bounds__(kFT) void row_threshold_kernel(FilterArgs f) {
   const float c = 0.5f * k, mc = mx * c;
   auto binof = [](float t) { return (int)__builtin_amdgcn_fmed3f(t, 0.f, 15.f); };
   int lv_j = 0;     // the bin a second level refines
-  uint32_t my_n = listed ? my_list : 0u;  // values this thread has in the candidate list
+  uint32_t my_n = 0;  // values this thread has in the candidate list
 
   // One pass over the row.  Values in range are those >= lo and, at level 1,
   // those of level-0 bin lv_j; `b` is the bin at the pass's level.
@@ -591,106 +738,7 @@ __global__ __launch_bounds__(kFT) void row_threshold_kernel(FilterArgs f) {
   // LDS atomics) and a list of close values needs few passes.  Keys are the
   // 16 significant bits for bf16 rows (the list holds widened bf16 values).
   auto pick = [&](auto mass_c, float lo, double base, double need) -> float {
-    constexpr bool MASS = decltype(mass_c)::value;
-    constexpr int KB = std::is_same<E, BF16>::value ? 16 : 32;
-    // key range of the listed values >= lo
-    if (tid == 0) {
-      L.kmin_s = 0xffffffffu;
-      L.kmax_s = 0u;
-    }
-    __syncthreads();
-    uint32_t kmn = 0xffffffffu, kmx = 0u;
-    for (uint32_t q = 0; q < my_n; ++q) {  // this thread's column of the list
-      const float x = L.big.cand[q * kFT + tid];
-      if (x >= lo) {
-        const uint32_t key = key_of<KB>(x);
-        kmn = min(kmn, key);
-        kmx = max(kmx, key);
-      }
-    }
-#pragma unroll
-    for (int off = kWave / 2; off >= 1; off >>= 1) {
-      kmn = min(kmn, (uint32_t)__shfl_xor((int)kmn, off));
-      kmx = max(kmx, (uint32_t)__shfl_xor((int)kmx, off));
-    }
-    if (lane == 0) {
-      atomicMin(&L.kmin_s, kmn);
-      atomicMax(&L.kmax_s, kmx);
-    }
-    __syncthreads();
-    const uint32_t kmin = L.kmin_s, span = L.kmax_s - L.kmin_s;
-    const int nbits = span ? 32 - __clz((int)span) : 0;
-    uint32_t prefix = 0;  // chosen high bits of (key - kmin)
-    // each pass picks bits [shift, hi) of (key - kmin), hi falling from nbits
-    // to 0; a span of one key still takes one pass (the mass total).  The
-    // bins are double-buffered: a pass clears the next pass's set, so it
-    // needs only the barrier after its additions and the one after the pick.
-    if (tid < 256) {
-      if constexpr (MASS) L.pmass[0][tid] = 0ull;
-      else L.pcnt[0][tid] = 0u;
-    }
-    __syncthreads();
-    int hi = nbits, buf = 0;
-    do {
-      const int shift = hi > 8 ? hi - 8 : 0;
-      const uint32_t hi_mask = hi >= 32 ? 0u : ~0u << hi;
-      const uint32_t dmask = (1u << (hi - shift)) - 1u;
-      if (tid < 256) {
-        if constexpr (MASS) L.pmass[buf ^ 1][tid] = 0ull;
-        else L.pcnt[buf ^ 1][tid] = 0u;
-      }
-      for (uint32_t q = 0; q < my_n; ++q) {
-        const float x = L.big.cand[q * kFT + tid];
-        const uint32_t d = key_of<KB>(x) - kmin;
-        if (x >= lo && (d & hi_mask) == prefix) {
-          if constexpr (MASS)
-            atomicAdd(&L.pmass[buf][(d >> shift) & dmask], fixed_mass(__builtin_amdgcn_exp2f((x - mx) * k)));
-          else
-            atomicAdd(&L.pcnt[buf][(d >> shift) & dmask], 1u);
-        }
-      }
-      __syncthreads();
-      auto binv = [&](int b) -> double {
-        if constexpr (MASS) return (double)L.pmass[buf][b] / kMassScale;
-        else return (double)L.pcnt[buf][b];
-      };
-      if (wid == 0) {
-        if constexpr (MASS) {
-          if (need < 0.0) {  // top_p of the listed total (wave 0 only needs it)
-            double s = 0.0;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) s += (double)L.pmass[buf][lane * 4 + i];
-            need = (double)f.top_p * (wave_sum(s) / kMassScale);
-            base = 0.0;
-          }
-        }
-        double before;
-        int b = wave_pick_desc(binv, need - base, &before);
-        if (b < 0) {
-          // the list's total fell short of need by rounding (the fixed-point
-          // list against the histogram's fp64 sum): keep all of this prefix
-          b = 0;
-          before = 0.0;
-          for (int q = 255; q >= 0; --q) {
-            if (binv(q) > 0.0) {
-              b = q;
-              break;
-            }
-          }
-          for (int q = 255; q > b; --q) before += binv(q);
-        }
-        if (lane == 0) {
-          L.pick_b = b;
-          L.pick_before = before;
-        }
-      }
-      __syncthreads();  // every read of this pass's bins is done
-      base += L.pick_before;
-      prefix |= (uint32_t)L.pick_b << shift;
-      hi = shift;
-      buf ^= 1;
-    } while (hi > 0);
-    return value_of<KB>(kmin + prefix);
+    return list_pick<E, kFT, decltype(mass_c)::value>(L, L.big.cand, my_n, lo, base, need, mx, k, f.top_p);
   };
   using BF = std::integral_constant<bool, false>;
   using BT = std::integral_constant<bool, true>;
@@ -709,11 +757,6 @@ __global__ __launch_bounds__(kFT) void row_threshold_kernel(FilterArgs f) {
   uint32_t n = 0;
   int j = 0;
   int state = fallback ? DONE : !use_k ? P_START : f.top_k <= kFT ? K_PIVOT : K_HIST0;
-  if (listed && !fallback) {  // the union holds every value >= tau_k
-    tau_k = select_kth((uint32_t)f.top_k, -INFINITY);
-    survivors_listed = true;
-    state = P_START;
-  }
   while (state != DONE) {
     if (state == P_START) {
       if (!use_p) {
@@ -823,7 +866,7 @@ size_t filter_list_bytes(int B, int gamma, int V) {
 }
 
 hipError_t filter_thresholds(const VerifyArgs& a, int top_k, float top_p, float* thr, void* lists, hipStream_t s) {
-  FilterArgs f{a.target, a.draft, a.B * (a.gamma + 1), a.V, a.k, top_k, top_p, thr, 0, nullptr, nullptr};
+  FilterArgs f{a.target, a.draft, a.B * (a.gamma + 1), a.V, a.k, top_k, top_p, thr, 0, nullptr, nullptr, 0};
   const int rows = a.B * (2 * a.gamma + 1);
   if (rows == 0) return hipSuccess;
   const size_t row_bytes = (size_t)a.V * (a.dtype == SPEC_BF16 ? 2 : 4);
@@ -852,6 +895,16 @@ hipError_t filter_thresholds(const VerifyArgs& a, int top_k, float top_p, float*
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (a.dtype == SPEC_BF16)
+      list_threshold_kernel<BF16><<<dim3(rows), dim3(kLTT), 0, s>>>(f);
+    else
+      list_threshold_kernel<F32><<<dim3(rows), dim3(kLTT), 0, s>>>(f);
+    const hipError_t e2 = hipGetLastError();
+    if (e2 != hipSuccess) return e2;
+    // the row kernel takes only the rows the lists left to it
+    f.marked_only = 1;
+    f.lcount = nullptr;
+    f.lvals = nullptr;
   }
   const dim3 grid(rows), block(kFT);
   if (a.dtype == SPEC_BF16) {
