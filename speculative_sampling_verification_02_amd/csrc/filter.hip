@@ -12,6 +12,12 @@
 // and the row keeps logit >= max(tau_k, tau_p).  The verification kernels then
 // read a dropped logit as -inf.
 //
+// With a workspace and top-k <= 64, three kernels: a streaming kernel lists
+// each 8192-token chunk's values at or above a pivot the chunk has k values
+// above (their union holds every value >= tau_k), a list-fed kernel (256
+// threads per row) runs the exact pick below on the union, and the row kernel
+// takes only the rows whose lists overflowed.  Otherwise the row kernel alone:
+//
 // One workgroup of 1024 threads per row, with the row held in registers (one
 // read from memory).  Every pass over the row is a few instructions per token:
 //   1. the row maximum (each thread keeps its own maximum too);
