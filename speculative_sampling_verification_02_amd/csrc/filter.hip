@@ -243,18 +243,17 @@ __global__ __launch_bounds__(kLT) void chunk_list_kernel(FilterArgs f) {
   float tm = -INFINITY;
 #pragma unroll
   for (int i = 0; i < NV * KV; ++i) tm = fmaxf(tm, x[i]);
-  // the wave's thread maxima in descending order across the lanes (bitonic)
-  float srt = tm;
-#pragma unroll
-  for (int k2 = 2; k2 <= kWave; k2 <<= 1) {
-#pragma unroll
-    for (int j = k2 >> 1; j > 0; j >>= 1) {
-      const float o = __shfl_xor(srt, j);
-      srt = (((lane & k2) == 0) == ((lane & j) == 0)) ? fmaxf(srt, o) : fminf(srt, o);
-    }
-  }
+  // the m-th largest of the wave's thread maxima: the largest key K with at
+  // least m keys >= K, bit by bit from the top (one ballot per bit)
   const int m = (f.top_k + NW - 1) / NW;  // <= kListK / 4 <= kWave
-  const float mth = __shfl(srt, m - 1);
+  const uint32_t key = key_of<32>(tm);
+  uint32_t pre = 0;
+#pragma unroll
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t t = pre | (1u << b);
+    if (__popcll(__ballot(key >= t)) >= m) pre = t;
+  }
+  const float mth = value_of<32>(pre);
   if (lane == 0) wm[wid] = mth;
   __syncthreads();
   float pivot = wm[0];
