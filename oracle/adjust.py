@@ -24,22 +24,11 @@ Readings taken where the pages are silent (each is listed in the design notes):
     dropped tokens get logit -inf, i.e. probability 0.
   * In argmax mode (T = 0) the filters change nothing: the argmax group is
     always kept.
-  * Precision of the nucleus decision.  Whether a tie group is kept is a
-    discrete outcome decided by comparing sums of floating-point weights with
-    top_p, so it is taken here in the same arithmetic as the GPU kernel:
-    weights exp2((l - m) k) in fp32 (l - m and the product by k = log2(e)/T
-    each rounded to fp32, m the row maximum), each rounded to a multiple of
-    2^-40 and summed exactly, then compared in fp64 with top_p times the total.
-    The kernel's exp2 may differ from the correctly rounded one by an ulp; the
-    returned margin says how close a row's decision came.
 """
 
 from __future__ import annotations
 
 import numpy as np
-
-LOG2E_F32 = np.float32(1.4426950408889634)
-MASS_SCALE = 2.0 ** 40
 
 
 def topk_threshold(row: np.ndarray, k: int) -> float:
@@ -53,29 +42,27 @@ def topk_threshold(row: np.ndarray, k: int) -> float:
 def topp_threshold(row: np.ndarray, temperature: float, top_p: float, tau_k: float = -np.inf):
     """Logit threshold of the nucleus of softmax(row / T) restricted to row >= tau_k.
 
+    The tie groups (equal logits) are walked from the most likely down, and
+    the walk stops at the first group where the cumulative mass, normalised
+    over the kept tokens, reaches top_p; that group's logit is the threshold.
+
     Returns (tau_p, margin): tau_p is the smallest logit kept; margin is the
-    distance of top_p from the nearest cumulative mass the decision compares it
-    with (the sum before and after the boundary tie group), so a margin below
-    the GPU's rounding marks a row whose kept set fp32 may legitimately choose
-    differently."""
+    distance of top_p from the two cumulative masses the decision compares it
+    with (the sum before and after the boundary tie group), as a fraction of
+    the total.  A decision taken in other arithmetic can only differ when its
+    error in those normalised sums reaches the margin."""
     if top_p >= 1.0 or temperature <= 0.0:
         return -np.inf, np.inf
-    m = np.float32(row.max())                                   # the whole row's maximum
     kept = row[(row >= tau_k) & (row != -np.inf)]
     vals, counts = np.unique(kept, return_counts=True)          # ascending distinct logits
     vals, counts = vals[::-1], counts[::-1]                      # descending
-    k32 = np.float32(LOG2E_F32 / np.float32(temperature))
-    arg = (vals.astype(np.float32) - m) * k32                   # fp32, two roundings
-    w32 = np.exp2(arg.astype(np.float64)).astype(np.float32)
-    fixed = np.floor(w32.astype(np.float64) * MASS_SCALE + 0.5).astype(np.uint64)
-    cum = np.cumsum(fixed * counts.astype(np.uint64))           # exact integer sums
-    total = float(cum[-1])
-    target = float(np.float32(top_p)) * total
-    cumf = cum.astype(np.float64)
-    hit = cumf >= target
+    m = vals[0]
+    w = counts * np.exp((vals - m) / temperature)                # mass of each tie group
+    cum = np.cumsum(w) / w.sum()
+    hit = cum >= top_p
     j = int(np.argmax(hit)) if hit.any() else len(cum) - 1
-    before = cumf[j - 1] if j > 0 else 0.0
-    margin = min(abs(cumf[j] - target), abs(target - before)) / total
+    before = cum[j - 1] if j > 0 else 0.0
+    margin = min(abs(cum[j] - top_p), abs(top_p - before))
     return float(vals[j]), float(margin)
 
 

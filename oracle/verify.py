@@ -26,11 +26,10 @@ draft rows q_0..q_{gamma-1}, drafted tokens x_0..x_{gamma-1}):
 Readings taken where the pages are silent (each is listed in the design notes):
   * u_gamma is a fresh uniform for the final sample; the rejecting u_n is not reused.
   * `sample()` is the inverse CDF with a strict ">" in token-index order.
-  * A residual with no mass falls back to p_n.  In exact arithmetic that needs
-    p_n = q_n (then only a draft outside the support, 0/0, is rejected); the
-    GPU computes p and q in fp32, where rows that agree leave a residual of
-    rounding noise, so a mass at most RESIDUAL_FLOOR = 2^-20 (of p_n's total)
-    counts as none on both sides.
+  * A residual with no mass falls back to p_n ([LH] "Three candidates explain
+    the acceptance rule": a zero-mass residual is never normalised).  In exact
+    arithmetic that needs p_n = q_n, where only a draft outside the support
+    (0/0) is rejected.  Any positive mass, however small, is sampled.
   * Argmax ties go to the lowest token index; alpha in argmax mode is the
     indicator that the two argmaxes agree.
   * alpha is reported for every draft position, whatever n is.
@@ -55,19 +54,16 @@ Two extensions, both off by default:
 
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
 
 import numpy as np
 
 from oracle import adjust
 
-# |u_i - min(1, p_i(x_i)/q_i(x_i))| below this marks a decision that fp32 on the
-# GPU and fp64 here may take differently.
+# |u_i - min(1, p_i(x_i)/q_i(x_i))| below this marks an accept decision that
+# other arithmetic may take differently; such sequences are flagged (u_band).
 U_BAND = 1e-6
-
-# A residual max(0, p - l q) with at most this mass is taken as empty (reading
-# above): the token is then drawn from p_n.
-RESIDUAL_FLOOR = 2.0 ** -20
 
 
 # ------------------------------------------------------------------ step 0
@@ -162,6 +158,23 @@ def inverse_cdf(probs: np.ndarray, u: np.ndarray):
     return token, cdf
 
 
+# ------------------------------------------------- decision margins
+#
+# How close each discrete decision came to going the other way, for comparing
+# with results computed in other arithmetic.  They change no result.
+
+def in_u_band(u: np.ndarray, capped: np.ndarray) -> np.ndarray:
+    """Accept tests whose uniform lies within U_BAND of min(1, ratio)."""
+    with np.errstate(invalid="ignore"):
+        return np.abs(u - capped) < U_BAND
+
+
+def cdf_margin(cdf: np.ndarray, u: np.ndarray) -> np.ndarray:
+    """min_j |cdf_j - u| per row: the distance of the uniform from the nearest
+    step of the sampled row's normalised cumulative weights."""
+    return np.abs(cdf - u[:, None]).min(axis=-1)
+
+
 # ------------------------------------------------------------ whole step
 
 @dataclasses.dataclass
@@ -178,6 +191,10 @@ class Result:
     weights: np.ndarray | None  # float64 [B, V] normalised sampling row, if requested
     filter_margin: np.ndarray | None = None  # float64 [B]: smallest top-p margin of the sequence's rows
     res_mass: np.ndarray | None = None  # float64 [B]: mass of the residual after a rejection, else NaN
+    # per row (target rows 0..gamma, then draft rows 0..gamma-1) with top-k /
+    # top-p: the keep threshold and the nucleus margin; None without filters
+    filter_tau: np.ndarray | None = None      # float64 [B, 2 gamma + 1]
+    filter_margins: np.ndarray | None = None  # float64 [B, 2 gamma + 1]
 
 
 def _verify_block(target, draft, tokens, u, temperature, dtype, keep_weights, lenience=1.0, gseq=None,
@@ -198,12 +215,15 @@ def _verify_block(target, draft, tokens, u, temperature, dtype, keep_weights, le
         tl = np.where((np.arange(g1)[None, :] <= gb[:, None])[..., None], tl, 0.0)
         dl = np.where(live[..., None], dl, 0.0)
     fmargin = np.full(nb, np.inf)
+    ftau = fmg = None
     if temperature > 0.0 and ((0 < top_k < V) or top_p < 1.0):
         # top-k / top-p adjust p and q the same way before anything else
         tau_t, mg_t = adjust.thresholds(tl, temperature, top_k, top_p)
         tau_d, mg_d = adjust.thresholds(dl, temperature, top_k, top_p)
         tl, dl = adjust.apply(tl, tau_t), adjust.apply(dl, tau_d)
         fmargin = np.minimum(mg_t.min(axis=-1), mg_d.min(axis=-1) if gamma else np.inf)
+        ftau = np.concatenate([tau_t, tau_d], axis=1)
+        fmg = np.concatenate([mg_t, mg_d], axis=1)
 
     if temperature == 0.0:
         a = argmax_first(tl)             # target argmax per position
@@ -219,7 +239,8 @@ def _verify_block(target, draft, tokens, u, temperature, dtype, keep_weights, le
             weights = np.zeros((nb, V))
             weights[rows, t] = 1.0
         return Result(n, t, alpha, 1.0 - alpha, p_x, q_x, np.zeros(nb, bool),
-                      np.full(nb, np.inf), np.zeros(nb, bool), weights, fmargin, np.full(nb, np.nan))
+                      np.full(nb, np.inf), np.zeros(nb, bool), weights, fmargin, np.full(nb, np.nan),
+                      ftau, fmg)
 
     p = softmax(tl, temperature)         # [b, gamma+1, V]
     q = softmax(dl, temperature)         # [b, gamma, V]
@@ -234,8 +255,7 @@ def _verify_block(target, draft, tokens, u, temperature, dtype, keep_weights, le
     q_x = np.where(live, q_x, np.nan)
 
     evaluated = (np.arange(gamma)[None, :] <= n[:, None]) & live
-    with np.errstate(invalid="ignore"):
-        near = np.abs(u[:, :gamma] - capped) < U_BAND
+    near = in_u_band(u[:, :gamma], capped)
     u_band = (near & evaluated).any(axis=-1) if gamma else np.zeros(nb, bool)
 
     residual = n < gb
@@ -246,18 +266,18 @@ def _verify_block(target, draft, tokens, u, temperature, dtype, keep_weights, le
         res = residual_weights(p[idx, n[idx]], q[idx, n[idx]], lenience)
         mass = res.sum(axis=-1)
         res_mass[idx] = mass
-        ok = mass > RESIDUAL_FLOOR                 # no mass: keep p_n
+        ok = mass > 0.0                            # no mass at all: keep p_n
         w[idx[ok]] = res[ok] / mass[ok][:, None]
     w /= w.sum(axis=-1, keepdims=True)
     t, cdf = inverse_cdf(w, u_final.astype(np.float64))
-    margin = np.abs(cdf - u_final[:, None]).min(axis=-1)
+    margin = cdf_margin(cdf, u_final)
     return Result(n, t, alpha, tv, p_x, q_x, u_band, margin, residual,
-                  w if keep_weights else None, fmargin, res_mass)
+                  w if keep_weights else None, fmargin, res_mass, ftau, fmg)
 
 
 def verify(target, draft, tokens, uniforms, temperature: float, dtype: str,
            keep_weights: bool = False, block_elems: int = 1 << 25, lenience: float = 1.0,
-           gamma_seq=None, top_k: int = 0, top_p: float = 1.0) -> Result:
+           gamma_seq=None, top_k: int = 0, top_p: float = 1.0, workers: int = 1) -> Result:
     """Run the verification step for every sequence of the batch.
 
     target [B, gamma+1, V], draft [B, gamma, V] (float32, or uint16 bf16 bits),
@@ -265,7 +285,11 @@ def verify(target, draft, tokens, uniforms, temperature: float, dtype: str,
     lenience l in (0, 1] and gamma_seq int [B] with 0 <= gamma_b <= gamma are the
     two extensions described in the module notes; top_k and top_p adjust every
     row first (oracle/adjust.py; top_k <= 0 and top_p >= 1 disable them).
-    Sequences are independent, so they are processed in blocks to bound memory.
+    temperature, lenience and top_p are taken as the 32-bit floats a caller of
+    the library passes.
+    Sequences are independent, so they are processed in blocks to bound memory,
+    on `workers` threads (NumPy releases the interpreter lock in its loops); the
+    blocks are computed exactly as on one thread.
     """
     target = np.asarray(target)
     draft = np.asarray(draft)
@@ -285,26 +309,37 @@ def verify(target, draft, tokens, uniforms, temperature: float, dtype: str,
             raise ValueError("every gamma_b must lie in [0, gamma]")
     u = np.asarray(uniforms, dtype=np.float32).astype(np.float64).reshape(B, g1)
     tokens = np.asarray(tokens).reshape(B, gamma)
+    temperature, lenience, top_p = (float(np.float32(v)) for v in (temperature, lenience, top_p))
     per_seq = max(1, (2 * gamma + 1) * V)
     step = max(1, block_elems // per_seq)
-    parts = [_verify_block(target[s:s + step], draft[s:s + step], tokens[s:s + step],
-                           u[s:s + step], temperature, dtype, keep_weights, lenience,
-                           None if gamma_seq is None else gamma_seq[s:s + step], top_k, top_p)
-             for s in range(0, B, step)]
+
+    def block(s):
+        return _verify_block(target[s:s + step], draft[s:s + step], tokens[s:s + step],
+                             u[s:s + step], temperature, dtype, keep_weights, lenience,
+                             None if gamma_seq is None else gamma_seq[s:s + step], top_k, top_p)
+
+    starts = range(0, B, step)
+    if workers > 1 and len(starts) > 1:
+        with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
+            parts = list(ex.map(block, starts))
+    else:
+        parts = [block(s) for s in starts]
     if not parts:
         z = np.zeros(0)
         return Result(z.astype(np.int64), z.astype(np.int64), np.zeros((0, gamma)),
                       np.zeros((0, gamma)), np.zeros((0, gamma)), np.zeros((0, gamma)),
                       z.astype(bool), z, z.astype(bool), None, z, z)
     cat = lambda f: np.concatenate([getattr(r, f) for r in parts])  # noqa: E731
+    filtered = parts[0].filter_tau is not None
     return Result(cat("n_accepted"), cat("next_token"), cat("alpha"), cat("tv"),
                   cat("p_draft"), cat("q_draft"), cat("u_band"), cat("cdf_margin"),
                   cat("residual"), cat("weights") if keep_weights else None, cat("filter_margin"),
-                  cat("res_mass"))
+                  cat("res_mass"), cat("filter_tau") if filtered else None,
+                  cat("filter_margins") if filtered else None)
 
 
 def verify_case(case, keep_weights: bool = False, seqs=None, lenience: float = 1.0, gamma_seq=None,
-                top_k: int = 0, top_p: float = 1.0) -> Result:
+                top_k: int = 0, top_p: float = 1.0, workers: int = 1) -> Result:
     """verify() on a workloads.VerifyCase, optionally on a subset of sequences."""
     if seqs is not None:
         case = case.subset(seqs)
@@ -312,4 +347,4 @@ def verify_case(case, keep_weights: bool = False, seqs=None, lenience: float = 1
             gamma_seq = np.asarray(gamma_seq)[np.asarray(seqs)]
     return verify(case.target, case.draft, case.tokens, case.uniforms,
                   case.temperature, case.dtype, keep_weights, lenience=lenience, gamma_seq=gamma_seq,
-                  top_k=top_k, top_p=top_p)
+                  top_k=top_k, top_p=top_p, workers=workers)

@@ -191,22 +191,61 @@ def test_inverse_cdf_strict_boundary_and_guard():
     assert ov.inverse_cdf(w, np.array([0.9]))[0][0] == 2
 
 
-# ------------------------------------------------------- residual floor
+# ------------------------------------------------ small residual masses
 
-@pytest.mark.parametrize("delta,expect", [(2.0 ** -16, 0), (2.0 ** -21, 1), (2.0 ** -8, 0)])
-def test_residual_mass_floor(delta, expect):
+@pytest.mark.parametrize("delta", [2.0 ** -8, 2.0 ** -16, 2.0 ** -21])
+def test_small_residual_mass_is_sampled(delta):
     """Two tokens: target logits (delta, 0), draft logits (0, 0), so p(0) =
     1/(1 + e^-delta), about 1/2 + delta/4, and q = (1/2, 1/2).  Draft x = 1 has
     ratio 1 - 2 (p(0) - 1/2), below the largest uniform 1 - 2^-24, so it is
-    rejected.  The residual max(0, p - q) sits on token 0 with mass about
-    delta/4.  Above the 2^-20 floor (delta = 2^-16, 2^-8) the token is 0 whatever
-    u is; below it (delta = 2^-21, mass about 2^-23) the token is drawn from p
-    itself, so u = 0.9 > p(0) gives token 1."""
+    rejected.  The residual max(0, p - q) sits on token 0 alone, with mass
+    about delta/4 (2^-23 at the smallest delta), and [FI] eq. (2) samples it
+    after any rejection: the token is 0 whatever the final uniform is."""
     target = np.array([[[delta, 0.0], [0.0, 0.0]]], np.float32)
     draft = np.zeros((1, 1, 2), np.float32)
-    u = np.array([[1.0 - 2.0 ** -24, 0.9]], np.float32)
-    res = ov.verify(target, draft, np.array([[1]]), u, 1.0, "f32")
-    assert res.n_accepted[0] == 0
-    mass = 1.0 / (1.0 + np.exp(-np.float64(np.float32(delta)))) - 0.5
-    np.testing.assert_allclose(res.res_mass[0], mass, rtol=1e-9)
-    assert res.next_token[0] == expect
+    for u_final in (0.01, 0.9, 1.0 - 2.0 ** -24):
+        u = np.array([[1.0 - 2.0 ** -24, u_final]], np.float32)
+        res = ov.verify(target, draft, np.array([[1]]), u, 1.0, "f32")
+        assert res.n_accepted[0] == 0
+        mass = 1.0 / (1.0 + np.exp(-np.float64(np.float32(delta)))) - 0.5
+        np.testing.assert_allclose(res.res_mass[0], mass, rtol=1e-6)
+        assert res.next_token[0] == 0
+
+
+def test_zero_residual_mass_samples_p():
+    """Identical rows and a draft token with p(x) = q(x) = 0 (logit -inf in both):
+    0/0 rejects, the residual has no mass, and the token is drawn from p_0
+    itself ([LH] "Three candidates explain the acceptance rule": a zero-mass
+    residual is not normalised)."""
+    row = np.array([0.0, 1.0, -np.inf, 0.5], np.float32)
+    target = np.stack([row, row])[None]
+    draft = row[None, None].copy()
+    p = np.exp(row.astype(np.float64) - 1.0)
+    p /= p.sum()
+    for u_final, want in ((0.01, 0), (p[0] + 0.01, 1), (p[0] + p[1] + 0.01, 3)):
+        u = np.array([[0.5, u_final]], np.float32)
+        res = ov.verify(target, draft, np.array([[2]]), u, 1.0, "f32")
+        assert res.n_accepted[0] == 0 and res.res_mass[0] == 0.0
+        assert res.next_token[0] == want
+
+
+@pytest.mark.parametrize("L", [-20.0, -45.0, -70.0])
+def test_tiny_residual_mass_is_sampled(L):
+    """Target logits (0, 0, -inf) give p = (1/2, 1/2, 0); draft logits (0, 0, L)
+    put q(2) = e^L / (2 + e^L) on the token the target excludes.  Drafting x = 2
+    is always rejected (p(x) = 0), and the residual is (q(2)/2, q(2)/2, 0): a
+    mass of about e^L (down to 1e-31 here), split evenly, which is sampled
+    like any other residual -- u below 1/2 gives token 0, above gives token 1,
+    never token 2 ([FI] eq. (2)).  In fp64 each p - q cancels to within an
+    ulp of 1/2, so the mass is checked to that absolute accuracy (below it the
+    fp64 residual is exactly zero and the fall-back p_0 is the same
+    distribution)."""
+    target = np.array([[[0.0, 0.0, -np.inf], [0.0, 0.0, -np.inf]]], np.float32)
+    draft = np.array([[[0.0, 0.0, L]]], np.float32)
+    q2 = np.exp(np.float64(np.float32(L))) / (2.0 + np.exp(np.float64(np.float32(L))))
+    for u_final, want in ((0.25, 0), (0.75, 1), (0.5 - 2.0 ** -20, 0), (0.5 + 2.0 ** -20, 1)):
+        u = np.array([[0.3, u_final]], np.float32)
+        res = ov.verify(target, draft, np.array([[2]]), u, 1.0, "f32")
+        assert res.n_accepted[0] == 0
+        np.testing.assert_allclose(res.res_mass[0], q2, rtol=1e-12, atol=2.0 ** -53)
+        assert res.next_token[0] == want
