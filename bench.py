@@ -21,8 +21,9 @@ Prints one JSON line (rank 0) with the throughput in verified target rows/s
   roofline:     algorithmic bytes of one launch / its average duration
                 (one pair of HIP events on the launch stream around the
                 back-to-back timed steps), against 8 TB/s;
-  cpu_baseline: the fp64 oracle (test infrastructure) timed on a bounded
-                sample of the same workload on this host.
+  cpu_baseline: the fp64 oracle (test infrastructure) timed on the same
+                workload on this host's cores (at most 16 threads), with the
+                CPU model named.
 """
 
 from __future__ import annotations
@@ -74,22 +75,47 @@ def algorithmic_bytes(n_accepted: np.ndarray, gamma: int, V: int, elem: int, gam
     return rows * V * elem + small
 
 
-def cpu_baseline(case, budget_s: float = 12.0) -> dict:
-    """The fp64 oracle as it stands on a sample of the same workload: the first
-    8 sequences, repeated until `budget_s` of CPU time has passed."""
+def host_threads() -> int:
+    """Threads for the CPU baseline: the CPUs this process may run on, at most
+    16 (one GPU's share of a shared host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(case, budget_s: float = 10.0) -> dict:
+    """The fp64 oracle as it stands, on the whole batch, repeated until
+    `budget_s` of wall time has passed (after one untimed call); its blocks of
+    sequences run on host_threads() threads."""
     from oracle import verify as ov
-    sample = case.subset(np.arange(8))
-    rows = 0
+    threads = host_threads()
+    ov.verify_case(case, workers=threads)            # untimed: first-touch page faults
+    rows = calls = 0
     t0 = time.perf_counter()
     while True:
-        ov.verify_case(sample)
-        rows += sample.B * (sample.gamma + 1)
+        ov.verify_case(case, workers=threads)
+        rows += case.B * (case.gamma + 1)
+        calls += 1
         if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
-    return {"value": rows / dt, "unit": "rows/s", "cores": 1, "kind": "oracle",
-            "sample": f"8 of the {case.B} sequences (rows of {case.V} bf16 logits), "
-                      f"repeated for {dt:.1f} s, single-threaded NumPy fp64"}
+    return {"value": rows / dt, "unit": "rows/s", "cores": threads, "kind": "oracle",
+            "cpu": cpu_model(),
+            "sample": f"the whole batch ({case.B} sequences, rows of {case.V} {case.dtype} logits), "
+                      f"{calls} call(s) in {dt:.1f} s, NumPy fp64 on {threads} threads"}
 
 
 def load_traffic(algo_name: str):
@@ -282,7 +308,7 @@ def main() -> int:
                      "alg_bytes": alg, "full_bytes": (2 * G + 1) * V * elem * B,
                      "stream_read_GBps": stream_gbs, "frac_of_stream_read": achieved / stream_gbs},
     }
-    if not args.no_cpu_baseline and args.workload == "verify" and default_path and not args.vocab:
+    if not args.no_cpu_baseline and default_path and not args.vocab:
         line["cpu_baseline"] = cpu_baseline(case)
     print(json.dumps(line), flush=True)
     return 0
@@ -358,8 +384,36 @@ def run_lmhead(args) -> int:
                      "launch_us_mean": launch_us.mean,
                      "step_bytes": step_bytes},
     }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = lmhead_cpu_baseline(case, out)
     print(json.dumps(line), flush=True)
     return 0
+
+
+def lmhead_cpu_baseline(case, out, cols: int = 4096) -> dict:
+    """The oracle's LM-head step on this host: the fp64 products of both heads
+    over `cols` columns (timed, then scaled to all V columns) plus the fp64
+    verification of the whole batch on the GPU's fp32 logits (timed)."""
+    from oracle import lmhead as olm
+    from oracle import verify as ov
+    import workloads as W
+    threads = host_threads()
+    t0 = time.perf_counter()
+    sl = slice(0, cols)
+    olm.logits(case.hidden, case.w_target, cols=sl)
+    olm.logits(case.hidden[case.draft_hidden_rows()], case.w_draft, cols=sl)
+    heads = (time.perf_counter() - t0) * case.V / cols
+    vc = W.VerifyCase("lmhead", out["target_logits"].cpu().numpy(), out["draft_logits"].cpu().numpy(), "f32",
+                      case.tokens, case.uniforms, case.temperature)
+    t1 = time.perf_counter()
+    ov.verify_case(vc, workers=threads)
+    verify_s = time.perf_counter() - t1
+    step = heads + verify_s
+    return {"value": case.B * (case.gamma + 1) / step, "unit": "rows/s", "cores": threads, "kind": "oracle",
+            "cpu": cpu_model(),
+            "sample": f"both heads' fp64 products over {cols} of {case.V} columns (scaled to all: {heads:.2f} s) "
+                      f"plus the fp64 verification of the whole batch ({verify_s:.2f} s); NumPy, "
+                      f"{threads} threads for the verification"}
 
 
 if __name__ == "__main__":

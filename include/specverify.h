@@ -90,9 +90,12 @@ size_t spec_verify_workspace_size(int B, int gamma, int V, int dtype);
  *     (the first token whose cumulative weight exceeds u * total).  The weights
  *     are max(0, p_n - q_n) when n < gamma (the residual, [FI] "Speculative
  *     sampling: the accept/reject rule", eq. (2)), and p_gamma when every draft
- *     was kept (the bonus token).  A residual whose mass is at most 2^-20 (the
- *     fp32 rounding noise of p_n - q_n when the two rows agree) is taken as
- *     empty, and next_token is drawn from p_n itself.
+ *     was kept (the bonus token).  Only a residual with no mass at all is not
+ *     sampled: next_token is then drawn from p_n itself ([LH] "Three candidates
+ *     explain the acceptance rule").  The weights are computed in fp32, so a
+ *     residual whose true mass is within fp32 rounding of zero may be found
+ *     empty, and a uniform within that rounding of a step of the CDF may pick
+ *     the neighbouring token.
  *   T == 0 is argmax mode: p_i and q_i are one-hot at the row argmax, with ties
  *     going to the lowest index.  A draft is kept iff it equals the target
  *     argmax.  next_token is the target argmax at position n.  alpha is 1 where
@@ -102,10 +105,11 @@ size_t spec_verify_workspace_size(int B, int gamma, int V, int dtype);
  *   A ratio with q_i(x_i) = 0 follows IEEE rules: p > 0 keeps the draft, 0/0 rejects.
  *   A draft token outside [0, V) is rejected (it has p = q = 0).
  *   n_accepted[b] = next_token[b] = -1 reports that the fused path gave up
- *     waiting on a partner workgroup (about a second of polling; only possible
- *     when another kernel occupies the device's compute units at the same
- *     time).  That sequence has no result and the workspace must be zero-filled
- *     again before its next use.
+ *     waiting on a partner workgroup (2^20 polls by default, see
+ *     spec_set_wait_limit; only possible when another kernel occupies the
+ *     device's compute units at the same time).  That sequence has no result,
+ *     and the waits that gave up may leave words in the workspace: it must be
+ *     zero-filled again before its next use.
  *
  * Arguments:
  *   target_logits  [B][gamma+1][V], dtype
@@ -222,13 +226,25 @@ int spec_verify_ex(int algo,
  *               the row; the thresholds are the same either way.  A smaller
  *               non-NULL workspace is SPEC_ENOSPACE.
  *   Ties are kept.  Masses are fp32 exp2((logit - max) log2(e) / T), summed in
- *   fp64 and 2^-40 fixed point; a nucleus boundary within about 2^-23 of
- *   top_p times the total may fall on either side of that tie group.
+ *   fp64 and 2^-40 fixed point; a nucleus boundary within the fp32 rounding of
+ *   those weights (a few 1e-7 of the total for the rows of the B=64, V=128256
+ *   workload) of top_p may fall on either side of that tie group.
  *   Returns SPEC_EINVAL for a bad shape, temperature or top_p.
  */
 int spec_filter_thresholds(const void* target_logits, const void* draft_logits, int dtype,
                            int B, int gamma, int V, float temperature, int top_k, float top_p,
                            float* thresholds, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * spec_set_wait_limit -- the number of polls after which every cross-workgroup
+ * wait of a later fused-path launch in this process gives up (the sequence
+ * then reports -1, see spec_verify).  0 restores the default, 2^20.  It exists
+ * for callers and tests that exercise the give-up path: a small limit makes
+ * waits give up whenever their data is late, and every kernel still exits
+ * normally.  A process-wide setting, read when a launch is queued; not for use
+ * while other threads queue launches.
+ */
+void spec_set_wait_limit(unsigned polls);
 
 /* Bytes of the optional spec_filter_thresholds() workspace; 0 for a bad shape. */
 size_t spec_filter_workspace_size(int B, int gamma, int V);

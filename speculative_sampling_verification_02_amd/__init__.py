@@ -47,6 +47,7 @@ SIGNATURES = {
     "spec_lmhead_logits": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_void_p, _c_void_p]),
     "spec_stream_read": (_c_int, [_c_void_p, _c_size_t, _c_void_p, _c_int, _c_void_p]),
     "spec_lmhead_workspace_size": (_c_size_t, [_c_int, _c_int, _c_int, _c_int]),
+    "spec_set_wait_limit": (None, [ctypes.c_uint]),
     "spec_lmhead_verify": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                     _c_int, _c_int, _c_int, _c_int,
                                     _c_void_p, _c_void_p, _c_float,
@@ -141,8 +142,9 @@ def verify(target_logits, draft_logits, draft_tokens, uniforms, temperature: flo
     is all-zero before its first use; every completed call leaves it zero, so
     one tensor serves a whole serving loop.  Without one, a zeroed tensor is
     allocated for this call.  n_accepted = -1 marks a sequence whose result
-    was lost because the device was shared (see include/specverify.h); the
-    workspace must then be zeroed again.
+    was lost because a wait gave up (the device was shared, see
+    include/specverify.h); the workspace must then be zeroed again
+    (workspace.zero_()) before its next use.
 
     top_k / top_p (filters of both models' rows), lenience (l in (0, 1]) and
     gamma_seq (int32 [B] on the same GPU, each gamma_b in [0, gamma]) are the
@@ -185,6 +187,12 @@ def verify(target_logits, draft_logits, draft_tokens, uniforms, temperature: flo
                                             outputs, workspace, dev)),
            "spec_verify")
     return outputs
+
+
+def set_wait_limit(polls: int) -> None:
+    """Polls after which every cross-workgroup wait of later fused launches gives
+    up (spec_set_wait_limit); 0 restores the default."""
+    lib.spec_set_wait_limit(int(polls))
 
 
 def filter_workspace_size(B: int, gamma: int, V: int) -> int:

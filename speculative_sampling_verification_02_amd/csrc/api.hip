@@ -153,6 +153,8 @@ int spec_verify(const void* target_logits, const void* draft_logits, int dtype,
                           workspace, workspace_bytes, stream);
 }
 
+void spec_set_wait_limit(unsigned polls) { specv::set_wait_limit(polls); }
+
 static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int spec_lmhead_logits(const void* hidden, const void* W, int M, int d, int V, float* logits,

@@ -11,14 +11,6 @@ namespace specv {
 
 constexpr int kWave = 64;
 
-// A residual max(0, p - l q) whose mass (in units of p's total) is at most
-// this is taken as having no mass, and the token is drawn from p itself.  Each
-// token's residual carries up to an ulp of its p and q (2^-24 relative), so a
-// p and q that agree to fp32 leave a residual of rounding noise that sums to
-// at most a few 2^-24; 2^-20 stays above that, and a rejection whose true
-// residual mass is below it has probability under 2^-20.
-constexpr double kResidualFloor = 0x1p-20;
-
 // 16 bytes as four 32-bit words (a native clang vector, so it can be used
 // with the nontemporal load builtin).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -442,6 +434,34 @@ __device__ int tile_search(const typename E::storage* r0, const typename E::stor
   ArgMax lp{last_pos >= 0 ? (float)(last_pos - tile_lo) : -1.f, last_pos};
   lp = block_argmax(lp, lds_f, lds_i);
   return lp.i;
+}
+
+// Inverse-CDF draw over a whole row [0, V) from per-token weights: their total
+// first (fp32 per thread, fp64 across the workgroup), then the first token
+// whose running weight exceeds u * total (range_search).  Returns -1 when no
+// token of the row has positive weight.  A fall-back for a search whose chunk
+// or tile turned out to hold no positive weight; called by the whole
+// workgroup.  VEC needs 16-byte aligned rows and V a multiple of kVec.
+template <class E, bool VEC, int kThreads, class W>
+__device__ int row_search(const typename E::storage* r0, const typename E::storage* r1, int V, double u,
+                          W&& weight, float* lds_f, int* lds_i, double* lds_d) {
+  constexpr int kPer = VEC ? E::kVec : 1;
+  float s = 0.f;
+  for (int j0 = (int)threadIdx.x * kPer; j0 < V; j0 += kThreads * kPer) {
+    float x0[kPer], x1[kPer];
+    if constexpr (VEC) {
+      E::unpack(load_cached(r0 + j0), x0);
+      if (r1) E::unpack(load_cached(r1 + j0), x1);
+    } else {
+      x0[0] = E::at(r0, j0);
+      if (r1) x1[0] = E::at(r1, j0);
+    }
+#pragma unroll
+    for (int t = 0; t < kPer; ++t) s += weight(x0[t], r1 ? x1[t] : 0.f);
+  }
+  const double total = block_sum((double)s, lds_d);
+  if (!(total > 0.0)) return -1;
+  return range_search<E, VEC, kThreads>(r0, r1, 0, V, (float)(u * total), weight, lds_f, lds_i);
 }
 
 // Row normaliser from nch chunk partials (max m_c, sum S_c relative to m_c),

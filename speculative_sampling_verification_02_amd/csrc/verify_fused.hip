@@ -58,42 +58,21 @@
 namespace specv {
 namespace {
 
-// Tokens per thread per row for each dtype (the wave tile is kWave times
-// this) and the share of resident workgroups that finish items
-// (1 / SPECV_FUSED_FIN_DIV).
-#ifndef SPECV_FUSED_PER_BF16
-#define SPECV_FUSED_PER_BF16 32
-#endif
-#ifndef SPECV_FUSED_PER_F32
-#define SPECV_FUSED_PER_F32 32
-#endif
-#ifndef SPECV_FUSED_FIN_DIV
-#define SPECV_FUSED_FIN_DIV 8
-#endif
-// Stage the next bf16 item in LDS while the current one is computed (1) or
-// load each item when its turn comes (0).
-#ifndef SPECV_FUSED_STAGE
-#define SPECV_FUSED_STAGE 1
-#endif
-// Rotate the compute waves' issue priority by item round (1) or leave every
-// wave at the default priority (0).  With three workgroups per compute unit,
-// the one dispatched first wins every tie in the instruction arbiter (the
-// oldest wave goes first), so on the hardware the teams made of the first,
-// second and third dispatched workgroups of each unit ran their items at
-// about 1 : 1.2 : 1.4 of the first's pace, and the kernel waited for the
-// slowest class.  Giving each class the top level one round in three levels
-// that out.
-#ifndef SPECV_FUSED_ROT_PRIO
-#define SPECV_FUSED_ROT_PRIO 1
-#endif
-// Minimum waves per SIMD the register allocation must allow (1: no limit).
-#ifndef SPECV_FUSED_MIN_WAVES
-#define SPECV_FUSED_MIN_WAVES 3
-#endif
+// Tokens per thread per row (the wave tile is kWave times this) for each
+// dtype, and the share of resident workgroups that finish items
+// (1 / kFinisherDiv).
+constexpr int kPerBF16 = 32;
+constexpr int kPerF32 = 32;
+constexpr int kFinisherDiv = 8;
+// Minimum waves per SIMD the register allocation must allow.
+constexpr int kMinWaves = 3;
 constexpr int kThreads = 256;
 constexpr int kWavesPerGroup = kThreads / kWave;
 constexpr int kMaxWaveTiles = 256;  // longest supported row: 256 wave tiles
-constexpr unsigned kSpinIters = 1u << 20;
+// Polls a cross-workgroup wait makes before it gives up (spec_set_wait_limit
+// can lower it for later launches, to test the give-up path).
+constexpr unsigned kDefaultWaitPolls = 1u << 20;
+unsigned g_wait_polls = kDefaultWaitPolls;
 
 // Published partials are 64-bit words.  A word whose low 32 bits are kEmpty
 // has not been written yet.  The low word of every published word is nonzero:
@@ -115,6 +94,7 @@ struct FusedParams {
   uint64_t* part1;     // [n_items][W][2]  (max, sum) of p and q, or argmax (value, index)
   uint64_t* part2;     // [n_pairs][W]     (overlap share, residual mass share)
   uint64_t* pair_res;  // [n_pairs]        (accept flag | kResMark, sampled token)
+  unsigned polls;      // bound of every wait
 };
 
 // ------------------------------------------------------------- cross-WG sync
@@ -159,10 +139,10 @@ __device__ inline void lds_barrier() {
 
 // One wave polls n consecutive 64-bit slots until every one is published and
 // copies them to lds[0..n).  Returns true, uniformly over the wave, if all
-// arrived and none is poisoned.  Gives up after kSpinIters polls, so the
-// kernel always terminates.  Called by all lanes of one wave.
+// arrived and none is poisoned.  Gives up after `limit` polls, so the kernel
+// always terminates.  Called by all lanes of one wave.
 __device__ inline bool wave_poll(const uint64_t* a, int na, uint64_t* la, const uint64_t* b, int nb,
-                                 uint64_t* lb) {
+                                 uint64_t* lb, unsigned limit) {
   const int lane = threadIdx.x & (kWave - 1), n = na + nb;
   unsigned it = 0;
   for (int base = 0; base < n; base += kWave) {
@@ -181,7 +161,7 @@ __device__ inline bool wave_poll(const uint64_t* a, int na, uint64_t* la, const 
         break;
       }
       __builtin_amdgcn_s_sleep(1);
-      if (++it >= kSpinIters) return false;
+      if (++it >= limit) return false;
     }
   }
   return true;
@@ -190,7 +170,7 @@ __device__ inline bool wave_poll(const uint64_t* a, int na, uint64_t* la, const 
 // The same for at most 2 kWave slots of one array: each poll reads every slot
 // at once, so it costs one memory round trip (wave_poll polls 64 slots at a
 // time, one round trip each).
-__device__ inline bool wave_poll_once(const uint64_t* a, int n, uint64_t* lds) {
+__device__ inline bool wave_poll_once(const uint64_t* a, int n, uint64_t* lds, unsigned limit) {
   // the lane index is made opaque here, so the per-lane offsets are formed
   // at each wait instead of being hoisted out of the compute loop (where they
   // would hold registers through the whole item)
@@ -210,7 +190,7 @@ __device__ inline bool wave_poll_once(const uint64_t* a, int n, uint64_t* lds) {
       return !__any(poisoned(v0) || poisoned(v1));
     }
     __builtin_amdgcn_s_sleep(1);
-    if (++it >= kSpinIters) return false;
+    if (++it >= limit) return false;
   }
 }
 
@@ -218,7 +198,7 @@ __device__ inline bool wave_poll_once(const uint64_t* a, int n, uint64_t* lds) {
 // (one memory round trip).
 template <int NL>
 __device__ inline bool wave_poll_all(const uint64_t* a, int na, uint64_t* la, const uint64_t* b, int nb,
-                                     uint64_t* lb) {
+                                     uint64_t* lb, unsigned limit) {
   const int lane = threadIdx.x & (kWave - 1), n = na + nb;
   unsigned it = 0;
   while (true) {
@@ -250,22 +230,24 @@ __device__ inline bool wave_poll_all(const uint64_t* a, int na, uint64_t* la, co
       return !__any(bad);
     }
     __builtin_amdgcn_s_sleep(1);
-    if (++it >= kSpinIters) return false;
+    if (++it >= limit) return false;
   }
 }
 
 // Whole-workgroup wait: wave 0 polls, then a barrier.  Finishers only.
-__device__ inline bool gather2(const uint64_t* a, int na, uint64_t* la, const uint64_t* b, int nb, uint64_t* lb) {
+__device__ inline bool gather2(const uint64_t* a, int na, uint64_t* la, const uint64_t* b, int nb, uint64_t* lb,
+                               unsigned limit) {
   __shared__ int ok_s;
   if (threadIdx.x < kWave) {
-    const bool ok = na + nb <= 4 * kWave ? wave_poll_all<4>(a, na, la, b, nb, lb) : wave_poll(a, na, la, b, nb, lb);
+    const bool ok = na + nb <= 4 * kWave ? wave_poll_all<4>(a, na, la, b, nb, lb, limit)
+                                         : wave_poll(a, na, la, b, nb, lb, limit);
     if (threadIdx.x == 0) ok_s = ok;
   }
   __syncthreads();
   return ok_s != 0;
 }
-__device__ inline bool gather(const uint64_t* slots, int n, uint64_t* lds) {
-  return gather2(slots, n, lds, nullptr, 0, nullptr);
+__device__ inline bool gather(const uint64_t* slots, int n, uint64_t* lds, unsigned limit) {
+  return gather2(slots, n, lds, nullptr, 0, nullptr, limit);
 }
 
 // Set n slots back to kEmpty (wave 0).  Only the last reader of a slot clears
@@ -640,8 +622,8 @@ __device__ __attribute__((always_inline)) inline NormMsg pair_wait(const FusedPa
                                                                    uint64_t* w1, NormMsg* msg) {
   if (threadIdx.x < kWave) {
     const uint64_t* part1 = P.part1 + (size_t)item * P.W * 2;
-    const bool ok = 2 * P.W <= 2 * kWave ? wave_poll_once(part1, 2 * P.W, w1)
-                                         : wave_poll(part1, 2 * P.W, w1, nullptr, 0, nullptr);
+    const bool ok = 2 * P.W <= 2 * kWave ? wave_poll_once(part1, 2 * P.W, w1, P.polls)
+                                         : wave_poll(part1, 2 * P.W, w1, nullptr, 0, nullptr, P.polls);
     NormMsg m{0.f, 0.f, 0.f, 0.f, 0, 0, 0, 0};
     if (ok) {
       const Norm2 n = wave_norm2(w1, P.W);
@@ -840,7 +822,7 @@ __device__ __attribute__((always_inline)) void compute_loop_staged(const FusedPa
   const int slot_class = (int)((blockIdx.x * 3u) / gridDim.x);
   int round = 0;
   while (item < P.n_items) {
-    if (SPECV_FUSED_ROT_PRIO) {
+    {
       switch ((round + slot_class) % 3) {  // s_setprio takes an immediate
         case 0: __builtin_amdgcn_s_setprio(0); break;
         case 1: __builtin_amdgcn_s_setprio(1); break;
@@ -939,6 +921,7 @@ __device__ void finish_pair(const FusedParams& P, int item, uint64_t* w1, uint64
   using S = SearchShape<E, PER>;
   __shared__ float lds_f[kMaxWaves];
   __shared__ int lds_i[kMaxWaves];
+  __shared__ double lds_d[kMaxWaves];
   __shared__ int tile_s, acc_s;
   __shared__ float rest_s;
   __shared__ float Mp_s, Mq_s;
@@ -966,7 +949,7 @@ __device__ void finish_pair(const FusedParams& P, int item, uint64_t* w1, uint64
   }
 
   if constexpr (ARGMAX) {
-    if (!gather(part1, 2 * W, w1)) {
+    if (!gather(part1, 2 * W, w1, P.polls)) {
       if (threadIdx.x == 0) st_u64(P.pair_res + item, pack2i(kPoison, 0u));
       return;
     }
@@ -999,7 +982,7 @@ __device__ void finish_pair(const FusedParams& P, int item, uint64_t* w1, uint64
     }
     // part2 is published after part1 by every wave; polling both in one pass
     // returns once both are complete
-    if (!gather2(part1, 2 * W, w1, part2, W, w2)) {
+    if (!gather2(part1, 2 * W, w1, part2, W, w2, P.polls)) {
       if (threadIdx.x == 0) st_u64(P.pair_res + item, pack2i(kPoison, 0u));
       return;
     }
@@ -1064,7 +1047,7 @@ __device__ void finish_pair(const FusedParams& P, int item, uint64_t* w1, uint64
       }, &tile_s, &rest_s);
     };
     if (!acc_i) {
-      if (sw_s > kResidualFloor) {
+      if (sw_s > 0.0) {
         mode = 1;  // residual max(0, p_i - l q_i) ([FI] eq. (2); [SD] "Exactness"; l = 1 there)
         wave_pick_tile(ng, uf * sw_s, [&](int g) {
           double m = 0.0;
@@ -1072,7 +1055,9 @@ __device__ void finish_pair(const FusedParams& P, int item, uint64_t* w1, uint64
           return m;
         }, &tile_s, &rest_s);
       } else {
-        mode = 2;  // no residual mass (at most kResidualFloor): sample p_i itself
+        // the residual has no mass: sample p_i itself ([LH] "Three candidates
+        // explain the acceptance rule": a zero-mass residual is not normalised)
+        mode = 2;
         pick_p_tile();
       }
     }
@@ -1083,17 +1068,21 @@ __device__ void finish_pair(const FusedParams& P, int item, uint64_t* w1, uint64
       const float tp = EXT && a.thr ? thr_target(a, b, i) : -INFINITY;
       const float tq = EXT && a.thr ? thr_draft(a, b, i) : -INFINITY;
       if (mode == 1) {
-        t = tile_search<E, S::kPer, kThreads>(prow, qrow, tile_s * S::kTokens, a.V, rest_s,
-                                              [&](float xp, float xq) {
+        auto residual = [&](float xp, float xq) {
           const float wp = xp >= tp ? fast_exp2(fmaf(xp, k, -Mp)) : 0.f;
           const float wq = xq >= tq ? fast_exp2(fmaf(xq, k, -Mq)) : 0.f;
           // both products rounded (no fused multiply-add), so equal p and q
           // give exactly 0
           return fmaxf(__fmul_rn(wp, invSp) - __fmul_rn(wq, invSq), 0.f);
-        }, lds_f, lds_i);
-        // No token of the picked tile has a positive residual: p_i and q_i
-        // agree to fp32 there, and the tile's positive sum came from rounding.
-        // That is the residual without mass: sample p_i itself.
+        };
+        t = tile_search<E, S::kPer, kThreads>(prow, qrow, tile_s * S::kTokens, a.V, rest_s, residual, lds_f, lds_i);
+        // No token of the picked tile has a positive residual in this
+        // arithmetic: the tile's mass, formed from the overlap identity over
+        // whole tiles, was rounding noise.  Draw from the residual of the whole
+        // row instead, token by token in the arithmetic of the search.
+        if (t < 0) t = row_search<E, true, kThreads>(prow, qrow, a.V, uf, residual, lds_f, lds_i, lds_d);
+        // No token of the row has a positive residual either: p_i and l q_i
+        // agree to fp32 everywhere, the residual without mass.  Sample p_i.
         if (t < 0) {
           mode = 2;
           pick_p_tile();
@@ -1141,7 +1130,7 @@ __device__ void finish_bonus(const FusedParams& P, int item, uint64_t* w1, uint6
   // finishers, usually long before) in one wait.  The bonus token is drawn
   // only when every draft was kept.
   uint64_t* pres = P.pair_res + (size_t)b * G;
-  const bool ok1 = gather2(part1, 2 * W, w1, pres, gb, res);
+  const bool ok1 = gather2(part1, 2 * W, w1, pres, gb, res, P.polls);
   if (ok1) {
     clear_slots(part1, 2 * W);
     clear_slots(pres, gb);
@@ -1218,7 +1207,7 @@ struct Pool {
   // arithmetic per token, the three workgroups of a compute unit cover each
   // other's load latency, and that measured faster than the stage (36.9 vs
   // 41.8 us on the B=64 workload); at T > 0 the stage wins (42.5 vs 51.0 us).
-  static constexpr bool kStaged = std::is_same<E, BF16>::value && SPECV_FUSED_STAGE && !ARGMAX;
+  static constexpr bool kStaged = std::is_same<E, BF16>::value && !ARGMAX;
   static constexpr int kFinBytes = (3 * kMaxWaveTiles + SPEC_MAX_GAMMA) * 8;
   static constexpr int kStageBytes = kStaged ? stage_vectors<PER>() * 16 : 0;
   static constexpr int kABytes = kStageBytes > kFinBytes ? kStageBytes : kFinBytes;
@@ -1226,7 +1215,7 @@ struct Pool {
 };
 
 template <class E, int PER, bool ARGMAX, bool EXT>
-__global__ __launch_bounds__(kThreads, SPECV_FUSED_MIN_WAVES) void fused_kernel(FusedParams P) {
+__global__ __launch_bounds__(kThreads, kMinWaves) void fused_kernel(FusedParams P) {
   using L = Pool<E, PER, ARGMAX>;
   __shared__ __align__(16) unsigned char pool[L::kBytes];
   uint64_t* poll_buf = reinterpret_cast<uint64_t*>(pool + L::kABytes);
@@ -1278,9 +1267,8 @@ __global__ __launch_bounds__(kThreads, SPECV_FUSED_MIN_WAVES) void fused_kernel(
   }
 }
 
-constexpr int kFinisherDiv = SPECV_FUSED_FIN_DIV;
 template <class E>
-constexpr int per_of() { return std::is_same<E, BF16>::value ? SPECV_FUSED_PER_BF16 : SPECV_FUSED_PER_F32; }
+constexpr int per_of() { return std::is_same<E, BF16>::value ? kPerBF16 : kPerF32; }
 static_assert(per_of<BF16>() % 8 == 0 && per_of<F32>() % 8 == 0, "tile shape");
 
 int per_for(int dtype) { return dtype == SPEC_BF16 ? per_of<BF16>() : per_of<F32>(); }
@@ -1334,6 +1322,7 @@ hipError_t launch(const VerifyArgs& a, hipStream_t s) {
   P.part1 = reinterpret_cast<uint64_t*>(ws + L.off_part1);
   P.part2 = reinterpret_cast<uint64_t*>(ws + L.off_part2);
   P.pair_res = reinterpret_cast<uint64_t*>(ws + L.off_res);
+  P.polls = g_wait_polls;
 
   auto kern = fused_kernel<E, per_of<E>(), ARGMAX, EXT>;
   long resident = 0;
@@ -1349,6 +1338,8 @@ hipError_t launch(const VerifyArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+void set_wait_limit(unsigned polls) { g_wait_polls = polls ? polls : kDefaultWaitPolls; }
 
 size_t fused_workspace_bytes(int B, int gamma, int V) { return layout(B, gamma, V).total; }
 

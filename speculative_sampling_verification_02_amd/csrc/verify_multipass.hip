@@ -362,8 +362,8 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(VerifyArgs a, float2* 
   // ---- the sampled row's chunk masses, in chunk order: the residual
   // max(0, p_n - l q_n) ([FI] eq. (2); [SD] "Exactness"; l = 1 there) when a
   // draft was rejected, else p_{gamma_b} (the bonus token).  A residual with no
-  // mass (at most kResidualFloor, the fp32 rounding of a p_n equal to q_n)
-  // falls back to p_n.
+  // mass falls back to p_n ([LH] "Three candidates explain the acceptance
+  // rule": a zero-mass residual is not normalised).
   const float2* res_st = n < Gb ? pair_stats + ((size_t)b * G + n) * nch : nullptr;
   const float2* row_st = stats + target_row(b, n, G) * nch;
   __shared__ RowNorm norm_s[2];
@@ -376,7 +376,7 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(VerifyArgs a, float2* 
   double part = 0.0;
   if (res_st)
     for (int c = tid; c < nch; c += kThreads) part += (double)res_st[c].y;
-  bool residual = res_st && block_sum(part, lds_d) > kResidualFloor;
+  bool residual = res_st && block_sum(part, lds_d) > 0.0;
   // chunk c's mass: R_c for the residual, S_c rescaled to the row maximum for p_n
   auto mass = [&](int c) -> float {
     if (residual) return res_st[c].y;
@@ -439,6 +439,10 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(VerifyArgs a, float2* 
         t = tile_search<E, kChunk / kThreads, kThreads>(p_row, q_row, lo, a.V, theta_s, w, lds_f, lds_i);
       else
         t = range_search<E, false, kThreads>(p_row, q_row, lo, hi, theta_s, w, lds_f, lds_i);
+      // The chunk masses sum these same per-token weights, so a chunk with
+      // positive mass holds a positive weight; should the compiled arithmetic
+      // of the two kernels ever differ, draw from the whole row's residual.
+      if (t < 0) t = row_search<E, VEC, kThreads>(p_row, q_row, a.V, (double)u[Gb], w, lds_f, lds_i, lds_d);
     } else {
       auto w = [&](float xp, float) { return fast_exp2((keep(xp, thp) - np.M) * k); };
       if constexpr (VEC)
@@ -446,9 +450,9 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(VerifyArgs a, float2* 
       else
         t = range_search<E, false, kThreads>(p_row, nullptr, lo, hi, theta_s, w, lds_f, lds_i);
     }
-    // No token of the picked chunk has a positive residual: p_n and q_n agree
-    // to fp32 there and the positive chunk sum came from rounding.  That is the
-    // residual without mass: sample p_n itself (t is the same in every thread).
+    // No token of the row has a positive residual: p_n and l q_n agree to fp32
+    // everywhere, the residual without mass.  Sample p_n itself (t is the same
+    // in every thread).
     if (!(residual && t < 0)) break;
     residual = false;
     __syncthreads();

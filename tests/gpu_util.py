@@ -46,3 +46,14 @@ def run_case(case, algo, tensors=None, dev=None, lenience: float = 1.0, gamma_se
         raise
     torch.cuda.synchronize(dev)
     return {k: v.cpu().numpy() for k, v in out.items()}
+
+
+def gpu_thresholds(case, top_k: int, top_p: float, dev=None, tensors=None):
+    """The GPU's keep thresholds for a case ([B, 2 gamma + 1]: target rows, then
+    draft rows), from spec_filter_thresholds -- the kernel the verification
+    itself launches first."""
+    import speculative_sampling_verification_02_amd as sv
+    dev = dev or device()
+    t = tensors or case_tensors(case, dev)
+    gt, gd = sv.filter_thresholds(t["target"], t["draft"], case.temperature, top_k, top_p)
+    return np.concatenate([gt.cpu().numpy(), gd.cpu().numpy()], axis=1)

@@ -2,11 +2,13 @@
 oracle's (oracle/adjust.py), row by row.
 
 top-k thresholds must be equal exactly.  top-p thresholds must be equal except
-in rows whose nucleus boundary lies within parity.FILTER_EPS of top_p times
-the total mass (the fp32 exponential may put such a tie group on either side);
-those rows are counted and may be at most a fifth of a case's rows.  (Untied
-fp32 logits put about 1/V of the mass in each tie group, so a few percent of
-rows fall in that band by chance.)
+in rows whose nucleus boundary lies within the derived band of top_p
+(parity.nucleus_bands: the kernels' fp32 weights may put such a tie group on
+either side).  The rows in the band are counted; the rows whose threshold
+actually differs must all lie in it, and may be at most a twentieth of a
+case's rows.  (Untied logits put about 1/V of the mass in each tie group, so
+the worst-case fp32 band of a few 1e-6 covers a fair share of rows, while the
+kernels' actual error is far smaller.)
 
 Every case also runs with the chunk-list workspace, where a top-k of at most
 64 selects from the chunks' candidate lists (rows of ties overflow the lists
@@ -63,14 +65,15 @@ def _check(dev, target, draft, dtype, T, k, p, where):
     assert int(torch.count_nonzero(ws)) == 0, f"{where}: workspace not left zeroed"
     rows = np.concatenate([target.reshape(-1, V), draft.reshape(-1, V)]).astype(np.float64)
     tau, margin = adjust.thresholds(rows, T, k, p)
-    ok = margin >= parity.FILTER_EPS
+    ok = margin > parity.nucleus_bands(rows, float(np.float32(T)), k)
     want = tau.astype(np.float32)
-    bad = np.nonzero(ok & (got != want))[0]
+    differ = got != want
+    bad = np.nonzero(ok & differ)[0]
     assert bad.size == 0, (f"{where}: rows {bad[:8]} thresholds {got[bad[:8]]} != oracle {want[bad[:8]]} "
                            f"(margins {margin[bad[:8]]})")
-    amb = int((~ok).sum())
-    _banner(f"  rows={len(got)} ambiguous={amb}")
-    assert amb <= max(1, len(got) // 5), f"{where}: {amb} of {len(got)} rows near a nucleus boundary"
+    amb, ndiff = int((~ok).sum()), int(differ.sum())
+    _banner(f"  rows={len(got)} in_band={amb} differ={ndiff}")
+    assert ndiff <= max(1, len(got) // 20), f"{where}: {ndiff} of {len(got)} thresholds differ"
 
 
 def _bf16(x):

@@ -1,0 +1,54 @@
+"""The fused path's bounded waits and their give-up path, forced from the host.
+
+spec_set_wait_limit(1) makes every cross-workgroup wait of the next fused
+launch give up unless its data is already there at the first poll, so most
+sequences of a batch lose their result while every kernel still runs to its
+end.  The contract (include/specverify.h): a sequence whose wait gave up
+reports n_accepted = next_token = -1, every other sequence has its full
+result, and the workspace must be zero-filled again before its next use; after
+that the next call is whole again.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import workloads as W
+from tests import gpu_util, parity
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return gpu_util.device()
+
+
+@pytest.mark.parametrize("T,dt", [(1.0, "bf16"), (0.0, "bf16"), (1.0, "f32")])
+def test_waits_that_give_up_report_minus_one(dev, T, dt):
+    import torch
+    import speculative_sampling_verification_02_amd as sv
+    case = W.gaussian_case(24, 4, 40000, dt, T, seed=90, target_std=2.5)
+    ws = torch.zeros(sv.workspace_size(case.B, case.gamma, case.V, sv.SPEC_BF16), dtype=torch.uint8, device=dev)
+    t = gpu_util.case_tensors(case, dev)
+    print(f"[giveup] B={case.B} gamma={case.gamma} V={case.V} {dt} T={T}, one poll per wait", flush=True)
+    sv.set_wait_limit(1)
+    try:
+        out = gpu_util.run_case(case, sv.ALGO_FUSED, tensors=t, dev=dev, workspace=ws)
+    finally:
+        sv.set_wait_limit(0)
+    n, tok = out["n_accepted"], out["next_token"]
+    lost = n == -1
+    print(f"[giveup] {int(lost.sum())} of {case.B} sequences gave up", flush=True)
+    assert lost.any(), "with one poll per wait some wait must find its data late"
+    assert np.array_equal(tok == -1, lost)
+    kept = np.nonzero(~lost)[0]
+    if kept.size:
+        parity.check(case, out, seqs=kept, where="the sequences that did not give up")
+    # recovery as documented: zero the workspace; the next call is whole again
+    ws.zero_()
+    again = gpu_util.run_case(case, sv.ALGO_FUSED, tensors=t, dev=dev, workspace=ws)
+    assert (again["n_accepted"] >= 0).all()
+    parity.check(case, again, where="after re-zeroing")
+    assert int(ws.count_nonzero()) == 0

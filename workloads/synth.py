@@ -156,6 +156,38 @@ def config2(seed: int = 0, temperature: float = 1.0, rounds: int = 1) -> VerifyC
     return gaussian_case(rounds, 7, 32128, "f32", temperature, seed, 3.0, 0.8, 0.5, name="cfg2")
 
 
+def _per_sequence(name: str, B: int, gamma: int, V: int, dtype: str, temperature: float, seed: int, tag: int,
+                  make_rows, offsets=None, workers: int = 8) -> VerifyCase:
+    """A batch built one sequence at a time on worker threads (numpy's
+    generators release the interpreter lock).  make_rows(rng, b) returns the
+    float32 target [gamma+1, V] and draft [gamma, V] rows of sequence b from
+    rng, a stream of its own spawned from (seed, tag); its drafted tokens come
+    from another stream of its own spawned from (seed, 0x70CE).  The result
+    depends only on the seed and the shape, never on `workers`."""
+    rows_ss = np.random.SeedSequence([seed, tag]).spawn(B)
+    tok_ss = np.random.SeedSequence([seed, 0x70CE]).spawn(B)
+    store = np.uint16 if dtype == "bf16" else np.float32
+    target = np.empty((B, gamma + 1, V), dtype=store)
+    draft = np.empty((B, gamma, V), dtype=store)
+    tokens = np.zeros((B, gamma), dtype=np.int32)
+
+    def work(b):
+        t32, d32 = make_rows(np.random.default_rng(rows_ss[b]), b)
+        if dtype == "bf16":
+            target[b] = f32_to_bf16_bits(t32)
+            draft[b] = f32_to_bf16_bits(d32)
+        else:
+            target[b], draft[b] = t32, d32
+        tokens[b] = gumbel_max_tokens(as_f32(draft[b:b + 1], dtype), temperature,
+                                      np.random.default_rng(tok_ss[b]))[0]
+
+    import concurrent.futures
+    with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
+        list(ex.map(work, range(B)))
+    u = make_uniforms(seed, B, gamma, offsets)
+    return VerifyCase(name, target, draft, dtype, tokens, u, float(temperature))
+
+
 def config3(seed: int = 0, temperature: float = 1.0, B: int = 64, V: int = 128256) -> VerifyCase:
     """B=64, gamma=4, V=128256, bf16.
 
@@ -165,15 +197,17 @@ def config3(seed: int = 0, temperature: float = 1.0, B: int = 64, V: int = 12825
     """
     gamma = 4
     rng = np.random.default_rng([seed, 0x30])
-    target = rng.standard_normal((B, gamma + 1, V), dtype=np.float32) * np.float32(3.0)
-    for b in range(B):
-        for i in range(gamma + 1):
-            peaks = rng.choice(V, size=min(8, V), replace=False)
-            target[b, i, peaks] += np.float32(8.0)
     sigma = rng.uniform(0.2, 2.0, size=B).astype(np.float32)
-    draft = target[:, :gamma] + rng.standard_normal((B, gamma, V), dtype=np.float32) * sigma[:, None, None]
     offsets = rng.integers(0, 2 ** 32, size=B, dtype=np.uint64)
-    return _finish("cfg3", target, draft, "bf16", temperature, seed, offsets)
+
+    def rows(r, b):
+        t = r.standard_normal((gamma + 1, V), dtype=np.float32) * np.float32(3.0)
+        for i in range(gamma + 1):
+            t[i, r.choice(V, size=min(8, V), replace=False)] += np.float32(8.0)
+        d = t[:gamma] + r.standard_normal((gamma, V), dtype=np.float32) * sigma[b]
+        return t, d
+
+    return _per_sequence("cfg3", B, gamma, V, "bf16", temperature, seed, 0x31, rows, offsets)
 
 
 def config5(seed: int = 0, temperature: float = 1.0, B: int = 256, V: int = 256000,
@@ -190,15 +224,18 @@ def config5(seed: int = 0, temperature: float = 1.0, B: int = 256, V: int = 2560
     perm = rng.permutation(V)
     bias = np.empty(V, dtype=np.float32)
     bias[perm] = (-1.1 * np.log(np.arange(1, V + 1, dtype=np.float64))).astype(np.float32)
-    target = rng.standard_normal((B, gamma + 1, V), dtype=np.float32) * np.float32(4.0)
-    target += bias
-    draft = target[:, :gamma] + rng.standard_normal((B, gamma, V), dtype=np.float32) * np.float32(1.5)
     wrong = rng.random((B, gamma)) < wrong_fraction
-    for b, i in zip(*np.nonzero(wrong)):
-        tstar = int(np.argmin(target[b, i]))
-        draft[b, i, tstar] = draft[b, i].max() + np.float32(20.0)
     offsets = rng.integers(0, 2 ** 32, size=B, dtype=np.uint64)
-    return _finish("cfg5", target, draft, "bf16", temperature, seed, offsets)
+
+    def rows(r, b):
+        t = r.standard_normal((gamma + 1, V), dtype=np.float32) * np.float32(4.0)
+        t += bias
+        d = t[:gamma] + r.standard_normal((gamma, V), dtype=np.float32) * np.float32(1.5)
+        for i in np.nonzero(wrong[b])[0]:
+            d[i, int(np.argmin(t[i]))] = d[i].max() + np.float32(20.0)
+        return t, d
+
+    return _per_sequence("cfg5", B, gamma, V, "bf16", temperature, seed, 0x51, rows, offsets)
 
 
 @dataclasses.dataclass
