@@ -312,6 +312,8 @@ def verify(target, draft, tokens, uniforms, temperature: float, dtype: str,
     temperature, lenience, top_p = (float(np.float32(v)) for v in (temperature, lenience, top_p))
     per_seq = max(1, (2 * gamma + 1) * V)
     step = max(1, block_elems // per_seq)
+    if workers > 1:
+        step = min(step, -(-B // workers))       # at least one block per worker
 
     def block(s):
         return _verify_block(target[s:s + step], draft[s:s + step], tokens[s:s + step],
