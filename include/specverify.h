@@ -236,6 +236,37 @@ int spec_filter_thresholds(const void* target_logits, const void* draft_logits, 
                            float* thresholds, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * spec_verify_noalloc -- spec_verify for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.  The same verification as spec_verify (the same kernels,
+ * outputs bit-identical to spec_verify's for the same inputs), with its scratch
+ * in a device array the library holds instead of a workspace argument.  The
+ * caller still passes every input and output.
+ *   Arguments, outputs and status codes as for spec_verify, without
+ *   workspace / workspace_bytes.
+ *   The array is spec_verify_noalloc_limit() bytes (16 MiB) on each device the
+ *   library runs on, kept until the process ends and zero-filled on the first
+ *   call on that device.  A shape whose scratch would exceed it returns
+ *   SPEC_ENOSPACE before anything is queued (B=256, gamma=8, V=256000 needs
+ *   6.8 MB).  No call allocates device or host memory.
+ *   Every call on a device uses that device's one array: calls that may run at
+ *   the same time on one device (two streams, two threads) race and must not
+ *   overlap.  A call that completes leaves the array zero again.  A sequence
+ *   that reports -1 (a wait gave up, see spec_verify) may leave stale words
+ *   in it: a call with B == 0 (and any valid gamma, V and temperature) queues a
+ *   kernel that zero-fills the whole array on `stream`, to run before the next
+ *   verification.
+ */
+int spec_verify_noalloc(const void* target_logits, const void* draft_logits, int dtype,
+                        const int32_t* draft_tokens, const float* uniforms,
+                        int B, int gamma, int V, float temperature,
+                        int32_t* n_accepted, int32_t* next_token, float* alpha,
+                        float* p_draft, float* q_draft, void* stream);
+
+/* Bytes of the device array spec_verify_noalloc uses on each device. */
+size_t spec_verify_noalloc_limit(void);
+
+/*
  * spec_set_wait_limit -- the number of polls after which every cross-workgroup
  * wait of a later fused-path launch in this process gives up (the sequence
  * then reports -1, see spec_verify).  0 restores the default, 2^20.  It exists

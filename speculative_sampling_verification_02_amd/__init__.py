@@ -48,6 +48,10 @@ SIGNATURES = {
     "spec_stream_read": (_c_int, [_c_void_p, _c_size_t, _c_void_p, _c_int, _c_void_p]),
     "spec_lmhead_workspace_size": (_c_size_t, [_c_int, _c_int, _c_int, _c_int]),
     "spec_set_wait_limit": (None, [ctypes.c_uint]),
+    "spec_verify_noalloc": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_void_p, _c_void_p,
+                                     _c_int, _c_int, _c_int, _c_float,
+                                     _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
+    "spec_verify_noalloc_limit": (_c_size_t, []),
     "spec_lmhead_verify": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                     _c_int, _c_int, _c_int, _c_int,
                                     _c_void_p, _c_void_p, _c_float,
@@ -187,6 +191,45 @@ def verify(target_logits, draft_logits, draft_tokens, uniforms, temperature: flo
                                             outputs, workspace, dev)),
            "spec_verify")
     return outputs
+
+
+def verify_noalloc(target_logits, draft_logits, draft_tokens, uniforms, temperature: float, outputs: dict):
+    """spec_verify_noalloc: verify() with the library's own per-device scratch
+    instead of a workspace, for callers that cannot allocate.  `outputs` is
+    the dict of preallocated output tensors (n_accepted, next_token, alpha,
+    p_draft, q_draft, as verify() returns them); nothing is allocated here."""
+    torch = _torch()
+    dev = target_logits.device
+    _need(target_logits, "target_logits")
+    B, g1, V = target_logits.shape
+    gamma = g1 - 1
+    if tuple(draft_logits.shape) != (B, gamma, V) or draft_logits.dtype != target_logits.dtype:
+        raise ValueError(f"draft_logits must be [{B}, {gamma}, {V}] with the target's dtype")
+    if tuple(draft_tokens.shape) != (B, gamma) or tuple(uniforms.shape) != (B, g1):
+        raise ValueError("draft_tokens must be [B, gamma] and uniforms [B, gamma+1]")
+    _need(draft_logits, "draft_logits", device=dev)
+    _need(draft_tokens, "draft_tokens", torch.int32, dev)
+    _need(uniforms, "uniforms", torch.float32, dev)
+    for name, shape in (("n_accepted", (B,)), ("next_token", (B,))):
+        _need(outputs[name], name, torch.int32, dev)
+        if tuple(outputs[name].shape) != shape:
+            raise ValueError(f"{name} must be {shape}")
+    for name in ("alpha", "p_draft", "q_draft"):
+        if outputs.get(name) is not None:
+            _need(outputs[name], name, torch.float32, dev)
+            if tuple(outputs[name].shape) != (B, gamma):
+                raise ValueError(f"{name} must be {(B, gamma)}")
+    _check(lib.spec_verify_noalloc(_ptr(target_logits), _ptr(draft_logits), _dtype_code(target_logits),
+                                   _ptr(draft_tokens), _ptr(uniforms), B, gamma, V, float(temperature),
+                                   _ptr(outputs["n_accepted"]), _ptr(outputs["next_token"]),
+                                   _ptr(outputs.get("alpha")), _ptr(outputs.get("p_draft")),
+                                   _ptr(outputs.get("q_draft")), _stream(dev)), "spec_verify_noalloc")
+    return outputs
+
+
+def noalloc_limit() -> int:
+    """Bytes of the per-device array spec_verify_noalloc uses."""
+    return int(lib.spec_verify_noalloc_limit())
 
 
 def set_wait_limit(polls: int) -> None:

@@ -34,7 +34,88 @@ int map_hip(hipError_t e) {
   return e == hipErrorNotSupported ? SPEC_EUNSUPPORTED : SPEC_EHIP;
 }
 
+// Both paths start their scratch at the workspace's base and both leave all
+// of it zero when they complete (the fused path needs zero slots on entry).
+// The top-k / top-p keep thresholds (one float per row) follow, and are
+// zeroed again after the verification that reads them; then the threshold
+// kernel's chunk lists, which it leaves zero.
+size_t paths_bytes(int B, int gamma, int V) {
+  const size_t b = std::max(specv::fused_workspace_bytes(B, gamma, V), specv::multipass_workspace_bytes(B, gamma, V));
+  return (std::max<size_t>(b, 256) + 255) & ~(size_t)255;
+}
+
+size_t thr_bytes(int B, int gamma) {
+  return ((size_t)B * (2 * gamma + 1) * sizeof(float) + 255) & ~(size_t)255;
+}
+
+VerifyArgs make_args(const void* target_logits, const void* draft_logits, int dtype, const int32_t* draft_tokens,
+                     const float* uniforms, int B, int gamma, int V, float temperature, int32_t* n_accepted,
+                     int32_t* next_token, float* alpha, float* p_draft, float* q_draft, void* workspace,
+                     size_t workspace_bytes) {
+  VerifyArgs a{};
+  a.target = target_logits;
+  a.draft = draft_logits;
+  a.dtype = dtype;
+  a.tokens = draft_tokens;
+  a.uniforms = uniforms;
+  a.B = B;
+  a.gamma = gamma;
+  a.V = V;
+  a.temperature = temperature;
+  a.k = temperature > 0.f ? kLog2e / temperature : 0.f;
+  a.n_out = n_accepted;
+  a.t_out = next_token;
+  a.alpha = gamma > 0 ? alpha : nullptr;
+  a.p_draft = gamma > 0 ? p_draft : nullptr;
+  a.q_draft = gamma > 0 ? q_draft : nullptr;
+  a.ws = workspace;
+  a.ws_bytes = workspace_bytes;
+  a.lenience = 1.f;
+  return a;
+}
+
+// The verification proper on the chosen path.
+int launch_paths(int algo, const VerifyArgs& a, hipStream_t s) {
+  if (algo == SPEC_ALGO_FUSED) return map_hip(specv::fused_launch(a, s));
+  if (algo == SPEC_ALGO_AUTO && specv::fused_supported(a.B, a.gamma, a.V, a.dtype)) {
+    // the fused path declines unaligned rows and teams that cannot be resident
+    const hipError_t e = specv::fused_launch(a, s);
+    if (e != hipErrorNotSupported) return map_hip(e);
+  }
+  return map_hip(specv::multipass_launch(a, s));
+}
+
 }  // namespace
+
+size_t specv::verify_scratch_bytes(int B, int gamma, int V) {
+  if (!valid_shape(B, gamma, V)) return 0;
+  return paths_bytes(B, gamma, V);
+}
+
+int specv::verify_check(const void* target_logits, const void* draft_logits, int dtype,
+                        const int32_t* draft_tokens, const float* uniforms, int B, int gamma, int V,
+                        float temperature, const int32_t* n_accepted, const int32_t* next_token) {
+  if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_EUNSUPPORTED;
+  if (!valid_shape(B, gamma, V) || !valid_temperature(temperature)) return SPEC_EINVAL;
+  if (B == 0) return SPEC_OK;
+  if (!target_logits || !uniforms || !n_accepted || !next_token) return SPEC_EINVAL;
+  if (gamma > 0 && (!draft_logits || !draft_tokens)) return SPEC_EINVAL;
+  return SPEC_OK;
+}
+
+int specv::verify_in_scratch(const void* target_logits, const void* draft_logits, int dtype,
+                             const int32_t* draft_tokens, const float* uniforms, int B, int gamma, int V,
+                             float temperature, int32_t* n_accepted, int32_t* next_token, float* alpha,
+                             float* p_draft, float* q_draft, void* scratch, size_t scratch_bytes, hipStream_t s) {
+  const int st = verify_check(target_logits, draft_logits, dtype, draft_tokens, uniforms, B, gamma, V, temperature,
+                              n_accepted, next_token);
+  if (st != SPEC_OK || B == 0) return st;
+  if (scratch_bytes < paths_bytes(B, gamma, V) || !scratch) return SPEC_ENOSPACE;
+  const VerifyArgs a = make_args(target_logits, draft_logits, dtype, draft_tokens, uniforms, B, gamma, V,
+                                 temperature, n_accepted, next_token, alpha, p_draft, q_draft, scratch,
+                                 scratch_bytes);
+  return launch_paths(SPEC_ALGO_AUTO, a, s);
+}
 
 extern "C" {
 
@@ -47,20 +128,6 @@ const char* spec_status_string(int status) {
     case SPEC_EHIP: return "HIP runtime error";
     default: return "unknown status";
   }
-}
-
-// Both paths start their scratch at the workspace's base and both leave all
-// of it zero when they complete (the fused path needs zero slots on entry).
-// The top-k / top-p keep thresholds (one float per row) follow, and are
-// zeroed again after the verification that reads them; then the threshold
-// kernel's chunk lists, which it leaves zero.
-static size_t paths_bytes(int B, int gamma, int V) {
-  const size_t b = std::max(specv::fused_workspace_bytes(B, gamma, V), specv::multipass_workspace_bytes(B, gamma, V));
-  return (std::max<size_t>(b, 256) + 255) & ~(size_t)255;
-}
-
-static size_t thr_bytes(int B, int gamma) {
-  return ((size_t)B * (2 * gamma + 1) * sizeof(float) + 255) & ~(size_t)255;
 }
 
 size_t spec_verify_workspace_size(int B, int gamma, int V, int dtype) {
@@ -91,24 +158,8 @@ int spec_verify_ex(int algo, const void* target_logits, const void* draft_logits
   if (workspace_bytes < spec_verify_workspace_size(B, gamma, V, dtype) || !workspace)
     return SPEC_ENOSPACE;
 
-  VerifyArgs a{};
-  a.target = target_logits;
-  a.draft = draft_logits;
-  a.dtype = dtype;
-  a.tokens = draft_tokens;
-  a.uniforms = uniforms;
-  a.B = B;
-  a.gamma = gamma;
-  a.V = V;
-  a.temperature = temperature;
-  a.k = temperature > 0.f ? kLog2e / temperature : 0.f;
-  a.n_out = n_accepted;
-  a.t_out = next_token;
-  a.alpha = gamma > 0 ? alpha : nullptr;
-  a.p_draft = gamma > 0 ? p_draft : nullptr;
-  a.q_draft = gamma > 0 ? q_draft : nullptr;
-  a.ws = workspace;
-  a.ws_bytes = workspace_bytes;
+  VerifyArgs a = make_args(target_logits, draft_logits, dtype, draft_tokens, uniforms, B, gamma, V, temperature,
+                           n_accepted, next_token, alpha, p_draft, q_draft, workspace, workspace_bytes);
   a.lenience = lenience;
   a.gamma_seq = gamma > 0 ? gamma_seq : nullptr;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -124,13 +175,7 @@ int spec_verify_ex(int algo, const void* target_logits, const void* draft_logits
     if (e != hipSuccess) return map_hip(e);
     a.thr = thr;
   }
-  if (algo == SPEC_ALGO_FUSED) return map_hip(specv::fused_launch(a, s));
-  if (algo == SPEC_ALGO_AUTO && specv::fused_supported(B, gamma, V, dtype)) {
-    // the fused path declines unaligned rows and teams that cannot be resident
-    const hipError_t e = specv::fused_launch(a, s);
-    if (e != hipErrorNotSupported) return map_hip(e);
-  }
-  return map_hip(specv::multipass_launch(a, s));
+  return launch_paths(algo, a, s);
 }
 
 int spec_verify_algo(int algo, const void* target_logits, const void* draft_logits, int dtype,

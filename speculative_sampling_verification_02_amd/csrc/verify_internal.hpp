@@ -46,6 +46,20 @@ __device__ inline int seq_gamma(const VerifyArgs& a, int b) {
   return g < 0 ? 0 : (g > a.gamma ? a.gamma : g);
 }
 
+// ---- scratch of a verification without top-k / top-p (both paths): the
+// bytes a workspace needs for it, 0 for an invalid shape
+size_t verify_scratch_bytes(int B, int gamma, int V);
+// The host-side argument checks of spec_verify (SPEC_OK or its status code)
+int verify_check(const void* target_logits, const void* draft_logits, int dtype, const int32_t* draft_tokens,
+                 const float* uniforms, int B, int gamma, int V, float temperature, const int32_t* n_accepted,
+                 const int32_t* next_token);
+// spec_verify on a zeroed scratch of at least verify_scratch_bytes(), with
+// the argument checks of spec_verify (its status codes)
+int verify_in_scratch(const void* target_logits, const void* draft_logits, int dtype, const int32_t* draft_tokens,
+                      const float* uniforms, int B, int gamma, int V, float temperature, int32_t* n_accepted,
+                      int32_t* next_token, float* alpha, float* p_draft, float* q_draft, void* scratch,
+                      size_t scratch_bytes, hipStream_t stream);
+
 // ---- multi-pass path
 size_t multipass_workspace_bytes(int B, int gamma, int V);
 hipError_t multipass_launch(const VerifyArgs& a, hipStream_t stream);
