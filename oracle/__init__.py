@@ -8,7 +8,8 @@ Pages cited in this package:
   [FI]  intuitivepapers.ai, "Fast Inference from Transformers via Speculative Decoding"
   [SD]  nonconvexcard course page, "Speculative Decoding"
   [LH]  lihaoran.work article on speculative decoding (sections "Three candidates
-        explain the acceptance rule", "What does 'unchanged output' mean?")
+        explain the acceptance rule", "What does 'unchanged output' mean?",
+        "Fix the benchmark conditions first")
   [DB]  deval-blog, "Speculative decoding"
   [NZ]  nazmi.tech, "Speculative decoding and self-speculative decoding"
 
@@ -18,10 +19,12 @@ Modules:
   exact   -- exact-rational (fractions.Fraction) statements of the single-step
              mass identity, the overlap, and the expected-yield formula.
   lmhead  -- fp64 LM-head product for the fused LM-head workload.
+  kvcache -- the KV-cache crop after a verification step, as plain slicing
+             (contiguous and paged caches).
 
 Parity status: every function here is pinned by a CPU test against values the
 pages print, closed forms, library routines or brute force.  None is marked
 "parity unpinned".
 """
 
-from . import exact, lmhead, verify  # noqa: F401
+from . import exact, kvcache, lmhead, verify  # noqa: F401
