@@ -188,10 +188,12 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (for counter calibration)")
-    ap.add_argument("--workload", default="verify", choices=["verify", "lmhead", "small1", "small2", "large5"],
+    ap.add_argument("--workload", default="verify",
+                    choices=["verify", "lmhead", "small1", "small2", "large5", "kvcrop"],
                     help="verify: B=64, gamma=4, V=128256 bf16 (the headline); lmhead: LM heads + verify at "
                          "B=8, d=4096; small1 / small2: B=1, gamma=3 / 7, V=32128 fp32; large5: B=256, "
-                         "gamma=8, V=256000 bf16")
+                         "gamma=8, V=256000 bf16; kvcrop: the KV-cache crop after the headline verification "
+                         "(64 K/V caches of B=64 x 8 heads x 512 positions x 128 bf16)")
     ap.add_argument("--temperature", type=float, default=1.0,
                     help="temperature of the verify workloads (0: argmax mode)")
     ap.add_argument("--lenience", type=float, default=1.0, help="lenience factor l in (0, 1] (spec_verify_ex)")
@@ -209,6 +211,8 @@ def main() -> int:
         return 2
     if args.workload == "lmhead":
         return run_lmhead(args)
+    if args.workload == "kvcrop":
+        return run_kvcrop(args)
 
     import torch
 
@@ -388,6 +392,125 @@ def run_lmhead(args) -> int:
         line["cpu_baseline"] = lmhead_cpu_baseline(case, out)
     print(json.dumps(line), flush=True)
     return 0
+
+
+def run_kvcrop(args) -> int:
+    """The KV-cache crop (spec_kv_crop) that follows the headline verification:
+    32 layers' K and V caches (64 contiguous caches of B=64 sequences x 8 heads
+    x 512 positions x 128 bf16), the pass having written gamma + 1 = 5 entries
+    per sequence (the previous step's final token and the 4 drafts; keep_extra
+    1), the discarded entries zero-filled.  n_accepted comes from one
+    verification of the B=64, gamma=4, V=128256 batch.  Every timed step crops
+    its own copy of the committed lengths, so each does the same work."""
+    import ctypes
+
+    import torch
+
+    import speculative_sampling_verification_02_amd as sv
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    B, G, H, S_max, D, n_caches = 64, 4, 8, 512, 128, 64
+    appended, keep_extra = G + 1, 1
+    case = W.config3(0, 1.0)
+    t = {k: v for k, v in zip(("target", "draft"),
+                              (torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+                               for a in (case.target, case.draft)))}
+    out = sv.verify(t["target"], t["draft"], torch.from_numpy(case.tokens).to(dev),
+                    torch.from_numpy(case.uniforms).to(dev), 1.0)
+    n_acc = out["n_accepted"]
+    n_np = n_acc.cpu().numpy()
+    del t
+    caches = [torch.ones(B, H, S_max, D, dtype=torch.bfloat16, device=dev) for _ in range(n_caches)]
+    rng = np.random.default_rng([0, 0x4B])
+    committed = torch.from_numpy(rng.integers(0, S_max - appended, size=B).astype(np.int32)).to(dev)
+    total = args.warmup + args.steps
+    lens = [committed.clone() for _ in range(total)]   # one copy of the lengths per step
+    print(f"[bench] KV crop: {n_caches} caches [{B}, {H}, {S_max}, {D}] bf16, n_accepted from the verification "
+          f"(mean {n_np.mean():.2f})", file=sys.stderr, flush=True)
+    ptrs = (ctypes.c_void_p * n_caches)(*[c.data_ptr() for c in caches])
+    fn, entry = sv.lib.spec_kv_crop, D * 2
+
+    def step(k, stream):
+        st = fn(ptrs, n_caches, B, H, S_max, entry, ctypes.c_void_p(lens[k].data_ptr()),
+                ctypes.c_void_p(n_acc.data_ptr()), appended, keep_extra, 1, stream)
+        if st != 0:
+            raise RuntimeError(f"spec_kv_crop: status {st}")
+
+    cur = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    for k in range(args.warmup):
+        step(k, cur)
+    torch.cuda.synchronize()
+    # The crop is two short launches, shorter than their host-side launch cost
+    # from Python; in a serving loop they queue behind the verification.  The
+    # timed steps are therefore captured once into a HIP graph and replayed,
+    # so the stream runs them back to back as it would there.
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        cap = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        for k in range(args.steps):
+            step(args.warmup + k, cap)
+    for l in lens:
+        l.copy_(committed)
+    torch.cuda.synchronize()
+    launch_us = timed_loop(torch, 1, lambda k: graph.replay())
+    launch_us.mean /= args.steps
+    ms_per_step = 1e3 * launch_us.wall_s / args.steps
+    # algorithmic bytes: the zero-filled entries, plus lengths read and written
+    # and n_accepted read
+    discarded = int((appended - keep_extra - n_np).sum())
+    alg = discarded * H * entry * n_caches + 3 * 4 * B
+    achieved = alg / (launch_us.mean * 1e-6) / 1e9
+    # the new lengths must be the oracle's (checked on the last step's copy)
+    want = committed.cpu().numpy() + keep_extra + n_np
+    assert np.array_equal(lens[-1].cpu().numpy(), want), "crop lengths"
+    line = {
+        "metric": METRIC,
+        "value": B * (G + 1) / (ms_per_step * 1e-3),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"spec_kv_crop after spec_verify B={B} gamma={G} V=128256: {n_caches} contiguous "
+                               f"caches [{B}, {H}, {S_max}, {D}] bf16, appended {appended}, keep_extra "
+                               f"{keep_extra}, discarded entries zero-filled",
+                   "B": B, "gamma": G, "H": H, "S_max": S_max, "D": D, "caches": n_caches},
+        # rows/s here: the verified rows whose cache state one crop settles
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "launch_us_mean": launch_us.mean,
+                     "alg_bytes": alg, "discarded_entries": discarded * H * n_caches},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = kvcrop_cpu_baseline(caches[0].shape, n_caches, committed.cpu().numpy(), n_np,
+                                                   appended, keep_extra)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def kvcrop_cpu_baseline(shape, n_caches, committed, n_np, appended, keep_extra, budget_s: float = 5.0) -> dict:
+    """The crop oracle on host copies of the same caches (bf16 as uint16):
+    whole calls over all caches, repeated for `budget_s`."""
+    from oracle import kvcache as okv
+    caches = [np.ones(shape, np.uint16) for _ in range(n_caches)]
+    B = shape[0]
+    calls = 0
+    t0 = time.perf_counter()
+    while True:
+        okv.crop_contiguous(caches, committed, n_np, appended, keep_extra, True)
+        calls += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": B * appended * calls / dt, "unit": "rows/s", "cores": 1, "kind": "oracle",
+            "cpu": cpu_model(),
+            "sample": f"the whole crop ({n_caches} caches of {shape}), {calls} call(s) in {dt:.1f} s, NumPy, "
+                      "one thread"}
 
 
 def lmhead_cpu_baseline(case, out, cols: int = 4096) -> dict:

@@ -321,6 +321,67 @@ int spec_lmhead_verify(const void* hidden, const void* hidden_draft,
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * spec_kv_crop -- the KV-cache crop that follows a verification step ([FI]
+ * "The loop: draft, verify in one pass, keep a prefix", the KV-cache paragraph:
+ * after the accept test the cache entries past the accepted prefix are
+ * discarded, one crop after the sampling function; [LH] "Fix the benchmark
+ * conditions first": the cache follows the committed prefix).  Contiguous
+ * caches, each [B][H][S_max][entry_bytes] (entry_bytes = head size times the
+ * element size), for example the K and V caches of every layer.
+ *   caches       HOST array of n_caches device pointers (1..SPEC_KV_MAX_CACHES,
+ *                16-byte aligned); may be NULL when clear == 0
+ *   seq_len      device int32 [B], in and out: on entry the committed length
+ *                of each sequence before the verification pass; the pass
+ *                wrote `appended` entries after it (seq_len .. seq_len +
+ *                appended - 1).  On return of the queued work: seq_len +
+ *                keep_extra + n_accepted.
+ *   n_accepted   device int32 [B], as spec_verify wrote it (read on the
+ *                device: queue this after the verification on the same stream,
+ *                no synchronisation needed).  A sequence with -1 is left as
+ *                it was.
+ *   keep_extra   entries kept besides the accepted drafts (0..appended; 1 when
+ *                the pass also wrote the entry of the previous step's final
+ *                token).  The new token of this step is not in the cache.
+ *   clear        nonzero: zero-fill the discarded entries [new length, seq_len
+ *                + appended) of every cache and head (positions at or past
+ *                S_max are never touched); zero: only the lengths change.
+ *   entry_bytes  a multiple of 16.
+ * Two launches on `stream` (the fill, then the lengths).  Returns SPEC_EINVAL
+ * for a bad argument; B == 0 returns SPEC_OK and queues nothing.
+ */
+#define SPEC_KV_MAX_CACHES 256
+#define SPEC_KV_MAX_APPENDED 1024
+int spec_kv_crop(void* const* caches, int n_caches, int B, int H, int S_max, int entry_bytes,
+                 int32_t* seq_len, const int32_t* n_accepted, int appended, int keep_extra, int clear,
+                 void* stream);
+
+/*
+ * spec_kv_crop_paged -- spec_kv_crop for a paged cache ([LH] "Fix the
+ * benchmark conditions first": with paged storage the rejected state is whole
+ * pages).  Each cache is [num_pages][page_size][token_bytes] (token_bytes =
+ * heads x head size x element size, a multiple of 16); sequence b's position s
+ * lives in page block_table[b][s / page_size] at slot s % page_size
+ * (an entry outside [0, num_pages), e.g. -1, is no page).
+ *   block_table  device int32 [B][max_blocks], in and out
+ *   seq_len, n_accepted, appended, keep_extra, clear  as for spec_kv_crop
+ *                (clear zero-fills the discarded slots of every cache);
+ *                appended <= SPEC_KV_MAX_APPENDED
+ *   free_pages   device int32 [free_capacity] (free_capacity >= num_pages),
+ *   free_count   device int32 [1]: the pool's free list.  Every page of a
+ *                cropped sequence at block index >= ceil(new length /
+ *                page_size) is released: its id is written to
+ *                free_pages[free_count++] -- sequences in order, blocks in
+ *                ascending order -- and its table entry becomes -1.  Pages past
+ *                a sequence's crop point must belong to that sequence alone.
+ * Two launches on `stream`, the second a single workgroup.  Returns SPEC_EINVAL
+ * for a bad argument; B == 0 returns SPEC_OK and queues nothing.
+ */
+int spec_kv_crop_paged(void* const* caches, int n_caches, int num_pages, int page_size, int token_bytes,
+                       int32_t* block_table, int B, int max_blocks, int32_t* seq_len,
+                       const int32_t* n_accepted, int appended, int keep_extra, int clear,
+                       int32_t* free_pages, int32_t* free_count, int free_capacity, void* stream);
+
+/*
  * spec_stream_read -- a plain streaming read of a device buffer, for the HBM
  * read rate the device sustains (the context the verification's bandwidth
  * is judged against; not part of the method).

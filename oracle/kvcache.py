@@ -38,7 +38,8 @@ import numpy as np
 
 def crop_contiguous(caches, seq_len, n_accepted, appended: int, keep_extra: int, clear: bool):
     """caches: arrays [B][H][S_max][D] (modified in place); seq_len: int [B]
-    (returned updated, the input untouched)."""
+    (returned updated, the input untouched).  Positions below 0 or at or past
+    S_max are never touched."""
     seq_len = np.asarray(seq_len, dtype=np.int64)
     out_len = seq_len.copy()
     for b in range(len(seq_len)):
@@ -50,7 +51,8 @@ def crop_contiguous(caches, seq_len, n_accepted, appended: int, keep_extra: int,
         if clear:
             for cache in caches:
                 s_max = cache.shape[2]
-                lo, hi = min(new_len, s_max), min(written_end, s_max)
+                lo = min(max(new_len, 0), s_max)
+                hi = min(max(written_end, 0), s_max)
                 if lo < hi:
                     cache[b, :, lo:hi, :] = 0
         out_len[b] = new_len
@@ -58,14 +60,15 @@ def crop_contiguous(caches, seq_len, n_accepted, appended: int, keep_extra: int,
 
 
 def crop_paged(caches, block_table, seq_len, n_accepted, appended: int, keep_extra: int, clear: bool,
-               free_pages, free_count: int):
-    """caches: arrays [num_pages][page_size][H][D] (modified in place);
-    block_table: int [B][max_blocks] (modified in place); free_pages: int
-    array with room for every page (modified in place from free_count on).
-    Returns (new seq_len, new free_count)."""
+               free_pages, free_count: int, page_size: int, num_pages: int):
+    """caches: arrays [num_pages][page_size][H][D] (modified in place; none
+    are needed without `clear`); block_table: int [B][max_blocks]
+    (modified in place; an entry outside [0, num_pages) names no page of these
+    caches); free_pages: int array with room for every page (modified in place
+    from free_count on).  Lengths below 0 count as 0.  Returns (new seq_len,
+    new free_count)."""
     seq_len = np.asarray(seq_len, dtype=np.int64)
     out_len = seq_len.copy()
-    page_size = caches[0].shape[1] if caches else 1
     B, max_blocks = block_table.shape
     for b in range(B):
         n = int(n_accepted[b])
@@ -74,13 +77,13 @@ def crop_paged(caches, block_table, seq_len, n_accepted, appended: int, keep_ext
         new_len = int(seq_len[b]) + keep_extra + n
         written_end = int(seq_len[b]) + appended
         if clear:
-            for s in range(new_len, written_end):
+            for s in range(max(new_len, 0), written_end):
                 j = s // page_size
-                if j >= max_blocks or block_table[b, j] < 0:
+                if j >= max_blocks or not 0 <= block_table[b, j] < num_pages:
                     continue
                 for cache in caches:
                     cache[block_table[b, j], s % page_size] = 0
-        first_free = -(-new_len // page_size)
+        first_free = -(-max(new_len, 0) // page_size)
         for j in range(first_free, max_blocks):
             if block_table[b, j] >= 0:
                 free_pages[free_count] = block_table[b, j]

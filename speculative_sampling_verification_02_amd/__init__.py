@@ -52,6 +52,11 @@ SIGNATURES = {
                                      _c_int, _c_int, _c_int, _c_float,
                                      _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
     "spec_verify_noalloc_limit": (_c_size_t, []),
+    "spec_kv_crop": (_c_int, [_c_void_p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_void_p, _c_void_p,
+                              _c_int, _c_int, _c_int, _c_void_p]),
+    "spec_kv_crop_paged": (_c_int, [_c_void_p, _c_int, _c_int, _c_int, _c_int, _c_void_p, _c_int, _c_int,
+                                    _c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_void_p, _c_void_p, _c_int,
+                                    _c_void_p]),
     "spec_lmhead_verify": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                     _c_int, _c_int, _c_int, _c_int,
                                     _c_void_p, _c_void_p, _c_float,
@@ -225,6 +230,69 @@ def verify_noalloc(target_logits, draft_logits, draft_tokens, uniforms, temperat
                                    _ptr(outputs.get("alpha")), _ptr(outputs.get("p_draft")),
                                    _ptr(outputs.get("q_draft")), _stream(dev)), "spec_verify_noalloc")
     return outputs
+
+
+def _cache_array(caches):
+    """A host array of the caches' device pointers (kept alive by the caller)."""
+    if not caches:
+        return None, 0
+    ptrs = (ctypes.c_void_p * len(caches))(*[c.data_ptr() for c in caches])
+    return ptrs, len(caches)
+
+
+def kv_crop(caches, seq_len, n_accepted, appended: int, keep_extra: int = 0, clear: bool = True):
+    """spec_kv_crop on the current stream.  caches: contiguous GPU tensors
+    [B, H, S_max, D] (any element type; entries of D elements, a multiple of
+    16 bytes); seq_len: int32 [B] (updated in place on the device); n_accepted:
+    int32 [B] as verify() returned it."""
+    torch = _torch()
+    dev = seq_len.device
+    _need(seq_len, "seq_len", torch.int32)
+    _need(n_accepted, "n_accepted", torch.int32, dev)
+    B = seq_len.numel()
+    H = S_max = entry = 1
+    for c in caches:
+        _need(c, "cache", device=dev)
+        if c.dim() != 4 or c.shape[0] != B:
+            raise ValueError("every cache must be [B, H, S_max, D]")
+    if caches:
+        _, H, S_max, D = caches[0].shape
+        entry = D * caches[0].element_size()
+        if any(tuple(c.shape) != tuple(caches[0].shape) or c.element_size() != caches[0].element_size()
+               for c in caches):
+            raise ValueError("the caches must share shape and element size")
+    ptrs, n = _cache_array(list(caches))
+    _check(lib.spec_kv_crop(ptrs, n, B, H, S_max, max(entry, 16), _ptr(seq_len), _ptr(n_accepted), int(appended),
+                            int(keep_extra), int(bool(clear)), _stream(dev)), "spec_kv_crop")
+
+
+def kv_crop_paged(caches, block_table, seq_len, n_accepted, appended: int, free_pages, free_count,
+                  keep_extra: int = 0, clear: bool = True, page_size: int = 0, num_pages: int = 0,
+                  token_bytes: int = 16):
+    """spec_kv_crop_paged on the current stream.  caches: GPU tensors
+    [num_pages, page_size, ...] (the rest of a page slot is one token's
+    entries, a multiple of 16 bytes); block_table int32 [B, max_blocks];
+    seq_len int32 [B]; free_pages int32 [>= num_pages]; free_count int32 [1]
+    (all updated in place on the device).  page_size / num_pages /
+    token_bytes come from the caches when they are given."""
+    torch = _torch()
+    dev = seq_len.device
+    for name, t in (("block_table", block_table), ("seq_len", seq_len), ("n_accepted", n_accepted),
+                    ("free_pages", free_pages), ("free_count", free_count)):
+        _need(t, name, torch.int32, dev)
+    B, max_blocks = block_table.shape
+    if caches:
+        num_pages, page_size = caches[0].shape[0], caches[0].shape[1]
+        token_bytes = caches[0][0, 0].numel() * caches[0].element_size()
+        for c in caches:
+            _need(c, "cache", device=dev)
+            if tuple(c.shape) != tuple(caches[0].shape) or c.element_size() != caches[0].element_size():
+                raise ValueError("the caches must share shape and element size")
+    ptrs, n = _cache_array(list(caches))
+    _check(lib.spec_kv_crop_paged(ptrs, n, int(num_pages), int(page_size), int(token_bytes), _ptr(block_table), B,
+                                  max_blocks, _ptr(seq_len), _ptr(n_accepted), int(appended), int(keep_extra),
+                                  int(bool(clear)), _ptr(free_pages), _ptr(free_count), free_pages.numel(),
+                                  _stream(dev)), "spec_kv_crop_paged")
 
 
 def noalloc_limit() -> int:

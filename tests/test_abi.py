@@ -126,3 +126,21 @@ def test_stream_read_argument_errors():
     assert lib.spec_stream_read(ctypes.c_void_p(0x1004), 64, FAKE, 8, None) == -1
     assert lib.spec_stream_read(FAKE, 64, FAKE, 0, None) == -1
     assert lib.spec_stream_read(FAKE, 0, FAKE, 8, None) == 0
+
+
+def test_kv_crop_rejects_bad_arguments_on_the_host():
+    import speculative_sampling_verification_02_amd as sv
+    lib = sv.lib
+    caches = (ctypes.c_void_p * 1)(0x1000)
+    # entry bytes not a multiple of 16, keep_extra above appended, too many caches
+    assert lib.spec_kv_crop(caches, 1, 2, 1, 8, 8, FAKE, FAKE, 3, 0, 1, None) == sv.SPEC_EINVAL
+    assert lib.spec_kv_crop(caches, 1, 2, 1, 8, 16, FAKE, FAKE, 3, 4, 1, None) == sv.SPEC_EINVAL
+    assert lib.spec_kv_crop(caches, 300, 2, 1, 8, 16, FAKE, FAKE, 3, 0, 1, None) == sv.SPEC_EINVAL
+    assert lib.spec_kv_crop(None, 0, 0, 1, 8, 16, None, None, 3, 0, 1, None) == sv.SPEC_OK   # B == 0
+    misaligned = (ctypes.c_void_p * 1)(0x1008)
+    assert lib.spec_kv_crop(misaligned, 1, 2, 1, 8, 16, FAKE, FAKE, 3, 0, 1, None) == sv.SPEC_EINVAL
+    # paged: a free list smaller than the pool, page size 0
+    assert lib.spec_kv_crop_paged(caches, 1, 10, 4, 16, FAKE, 2, 3, FAKE, FAKE, 3, 0, 1, FAKE, FAKE, 9,
+                                  None) == sv.SPEC_EINVAL
+    assert lib.spec_kv_crop_paged(caches, 1, 10, 0, 16, FAKE, 2, 3, FAKE, FAKE, 3, 0, 1, FAKE, FAKE, 10,
+                                  None) == sv.SPEC_EINVAL

@@ -26,11 +26,11 @@ def dev():
 
 
 @pytest.mark.parametrize("T,dt,polls", [(1.0, "bf16", 1), (0.0, "bf16", 1), (1.0, "f32", 1),
-                                         (1.0, "bf16", 24), (0.0, "bf16", 24)])
+                                         (1.0, "bf16", 2), (1.0, "bf16", 4), (1.0, "bf16", 8), (0.0, "bf16", 4)])
 def test_waits_that_give_up_report_minus_one(dev, T, dt, polls):
     """One poll per wait: every wait whose data is late gives up (nearly every
-    sequence).  24 polls (about as many microseconds): the sequences whose
-    items come first finish, the later ones give up -- in either case each
+    sequence).  A few polls on the B=64, V=128256 batch: the sequences whose
+    items come first can finish while later ones give up -- in every case each
     sequence is -1 or the oracle's result."""
     import torch
     import speculative_sampling_verification_02_amd as sv

@@ -58,7 +58,7 @@ def test_paged_hand_case():
     free = np.full(6, -9, np.int32)
     free[0] = 4                                   # one page already free
     new, count = kv.crop_paged([cache], table, [3, 1], [0, 2], appended=3, keep_extra=0, clear=True,
-                               free_pages=free, free_count=1)
+                               free_pages=free, free_count=1, page_size=P, num_pages=6)
     assert new.tolist() == [3, 3]
     # sequence 0 keeps 3 positions = blocks 0, 1; block 2 (page 5) is released
     assert table.tolist() == [[0, 3, -1, -1], [1, 2, -1, -1]]
@@ -72,11 +72,10 @@ def test_paged_hand_case():
 
 def test_paged_release_order_and_failed_sequence():
     # sequences in order, blocks ascending; a -1 sequence keeps its pages
-    cache = np.zeros((8, 4, 1, 1), np.int8)
     table = np.array([[0, 1, 2, 3], [4, 5, 6, 7], [-1, -1, -1, -1]], np.int32)
     free = np.full(8, -1, np.int32)
-    new, count = kv.crop_paged([cache], table, [1, 4, 0], [0, -1, 2], appended=4, keep_extra=0, clear=False,
-                               free_pages=free, free_count=0)
+    new, count = kv.crop_paged([], table, [1, 4, 0], [0, -1, 2], appended=4, keep_extra=0, clear=False,
+                               free_pages=free, free_count=0, page_size=4, num_pages=8)
     assert new.tolist() == [1, 4, 2]
     assert table.tolist() == [[0, -1, -1, -1], [4, 5, 6, 7], [-1, -1, -1, -1]]
     assert count == 3 and free[:3].tolist() == [1, 2, 3]
@@ -108,11 +107,11 @@ def test_paged_invariants(seed):
     orig = [c.copy() for c in caches]
     t0 = table.copy()
     n = rng.integers(-1, 5, size=len(seq_len))
-    new, count2 = kv.crop_paged(caches, table, seq_len, n, appended, 0, True, free, count)
+    P = caches[0].shape[1]
+    new, count2 = kv.crop_paged(caches, table, seq_len, n, appended, 0, True, free, count, P, caches[0].shape[0])
     after_pages = set(table[table >= 0].tolist()) | set(free[:count2].tolist())
     assert before_pages == after_pages                                     # nothing lost
     assert len(table[table >= 0]) + count2 == len(before_pages)           # nothing duplicated
-    P = caches[0].shape[1]
     for b in range(len(seq_len)):
         if n[b] < 0:
             assert (table[b] == t0[b]).all() and new[b] == seq_len[b]
@@ -139,10 +138,12 @@ def test_planted_mistakes_in_the_crop_are_caught(mutant, monkeypatch):
         monkeypatch.setattr(kv, "crop_contiguous", bad)
         check = test_contiguous_hand_case
     elif mutant == "release_kept_block":
-        def bad(caches, table, seq_len, n, appended, keep_extra, clear, free_pages, free_count):
-            new, cnt = orig_p(caches, table, seq_len, n, appended, keep_extra, clear, free_pages, free_count)
+        def bad(caches, table, seq_len, n, appended, keep_extra, clear, free_pages, free_count, page_size,
+                num_pages):
+            new, cnt = orig_p(caches, table, seq_len, n, appended, keep_extra, clear, free_pages, free_count,
+                              page_size, num_pages)
             for b in range(table.shape[0]):        # also release the last kept block
-                j = -(-int(new[b]) // caches[0].shape[1]) - 1
+                j = -(-int(new[b]) // page_size) - 1
                 if j >= 0 and table[b, j] >= 0:
                     free_pages[cnt] = table[b, j]
                     cnt += 1
