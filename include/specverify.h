@@ -55,7 +55,7 @@ enum { SPEC_F32 = 0, SPEC_BF16 = 1 };
 
 /* Algorithm selector for spec_verify_algo(). */
 enum {
-  SPEC_ALGO_AUTO = 0,      /* the fastest available path for the shape */
+  SPEC_ALGO_AUTO = 0,      /* the faster path: fused at T > 0 where it takes the shape, else multipass */
   SPEC_ALGO_MULTIPASS = 1, /* row statistics, then pair overlap, then a per-sequence finish */
   SPEC_ALGO_FUSED = 2      /* one persistent kernel; every logit is read from HBM once */
 };

@@ -395,11 +395,12 @@ __device__ __attribute__((always_inline)) inline float radix_threshold(const typ
 // width); otherwise elements are loaded one by one and checked against V.
 // The radix pick of the threshold kernels (see the row kernel): over the
 // listed values >= lo, slot q of thread t at cand[q NT + t], my_n of them in
-// this thread's column.  Called by all NT threads of the workgroup.
-template <class E, int NT, bool MASS, class LdsT>
+// this thread's column.  `weight(x)` is the softmax weight of value x on the
+// scale of base and need (MASS only).  Called by all NT threads of the
+// workgroup.
+template <class E, int NT, bool MASS, class LdsT, class WFn>
 __device__ __attribute__((always_inline)) inline float list_pick(LdsT& L, const float* cand, uint32_t my_n, float lo,
-                                                               double base, double need, float mx, float k,
-                                                               float top_p) {
+                                                               double base, double need, WFn weight, float top_p) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
   constexpr int KB = std::is_same<E, BF16>::value ? 16 : 32;
   // key range of the listed values >= lo
@@ -453,7 +454,7 @@ __device__ __attribute__((always_inline)) inline float list_pick(LdsT& L, const 
       const uint32_t d = key_of<KB>(x) - kmin;
       if (x >= lo && (d & hi_mask) == prefix) {
         if constexpr (MASS)
-          atomicAdd(&L.pmass[buf][(d >> shift) & dmask], fixed_mass(__builtin_amdgcn_exp2f((x - mx) * k)));
+          atomicAdd(&L.pmass[buf][(d >> shift) & dmask], fixed_mass(weight(x)));
         else
           atomicAdd(&L.pcnt[buf][(d >> shift) & dmask], 1u);
       }
@@ -568,9 +569,11 @@ __global__ __launch_bounds__(kLTT) void list_threshold_kernel(FilterArgs f) {
     if (tid == 0) f.thr[r] = __uint_as_float(kMarkedBits);
     return;
   }
-  const float tau_k = list_pick<E, kLTT, false>(L, L.cand, my_n, -INFINITY, 0.0, (double)f.top_k, mx, f.k, f.top_p);
+  const float k = f.k;
+  auto weight = [&](float x) { return __builtin_amdgcn_exp2f((x - mx) * k); };
+  const float tau_k = list_pick<E, kLTT, false>(L, L.cand, my_n, -INFINITY, 0.0, (double)f.top_k, weight, f.top_p);
   float tau_p = -INFINITY;
-  if (f.top_p < 1.f) tau_p = list_pick<E, kLTT, true>(L, L.cand, my_n, tau_k, 0.0, -1.0, mx, f.k, f.top_p);
+  if (f.top_p < 1.f) tau_p = list_pick<E, kLTT, true>(L, L.cand, my_n, tau_k, 0.0, -1.0, weight, f.top_p);
   if (tid == 0) f.thr[r] = fmaxf(tau_k, tau_p);
 }
 
@@ -745,7 +748,9 @@ __global__ __launch_bounds__(kFT) void row_threshold_kernel(FilterArgs f) {
   // LDS atomics) and a list of close values needs few passes.  Keys are the
   // 16 significant bits for bf16 rows (the list holds widened bf16 values).
   auto pick = [&](auto mass_c, float lo, double base, double need) -> float {
-    return list_pick<E, kFT, decltype(mass_c)::value>(L, L.big.cand, my_n, lo, base, need, mx, k, f.top_p);
+    return list_pick<E, kFT, decltype(mass_c)::value>(L, L.big.cand, my_n, lo, base, need,
+                                                      [&](float x) { return __builtin_amdgcn_exp2f((x - mx) * k); },
+                                                      f.top_p);
   };
   using BF = std::integral_constant<bool, false>;
   using BT = std::integral_constant<bool, true>;
@@ -864,12 +869,404 @@ __global__ __launch_bounds__(kFT) void row_threshold_kernel(FilterArgs f) {
   if (tid == 0) f.thr[r] = t;
 }
 
+// ------------------------------------------------- streaming nucleus path
+//
+// top-p without top-k, on aligned rows, with a workspace: four launches that
+// spread every row over the whole device (the row kernel holds one row per
+// compute unit at a time).
+//   1. nucleus_stats_kernel, one 128-thread workgroup per chunk of kNChunk
+//      tokens of a row (eight share a compute unit, so one's loads overlap
+//      another's arithmetic): the chunk's maximum scaled logit c = fl(m k)
+//      and its softmax weights exp2(fma(l, k, -c)) summed per octave.  Token
+//      l falls in octave floor(fl(l k)), a function of l alone, so a tie
+//      group never straddles two octaves, within a chunk or across chunks.
+//      The bins are the 31 octaves from floor(c) down and a tail bin for
+//      every lower one.  A weight in bin b lies in [2^-b-1, 2^-b+1) and is
+//      added as the integer trunc(w 2^(24 + b)) < 2^25 (at most 2^-23 of it
+//      lost) to the thread's own LDS column with an integer atomic (LDS float
+//      atomics are an order of magnitude slower on gfx950); integer sums are
+//      exact, so the order of the additions does not matter.
+//   2. nucleus_cross_kernel, one wave per row: the row's octave masses (each
+//      chunk's scaled by exp2(c_chunk - C), C the row's maximum, in fp64 and
+//      one fixed order), the total Z, the crossing octave o* (the first from
+//      the top at which the running mass reaches top_p Z) with the mass above
+//      it, and the logit interval [lo, hi) of octave o*.
+//   3. nucleus_list_kernel, per chunk: lists the chunk's values in [lo, hi)
+//      (at most kNThreadCap per thread and kChunkCap per chunk).
+//   4. nucleus_pick_kernel, per row: the exact threshold within the row's
+//      lists (the row kernel's radix pick over 2^-40 fixed-point weights
+//      exp2(fma(l, k, -C)), starting from the mass above o*).
+// A row the path cannot finish (no finite logit, a crossing inside a chunk's
+// tail bin or more than 64 octaves down, an overflowing list) gets
+// kMarkedBits, and the row kernel takes it.  The path leaves its workspace
+// zero: the cross kernel clears the chunk records it read, and the pick
+// kernel the row's record, list counts and lists.
+constexpr int kNT = 128;              // threads of the chunk kernels
+constexpr int kNPer = 64;             // tokens per thread
+constexpr int kNChunk = kNT * kNPer;  // tokens per chunk
+constexpr int kOB = 32;               // octave bins of a chunk, the last one the tail
+constexpr int kNThreadCap = 16;       // values a thread may list per chunk
+constexpr int kChunkCap = 512;        // values a chunk may list
+constexpr int kNCap = kListSlots;     // values a row may list in all
+constexpr uint32_t kChunkOverflow = kChunkCap + 1;
+// Waves per SIMD the chunk kernels' registers allow (an fp32 chunk's raw words
+// take twice a bf16 chunk's).
+template <class E>
+constexpr int chunk_waves() { return std::is_same<E, BF16>::value ? 4 : 3; }
+
+struct ChunkStat {
+  float c;  // fl(m k), m the chunk's maximum logit (-inf: no finite logit)
+  float pad;
+  double mass[kOB];  // weights relative to exp2(c), per octave below floor(c)
+};
+struct RowCross {
+  float C;       // the row's maximum scaled logit
+  float octave;  // o*, an integer as a float; NaN: the row is left to the row kernel
+  float lo, hi;  // the logits of octave o*: lo <= l < hi
+  double base;   // mass of the octaves above o*, relative to exp2(C)
+  double target;  // top_p times the row's total mass
+};
+
+template <class E>
+__device__ inline const typename E::storage* filter_row(const FilterArgs& f, int r) {
+  return r < f.nt ? static_cast<const typename E::storage*>(f.target) + (size_t)r * f.V
+                  : static_cast<const typename E::storage*>(f.draft) + (size_t)(r - f.nt) * f.V;
+}
+
+// The raw vectors of one chunk: vector s of thread t at lo + (s kNT + t) kVec.
+template <class E>
+struct ChunkRaw {
+  u32x4 v[kNPer / E::kVec];
+};
+
+// Loads chunk q (row q / nch); vectors past V read as zero (V is a multiple
+// of kVec) and are masked to -inf by unpack_chunk.
+template <class E>
+__device__ inline void issue_chunk(const FilterArgs& f, int nch, int q, ChunkRaw<E>& raw) {
+  const int lo = (q % nch) * kNChunk;
+  const auto* row = filter_row<E>(f, q / nch);
+#pragma unroll
+  for (int s = 0; s < kNPer / E::kVec; ++s) {
+    const int j0 = lo + (s * kNT + (int)threadIdx.x) * E::kVec;
+    raw.v[s] = j0 < f.V ? load_cached(row + j0) : u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+template <class E>
+__device__ inline void unpack_chunk(const ChunkRaw<E>& raw, int lo, int V, float (&x)[kNPer]) {
+  constexpr int NS = kNPer / E::kVec;
+  if (lo + kNChunk <= V) {  // no per-token select
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      float t[E::kVec];
+      E::unpack(raw.v[s], t);
+#pragma unroll
+      for (int e = 0; e < E::kVec; ++e) x[s * E::kVec + e] = t[e];
+    }
+    return;
+  }
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int j0 = lo + (s * kNT + (int)threadIdx.x) * E::kVec;
+    float t[E::kVec];
+    E::unpack(raw.v[s], t);
+#pragma unroll
+    for (int e = 0; e < E::kVec; ++e) x[s * E::kVec + e] = j0 < V ? t[e] : -INFINITY;
+  }
+}
+
+// floor(x) as an integer in one instruction; out of range saturates (-inf
+// gives INT_MIN), which a C++ conversion would leave undefined.
+__device__ inline int floor_i32(float x) {
+  int r;
+  asm("v_cvt_flr_i32_f32 %0, %1" : "=v"(r) : "v"(x));
+  return r;
+}
+// Octave of a token: floor(fl(l k)).
+__device__ inline int octave_of(float x, float k) { return floor_i32(x * k); }
+
+// The smallest float v (-inf included) with octave_of(v, k) >= o, by a binary
+// search over the order-preserving keys of the floats (octave_of is
+// non-decreasing in v for k > 0).  +inf if there is none below +inf.
+__device__ inline float first_in_octave(int o, float k) {
+  auto value = [](uint32_t key) {
+    return __uint_as_float((key & 0x80000000u) ? (key ^ 0x80000000u) : ~key);
+  };
+  uint32_t lo = 0x007fffffu, hi = 0xff800000u;  // the keys of -inf and +inf
+  if (octave_of(value(lo), k) >= o) return -INFINITY;
+  while (hi - lo > 1u) {  // octave_of(value(lo)) < o <= octave_of(value(hi))
+    const uint32_t mid = lo + (hi - lo) / 2u;
+    if (octave_of(value(mid), k) >= o)
+      hi = mid;
+    else
+      lo = mid;
+  }
+  return value(hi);
+}
+
+// One chunk per workgroup: work(raw, q) on chunk q = the workgroup's index
+// (called by the whole workgroup).
+template <class E, class Work>
+__device__ __attribute__((always_inline)) inline void chunk_loop(const FilterArgs& f, int nch, int nq, Work work) {
+  const int q = blockIdx.x;
+  if (q >= nq) return;
+  ChunkRaw<E> A;
+  issue_chunk<E>(f, nch, q, A);
+  work(A, q);
+}
+
+template <class E>
+__global__ __launch_bounds__(kNT, chunk_waves<E>()) void nucleus_stats_kernel(FilterArgs f, int nch, int nq,
+                                                                              ChunkStat* stats) {
+  // hist[b][t] (bin b of thread t's column: the lanes of an addition hit
+  // distinct banks) and, after the transpose, hist as [t][kOB + 1] (a
+  // thread's bins in a padded row: summing one bin over rows hits distinct
+  // banks)
+  __shared__ uint32_t hist[kNT * (kOB + 1)];
+  __shared__ uint64_t part[kNT / kOB][kOB];
+  __shared__ float redf[2 * kMaxWaves];
+  const int tid = threadIdx.x;
+  const float k = f.k;
+  // LDS byte address of hist[b][tid] is col + (24 + b) * 4 kNT: one shift-add
+  // from the exponent e = 24 + b below
+  const uint32_t col = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint32_t*)&hist[tid] -
+                       24u * 4u * (uint32_t)kNT;
+  chunk_loop<E>(f, nch, nq, [&](const ChunkRaw<E>& raw, int q) {
+    float x[kNPer];
+    unpack_chunk<E>(raw, (q % nch) * kNChunk, f.V, x);
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < kNPer; ++i) tmax = fmaxf(tmax, x[i]);
+    const float m = block_max(tmax, redf);  // its first barrier also ends the last chunk's reads of hist
+#pragma unroll
+    for (int b = 0; b < kOB; ++b) hist[b * kNT + tid] = 0u;
+    const float c = m * k;
+    if (c != -INFINITY) {  // uniform over the workgroup
+      const uint32_t top = (uint32_t)floor_i32(c);
+#pragma unroll
+      for (int i = 0; i < kNPer; ++i) {
+        const float w = fast_exp2(fmaf(x[i], k, -c));
+        // e = 24 + the octaves below the top one, at most 24 + the tail bin
+        // (-inf, octave INT_MIN, wraps to a large value and lands in the tail
+        // with weight 0)
+        const uint32_t e = min(top + 24u - (uint32_t)octave_of(x[i], k), (uint32_t)(24 + kOB - 1));
+        const uint32_t qw = (uint32_t)__builtin_amdgcn_ldexpf(w, (int)e);
+        __hip_atomic_fetch_add((__attribute__((address_space(3))) uint32_t*)(uintptr_t)(col + e * 4u * (uint32_t)kNT),
+                               qw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      }
+    }
+    __syncthreads();
+    uint32_t colv[kOB];
+#pragma unroll
+    for (int b = 0; b < kOB; ++b) colv[b] = hist[b * kNT + tid];
+    __syncthreads();
+#pragma unroll
+    for (int b = 0; b < kOB; ++b) hist[tid * (kOB + 1) + b] = colv[b];
+    __syncthreads();
+    {  // thread t sums bin t % kOB over one group of kNT / kG columns (exact)
+      constexpr int kG = kNT / kOB;
+      const int b = tid % kOB, g = tid / kOB;
+      uint64_t sum = 0;
+#pragma unroll 8
+      for (int j = 0; j < kNT / kG; ++j) sum += hist[(g * (kNT / kG) + j) * (kOB + 1) + b];
+      part[g][b] = sum;
+    }
+    __syncthreads();
+    ChunkStat* st = stats + (size_t)q;
+    if (tid < kOB) {
+      uint64_t sum = 0;  // below 2^39: exact in fp64
+#pragma unroll
+      for (int g = 0; g < kNT / kOB; ++g) sum += part[g][tid];
+      st->mass[tid] = __builtin_amdgcn_ldexp((double)sum, -(24 + tid));
+    }
+    if (tid == 0) st->c = c;
+  });
+}
+
+__global__ __launch_bounds__(kWave) void nucleus_cross_kernel(FilterArgs f, int nch, ChunkStat* stats,
+                                                               RowCross* rc) {
+  const int lane = threadIdx.x, r = blockIdx.x;
+  ChunkStat* st = stats + (size_t)r * nch;
+  float cm = -INFINITY;
+  for (int c = lane; c < nch; c += kWave) cm = fmaxf(cm, st[c].c);
+  const float C = wave_max(cm);
+  const float nan = __uint_as_float(0x7fc00000u);
+  RowCross out{C, nan, 0.f, 0.f, 0.0, 0.0};
+  if (C != -INFINITY) {
+    const int R = floor_i32(C);
+    // lane j: the row's octave R - j, from every chunk's bin j - d (d the
+    // chunk's top octave below R), the chunks in order; bins past a chunk's
+    // tail start are not resolved, so the crossing must lie above `limit`.
+    // The chunks' offsets and scale factors are formed by the lanes in
+    // parallel, kWave chunks at a time.
+    double bin = 0.0, zpart = 0.0;
+    int limit = kWave;
+    for (int c0 = 0; c0 < nch; c0 += kWave) {
+      const int cl = c0 + lane;
+      const float cc = cl < nch ? st[cl].c : -INFINITY;
+      const int dl = cc == -INFINITY ? kWave + kOB : R - floor_i32(cc);
+      const double sl = cc == -INFINITY ? 0.0 : exp2((double)cc - (double)C);
+      const int n = min(kWave, nch - c0);
+      for (int i = 0; i < n; ++i) {
+        const int d = __builtin_amdgcn_readlane(dl, i);
+        const double sc = lane_d(sl, i);
+        const ChunkStat& cs = st[c0 + i];
+        const int b = lane - d;
+        if (b >= 0 && b < kOB - 1) bin += cs.mass[b] * sc;
+        if (lane < kOB) zpart += cs.mass[lane] * sc;
+        limit = min(limit, d + kOB - 1);
+      }
+    }
+    const double Z = wave_sum(zpart);
+    const double target = (double)f.top_p * Z;
+    const double incl = wave_inclusive_scan(bin);
+    const unsigned long long reach = __ballot(incl >= target);
+    if (reach) {
+      const int j = __ffsll((long long)reach) - 1;
+      const double above = j > 0 ? lane_d(incl, j - 1) : 0.0;
+      if (j < limit) {
+        out.octave = (float)(R - j);
+        out.base = above;
+        out.target = target;
+        out.lo = first_in_octave(R - j, f.k);
+        out.hi = first_in_octave(R - j + 1, f.k);
+      }
+    }
+  }
+  // every record of the row has been read: clear them
+  for (int c = 0; c < nch; ++c) {
+    double* w = reinterpret_cast<double*>(st + c);
+    for (int i = lane; i < (int)(sizeof(ChunkStat) / sizeof(double)); i += kWave) w[i] = 0.0;
+  }
+  if (lane == 0) rc[r] = out;
+}
+
+template <class E>
+__global__ __launch_bounds__(kNT, chunk_waves<E>()) void nucleus_list_kernel(FilterArgs f, int nch, int nq,
+                                                                             const RowCross* rc, uint32_t* lcnt,
+                                                                             float* lvals) {
+  __shared__ float cand[kNThreadCap + 1][kNT];  // slot s of thread t at cand[s][t]; slot kNThreadCap spare
+  __shared__ float redf[2 * kMaxWaves];
+  const int tid = threadIdx.x;
+  chunk_loop<E>(f, nch, nq, [&](const ChunkRaw<E>& raw, int q) {
+    // a row left to the row kernel has the empty interval [0, 0) and lists
+    // nothing
+    const float lo = rc[q / nch].lo, hi = rc[q / nch].hi;
+    float x[kNPer];
+    unpack_chunk<E>(raw, (q % nch) * kNChunk, f.V, x);
+    // branchless: every value is written to the thread's next free slot (the
+    // spare slot once the column is full), and only a value in [lo, hi)
+    // advances it
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int i = 0; i < kNPer; ++i) {
+      cand[min(cnt, (uint32_t)kNThreadCap)][tid] = x[i];
+      cnt += (x[i] >= lo && x[i] < hi) ? 1u : 0u;
+    }
+    const uint32_t mine = min(cnt, (uint32_t)kNThreadCap);
+    float excl, total;
+    block_scan((float)mine, redf, &excl, &total);  // exact: at most kNT kNThreadCap
+    const int over = __syncthreads_or(cnt > (uint32_t)kNThreadCap) || total > (float)kChunkCap;
+    if (!over) {
+      float* dst = lvals + (size_t)q * kChunkCap + (uint32_t)excl;
+      for (uint32_t j = 0; j < mine; ++j) dst[j] = cand[j][tid];
+    }
+    if (tid == 0) lcnt[q] = over ? kChunkOverflow : (uint32_t)total;
+  });
+}
+
+// The pick kernel's gather: the row's listed values, entry i in slot i / kLTT
+// of thread i % kLTT, at most kNCap of them.
+constexpr int kGatherSteps = kNCap / kLTT;
+
+template <class E>
+__global__ __launch_bounds__(kLTT) void nucleus_pick_kernel(FilterArgs f, int nch, RowCross* rc, uint32_t* lcnt,
+                                                           float* lvals) {
+  __shared__ ListLds L;
+  const int tid = threadIdx.x, r = blockIdx.x;
+  const RowCross x = rc[r];
+  uint32_t* cnt = lcnt + (size_t)r * nch;
+  if (tid == 0) {  // exclusive prefix of the chunk counts
+    uint32_t acc = 0, ovf = 0;
+    for (int c = 0; c < nch; ++c) {
+      const uint32_t n = cnt[c];
+      L.lpre[c] = acc;
+      ovf |= n > (uint32_t)kChunkCap ? 1u : 0u;
+      acc += min(n, (uint32_t)kChunkCap);
+    }
+    L.lpre[nch] = acc;
+    L.lovf = ovf;
+  }
+  __syncthreads();
+  const uint32_t n_all = L.lpre[nch];
+  const bool ok = x.octave == x.octave && L.lovf == 0u && n_all > 0u && n_all <= (uint32_t)kNCap;
+  const uint32_t n = min(n_all, (uint32_t)kNCap);
+  float v[kGatherSteps];
+  float* src[kGatherSteps];
+  int c = 0;
+#pragma unroll
+  for (int j = 0; j < kGatherSteps; ++j) {  // every load first, then every use
+    const uint32_t i = (uint32_t)(tid + j * kLTT);
+    src[j] = nullptr;
+    v[j] = 0.f;
+    if (i < n) {
+      while (L.lpre[c + 1] <= i) ++c;  // i grows, so the chunk only advances
+      src[j] = lvals + ((size_t)r * nch + c) * kChunkCap + (i - L.lpre[c]);
+      v[j] = *src[j];
+    }
+  }
+  uint32_t my_n = 0;
+#pragma unroll
+  for (int j = 0; j < kGatherSteps; ++j) {
+    if (src[j]) {
+      *src[j] = 0.f;
+      if (ok) {
+        L.cand[j * kLTT + tid] = v[j];
+        ++my_n;
+      }
+    }
+  }
+  __syncthreads();  // every thread has read the row's record and counts
+  if (tid < nch) cnt[tid] = 0u;
+  if (tid == 0) rc[r] = RowCross{0.f, 0.f, 0.f, 0.f, 0.0, 0.0};
+  if (!ok) {
+    if (tid == 0) f.thr[r] = __uint_as_float(kMarkedBits);
+    return;
+  }
+  const float C = x.C, k = f.k;
+  const float tau = list_pick<E, kLTT, true>(L, L.cand, my_n, -INFINITY, x.base, x.target,
+                                             [&](float w) { return fast_exp2(fmaf(w, k, -C)); }, f.top_p);
+  if (tid == 0) f.thr[r] = tau;
+}
+}  // namespace
+
+namespace {
+// Layout of the streaming nucleus path in the filter workspace: row records,
+// chunk records, row lists.
+struct NucleusLayout {
+  int nch;
+  size_t off_stats, off_counts, off_lists, total;
+};
+NucleusLayout nucleus_layout(size_t rows, int V) {
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  NucleusLayout L{};
+  L.nch = (V + kNChunk - 1) / kNChunk;
+  const size_t nq = rows * (size_t)L.nch;
+  L.off_stats = up(rows * sizeof(RowCross));
+  L.off_counts = L.off_stats + up(nq * sizeof(ChunkStat));
+  L.off_lists = L.off_counts + up(nq * sizeof(uint32_t));
+  L.total = L.off_lists + up(nq * (size_t)kChunkCap * sizeof(float));
+  return L;
+}
+
 }  // namespace
 
 size_t filter_list_bytes(int B, int gamma, int V) {
   const size_t rows = (size_t)B * (2 * gamma + 1), nch = ((size_t)V + kLChunk - 1) / kLChunk;
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  return up(rows * nch * sizeof(uint32_t)) + up(rows * nch * kListCap * sizeof(float));
+  // the chunk lists of a small top-k and the nucleus path share the region
+  return std::max(up(rows * nch * sizeof(uint32_t)) + up(rows * nch * kListCap * sizeof(float)),
+                  nucleus_layout(rows, V).total);
 }
 
 hipError_t filter_thresholds(const VerifyArgs& a, int top_k, float top_p, float* thr, void* lists, hipStream_t s) {
@@ -883,7 +1280,35 @@ hipError_t filter_thresholds(const VerifyArgs& a, int top_k, float top_p, float*
   // left zero by the row kernel)
   // (rows of more than 256 chunks keep to the row path: the row kernel holds
   // at most 256 chunk offsets)
-  if (lists != nullptr && top_k > 0 && top_k <= kListK && top_k < a.V && (a.V + kLChunk - 1) / kLChunk <= 256) {
+  if (lists != nullptr && aligned && !(top_k > 0 && top_k < a.V) && top_p < 1.f &&
+      (a.V + kNChunk - 1) / kNChunk <= 256) {
+    // top-p alone: the streaming nucleus path (the region is zero on entry
+    // and is left zero; the pick kernel holds at most 256 chunk offsets)
+    const NucleusLayout NL = nucleus_layout((size_t)rows, a.V);
+    char* base = static_cast<char*>(lists);
+    RowCross* rc = reinterpret_cast<RowCross*>(base);
+    ChunkStat* stats = reinterpret_cast<ChunkStat*>(base + NL.off_stats);
+    uint32_t* lcnt = reinterpret_cast<uint32_t*>(base + NL.off_counts);
+    float* lvals = reinterpret_cast<float*>(base + NL.off_lists);
+    const int nq = rows * NL.nch;
+    if (a.dtype == SPEC_BF16)
+      nucleus_stats_kernel<BF16><<<dim3(nq), dim3(kNT), 0, s>>>(f, NL.nch, nq, stats);
+    else
+      nucleus_stats_kernel<F32><<<dim3(nq), dim3(kNT), 0, s>>>(f, NL.nch, nq, stats);
+    nucleus_cross_kernel<<<dim3(rows), dim3(kWave), 0, s>>>(f, NL.nch, stats, rc);
+    if (a.dtype == SPEC_BF16)
+      nucleus_list_kernel<BF16><<<dim3(nq), dim3(kNT), 0, s>>>(f, NL.nch, nq, rc, lcnt, lvals);
+    else
+      nucleus_list_kernel<F32><<<dim3(nq), dim3(kNT), 0, s>>>(f, NL.nch, nq, rc, lcnt, lvals);
+    if (a.dtype == SPEC_BF16)
+      nucleus_pick_kernel<BF16><<<dim3(rows), dim3(kLTT), 0, s>>>(f, NL.nch, rc, lcnt, lvals);
+    else
+      nucleus_pick_kernel<F32><<<dim3(rows), dim3(kLTT), 0, s>>>(f, NL.nch, rc, lcnt, lvals);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // the row kernel takes only the rows the nucleus path left to it
+    f.marked_only = 1;
+  } else if (lists != nullptr && top_k > 0 && top_k <= kListK && top_k < a.V && (a.V + kLChunk - 1) / kLChunk <= 256) {
     f.nch = (a.V + kLChunk - 1) / kLChunk;
     f.lcount = static_cast<uint32_t*>(lists);
     f.lvals = reinterpret_cast<float*>(static_cast<char*>(lists) +

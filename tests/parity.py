@@ -65,10 +65,14 @@ D_j = sum_{x <= j} d_x + 20 u (P_j + l Q_j), and the normalised step by
 computed as empty, and then p_n is sampled (the pages' zero-mass reading):
 either reading is valid there.
 
-Nucleus: the threshold kernels weigh tokens by exp2((l - m) k~) in fp32 (the
-tilt, the argument rounded twice, exp2 at 2 ulp) and sum the weights in fp64,
-so the normalised masses compared with top_p are off by at most 2 E_nuc, with
-e_x = ln2 (d_k + 2 u) A_x + 4 u over the top-k survivors.
+Nucleus: the row and list threshold kernels weigh tokens by exp2((l - m) k~)
+in fp32 (the tilt, the argument rounded twice, exp2 at 2 ulp) and sum the
+weights in fp64 or 2^-40 fixed point; the streaming nucleus path weighs them by
+exp2(fma(l, k~, -c)) (the argument rounded once, exp2 at 2 ulp) and truncates
+each to 24 fractional bits of its octave (at most 2 u) before exact integer
+sums.  Both stay within e_x = ln2 (d_k + 2 u) A_x + 4 u over the top-k
+survivors, and the normalised masses compared with top_p are off by at most
+2 E_nuc.
 """
 
 from __future__ import annotations

@@ -107,13 +107,19 @@ def test_filter_threshold_argument_errors(kw, status):
 
 
 def test_filter_workspace_size():
-    """One count and 256 list slots per row and 8192-token chunk, each part
-    rounded up to 256 bytes; 0 for a bad shape."""
+    """The larger of two layouts that share the region, each part rounded up
+    to 256 bytes: the top-k chunk lists (one count and 256 list slots per row
+    and 8192-token chunk) and the nucleus path (a 32-byte record per row, and
+    per row and 8192-token chunk a 264-byte record, a count and 512 list
+    slots); 0 for a bad shape."""
     import speculative_sampling_verification_02_amd as sv
     up = lambda x: (x + 255) // 256 * 256  # noqa: E731
     for B, g, V in ((64, 4, 128256), (1, 3, 32128), (3, 0, 100)):
         rows, nch = B * (2 * g + 1), (V + 8191) // 8192
-        assert sv.filter_workspace_size(B, g, V) == up(4 * rows * nch) + up(4 * rows * nch * 256)
+        lists = up(4 * rows * nch) + up(4 * rows * nch * 256)
+        nq = rows * nch
+        nucleus = up(32 * rows) + up(264 * nq) + up(4 * nq) + up(4 * nq * 512)
+        assert sv.filter_workspace_size(B, g, V) == max(lists, nucleus)
     assert sv.filter_workspace_size(-1, 3, 100) == 0
 
 
