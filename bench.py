@@ -42,8 +42,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "verified logit rows/s (B*(gamma+1) x V) and % of peak HBM GB/s at V=128256"
 HBM_PEAK_GBS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = ["verify_multipass.hip", "verify_fused.hip", "common.hpp"]
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters.json")
+CSRC = os.path.join(ROOT, "speculative_sampling_verification_02_amd", "csrc")
 WORKLOAD_TEXT = {
     "verify": "Gaussian rows with 8 peaked tokens, per-sequence draft noise",
     "small1": "target N(0, 2^2), draft = target + N(0, 1)",
@@ -54,11 +54,13 @@ WORKLOAD_TEXT = {
 
 
 def kernel_source_hash() -> str:
+    """Hash of every kernel source: a counter record taken on other sources is
+    not reported."""
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
-        path = os.path.join(ROOT, "speculative_sampling_verification_02_amd", "csrc", name)
-        with open(path, "rb") as f:
-            h.update(f.read())
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".hpp")):
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 
@@ -118,16 +120,18 @@ def cpu_baseline(case, budget_s: float = 10.0) -> dict:
                       f"{calls} call(s) in {dt:.1f} s, NumPy fp64 on {threads} threads"}
 
 
-def load_traffic(algo_name: str):
+def load_counters(key: str) -> dict:
+    """The rocprofv3 counter record of one workload (profiles/counters.json:
+    HBM bytes per launch from FETCH_SIZE and WRITE_SIZE scaled by a copy of
+    known size, vector-ALU or matrix-core busy), or {} when it is missing or
+    was taken on other kernel sources."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(COUNTERS_FILE) as f:
             rec = json.load(f)
     except (OSError, ValueError):
-        return None
-    entry = rec.get(algo_name)
-    if not entry or entry.get("source_hash") != kernel_source_hash():
-        return None
-    return entry.get("bytes_per_launch")
+        return {}
+    entry = rec.get(key) or {}
+    return entry if entry.get("source_hash") == kernel_source_hash() else {}
 
 
 class LoopTime:
@@ -153,6 +157,16 @@ def timed_loop(torch, steps: int, step) -> LoopTime:
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     return LoopTime(1e3 * e0.elapsed_time(e1) / steps, wall)
+
+
+def copy_calibration(torch, dev) -> None:
+    """One plain 1 GiB device-to-device copy: under rocprofv3 --pmc it gives the
+    scale of FETCH_SIZE and WRITE_SIZE for bytes of known count."""
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def stream_read_rate(torch, sv, dev, nbytes: int = 1 << 30, reps: int = 20) -> float:
@@ -259,11 +273,7 @@ def main() -> int:
         launches[k % len(sets)]()
 
     if args.copy_calibration:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        copy_calibration(torch, dev)
 
     for k in range(args.warmup):
         step(k)
@@ -283,10 +293,14 @@ def main() -> int:
     achieved = alg / avg_launch_s / 1e9
     algo_name = {sv.ALGO_AUTO: "auto", sv.ALGO_MULTIPASS: "multipass", sv.ALGO_FUSED: "fused"}[algo]
     # AUTO dispatches the headline workload (aligned bf16 rows, 16 workgroups
-    # per row) to the fused kernel, whose counters the traffic record holds
-    traffic = None
-    if args.workload == "verify" and T == 1.0 and default_path and not args.vocab:
-        traffic = load_traffic("fused" if algo_name == "auto" else algo_name)
+    # per row) to the fused kernel at T = 1 and to the multipass path at T = 0;
+    # the counter record holds both
+    counters = {}
+    if args.workload == "verify" and default_path and not args.vocab:
+        if T == 1.0 and algo_name in ("auto", "fused"):
+            counters = load_counters("fused_verify_T1")
+        elif T == 0.0 and algo_name in ("auto", "multipass"):
+            counters = load_counters("multipass_verify_T0")
     line = {
         "metric": METRIC,
         "value": rows / (ms_per_step * 1e-3),
@@ -307,10 +321,11 @@ def main() -> int:
                    "gamma_seq": None if gseq_np is None else "U{1..gamma}, mean %.2f" % gseq_np.mean(),
                    "top_k": args.top_k, "top_p": args.top_p},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": counters.get("traffic_bytes"),
                      "launch_us_mean": launch_us.mean,
                      "alg_bytes": alg, "full_bytes": (2 * G + 1) * V * elem * B,
-                     "stream_read_GBps": stream_gbs, "frac_of_stream_read": achieved / stream_gbs},
+                     "stream_read_GBps": stream_gbs, "frac_of_stream_read": achieved / stream_gbs,
+                     "valu_busy_pct": counters.get("valu_busy_pct")},
     }
     if not args.no_cpu_baseline and default_path and not args.vocab:
         line["cpu_baseline"] = cpu_baseline(case)
@@ -357,6 +372,8 @@ def run_lmhead(args) -> int:
     def step():
         sv.lmhead_verify(hidden, wp, wq, B, G, tokens, uniforms, 1.0, workspace=ws, outputs=out)
 
+    if args.copy_calibration:
+        copy_calibration(torch, dev)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -364,6 +381,9 @@ def run_lmhead(args) -> int:
     ms_per_step = 1e3 * launch_us.wall_s / args.steps
     step_bytes = lmhead_step_bytes(out["n_accepted"].cpu().numpy(), B, G, d, V)
     achieved = step_bytes / (launch_us.mean * 1e-6) / 1e9
+    # counters of the step's two kernels (the LM-head GEMM and the
+    # verification), and the GEMM's matrix-core busy share of its span
+    counters = load_counters("lmhead")
     line = {
         "metric": METRIC,
         "value": B * (G + 1) / (ms_per_step * 1e-3),
@@ -384,9 +404,11 @@ def run_lmhead(args) -> int:
         # verification launch on its fp32 logits; the bytes and the duration
         # are those of the whole step
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": counters.get("traffic_bytes"),
                      "launch_us_mean": launch_us.mean,
-                     "step_bytes": step_bytes},
+                     "step_bytes": step_bytes,
+                     "lmhead_traffic_bytes": counters.get("lmhead_traffic_bytes"),
+                     "mfma_util_pct": counters.get("mfma_util_pct")},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = lmhead_cpu_baseline(case, out)

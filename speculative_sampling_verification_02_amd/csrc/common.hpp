@@ -135,6 +135,29 @@ __device__ inline ArgMax argmax_better(ArgMax a, ArgMax b) {
   return a;
 }
 
+// Argmax of a thread's N values visited in increasing token order (token(t)
+// increasing in t): the maximum by a tree of three-input maxima, then the
+// first value equal to it, found backwards.  About two instructions per value
+// instead of a compare-and-select of the (value, index) pair for each.  Equal
+// values include -0 and +0 and, for a thread of -inf only, every value: the
+// lowest index wins, as argmax_better would choose.
+template <int N, class TokenFn>
+__device__ inline ArgMax thread_argmax_first(const float (&x)[N], TokenFn token) {
+  static_assert(N % 2 == 0, "pairs of values");
+  float m0 = x[0], m1 = x[1];
+#pragma unroll
+  for (int t = 2; t + 3 < N; t += 4) {
+    m0 = __builtin_fmaxf(m0, __builtin_fmaxf(x[t], x[t + 1]));
+    m1 = __builtin_fmaxf(m1, __builtin_fmaxf(x[t + 2], x[t + 3]));
+  }
+  if constexpr (N % 4 == 0) m0 = __builtin_fmaxf(m0, __builtin_fmaxf(x[N - 2], x[N - 1]));
+  const float m = __builtin_fmaxf(m0, m1);
+  int first = 0;  // (some value equals m, so the last assignment is to the first of them)
+#pragma unroll
+  for (int t = N - 1; t >= 0; --t) first = x[t] == m ? t : first;
+  return ArgMax{m, token(first)};
+}
+
 template <int CTRL>
 __device__ inline ArgMax dpp_argmax(ArgMax a) {
   return argmax_better(a, ArgMax{dpp_f<CTRL>(a.v), dpp_i<CTRL>(a.i)});

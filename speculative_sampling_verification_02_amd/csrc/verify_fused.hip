@@ -387,10 +387,7 @@ __device__ inline float2 wave_lse(float c, float s) {
 
 template <class E, int PER>
 __device__ inline ArgMax thread_argmax(const float (&x)[PER], int tile_lo) {
-  ArgMax best{-INFINITY, 0x7fffffff};
-#pragma unroll
-  for (int i = 0; i < PER; ++i) best = argmax_better(best, ArgMax{x[i], tile_token<E::kVec>(tile_lo, i)});
-  return best;
+  return thread_argmax_first(x, [&](int i) { return tile_token<E::kVec>(tile_lo, i); });
 }
 
 // Row normalisers of both rows of an item from its W published word pairs

@@ -83,6 +83,16 @@ struct ChunkRegs {
     }
   }
   __device__ inline void unpack(int lo, int hi) {
+    if (lo + kChunk <= hi) {  // the whole chunk is in range: no per-token select
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        float t[E::kVec];
+        E::unpack(raw[s], t);
+#pragma unroll
+        for (int v = 0; v < E::kVec; ++v) x[s * E::kVec + v] = t[v];
+      }
+      return;
+    }
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       const int j0 = lo + (s * kThreads + (int)threadIdx.x) * E::kVec;
@@ -122,9 +132,7 @@ __global__ __launch_bounds__(kThreads) void row_stats_kernel(VerifyArgs a, float
     ChunkRegs<E> ch;
     ch.load(r, lo, hi);
     if constexpr (ARGMAX) {
-      ArgMax best{-INFINITY, 0x7fffffff};
-#pragma unroll
-      for (int t = 0; t < ChunkRegs<E>::kPer; ++t) best = argmax_better(best, ArgMax{ch.x[t], ch.token(lo, t)});
+      ArgMax best = thread_argmax_first(ch.x, [&](int t) { return ch.token(lo, t); });
       best = block_argmax(best, lds_f, lds_i);
       if (threadIdx.x == 0) stats[blockIdx.x] = make_float2(best.v, __int_as_float(best.i));
     } else {
