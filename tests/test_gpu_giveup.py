@@ -26,7 +26,8 @@ def dev():
 
 
 @pytest.mark.parametrize("T,dt,polls", [(1.0, "bf16", 1), (0.0, "bf16", 1), (1.0, "f32", 1),
-                                         (1.0, "bf16", 2), (1.0, "bf16", 4), (1.0, "bf16", 8), (0.0, "bf16", 4)])
+                                         (1.0, "bf16", 2), (1.0, "bf16", 4), (1.0, "bf16", 8), (0.0, "bf16", 4),
+                                         (1.0, "bf16", 16), (1.0, "bf16", 64)])
 def test_waits_that_give_up_report_minus_one(dev, T, dt, polls):
     """One poll per wait: every wait whose data is late gives up (nearly every
     sequence).  A few polls on the B=64, V=128256 batch: the sequences whose
