@@ -1107,14 +1107,29 @@ __global__ __launch_bounds__(kWave) void nucleus_cross_kernel(FilterArgs f, int 
       const int dl = cc == -INFINITY ? kWave + kOB : R - floor_i32(cc);
       const double sl = cc == -INFINITY ? 0.0 : exp2((double)cc - (double)C);
       const int n = min(kWave, nch - c0);
-      for (int i = 0; i < n; ++i) {
-        const int d = __builtin_amdgcn_readlane(dl, i);
-        const double sc = lane_d(sl, i);
-        const ChunkStat& cs = st[c0 + i];
-        const int b = lane - d;
-        if (b >= 0 && b < kOB - 1) bin += cs.mass[b] * sc;
-        if (lane < kOB) zpart += cs.mass[lane] * sc;
-        limit = min(limit, d + kOB - 1);
+      // kU chunks at a time: every record load is issued before any is used
+      constexpr int kU = 16;
+      for (int i0 = 0; i0 < n; i0 += kU) {
+        double mb[kU], mz[kU];
+        int d[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          const int i = i0 + u < n ? i0 + u : n - 1;  // past the end: a repeat, not added
+          d[u] = __builtin_amdgcn_readlane(dl, i);
+          const ChunkStat& cs = st[c0 + i];
+          const int b = lane - d[u];
+          mb[u] = b >= 0 && b < kOB - 1 ? cs.mass[b] : 0.0;
+          mz[u] = lane < kOB ? cs.mass[lane] : 0.0;
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          if (i0 + u < n) {
+            const double sc = lane_d(sl, i0 + u);
+            bin += mb[u] * sc;
+            zpart += mz[u] * sc;
+            limit = min(limit, d[u] + kOB - 1);
+          }
+        }
       }
     }
     const double Z = wave_sum(zpart);
