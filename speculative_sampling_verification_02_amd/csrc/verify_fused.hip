@@ -614,13 +614,22 @@ __device__ __attribute__((always_inline)) inline NormMsg lds_exchange_msg(const 
 // The team wait: wave 0 polls until every wave of the team has published its
 // phase-1 partials, combines them in one fixed order and hands both row
 // normalisers to the other waves through msg[parity] (one LDS-only barrier).
-// Called by the whole workgroup.
+// Called by the whole workgroup.  WIDE kernels (rows of more than 64 wave
+// tiles, up to 128) read all 4 kWave slots in each poll; the others poll at
+// most 2 kWave (a separate instantiation: the wider poll's code slowed the
+// narrow kernel by 8% though it never ran there).
+template <bool WIDE>
 __device__ __attribute__((always_inline)) inline NormMsg pair_wait(const FusedParams& P, int item, int parity,
                                                                    uint64_t* w1, NormMsg* msg) {
   if (threadIdx.x < kWave) {
     const uint64_t* part1 = P.part1 + (size_t)item * P.W * 2;
-    const bool ok = 2 * P.W <= 2 * kWave ? wave_poll_once(part1, 2 * P.W, w1, P.polls)
-                                         : wave_poll(part1, 2 * P.W, w1, nullptr, 0, nullptr, P.polls);
+    bool ok;
+    if constexpr (WIDE)
+      ok = 2 * P.W <= 4 * kWave ? wave_poll_all<4>(part1, 2 * P.W, w1, nullptr, 0, nullptr, P.polls)
+                                : wave_poll(part1, 2 * P.W, w1, nullptr, 0, nullptr, P.polls);
+    else
+      ok = 2 * P.W <= 2 * kWave ? wave_poll_once(part1, 2 * P.W, w1, P.polls)
+                                : wave_poll(part1, 2 * P.W, w1, nullptr, 0, nullptr, P.polls);
     NormMsg m{0.f, 0.f, 0.f, 0.f, 0, 0, 0, 0};
     if (ok) {
       const Norm2 n = wave_norm2(w1, P.W);
@@ -688,13 +697,13 @@ __device__ __attribute__((always_inline)) void pair_phase2(const FusedParams& P,
 }
 
 // The three steps back to back: the tile stays in registers across the wait.
-template <class E, int PER, bool EXT>
+template <class E, int PER, bool EXT, bool WIDE>
 __device__ __attribute__((always_inline)) void pair_compute_sample(const FusedParams& P, int item, int c, int lo,
                                                                    int parity, const RawPair<E, PER>& raw,
                                                                    uint64_t* w1, NormMsg* msg) {
   float ep[PER], eq[PER], mp, mq, sp, sq;
   pair_phase1<E, PER, EXT>(P, item, c, lo, raw, ep, eq, mp, mq, sp, sq);
-  const NormMsg m = pair_wait(P, item, parity, w1, msg);
+  const NormMsg m = pair_wait<WIDE>(P, item, parity, w1, msg);
   pair_phase2<PER, EXT>(P, item, c, m, ep, eq, mp, mq, sp, sq);
 }
 
@@ -756,7 +765,7 @@ __device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 template <int PER>
 constexpr int stage_vectors() { return 2 * kWavesPerGroup * (PER / BF16::kVec) * kWave; }
 
-template <int PER, bool ARGMAX, bool EXT>
+template <int PER, bool ARGMAX, bool EXT, bool WIDE>
 __device__ __attribute__((always_inline)) void compute_loop_staged(const FusedParams& P, int team, int rank,
                                                                    u32x4* stage, uint64_t* w1, NormMsg* msg) {
   using E = BF16;
@@ -849,7 +858,7 @@ __device__ __attribute__((always_inline)) void compute_loop_staged(const FusedPa
         float xp[PER], xq[PER], cp, cq, s_p, s_q;
         pair_phase1<E, PER, EXT>(P, item, c, lo, A, xp, xq, cp, cq, s_p, s_q);
         if (pend >= 0) {
-          const NormMsg m = pair_wait(P, pend, parity, w1, msg);
+          const NormMsg m = pair_wait<WIDE>(P, pend, parity, w1, msg);
           pair_phase2<PER, EXT>(P, pend, c, m, ep, eq, mp, mq, sp, sq);
           parity ^= 1;
         }
@@ -866,7 +875,7 @@ __device__ __attribute__((always_inline)) void compute_loop_staged(const FusedPa
       } else {
         single_pass_compute<E, PER, ARGMAX, EXT>(P, item, c, lo, A);
         if (pend >= 0) {
-          const NormMsg m = pair_wait(P, pend, parity, w1, msg);
+          const NormMsg m = pair_wait<WIDE>(P, pend, parity, w1, msg);
           pair_phase2<PER, EXT>(P, pend, c, m, ep, eq, mp, mq, sp, sq);
           parity ^= 1;
           pend = -1;
@@ -879,7 +888,7 @@ __device__ __attribute__((always_inline)) void compute_loop_staged(const FusedPa
     d = next_d;
   }
   if (pend >= 0) {
-    const NormMsg m = pair_wait(P, pend, parity, w1, msg);
+    const NormMsg m = pair_wait<WIDE>(P, pend, parity, w1, msg);
     pair_phase2<PER, EXT>(P, pend, c, m, ep, eq, mp, mq, sp, sq);
   }
 }
@@ -1211,7 +1220,7 @@ struct Pool {
   static constexpr int kBytes = kABytes + 2 * kMaxWaveTiles * 8 + 2 * (int)sizeof(NormMsg);
 };
 
-template <class E, int PER, bool ARGMAX, bool EXT>
+template <class E, int PER, bool ARGMAX, bool EXT, bool WIDE>
 __global__ __launch_bounds__(kThreads, kMinWaves) void fused_kernel(FusedParams P) {
   using L = Pool<E, PER, ARGMAX>;
   __shared__ __align__(16) unsigned char pool[L::kBytes];
@@ -1231,7 +1240,7 @@ __global__ __launch_bounds__(kThreads, kMinWaves) void fused_kernel(FusedParams 
   }
   if (team >= 0) {
     if constexpr (L::kStaged) {
-      compute_loop_staged<PER, ARGMAX, EXT>(P, team, rank, reinterpret_cast<u32x4*>(pool), poll_buf, msg);
+      compute_loop_staged<PER, ARGMAX, EXT, WIDE>(P, team, rank, reinterpret_cast<u32x4*>(pool), poll_buf, msg);
     } else {
       const int c = rank * kWavesPerGroup + (int)threadIdx.x / kWave;  // this wave's tile
       const int lo = c * kWave * PER;
@@ -1243,7 +1252,7 @@ __global__ __launch_bounds__(kThreads, kMinWaves) void fused_kernel(FusedParams 
         RawPair<E, PER> A;
         issue_item<E, PER, EXT>(P, item, lo, A);
         if (!ARGMAX && item < P.n_pairs) {
-          pair_compute_sample<E, PER, EXT>(P, item, c, lo, parity, A, poll_buf, msg);
+          pair_compute_sample<E, PER, EXT, WIDE>(P, item, c, lo, parity, A, poll_buf, msg);
           parity ^= 1;
         } else {
           single_pass_compute<E, PER, ARGMAX, EXT>(P, item, c, lo, A);
@@ -1321,7 +1330,9 @@ hipError_t launch(const VerifyArgs& a, hipStream_t s) {
   P.pair_res = reinterpret_cast<uint64_t*>(ws + L.off_res);
   P.polls = g_wait_polls;
 
-  auto kern = fused_kernel<E, per_of<E>(), ARGMAX, EXT>;
+  // rows of more than 64 wave tiles take the wide team wait (T > 0 only)
+  auto kern = !ARGMAX && P.W > kWave ? fused_kernel<E, per_of<E>(), ARGMAX, EXT, !ARGMAX>
+                                       : fused_kernel<E, per_of<E>(), ARGMAX, EXT, false>;
   long resident = 0;
   hipError_t e = resident_blocks(kern, &resident);
   if (e != hipSuccess) return e;
