@@ -530,6 +530,24 @@ __device__ inline int live_item(const FusedParams& P, int d) {
   return P.n_pairs + (d - acc);  // a bonus item
 }
 
+
+// The k-th live item (dense index) of team t, or n_live after its last.  The
+// pairs go round-robin, so the first n_pairs mod nteams teams hold one more;
+// the bonus items, half a pair's work each, then fill the lighter teams two
+// deep before any team gets a third, which keeps every team within half a
+// pair of the mean.
+__device__ inline int team_dense(int t, int k, int nt, int n_live, int n_lpairs) {
+  const int np_t = t < n_lpairs ? (n_lpairs - 1 - t) / nt + 1 : 0;
+  if (k < np_t) return t + k * nt;
+  const int j = k - np_t;                   // this team's j-th bonus item
+  const int r = n_lpairs % nt, light = nt - r;
+  int bonus;
+  if (t >= r && j < 2) bonus = j * light + (t - r);
+  else bonus = 2 * light + (j - (t >= r ? 2 : 0)) * nt + t;
+  const int d = n_lpairs + bonus;
+  return d < n_live ? d : n_live;
+}
+
 template <class E, int PER, bool EXT>
 __device__ __attribute__((always_inline)) void issue_item(const FusedParams& P, int item, int lo, RawPair<E, PER>& r) {
   const VerifyArgs& a = P.a;
@@ -815,7 +833,9 @@ __device__ __attribute__((always_inline)) void compute_loop_staged(const FusedPa
   };
 
   const int n_live = live_count<EXT>(P);
-  int d = team;  // dense index over the live items
+  const int n_lpairs = n_live - a.B;
+  int kth = 0;
+  int d = team_dense(team, 0, P.nteams, n_live, n_lpairs);  // dense index over the live items
   int item = d < n_live ? live_item<EXT>(P, d) : P.n_items;
   if (wave != 0 && item < P.n_items && !empty_item<EXT>(P, item)) issue(item);
   if (wave != 0) wait_vmem();
@@ -843,7 +863,7 @@ __device__ __attribute__((always_inline)) void compute_loop_staged(const FusedPa
       A.q.v[v] = stage[((kWavesPerGroup + wave) * NS + v) * kWave + lane];
     }
     lds_barrier();
-    const int next_d = d + P.nteams;
+    const int next_d = team_dense(team, ++kth, P.nteams, n_live, n_lpairs);
     const int next = next_d < n_live ? live_item<EXT>(P, next_d) : P.n_items;
     if (wave != 0 && next < P.n_items && !empty_item<EXT>(P, next)) issue(next);
     {
@@ -1246,7 +1266,10 @@ __global__ __launch_bounds__(kThreads, kMinWaves) void fused_kernel(FusedParams 
       const int lo = c * kWave * PER;
       int parity = 0;
       const int n_live = live_count<EXT>(P);
-      for (int d = team; d < n_live; d += P.nteams) {
+      const int n_lpairs = n_live - P.a.B;
+      for (int kth = 0;; ++kth) {
+        const int d = team_dense(team, kth, P.nteams, n_live, n_lpairs);
+        if (d >= n_live) break;
         const int item = live_item<EXT>(P, d);
         if (empty_item<EXT>(P, item)) continue;
         RawPair<E, PER> A;
