@@ -65,15 +65,20 @@ __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 // ------------------------------------------------------------ wave reductions
 //
 // All-reduce across a wave64 with DPP lane moves inside each 16-lane row
-// (xor 1, xor 2, half-row mirror, row mirror), then the four row results
-// combined in row order through readlane.  Every step combines two values with
-// a commutative operation, so all lanes end with bit-identical results and the
-// order of operations is fixed: results are reproducible run to run.
+// (xor 1, xor 2, half-row mirror, row mirror), after which every lane of row j
+// holds the row's result r_j; then two row broadcasts (lane 15 of rows 0 and 2
+// into rows 1 and 3, lane 31 into rows 2 and 3) leave (r3 . r2) . (r1 . r0) in
+// lane 63, which readlane returns to every lane.  Every step combines two
+// values with a commutative operation, so the result equals
+// (r0 . r1) . (r2 . r3) bit for bit and the order of operations is fixed:
+// results are reproducible run to run.
 
 constexpr int kDppXor1 = 0xB1;         // quad_perm [1, 0, 3, 2]
 constexpr int kDppXor2 = 0x4E;         // quad_perm [2, 3, 0, 1]
 constexpr int kDppHalfMirror = 0x141;  // lane i <-> 7 - i within each 8 lanes
 constexpr int kDppMirror = 0x140;      // lane i <-> 15 - i within each 16 lanes
+constexpr int kDppBcast15 = 0x142;     // lane 15 of each row to all of the next row
+constexpr int kDppBcast31 = 0x143;     // lane 31 to all of rows 2 and 3
 
 template <int CTRL>
 __device__ inline int dpp_i(int v) {
@@ -99,12 +104,27 @@ __device__ inline double lane_d(double v, int lane) {
   return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
 }
 
+// A row broadcast into the rows of ROWS; the other rows read `old`.
+template <int CTRL, int ROWS>
+__device__ inline float bcast_f(float old, float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), CTRL, ROWS, 0xF, false));
+}
+template <int CTRL, int ROWS>
+__device__ inline double bcast_d(double v) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(b & 0xffffffffll), CTRL, ROWS, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(b >> 32), CTRL, ROWS, 0xF, false);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+}
+
 __device__ inline float wave_max(float v) {
   v = fmaxf(v, dpp_f<kDppXor1>(v));
   v = fmaxf(v, dpp_f<kDppXor2>(v));
   v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
   v = fmaxf(v, dpp_f<kDppMirror>(v));
-  return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
+  v = fmaxf(v, bcast_f<kDppBcast15, 0xA>(v, v));
+  v = fmaxf(v, bcast_f<kDppBcast31, 0xC>(v, v));
+  return lane_f(v, kWave - 1);
 }
 
 __device__ inline float wave_sum(float v) {
@@ -112,7 +132,9 @@ __device__ inline float wave_sum(float v) {
   v += dpp_f<kDppXor2>(v);
   v += dpp_f<kDppHalfMirror>(v);
   v += dpp_f<kDppMirror>(v);
-  return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
+  v += bcast_f<kDppBcast15, 0xA>(0.f, v);  // rows 0 and 2 add 0 (lane 63 never reads them again)
+  v += bcast_f<kDppBcast31, 0xC>(0.f, v);
+  return lane_f(v, kWave - 1);
 }
 
 __device__ inline double wave_sum(double v) {
@@ -120,7 +142,9 @@ __device__ inline double wave_sum(double v) {
   v += dpp_d<kDppXor2>(v);
   v += dpp_d<kDppHalfMirror>(v);
   v += dpp_d<kDppMirror>(v);
-  return (lane_d(v, 0) + lane_d(v, 16)) + (lane_d(v, 32) + lane_d(v, 48));
+  v += bcast_d<kDppBcast15, 0xA>(v);
+  v += bcast_d<kDppBcast31, 0xC>(v);
+  return lane_d(v, kWave - 1);
 }
 
 // (value, index) with "greater value wins, lower index breaks ties".
