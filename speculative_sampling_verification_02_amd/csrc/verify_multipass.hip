@@ -39,9 +39,12 @@ constexpr int kChunk = 8192;  // tokens per chunk; a multiple of 256 * 8
 // gamma = 8, V = 256000.  At T > 0 the smaller chunk measured faster.
 constexpr int kChunkArgmax = 16384;
 
+// Chunks per row.  Argmax chunks tile V + 7 positions: a row that does not
+// start on 16 bytes is read from its aligned-down start, up to 7 positions
+// early (row_stats_kernel); for aligned rows the count is the same.
 __host__ __device__ inline int num_chunks(int V, bool argmax = false) {
   const int ch = argmax ? kChunkArgmax : kChunk;
-  return (V + ch - 1) / ch;
+  return ((argmax ? V + 7 : V) + ch - 1) / ch;
 }
 
 // Row numbering shared by every kernel here: target rows first, then draft rows.
@@ -174,7 +177,47 @@ __global__ __launch_bounds__(kThreads) void row_stats_kernel(VerifyArgs a, float
       if (threadIdx.x == 0) stats[blockIdx.x] = make_float2(M, s);
     }
   } else {
-    // unaligned rows: scalar loads, two sweeps over the chunk (the second hits cache)
+    if constexpr (ARGMAX) {
+      // the tensors start on 16 bytes (the rows need not)
+      if (((uintptr_t)a.target & 15u) == 0 && (a.gamma == 0 || ((uintptr_t)a.draft & 15u) == 0)) {
+        // A row that does not start on 16 bytes: 16-byte loads from the
+        // aligned-down start ra = r - sh, so position j of the row's stream
+        // holds token j - sh.  The chunks tile the positions [0, V + sh); the
+        // first sh positions belong to the previous row and are skipped, and
+        // the last vector, which may run past the row's end, is read token by
+        // token.
+        constexpr int kPer = CH / kThreads, NS = kPer / E::kVec;
+        const int sh = (int)(((uintptr_t)r & 15u) / sizeof(typename E::storage));
+        const auto* ra = r - sh;
+        const int end = a.V + sh, plo = c * CH;
+        u32x4 raw[NS];
+#pragma unroll
+        for (int q = 0; q < NS; ++q) {
+          const int j0 = plo + (q * kThreads + (int)threadIdx.x) * E::kVec;
+          raw[q] = j0 + E::kVec <= end ? load_stream(ra + j0) : u32x4{0u, 0u, 0u, 0u};
+        }
+        // skipped positions carry index INT_MAX, so a row of -inf still
+        // returns its lowest token
+        ArgMax best{-INFINITY, 0x7fffffff};
+#pragma unroll
+        for (int q = 0; q < NS; ++q) {
+          const int j0 = plo + (q * kThreads + (int)threadIdx.x) * E::kVec;
+          float t[E::kVec];
+          E::unpack(raw[q], t);
+#pragma unroll
+          for (int v = 0; v < E::kVec; ++v) {
+            const int j = j0 + v;
+            if (j >= sh && j < end)
+              best = argmax_better(best, ArgMax{j0 + E::kVec <= end ? t[v] : E::at(ra, j), j - sh});
+          }
+        }
+        best = block_argmax(best, lds_f, lds_i);
+        if (threadIdx.x == 0) stats[blockIdx.x] = make_float2(best.v, __int_as_float(best.i));
+        return;
+      }
+    }
+    // scalar loads (tensors that do not start on 16 bytes, and unaligned rows
+    // at T > 0); at T > 0 two sweeps over the chunk (the second hits cache)
     if constexpr (ARGMAX) {
       ArgMax best{-INFINITY, 0x7fffffff};
       for (int j = lo + threadIdx.x; j < hi; j += kThreads) best = argmax_better(best, ArgMax{E::at(r, j), j});

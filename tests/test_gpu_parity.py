@@ -101,6 +101,8 @@ SHAPES = [
     (2, 32, 300, "bf16", 1.3),             # the largest gamma
     (5, 3, 1, "f32", 1.0),                 # one-token vocabulary
     (3, 2, 7, "bf16", 0.0),
+    (3, 5, 16384 * 2 + 77, "bf16", 0.0),   # unaligned rows in argmax mode: shifted 16-byte loads
+    (2, 3, 16384 + 5, "f32", 0.0),
     (3, 6, 5000, "f32", 1e-3),             # cold temperature
     (3, 6, 5000, "bf16", 10.0),            # hot temperature
     (7, 1, 40000, "bf16", 1.0),
@@ -180,13 +182,16 @@ def test_rejection_with_zero_residual_samples_p(dev, algo):
 
 
 @pytest.mark.parametrize("algo", list(ALGOS))
-def test_argmax_ties_lowest_index(dev, algo):
+@pytest.mark.parametrize("V", [20000, 20003])  # 20003: rows that do not start on 16 bytes
+def test_argmax_ties_lowest_index(dev, algo, V):
     rng = np.random.default_rng(4)
-    B, G, V = 8, 3, 20000
+    B, G = 8, 3
     tl = rng.integers(0, 4, size=(B, G + 1, V)).astype(np.float32)   # every max is tied
     dl = rng.integers(0, 4, size=(B, G, V)).astype(np.float32)
     tl[0, 0, :] = -0.0
     tl[0, 0, 5] = 0.0                                                 # -0 and +0 tie
+    tl[1, 1, :] = -np.inf                                             # all tied at -inf: token 0
+    dl[2, 0, :] = -np.inf
     tokens = np.where(rng.random((B, G)) < 0.5, tl[:, :G].argmax(-1), 7).astype(np.int32)
     for dt in ("f32", "bf16"):
         t, d = (tl, dl) if dt == "f32" else (W.f32_to_bf16_bits(tl), W.f32_to_bf16_bits(dl))
