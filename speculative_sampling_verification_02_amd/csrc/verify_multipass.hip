@@ -119,6 +119,146 @@ struct ChunkRegs {
   }
 };
 
+// Bytes [o, o + 16) of the 32 bytes a || b (o < 16, the same in every lane
+// of the workgroup): each output word is one v_alignbyte of two input words.
+__device__ inline u32x4 cut_vector(const u32x4& a, const u32x4& b, int o) {
+  const uint32_t c[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  const uint32_t r = (uint32_t)o & 3u;
+  auto w = [&](int k) { return __builtin_amdgcn_alignbyte(c[k + 1], c[k], r); };
+  switch (o >> 2) {
+    case 0: return u32x4{w(0), w(1), w(2), w(3)};
+    case 1: return u32x4{w(1), w(2), w(3), w(4)};
+    case 2: return u32x4{w(2), w(3), w(4), w(5)};
+    default: return u32x4{w(3), w(4), w(5), w(6)};
+  }
+}
+
+// ChunkRegs for a row that does not start on 16 bytes, in a tensor that does:
+// the same tokens per thread, each vector of kVec tokens cut out of the two
+// aligned vectors that cover it (the second is the next thread's first, a
+// cache hit).  A vector whose pair would run past the row's end is read
+// token by token.
+template <class E, int CH = kChunk>
+struct ShiftedChunk {
+  static constexpr int kPer = CH / kThreads;
+  static constexpr int NS = kPer / E::kVec;
+  float x[kPer];
+  __device__ inline int token(int lo, int t) const {
+    return lo + ((t / E::kVec) * kThreads + (int)threadIdx.x) * E::kVec + t % E::kVec;
+  }
+  u32x4 ra_[NS], rb_[NS];
+  const typename E::storage* row_;
+  int sh_, V_;
+  // vector s of this thread is cut from aligned vectors when both lie in the row
+  __device__ inline bool whole(int j0) const { return j0 + 2 * E::kVec - sh_ <= V_; }
+  __device__ inline void issue(const typename E::storage* row, int lo, int hi, int V) {
+    row_ = row;
+    V_ = V;
+    sh_ = (int)(((uintptr_t)row & 15u) / sizeof(typename E::storage));
+    const auto* ra = row - sh_;  // 16-byte aligned; inside the tensor (sh_ > 0 only past its first row)
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int j0 = lo + (s * kThreads + (int)threadIdx.x) * E::kVec;
+      const bool w = j0 < hi && whole(j0);
+      ra_[s] = w ? load_stream(ra + j0) : u32x4{0u, 0u, 0u, 0u};
+      rb_[s] = w ? load_stream(ra + j0 + E::kVec) : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  __device__ inline void unpack(int lo, int hi) {
+    const int o = sh_ * (int)sizeof(typename E::storage);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int j0 = lo + (s * kThreads + (int)threadIdx.x) * E::kVec;
+      float t[E::kVec];
+      if (j0 < hi && whole(j0)) {
+        E::unpack(cut_vector(ra_[s], rb_[s], o), t);
+      } else {
+#pragma unroll
+        for (int v = 0; v < E::kVec; ++v) t[v] = j0 + v < hi ? E::at(row_, j0 + v) : -INFINITY;
+      }
+#pragma unroll
+      for (int v = 0; v < E::kVec; ++v) x[s * E::kVec + v] = t[v];
+    }
+  }
+  __device__ inline void load(const typename E::storage* row, int lo, int hi, int V) {
+    issue(row, lo, hi, V);
+    unpack(lo, hi);
+  }
+};
+
+// Tokens [j0, j0 + kVec) of a row that need not start on 16 bytes (its tensor
+// does), as floats; tokens at or past V read as -inf.  Cut from the two
+// aligned vectors that cover them when both lie in the row, else token by token.
+template <class E>
+__device__ inline void shifted_vector(const typename E::storage* row, int j0, int V, float* out) {
+  const int sh = (int)(((uintptr_t)row & 15u) / sizeof(typename E::storage));
+  if (j0 + 2 * E::kVec - sh <= V) {
+    const auto* ra = row - sh;
+    E::unpack(cut_vector(load_cached(ra + j0), load_cached(ra + j0 + E::kVec), sh * (int)sizeof(typename E::storage)),
+              out);
+  } else {
+#pragma unroll
+    for (int v = 0; v < E::kVec; ++v) out[v] = j0 + v < V ? E::at(row, j0 + v) : -INFINITY;
+  }
+}
+
+// tile_search (inverse-CDF draw over one tile of kThreads * PER tokens, one
+// memory round trip and one workgroup scan) for rows that need not start on
+// 16 bytes: thread t owns the PER tokens from tile_lo + t * PER, each vector
+// from shifted_vector.  Tokens at or past V have weight 0.  Returns the first
+// token whose running weight exceeds theta, or the tile's last positive-weight
+// token if rounding leaves the whole tile at or below theta, or -1 if no
+// token has positive weight.  Called by the whole workgroup.
+template <class E, int PER, class W>
+__device__ int shifted_tile_search(const typename E::storage* r0, const typename E::storage* r1, int tile_lo, int V,
+                                   float theta, W&& weight, float* lds_f, int* lds_i) {
+  constexpr int NS = PER / E::kVec;
+  __shared__ int found;
+  const int base = tile_lo + (int)threadIdx.x * PER;
+  float x0[PER], x1[PER];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    shifted_vector<E>(r0, base + s * E::kVec, V, x0 + s * E::kVec);
+    if (r1) shifted_vector<E>(r1, base + s * E::kVec, V, x1 + s * E::kVec);
+  }
+  if (threadIdx.x == 0) found = -1;
+  float w[PER];
+  float sum = 0.f;
+  int last_pos = -1;
+#pragma unroll
+  for (int t = 0; t < PER; ++t) {
+    const float wv = base + t < V ? weight(x0[t], r1 ? x1[t] : 0.f) : 0.f;
+    w[t] = wv;
+    if (wv > 0.f) last_pos = base + t;
+    sum += wv;
+  }
+  float excl, total;
+  const float incl = block_scan(sum, lds_f, &excl, &total);
+  if (excl <= theta && theta < incl) {  // exactly one thread owns theta
+    float run = excl;
+    int pick = -1, lastp = -1;
+#pragma unroll
+    for (int t = 0; t < PER; ++t) {
+      if (w[t] > 0.f) lastp = base + t;
+      run += w[t];
+      if (pick < 0 && run > theta) pick = base + t;
+    }
+    found = pick >= 0 ? pick : lastp;
+  }
+  __syncthreads();
+  const int f = found;
+  __syncthreads();
+  if (f >= 0) return f;
+  ArgMax lp{last_pos >= 0 ? (float)(last_pos - tile_lo) : -1.f, last_pos};
+  lp = block_argmax(lp, lds_f, lds_i);
+  return lp.i;
+}
+
+// Whether both logit tensors start on 16 bytes (their rows need not).
+__device__ inline bool bases_aligned(const VerifyArgs& a) {
+  return ((uintptr_t)a.target & 15u) == 0 && (a.gamma == 0 || ((uintptr_t)a.draft & 15u) == 0);
+}
+
 // ------------------------------------------------------------------ K1
 
 template <class E, bool VEC, bool ARGMAX>
@@ -140,6 +280,38 @@ __global__ __launch_bounds__(kThreads) void row_stats_kernel(VerifyArgs a, float
     if (i > seq_gamma(a, b) - (target ? 0 : 1)) return;
   }
 
+  // the chunk's (max, sum of exp2((x - max) k)) from its tokens in registers
+  auto chunk_stats = [&](auto& ch) {
+    constexpr int kPer = sizeof(ch.x) / sizeof(float);
+    if (a.thr) {
+      const float th = a.thr[row];
+#pragma unroll
+      for (int t = 0; t < kPer; ++t) ch.x[t] = keep(ch.x[t], th);
+    }
+    // four independent chains keep the dependency chains short
+    float m0 = -INFINITY, m1 = -INFINITY, m2 = -INFINITY, m3 = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < kPer; t += 4) {
+      m0 = fmaxf(m0, ch.x[t]);
+      m1 = fmaxf(m1, ch.x[t + 1]);
+      m2 = fmaxf(m2, ch.x[t + 2]);
+      m3 = fmaxf(m3, ch.x[t + 3]);
+    }
+    const float M = block_max(fmaxf(fmaxf(m0, m1), fmaxf(m2, m3)), lds_f);
+    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int t = 0; t < kPer; t += 4) {
+        s0 += fast_exp2((ch.x[t] - M) * a.k);
+        s1 += fast_exp2((ch.x[t + 1] - M) * a.k);
+        s2 += fast_exp2((ch.x[t + 2] - M) * a.k);
+        s3 += fast_exp2((ch.x[t + 3] - M) * a.k);
+      }
+    }
+    const float s = block_sum((s0 + s1) + (s2 + s3), lds_f);
+    if (threadIdx.x == 0) stats[blockIdx.x] = make_float2(M, s);
+  };
+
   if constexpr (VEC) {
     ChunkRegs<E, CH> ch;
     ch.load(r, lo, hi);
@@ -148,38 +320,11 @@ __global__ __launch_bounds__(kThreads) void row_stats_kernel(VerifyArgs a, float
       best = block_argmax(best, lds_f, lds_i);
       if (threadIdx.x == 0) stats[blockIdx.x] = make_float2(best.v, __int_as_float(best.i));
     } else {
-      if (a.thr) {
-        const float th = a.thr[row];
-#pragma unroll
-        for (int t = 0; t < ChunkRegs<E, CH>::kPer; ++t) ch.x[t] = keep(ch.x[t], th);
-      }
-      // four independent chains keep the dependency chains short
-      float m0 = -INFINITY, m1 = -INFINITY, m2 = -INFINITY, m3 = -INFINITY;
-#pragma unroll
-      for (int t = 0; t < ChunkRegs<E, CH>::kPer; t += 4) {
-        m0 = fmaxf(m0, ch.x[t]);
-        m1 = fmaxf(m1, ch.x[t + 1]);
-        m2 = fmaxf(m2, ch.x[t + 2]);
-        m3 = fmaxf(m3, ch.x[t + 3]);
-      }
-      const float M = block_max(fmaxf(fmaxf(m0, m1), fmaxf(m2, m3)), lds_f);
-      float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
-      if (M != -INFINITY) {
-#pragma unroll
-        for (int t = 0; t < ChunkRegs<E, CH>::kPer; t += 4) {
-          s0 += fast_exp2((ch.x[t] - M) * a.k);
-          s1 += fast_exp2((ch.x[t + 1] - M) * a.k);
-          s2 += fast_exp2((ch.x[t + 2] - M) * a.k);
-          s3 += fast_exp2((ch.x[t + 3] - M) * a.k);
-        }
-      }
-      const float s = block_sum((s0 + s1) + (s2 + s3), lds_f);
-      if (threadIdx.x == 0) stats[blockIdx.x] = make_float2(M, s);
+      chunk_stats(ch);
     }
   } else {
     if constexpr (ARGMAX) {
-      // the tensors start on 16 bytes (the rows need not)
-      if (((uintptr_t)a.target & 15u) == 0 && (a.gamma == 0 || ((uintptr_t)a.draft & 15u) == 0)) {
+      if (bases_aligned(a)) {
         // A row that does not start on 16 bytes: 16-byte loads from the
         // aligned-down start ra = r - sh, so position j of the row's stream
         // holds token j - sh.  The chunks tile the positions [0, V + sh); the
@@ -216,8 +361,16 @@ __global__ __launch_bounds__(kThreads) void row_stats_kernel(VerifyArgs a, float
         return;
       }
     }
-    // scalar loads (tensors that do not start on 16 bytes, and unaligned rows
-    // at T > 0); at T > 0 two sweeps over the chunk (the second hits cache)
+    if constexpr (!ARGMAX) {
+      if (bases_aligned(a)) {
+        ShiftedChunk<E, CH> ch;
+        ch.load(r, lo, hi, a.V);
+        chunk_stats(ch);
+        return;
+      }
+    }
+    // scalar loads (tensors that do not start on 16 bytes); at T > 0 two
+    // sweeps over the chunk (the second hits cache)
     if constexpr (ARGMAX) {
       ArgMax best{-INFINITY, 0x7fffffff};
       for (int j = lo + threadIdx.x; j < hi; j += kThreads) best = argmax_better(best, ArgMax{E::at(r, j), j});
@@ -266,33 +419,49 @@ __global__ __launch_bounds__(kThreads) void pair_overlap_kernel(VerifyArgs a, co
   const int lo = c * kChunk, hi = min(a.V, lo + kChunk);
   const auto* p_row = row_ptr<E>(a, rp);
   const auto* q_row = row_ptr<E>(a, rq);
-  ChunkRegs<E> cp, cq;
-  if constexpr (VEC) {
-    cp.issue(p_row, lo, hi);  // in flight while the normalisers are combined
-    cq.issue(q_row, lo, hi);
-  }
   const int wid = threadIdx.x / kWave;
-  if (wid < 2) {
-    const RowNorm n = row_norm(stats, wid == 0 ? rp : rq, nch, k);
-    if ((threadIdx.x & (kWave - 1)) == 0) norm_s[wid] = n;
-  }
-  __syncthreads();
-  const RowNorm np = norm_s[0], nq = norm_s[1];
-
+  // the row normalisers, combined while the chunk's loads are in flight
+  auto norms = [&]() {
+    if (wid < 2) {
+      const RowNorm n = row_norm(stats, wid == 0 ? rp : rq, nch, k);
+      if ((threadIdx.x & (kWave - 1)) == 0) norm_s[wid] = n;
+    }
+    __syncthreads();
+  };
   float acc_min = 0.f, acc_res = 0.f;
-  if constexpr (VEC) {
-    cp.unpack(lo, hi);
-    cq.unpack(lo, hi);
+  auto overlap = [&](auto& cp, auto& cq) {
+    const RowNorm np = norm_s[0], nq = norm_s[1];
+    constexpr int kPer = sizeof(cp.x) / sizeof(float);
     float mn[2] = {0.f, 0.f}, rs[2] = {0.f, 0.f};
 #pragma unroll
-    for (int t = 0; t < ChunkRegs<E>::kPer; ++t) {
+    for (int t = 0; t < kPer; ++t) {
       const float p = prob(keep(cp.x[t], thp), np.M, np.invS, k), q = prob(keep(cq.x[t], thq), nq.M, nq.invS, k);
       mn[t & 1] += fminf(p, q);
       rs[t & 1] += fmaxf(p - l * q, 0.f);
     }
     acc_min = mn[0] + mn[1];
     acc_res = rs[0] + rs[1];
+  };
+  if constexpr (VEC) {
+    ChunkRegs<E> cp, cq;
+    cp.issue(p_row, lo, hi);
+    cq.issue(q_row, lo, hi);
+    norms();
+    cp.unpack(lo, hi);
+    cq.unpack(lo, hi);
+    overlap(cp, cq);
+  } else if (bases_aligned(a)) {
+    // p and q cut from their own aligned vectors: the same tokens in both
+    ShiftedChunk<E> cp, cq;
+    cp.issue(p_row, lo, hi, a.V);
+    cq.issue(q_row, lo, hi, a.V);
+    norms();
+    cp.unpack(lo, hi);
+    cq.unpack(lo, hi);
+    overlap(cp, cq);
   } else {
+    norms();
+    const RowNorm np = norm_s[0], nq = norm_s[1];
     for (int j = lo + threadIdx.x; j < hi; j += kThreads) {
       const float p = prob(keep(E::at(p_row, j), thp), np.M, np.invS, k);
       const float q = prob(keep(E::at(q_row, j), thq), nq.M, nq.invS, k);
@@ -497,6 +666,8 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(VerifyArgs a, float2* 
       };
       if constexpr (VEC)
         t = tile_search<E, kChunk / kThreads, kThreads>(p_row, q_row, lo, a.V, theta_s, w, lds_f, lds_i);
+      else if (bases_aligned(a))
+        t = shifted_tile_search<E, kChunk / kThreads>(p_row, q_row, lo, a.V, theta_s, w, lds_f, lds_i);
       else
         t = range_search<E, false, kThreads>(p_row, q_row, lo, hi, theta_s, w, lds_f, lds_i);
       // The chunk masses sum these same per-token weights, so a chunk with
@@ -507,6 +678,8 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(VerifyArgs a, float2* 
       auto w = [&](float xp, float) { return fast_exp2((keep(xp, thp) - np.M) * k); };
       if constexpr (VEC)
         t = tile_search<E, kChunk / kThreads, kThreads>(p_row, nullptr, lo, a.V, theta_s, w, lds_f, lds_i);
+      else if (bases_aligned(a))
+        t = shifted_tile_search<E, kChunk / kThreads>(p_row, nullptr, lo, a.V, theta_s, w, lds_f, lds_i);
       else
         t = range_search<E, false, kThreads>(p_row, nullptr, lo, hi, theta_s, w, lds_f, lds_i);
     }
