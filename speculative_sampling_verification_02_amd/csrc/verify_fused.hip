@@ -992,10 +992,13 @@ __device__ void finish_pair(const FusedParams& P, int item, uint64_t* w1, uint64
     }
     return;
   } else {
-    // the ratio-test inputs do not depend on the partials: fetch them first
+    // the ratio-test inputs and both uniforms do not depend on the partials:
+    // fetch them first, so that their round trips overlap the wait
     int x = 0;
-    float lp = 0.f, lq = 0.f;
+    float lp = 0.f, lq = 0.f, u_i = 0.f;
+    const float u_fin = a.uniforms[(size_t)b * (G + 1) + gb];  // the final sample's uniform
     if (threadIdx.x == 0) {
+      u_i = a.uniforms[(size_t)b * (G + 1) + i];
       x = a.tokens[o];
       if (x >= 0 && x < a.V) {
         lp = E::at(prow, x);
@@ -1012,10 +1015,10 @@ __device__ void finish_pair(const FusedParams& P, int item, uint64_t* w1, uint64
       if (threadIdx.x == 0) st_u64(P.pair_res + item, pack2i(kPoison, 0u));
       return;
     }
-    // every wave has published part2, so every wave is done reading part1
-    clear_slots(part1, 2 * W);
-    clear_slots(part2, W);
-    // normalisers, alpha and the residual mass (wave 0, fixed order)
+    // Every wave has published part2, so every wave is done reading part1.
+    // The slots are cleared after the result is out: stores issued here would
+    // hold up the barriers below.
+    // Normalisers, alpha and the residual mass (wave 0, fixed order):
     if (threadIdx.x < kWave) {
       const Norm2 n = wave_norm2(w1, W);
       double al = 0.0, sw = 0.0;
@@ -1037,8 +1040,8 @@ __device__ void finish_pair(const FusedParams& P, int item, uint64_t* w1, uint64
     __syncthreads();
     const float Mp = Mp_s, Mq = Mq_s;
     const double Sp = Sp_s, Sq = Sq_s;
+    double px = 0.0, qx = 0.0;  // thread 0's; stored with the result, after the search
     if (threadIdx.x == 0) {
-      double px = 0.0, qx = 0.0;
       if (x >= 0 && x < a.V) {
         px = exp2((double)lp * (double)k - (double)Mp) / Sp;
         qx = exp2((double)lq * (double)k - (double)Mq) / Sq;
@@ -1048,21 +1051,18 @@ __device__ void finish_pair(const FusedParams& P, int item, uint64_t* w1, uint64
       // is +inf) and rejects it when p(x) = 0 (0/0).
       // With lenience l the comparison is against p(x) / (l q(x)) ([FI]
       // "The acceptance rate is the overlap of p and q", lenience factor).
-      const double u = (double)a.uniforms[(size_t)b * (G + 1) + i];
+      const double u = (double)u_i;
       if (qx > 0.0) {
         const double ratio = px / ((double)a.lenience * qx);
         acc_s = (ratio >= 1.0) || (u <= ratio);
       } else {
         acc_s = px > 0.0;
       }
-      if (a.p_draft) a.p_draft[o] = (float)px;
-      if (a.q_draft) a.q_draft[o] = (float)qx;
-      if (a.alpha) a.alpha[o] = (float)alpha_s;
     }
     __syncthreads();
     const int acc_i = acc_s;
     int mode = 0;
-    const double uf = (double)a.uniforms[(size_t)b * (G + 1) + gb];  // the final sample's uniform
+    const double uf = (double)u_fin;
     // search groups of S::kGroup consecutive wave tiles, in token order
     const int ng = (W + S::kGroup - 1) / S::kGroup;
     auto pick_p_tile = [&]() {
@@ -1122,6 +1122,13 @@ __device__ void finish_pair(const FusedParams& P, int item, uint64_t* w1, uint64
     }
     if (threadIdx.x == 0) {
       st_u64(P.pair_res + item, pack2i((uint32_t)acc_s | kResMark, (uint32_t)t));
+      if (a.p_draft) a.p_draft[o] = (float)px;
+      if (a.q_draft) a.q_draft[o] = (float)qx;
+      if (a.alpha) a.alpha[o] = (float)alpha_s;
+    }
+    clear_slots(part1, 2 * W);
+    clear_slots(part2, W);
+    if (threadIdx.x == 0) {
       if constexpr (EXT) {
         // this finisher is the last reader of the pair's two keep thresholds
         // (the compute workgroups read them before publishing): zero them, so
@@ -1156,11 +1163,8 @@ __device__ void finish_bonus(const FusedParams& P, int item, uint64_t* w1, uint6
   // finishers, usually long before) in one wait.  The bonus token is drawn
   // only when every draft was kept.
   uint64_t* pres = P.pair_res + (size_t)b * G;
+  const float u_fin = a.uniforms[(size_t)b * (G + 1) + gb];  // fetched before the wait
   const bool ok1 = gather2(part1, 2 * W, w1, pres, gb, res, P.polls);
-  if (ok1) {
-    clear_slots(part1, 2 * W);
-    clear_slots(pres, gb);
-  }
   int n_acc = 0;
   while (n_acc < gb && ((uint32_t)res[n_acc] & 1u) != 0u) ++n_acc;
   int t_bonus = -1;
@@ -1178,7 +1182,7 @@ __device__ void finish_bonus(const FusedParams& P, int item, uint64_t* w1, uint6
     __syncthreads();
     const float M = M_s;
     const float tb = EXT && a.thr ? thr_target(a, b, gb) : -INFINITY;  // the bonus row's keep threshold
-    const double uf = (double)a.uniforms[(size_t)b * (G + 1) + gb];
+    const double uf = (double)u_fin;
     wave_pick_tile((W + S::kGroup - 1) / S::kGroup, uf * S_s, [&](int g) {
       double m = 0.0;
       for (int c = g * S::kGroup; c < min(W, (g + 1) * S::kGroup); ++c) m += p_tile_mass(w1, c, M);
@@ -1208,6 +1212,10 @@ __device__ void finish_bonus(const FusedParams& P, int item, uint64_t* w1, uint6
       for (int i = gb + (int)threadIdx.x; i < G; i += (int)blockDim.x)
         a.thr[(size_t)a.B * (G + 1) + (size_t)b * G + i] = 0.f;
     }
+  }
+  if (ok1) {  // the last reader of both; cleared after the draw, whose barriers would wait for the stores
+    clear_slots(part1, 2 * W);
+    clear_slots(pres, gb);
   }
   if (threadIdx.x == 0) {
     if (ok1) {
