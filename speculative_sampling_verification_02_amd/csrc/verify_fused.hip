@@ -567,6 +567,30 @@ struct __align__(16) NormMsg {
   int ok, pad0, pad1, pad2;
 };
 
+// The keep thresholds of an item's rows: the target row's and, for a pair, the
+// draft row's (-inf: nothing filtered).  Loaded ahead of the item's compute.
+struct ItemThr {
+  float p, q;
+};
+template <bool EXT, bool THR>
+__device__ inline ItemThr item_thr(const FusedParams& P, int item) {
+  ItemThr t{-INFINITY, -INFINITY};
+  if constexpr (THR) {
+    const VerifyArgs& a = P.a;
+    if (a.thr && item < P.n_items) {
+      if (item < P.n_pairs) {
+        const int b = item / a.gamma, i = item % a.gamma;
+        t.p = thr_target(a, b, i);
+        t.q = thr_draft(a, b, i);
+      } else {
+        const int b = item - P.n_pairs;  // the bonus row is target row gamma_b
+        t.p = thr_target(a, b, seq_gamma_of<EXT>(a, b));
+      }
+    }
+  }
+  return t;
+}
+
 // Top-k / top-p filtering (extended kernels): a logit below its row's keep
 // threshold becomes -inf, i.e. probability 0.
 template <int PER>
@@ -577,21 +601,18 @@ __device__ inline void mask_below(float (&x)[PER], float t) {
 
 // Pair item, T > 0, in three steps.  Phase 1 turns the wave tile into kept
 // weights and publishes the wave's (scaled max, sum) of both rows.
-template <class E, int PER, bool EXT>
+template <class E, int PER, bool THR>
 __device__ __attribute__((always_inline)) void pair_phase1(const FusedParams& P, int item, int c, int lo,
-                                                           const RawPair<E, PER>& raw, float (&ep)[PER],
-                                                           float (&eq)[PER], float& mp, float& mq, float& sp,
-                                                           float& sq) {
+                                                           const RawPair<E, PER>& raw, const ItemThr& th,
+                                                           float (&ep)[PER], float (&eq)[PER], float& mp, float& mq,
+                                                           float& sp, float& sq) {
   const VerifyArgs& a = P.a;
   const float k = a.k;
   unpack_tile<E, PER>(raw.p, lo, a.V, ep);
   unpack_tile<E, PER>(raw.q, lo, a.V, eq);
-  if constexpr (EXT) {
-    if (a.thr) {
-      const int b = item / a.gamma, i = item % a.gamma;
-      mask_below<PER>(ep, thr_target(a, b, i));
-      mask_below<PER>(eq, thr_draft(a, b, i));
-    }
+  if constexpr (THR) {
+    mask_below<PER>(ep, th.p);
+    mask_below<PER>(eq, th.q);
   }
   mp = thread_max<PER>(ep) * k;  // scaled maxima
   mq = thread_max<PER>(eq) * k;
@@ -715,20 +736,20 @@ __device__ __attribute__((always_inline)) void pair_phase2(const FusedParams& P,
 }
 
 // The three steps back to back: the tile stays in registers across the wait.
-template <class E, int PER, bool EXT, bool WIDE>
+template <class E, int PER, bool EXT, bool WIDE, bool THR>
 __device__ __attribute__((always_inline)) void pair_compute_sample(const FusedParams& P, int item, int c, int lo,
                                                                    int parity, const RawPair<E, PER>& raw,
                                                                    uint64_t* w1, NormMsg* msg) {
   float ep[PER], eq[PER], mp, mq, sp, sq;
-  pair_phase1<E, PER, EXT>(P, item, c, lo, raw, ep, eq, mp, mq, sp, sq);
+  pair_phase1<E, PER, THR>(P, item, c, lo, raw, item_thr<EXT, THR>(P, item), ep, eq, mp, mq, sp, sq);
   const NormMsg m = pair_wait<WIDE>(P, item, parity, w1, msg);
   pair_phase2<PER, EXT>(P, item, c, m, ep, eq, mp, mq, sp, sq);
 }
 
 // Pair item at T = 0, or a bonus item: one pass, no waiting.
-template <class E, int PER, bool ARGMAX, bool EXT>
+template <class E, int PER, bool ARGMAX, bool THR>
 __device__ __attribute__((always_inline)) void single_pass_compute(const FusedParams& P, int item, int c, int lo,
-                                                                   const RawPair<E, PER>& raw) {
+                                                                   const RawPair<E, PER>& raw, const ItemThr& th) {
   const VerifyArgs& a = P.a;
   uint64_t w0, w1;
   if (item < P.n_pairs) {  // argmax pair
@@ -746,12 +767,7 @@ __device__ __attribute__((always_inline)) void single_pass_compute(const FusedPa
       const ArgMax ab = wave_argmax(thread_argmax<E, PER>(x, lo));
       w0 = pack2i(nz_bits(ab.v), (uint32_t)ab.i);
     } else {
-      if constexpr (EXT) {
-        if (a.thr) {  // the bonus row is target row gamma_b
-          const int b = item - P.n_pairs;
-          mask_below<PER>(x, thr_target(a, b, seq_gamma_of<EXT>(a, b)));
-        }
-      }
+      if constexpr (THR) mask_below<PER>(x, th.p);
       const float m = thread_max<PER>(x) * a.k;
       const float sm = thread_exp_sum<PER, false>(x, m, a.k);
       const float2 l = wave_lse(m, sm);
@@ -783,7 +799,7 @@ __device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 template <int PER>
 constexpr int stage_vectors() { return 2 * kWavesPerGroup * (PER / BF16::kVec) * kWave; }
 
-template <int PER, bool ARGMAX, bool EXT, bool WIDE>
+template <int PER, bool ARGMAX, bool EXT, bool WIDE, bool THR>
 __device__ __attribute__((always_inline)) void compute_loop_staged(const FusedParams& P, int team, int rank,
                                                                    u32x4* stage, uint64_t* w1, NormMsg* msg) {
   using E = BF16;
@@ -840,6 +856,8 @@ __device__ __attribute__((always_inline)) void compute_loop_staged(const FusedPa
   if (wave != 0 && item < P.n_items && !empty_item<EXT>(P, item)) issue(item);
   if (wave != 0) wait_vmem();
   lds_barrier();
+  // keep thresholds, loaded when the item's tiles are issued (one item ahead)
+  ItemThr th = item_thr<EXT, THR>(P, item);
   int parity = 0;
   int pend = -1;  // pipelined: the pair item whose kept weights wait in (ep, eq)
   float ep[PER], eq[PER], mp = 0.f, mq = 0.f, sp = 0.f, sq = 0.f;
@@ -866,6 +884,7 @@ __device__ __attribute__((always_inline)) void compute_loop_staged(const FusedPa
     const int next_d = team_dense(team, ++kth, P.nteams, n_live, n_lpairs);
     const int next = next_d < n_live ? live_item<EXT>(P, next_d) : P.n_items;
     if (wave != 0 && next < P.n_items && !empty_item<EXT>(P, next)) issue(next);
+    const ItemThr th_next = item_thr<EXT, THR>(P, next);
     {
       // Two pair items in flight: phase 1 of this item runs while the team
       // exchange of the previous one completes, and only then is the previous
@@ -876,7 +895,7 @@ __device__ __attribute__((always_inline)) void compute_loop_staged(const FusedPa
       if (empty_item<EXT>(P, item)) {
       } else if (item < P.n_pairs) {
         float xp[PER], xq[PER], cp, cq, s_p, s_q;
-        pair_phase1<E, PER, EXT>(P, item, c, lo, A, xp, xq, cp, cq, s_p, s_q);
+        pair_phase1<E, PER, THR>(P, item, c, lo, A, th, xp, xq, cp, cq, s_p, s_q);
         if (pend >= 0) {
           const NormMsg m = pair_wait<WIDE>(P, pend, parity, w1, msg);
           pair_phase2<PER, EXT>(P, pend, c, m, ep, eq, mp, mq, sp, sq);
@@ -893,7 +912,7 @@ __device__ __attribute__((always_inline)) void compute_loop_staged(const FusedPa
         sq = s_q;
         pend = item;
       } else {
-        single_pass_compute<E, PER, ARGMAX, EXT>(P, item, c, lo, A);
+        single_pass_compute<E, PER, ARGMAX, THR>(P, item, c, lo, A, th);
         if (pend >= 0) {
           const NormMsg m = pair_wait<WIDE>(P, pend, parity, w1, msg);
           pair_phase2<PER, EXT>(P, pend, c, m, ep, eq, mp, mq, sp, sq);
@@ -906,6 +925,7 @@ __device__ __attribute__((always_inline)) void compute_loop_staged(const FusedPa
     lds_barrier();
     item = next;
     d = next_d;
+    th = th_next;
   }
   if (pend >= 0) {
     const NormMsg m = pair_wait<WIDE>(P, pend, parity, w1, msg);
@@ -1248,7 +1268,8 @@ struct Pool {
   static constexpr int kBytes = kABytes + 2 * kMaxWaveTiles * 8 + 2 * (int)sizeof(NormMsg);
 };
 
-template <class E, int PER, bool ARGMAX, bool EXT, bool WIDE>
+// THR: the launch filters by keep thresholds (extended kernels at T > 0 only).
+template <class E, int PER, bool ARGMAX, bool EXT, bool WIDE, bool THR>
 __global__ __launch_bounds__(kThreads, kMinWaves) void fused_kernel(FusedParams P) {
   using L = Pool<E, PER, ARGMAX>;
   __shared__ __align__(16) unsigned char pool[L::kBytes];
@@ -1268,7 +1289,7 @@ __global__ __launch_bounds__(kThreads, kMinWaves) void fused_kernel(FusedParams 
   }
   if (team >= 0) {
     if constexpr (L::kStaged) {
-      compute_loop_staged<PER, ARGMAX, EXT, WIDE>(P, team, rank, reinterpret_cast<u32x4*>(pool), poll_buf, msg);
+      compute_loop_staged<PER, ARGMAX, EXT, WIDE, THR>(P, team, rank, reinterpret_cast<u32x4*>(pool), poll_buf, msg);
     } else {
       const int c = rank * kWavesPerGroup + (int)threadIdx.x / kWave;  // this wave's tile
       const int lo = c * kWave * PER;
@@ -1283,10 +1304,10 @@ __global__ __launch_bounds__(kThreads, kMinWaves) void fused_kernel(FusedParams 
         RawPair<E, PER> A;
         issue_item<E, PER, EXT>(P, item, lo, A);
         if (!ARGMAX && item < P.n_pairs) {
-          pair_compute_sample<E, PER, EXT, WIDE>(P, item, c, lo, parity, A, poll_buf, msg);
+          pair_compute_sample<E, PER, EXT, WIDE, THR>(P, item, c, lo, parity, A, poll_buf, msg);
           parity ^= 1;
         } else {
-          single_pass_compute<E, PER, ARGMAX, EXT>(P, item, c, lo, A);
+          single_pass_compute<E, PER, ARGMAX, THR>(P, item, c, lo, A, item_thr<EXT, THR>(P, item));
         }
       }
     }
@@ -1362,8 +1383,15 @@ hipError_t launch(const VerifyArgs& a, hipStream_t s) {
   P.polls = g_wait_polls;
 
   // rows of more than 64 wave tiles take the wide team wait (T > 0 only)
-  auto kern = !ARGMAX && P.W > kWave ? fused_kernel<E, per_of<E>(), ARGMAX, EXT, !ARGMAX>
-                                       : fused_kernel<E, per_of<E>(), ARGMAX, EXT, false>;
+  // keep thresholds take their own instantiations, so the other extended
+  // launches carry no code for them
+  constexpr bool kThrOk = EXT && !ARGMAX;
+  const bool thr = kThrOk && a.thr != nullptr;
+  auto kern = !ARGMAX && P.W > kWave
+                  ? (thr ? fused_kernel<E, per_of<E>(), ARGMAX, EXT, !ARGMAX, kThrOk>
+                         : fused_kernel<E, per_of<E>(), ARGMAX, EXT, !ARGMAX, false>)
+                  : (thr ? fused_kernel<E, per_of<E>(), ARGMAX, EXT, false, kThrOk>
+                         : fused_kernel<E, per_of<E>(), ARGMAX, EXT, false, false>);
   long resident = 0;
   hipError_t e = resident_blocks(kern, &resident);
   if (e != hipSuccess) return e;
