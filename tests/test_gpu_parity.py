@@ -312,3 +312,32 @@ def test_stream_read_reads_every_word(dev):
         sv.stream_read(buf, sink, blocks)
         got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
         assert got == np.bitwise_xor.reduce(words), blocks
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("T", [1.0, 0.0])
+def test_tensor_base_not_16_byte_aligned(dev, dt, T):
+    """Logit tensors whose first element is not on 16 bytes (a view one element
+    into a buffer): the fused path declines them, the default path takes the
+    multipass kernels' scalar loads, and the results still match the oracle."""
+    import torch
+    sv = _sv()
+    case = W.gaussian_case(3, 3, 8192 + 96, dt, T, seed=83, target_std=2.5)
+    t = gpu_util.case_tensors(case, dev)
+
+    def shifted(x):
+        buf = torch.empty(x.numel() + 1, dtype=x.dtype, device=dev)
+        v = buf[1:].view(x.shape)
+        v.copy_(x)
+        assert v.data_ptr() % 16 != 0
+        return v
+
+    tgt, drf = shifted(t["target"]), shifted(t["draft"])
+    with pytest.raises(sv.SpecVerifyError) as e:
+        sv.verify(tgt, drf, t["tokens"], t["uniforms"], T, algo=sv.ALGO_FUSED)
+    assert e.value.status == sv.SPEC_EUNSUPPORTED
+    out = sv.verify(tgt, drf, t["tokens"], t["uniforms"], T)
+    torch.cuda.synchronize(dev)
+    gpu = {k: v.cpu().numpy() for k, v in out.items()}
+    rep = parity.check(case, gpu, where=f"unaligned base {dt} T={T}")
+    _banner(f"unaligned base {dt} T={T}: {rep}")
