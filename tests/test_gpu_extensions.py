@@ -127,6 +127,22 @@ def test_topk_topp(dev, dt, k, p, algo):
 
 
 @pytest.mark.parametrize("algo", list(ALGOS))
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("k,p", [(64, 1.0), (0, 0.9)])
+def test_topk_topp_long_rows(dev, dt, k, p, algo):
+    """Rows of 160000 tokens (80 wave tiles, more than 64): the fused kernel's
+    wide team wait, with keep thresholds."""
+    case = W.gaussian_case(4, 3, 160000, dt, 1.0, seed=49, target_std=2.5, draft_noise=1.0)
+    _banner(f"long-row filter {dt} top_k={k} top_p={p} {algo}")
+    gpu = gpu_util.run_case(case, ALGOS[algo], dev=dev, top_k=k, top_p=p)
+    thr = gpu_util.gpu_thresholds(case, k, p, dev=dev)
+    rep = parity.check(case, gpu, where=f"long-row filter {dt} k{k} p{p}", top_k=k, top_p=p, gpu_thresholds=thr)
+    _banner(f"  {rep}")
+    assert rep.thresholds_differ <= 1
+    assert rep.token_mismatch_valid <= 1
+
+
+@pytest.mark.parametrize("algo", list(ALGOS))
 @pytest.mark.parametrize("T", [1.0, 0.5])
 def test_full_size_filtered_with_every_extension(dev, T, algo):
     """The B=64, gamma=4, V=128256 bf16 workload (many bf16 ties) with top-k 64,
