@@ -104,8 +104,9 @@ size_t spec_verify_workspace_size(int B, int gamma, int V, int dtype);
  *     The uniforms are not read.
  *   A ratio with q_i(x_i) = 0 follows IEEE rules: p > 0 keeps the draft, 0/0 rejects.
  *   A draft token outside [0, V) is rejected (it has p = q = 0).
- *   n_accepted[b] = next_token[b] = -1 reports that the fused path gave up
- *     waiting on a partner workgroup (2^20 polls by default, see
+ *   n_accepted[b] = next_token[b] = -1 reports that a workgroup gave up
+ *     waiting on a partner workgroup (the fused path, and in argmax mode the
+ *     multipass path's finishing workgroups; 2^20 polls by default, see
  *     spec_set_wait_limit; only possible when another kernel occupies the
  *     device's compute units at the same time).  That sequence has no result,
  *     and the waits that gave up may leave words in the workspace: it must be
@@ -268,7 +269,8 @@ size_t spec_verify_noalloc_limit(void);
 
 /*
  * spec_set_wait_limit -- the number of polls after which every cross-workgroup
- * wait of a later fused-path launch in this process gives up (the sequence
+ * wait of a later launch in this process gives up (the fused path, and the
+ * multipass path's argmax finishing; the sequence
  * then reports -1, see spec_verify).  0 restores the default, 2^20.  It exists
  * for callers and tests that exercise the give-up path: a small limit makes
  * waits give up whenever their data is late, and every kernel still exits

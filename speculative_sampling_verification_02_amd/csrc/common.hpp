@@ -62,6 +62,20 @@ __device__ inline u32x4 load_cached(const void* p) { return *reinterpret_cast<co
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// ------------------------------------------------- cross-workgroup words
+//
+// Naturally aligned 64-bit relaxed agent-scope atomic stores and loads: single-
+// copy atomic and, on gfx950, device-coherent across XCDs (the SC1 scope bit),
+// with no cache writeback or invalidate.  A reader polls a word until it is
+// published (nonzero low half) and the poll returns the data itself.
+
+__device__ inline void st_u64(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline uint64_t ld_u64(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // ------------------------------------------------------------ wave reductions
 //
 // All-reduce across a wave64 with DPP lane moves inside each 16-lane row

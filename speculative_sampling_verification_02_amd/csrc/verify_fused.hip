@@ -121,13 +121,6 @@ __device__ inline float hi_f(uint64_t v) { return __uint_as_float((uint32_t)(v >
 __device__ inline bool published(uint64_t v) { return (uint32_t)v != kEmpty; }
 __device__ inline bool poisoned(uint64_t v) { return (uint32_t)v == kPoison; }
 
-__device__ inline void st_u64(uint64_t* p, uint64_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline uint64_t ld_u64(const uint64_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // Workgroup barrier for LDS data only: the fences order LDS accesses, so the
 // barrier waits for this wave's LDS operations but not for its outstanding
 // global loads (a full __syncthreads() would drain those too).
@@ -1407,6 +1400,7 @@ hipError_t launch(const VerifyArgs& a, hipStream_t s) {
 }  // namespace
 
 void set_wait_limit(unsigned polls) { g_wait_polls = polls ? polls : kDefaultWaitPolls; }
+unsigned wait_limit() { return g_wait_polls; }
 
 size_t fused_workspace_bytes(int B, int gamma, int V) { return layout(B, gamma, V).total; }
 

@@ -71,9 +71,10 @@ size_t fused_workspace_bytes(int B, int gamma, int V);
 // Returns hipErrorNotSupported when the shape does not fit the fused design.
 hipError_t fused_launch(const VerifyArgs& a, hipStream_t stream);
 bool fused_supported(int B, int gamma, int V, int dtype);
-// Bound (polls) of every cross-workgroup wait of later fused launches; 0
-// restores the default.
+// Bound (polls) of every cross-workgroup wait of later launches (the fused
+// path; the multipass path's argmax finishing); 0 restores the default.
 void set_wait_limit(unsigned polls);
+unsigned wait_limit();
 
 // ---- top-k / top-p keep thresholds (filter.hip): one float per row into thr,
 // and a fill kernel that zeroes them again after the verification

@@ -47,6 +47,19 @@ __host__ __device__ inline int num_chunks(int V, bool argmax = false) {
   return ((argmax ? V + 7 : V) + ch - 1) / ch;
 }
 
+// Argmax mode: a row chunk publishes its (value, index) as one 64-bit word,
+// and finishing workgroups at the end of the same grid wait for a sequence's
+// words, up to kArgFinSlots of them per sequence (beyond that a separate
+// finish launch reads them).  The low half is the value's bits with +0.0
+// stored as -0.0 (the same value), so a published word is never zero.
+constexpr int kArgFinSlots = 1024;
+constexpr int kArgFinGroups = 256;  // finishing workgroups at most
+
+__device__ inline void publish_argmax(float2* stats, size_t i, ArgMax best) {
+  const uint32_t v = __float_as_uint(best.v);
+  st_u64(reinterpret_cast<uint64_t*>(stats) + i, (uint64_t)(v == 0u ? 0x80000000u : v) | ((uint64_t)(uint32_t)best.i << 32));
+}
+
 // Row numbering shared by every kernel here: target rows first, then draft rows.
 __device__ inline size_t target_row(int b, int i, int gamma) { return (size_t)b * (gamma + 1) + i; }
 __device__ inline size_t draft_row(int b, int i, int gamma, int B) {
@@ -261,12 +274,96 @@ __device__ inline bool bases_aligned(const VerifyArgs& a) {
 
 // ------------------------------------------------------------------ K1
 
+// Argmax mode, sequence b: waits for the chunk words of its rows (target rows
+// 0..gamma_b, then draft rows 0..gamma_b - 1; the padding rows are never
+// written), combines each row's argmax in chunk order and writes the outputs
+// ([FI] "Speculative sampling", temperature to zero: keep x_i iff it is the
+// target's argmax; alpha_i is 1 iff the two argmaxes agree).  It is the last
+// reader of the words and clears them.  A wait that gives up after `polls`
+// polls reports -1.
+__device__ void argmax_finish(const VerifyArgs& a, float2* stats, int b, int nch, unsigned polls) {
+  __shared__ uint64_t w[kArgFinSlots];
+  __shared__ int ok_s;
+  __shared__ int amax_t[SPEC_MAX_GAMMA + 1], amax_d[SPEC_MAX_GAMMA], acc_s[SPEC_MAX_GAMMA];
+  const int tid = threadIdx.x, G = a.gamma, Gb = seq_gamma(a, b);
+  uint64_t* words = reinterpret_cast<uint64_t*>(stats);
+  uint64_t* wt = words + target_row(b, 0, G) * nch;
+  uint64_t* wd = words + draft_row(b, 0, G, a.B) * nch;
+  const int nt = (Gb + 1) * nch, nd = Gb * nch, n = nt + nd;
+  const int x = tid < Gb ? a.tokens[(size_t)b * G + tid] : 0;  // fetched before the wait
+  if (tid >= Gb && tid < G) {
+    // padding positions report NaN
+    const float nan = __uint_as_float(0x7fc00000u);
+    const size_t o = (size_t)b * G + tid;
+    if (a.alpha) a.alpha[o] = nan;
+    if (a.p_draft) a.p_draft[o] = nan;
+    if (a.q_draft) a.q_draft[o] = nan;
+  }
+  if (tid < kWave) {  // one wave polls every word of the sequence at once
+    bool ok = false;
+    for (unsigned it = 0; it < polls; ++it) {
+      bool all = true;
+      for (int j = tid; j < n; j += kWave) {
+        const uint64_t v = j < nt ? ld_u64(wt + j) : ld_u64(wd + (j - nt));
+        w[j] = v;
+        all = all && (uint32_t)v != 0u;
+      }
+      if (__all(all)) {
+        ok = true;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    if (tid == 0) ok_s = ok;
+  }
+  __syncthreads();
+  if (!ok_s) {
+    if (tid == 0) {
+      a.n_out[b] = -1;  // a wait gave up: no result
+      a.t_out[b] = -1;
+    }
+    return;
+  }
+  auto row_argmax = [&](const uint64_t* r) {
+    ArgMax best{-INFINITY, 0x7fffffff};
+    for (int c = 0; c < nch; ++c)
+      best = argmax_better(best, ArgMax{__uint_as_float((uint32_t)r[c]), (int)(uint32_t)(r[c] >> 32)});
+    return best.i;
+  };
+  if (tid <= Gb) amax_t[tid] = row_argmax(w + tid * nch);
+  if (tid < Gb) amax_d[tid] = row_argmax(w + nt + tid * nch);
+  __syncthreads();
+  for (int j = tid; j < n; j += kThreads) st_u64(j < nt ? wt + j : wd + (j - nt), 0ull);
+  if (tid < Gb) {
+    const size_t o = (size_t)b * G + tid;
+    acc_s[tid] = x == amax_t[tid];
+    if (a.alpha) a.alpha[o] = (amax_t[tid] == amax_d[tid]) ? 1.f : 0.f;
+    if (a.p_draft) a.p_draft[o] = (x == amax_t[tid]) ? 1.f : 0.f;
+    if (a.q_draft) a.q_draft[o] = (x == amax_d[tid]) ? 1.f : 0.f;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int nacc = 0;
+    while (nacc < Gb && acc_s[nacc]) ++nacc;
+    a.n_out[b] = nacc;
+    a.t_out[b] = amax_t[nacc];
+  }
+  __syncthreads();  // amax_t / amax_d are rewritten by the next sequence
+}
+
 template <class E, bool VEC, bool ARGMAX>
-__global__ __launch_bounds__(kThreads) void row_stats_kernel(VerifyArgs a, float2* stats) {
+__global__ __launch_bounds__(kThreads) void row_stats_kernel(VerifyArgs a, float2* stats, int nfin, unsigned polls) {
   __shared__ float lds_f[kMaxWaves];
   __shared__ int lds_i[kMaxWaves];
   constexpr int CH = ARGMAX ? kChunkArgmax : kChunk;
   const int nch = num_chunks(a.V, ARGMAX);
+  if constexpr (ARGMAX) {
+    const size_t nrc = (size_t)a.B * (2 * a.gamma + 1) * nch;  // row chunks
+    if (blockIdx.x >= nrc) {  // a finishing workgroup
+      for (int b = (int)(blockIdx.x - nrc); b < a.B; b += nfin) argmax_finish(a, stats, b, nch, polls);
+      return;
+    }
+  }
   const size_t row = blockIdx.x / nch;
   const int c = blockIdx.x % nch;
   const int lo = c * CH, hi = min(a.V, lo + CH);
@@ -318,7 +415,7 @@ __global__ __launch_bounds__(kThreads) void row_stats_kernel(VerifyArgs a, float
     if constexpr (ARGMAX) {
       ArgMax best = thread_argmax_first(ch.x, [&](int t) { return ch.token(lo, t); });
       best = block_argmax(best, lds_f, lds_i);
-      if (threadIdx.x == 0) stats[blockIdx.x] = make_float2(best.v, __int_as_float(best.i));
+      if (threadIdx.x == 0) publish_argmax(stats, blockIdx.x, best);
     } else {
       chunk_stats(ch);
     }
@@ -357,7 +454,7 @@ __global__ __launch_bounds__(kThreads) void row_stats_kernel(VerifyArgs a, float
           }
         }
         best = block_argmax(best, lds_f, lds_i);
-        if (threadIdx.x == 0) stats[blockIdx.x] = make_float2(best.v, __int_as_float(best.i));
+        if (threadIdx.x == 0) publish_argmax(stats, blockIdx.x, best);
         return;
       }
     }
@@ -375,7 +472,7 @@ __global__ __launch_bounds__(kThreads) void row_stats_kernel(VerifyArgs a, float
       ArgMax best{-INFINITY, 0x7fffffff};
       for (int j = lo + threadIdx.x; j < hi; j += kThreads) best = argmax_better(best, ArgMax{E::at(r, j), j});
       best = block_argmax(best, lds_f, lds_i);
-      if (threadIdx.x == 0) stats[blockIdx.x] = make_float2(best.v, __int_as_float(best.i));
+      if (threadIdx.x == 0) publish_argmax(stats, blockIdx.x, best);
     } else {
       const float th = row_thr(a, row);
       float m = -INFINITY;
@@ -729,10 +826,17 @@ hipError_t launch_typed(const VerifyArgs& a, hipStream_t s) {
   const bool argmax = a.temperature == 0.f;
   const dim3 blk(kThreads);
   if (argmax) {
-    row_stats_kernel<E, VEC, true><<<dim3(rows * num_chunks(a.V, true)), blk, 0, s>>>(a, stats);
+    // the finishing workgroups run in the same launch when a sequence's chunk
+    // words fit their LDS; they are the last in the grid, so they start only
+    // once every row chunk has been dispatched
+    const int ncha = num_chunks(a.V, true);
+    const bool inline_fin = (size_t)(2 * a.gamma + 1) * ncha <= (size_t)kArgFinSlots;
+    const int nfin = inline_fin ? std::min(a.B, kArgFinGroups) : 0;
+    row_stats_kernel<E, VEC, true><<<dim3(rows * ncha + nfin), blk, 0, s>>>(a, stats, nfin, wait_limit());
+    if (inline_fin) return hipGetLastError();
   } else {
     const int nch = num_chunks(a.V);
-    row_stats_kernel<E, VEC, false><<<dim3(rows * nch), blk, 0, s>>>(a, stats);
+    row_stats_kernel<E, VEC, false><<<dim3(rows * nch), blk, 0, s>>>(a, stats, 0, 0u);
     if (a.gamma > 0)
       pair_overlap_kernel<E, VEC><<<dim3((size_t)a.B * a.gamma * nch), blk, 0, s>>>(a, stats, pair_stats);
   }
