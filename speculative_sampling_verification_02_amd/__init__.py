@@ -301,8 +301,8 @@ def noalloc_limit() -> int:
 
 
 def set_wait_limit(polls: int) -> None:
-    """Polls after which every cross-workgroup wait of later fused launches gives
-    up (spec_set_wait_limit); 0 restores the default."""
+    """Polls after which every cross-workgroup wait of later launches gives up
+    (spec_set_wait_limit); 0 restores the default."""
     lib.spec_set_wait_limit(int(polls))
 
 

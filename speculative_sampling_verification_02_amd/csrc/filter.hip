@@ -985,16 +985,48 @@ __device__ inline int floor_i32(float x) {
 // Octave of a token: floor(fl(l k)).
 __device__ inline int octave_of(float x, float k) { return floor_i32(x * k); }
 
-// The smallest float v (-inf included) with octave_of(v, k) >= o, by a binary
-// search over the order-preserving keys of the floats (octave_of is
-// non-decreasing in v for k > 0).  +inf if there is none below +inf.
+// The smallest float v (-inf included) with octave_of(v, k) >= o, over the
+// order-preserving keys of the floats (octave_of is non-decreasing in v for
+// k > 0).  +inf if there is none below +inf.  The search starts from the key
+// of o / k, which lies within a few keys of the answer, and steps one key at a
+// time (at most kOctSteps each way); a start that far off takes a binary
+// search instead.  Either way the answer is the same float.
+constexpr int kOctSteps = 8;
 __device__ inline float first_in_octave(int o, float k) {
   auto value = [](uint32_t key) {
     return __uint_as_float((key & 0x80000000u) ? (key ^ 0x80000000u) : ~key);
   };
-  uint32_t lo = 0x007fffffu, hi = 0xff800000u;  // the keys of -inf and +inf
-  if (octave_of(value(lo), k) >= o) return -INFINITY;
-  while (hi - lo > 1u) {  // octave_of(value(lo)) < o <= octave_of(value(hi))
+  auto key_of_f = [](float v) {
+    const uint32_t u = __float_as_uint(v);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  };
+  const uint32_t kmin = 0x007fffffu, kmax = 0xff800000u;  // the keys of -inf and +inf
+  if (octave_of(value(kmin), k) >= o) return -INFINITY;
+  // invariant of the search: octave_of(value(lo)) < o <= octave_of(value(hi))
+  uint32_t lo = kmin, hi = kmax;
+  const float guess = (float)((double)o / (double)k);
+  uint32_t g = guess != guess ? kmax : key_of_f(guess);
+  g = g < kmin ? kmin : (g > kmax ? kmax : g);
+  if (octave_of(value(g), k) >= o) {
+    hi = g;
+    for (int i = 0; i < kOctSteps && hi - 1u > kmin; ++i) {  // step down while the key below still qualifies
+      if (octave_of(value(hi - 1u), k) < o) {
+        lo = hi - 1u;
+        break;
+      }
+      --hi;
+    }
+  } else {
+    lo = g;
+    for (int i = 0; i < kOctSteps && lo + 1u < kmax; ++i) {  // step up until a key qualifies
+      if (octave_of(value(lo + 1u), k) >= o) {
+        hi = lo + 1u;
+        break;
+      }
+      ++lo;
+    }
+  }
+  while (hi - lo > 1u) {
     const uint32_t mid = lo + (hi - lo) / 2u;
     if (octave_of(value(mid), k) >= o)
       hi = mid;
@@ -1241,6 +1273,15 @@ __global__ __launch_bounds__(kLTT) void nucleus_pick_kernel(FilterArgs f, int nc
       }
     }
   }
+  // entries past the kNCap gathered ones (a row marked for listing too many):
+  // cleared too
+  {
+    int c2 = 0;
+    for (uint32_t i = (uint32_t)kNCap + tid; i < n_all; i += kLTT) {
+      while (L.lpre[c2 + 1] <= i) ++c2;
+      lvals[((size_t)r * nch + c2) * kChunkCap + (i - L.lpre[c2])] = 0.f;
+    }
+  }
   __syncthreads();  // every thread has read the row's record and counts
   if (tid < nch) cnt[tid] = 0u;
   if (tid == 0) rc[r] = RowCross{0.f, 0.f, 0.f, 0.f, 0.0, 0.0};
@@ -1291,12 +1332,12 @@ hipError_t filter_thresholds(const VerifyArgs& a, int top_k, float top_p, float*
   const size_t row_bytes = (size_t)a.V * (a.dtype == SPEC_BF16 ? 2 : 4);
   const bool aligned = row_bytes % 16 == 0 && (uintptr_t)a.target % 16 == 0 &&
                        (a.gamma == 0 || (uintptr_t)a.draft % 16 == 0);
+  const bool topp_alone = !(top_k > 0 && top_k < a.V) && top_p < 1.f;
   // chunk lists for a small top-k (the lists region is zero on entry and is
   // left zero by the row kernel)
   // (rows of more than 256 chunks keep to the row path: the row kernel holds
   // at most 256 chunk offsets)
-  if (lists != nullptr && aligned && !(top_k > 0 && top_k < a.V) && top_p < 1.f &&
-      (a.V + kNChunk - 1) / kNChunk <= 256) {
+  if (lists != nullptr && aligned && topp_alone && (a.V + kNChunk - 1) / kNChunk <= 256) {
     // top-p alone: the streaming nucleus path (the region is zero on entry
     // and is left zero; the pick kernel holds at most 256 chunk offsets)
     const NucleusLayout NL = nucleus_layout((size_t)rows, a.V);

@@ -50,10 +50,15 @@ def run_case(case, algo, tensors=None, dev=None, lenience: float = 1.0, gamma_se
 
 def gpu_thresholds(case, top_k: int, top_p: float, dev=None, tensors=None):
     """The GPU's keep thresholds for a case ([B, 2 gamma + 1]: target rows, then
-    draft rows), from spec_filter_thresholds -- the kernel the verification
-    itself launches first."""
+    draft rows), from spec_filter_thresholds with a workspace -- the kernels
+    the verification itself launches first (its workspace holds the filter's:
+    with top-p alone the streaming nucleus launches, whose thresholds may
+    differ from the row kernel's by a tie group in rows within the nucleus
+    band)."""
+    import torch
     import speculative_sampling_verification_02_amd as sv
     dev = dev or device()
     t = tensors or case_tensors(case, dev)
-    gt, gd = sv.filter_thresholds(t["target"], t["draft"], case.temperature, top_k, top_p)
+    ws = torch.zeros(sv.filter_workspace_size(case.B, case.gamma, case.V), dtype=torch.uint8, device=dev)
+    gt, gd = sv.filter_thresholds(t["target"], t["draft"], case.temperature, top_k, top_p, workspace=ws)
     return np.concatenate([gt.cpu().numpy(), gd.cpu().numpy()], axis=1)

@@ -126,6 +126,15 @@ def _row(case, b: int, r: int):
     return ov.widen(src, case.dtype)
 
 
+def adjacent_values(x: np.ndarray, tau: float) -> np.ndarray:
+    """The keep thresholds a kernel may return for a row whose nucleus boundary
+    lies within the band: the oracle's tau or the row's next distinct finite
+    logit above or below it (one tie group kept more or less), as float32."""
+    vals = np.unique(np.asarray(x, np.float64)[np.isfinite(x)]).astype(np.float32)
+    q = int(np.searchsorted(vals, np.float32(tau)))
+    return vals[max(q - 1, 0):q + 2]
+
+
 def row_errors(x: np.ndarray, T: float, tau: float = -np.inf, nucleus: bool = False):
     """(p, e, E) for a row of fp64 logits: p = softmax(x / T) over the kept
     tokens (x >= tau, zero elsewhere), e the per-token relative error bound of
@@ -231,6 +240,10 @@ def check(case, gpu: dict, seqs=None, where: str = "", lenience: float = 1.0, ga
                         assert in_filter_band[r], (f"{where}: keep threshold of row {j} of sequence {seqs[r]} "
                                                    f"differs ({thr[r, j]} vs {res.filter_tau[r, j]}) "
                                                    f"outside the nucleus band")
+                        near = adjacent_values(_row(case, int(seqs[r]), j), res.filter_tau[r, j])
+                        assert thr[r, j] in near, (f"{where}: keep threshold of row {j} of sequence {seqs[r]} "
+                                                   f"is {thr[r, j]}, not the oracle's {res.filter_tau[r, j]} "
+                                                   f"or an adjacent logit {near}")
             rep.thresholds_differ = int(differs.sum())
             in_filter_band = differs
 

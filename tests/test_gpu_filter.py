@@ -78,6 +78,10 @@ def _check(dev, target, draft, dtype, T, k, p, where):
         bad = np.nonzero(ok & differ)[0]
         assert bad.size == 0, (f"{where} ({name}): rows {bad[:8]} thresholds {g[bad[:8]]} != oracle "
                                f"{want[bad[:8]]} (margins {margin[bad[:8]]})")
+        for i in np.nonzero(differ)[0]:  # in the band: one tie group kept more or less at most
+            near = parity.adjacent_values(rows[i], tau[i])
+            assert g[i] in near, (f"{where} ({name}): row {i} threshold {g[i]} is not the oracle's {want[i]} "
+                                  f"or an adjacent logit {near}")
         amb, ndiff = int((~ok).sum()), int(differ.sum())
         _banner(f"  {name}: rows={len(g)} in_band={amb} differ={ndiff}")
         assert ndiff <= max(1, len(g) // 20), f"{where} ({name}): {ndiff} of {len(g)} thresholds differ"
@@ -229,3 +233,28 @@ def test_nucleus_path_crossing_in_a_tail_bin(dev):
     x[1, 1, 40000] = 27.0
     x = _bf16(x)
     _check(dev, x, x[:, :1].copy(), "bf16", 1.0, 0, float(np.float32(0.9999999)), "tail crossing")
+
+
+def test_nucleus_rows_listing_more_than_the_pick_holds(dev):
+    """fp32 rows of 270000 tokens (33 chunks of 8192) of N(0, 2.5) logits: at
+    top_p 0.9 the crossing octave holds about 14000 logits, more than the pick
+    kernel gathers (8192), so those rows go to the row kernel and the pick
+    kernel must still clear every listed entry (the workspace comes back
+    zeroed)."""
+    case = W.gaussian_case(2, 1, 270000, "f32", 1.0, seed=82, target_std=2.5)
+    for p in (0.9, 0.5):
+        _check(dev, case.target, case.draft, "f32", 1.0, 0, p, f"33 chunks p={p}")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_nucleus_rows_near_the_band(dev, dt):
+    """The top-p rows of the filtered verification tests (V = 20008, N(0, 2.5)
+    logits, top_p 0.9): several rows' nucleus boundaries lie within the band,
+    where the row kernel and the streaming launches may keep a tie group more
+    or less; each is held to the oracle on its own."""
+    case = W.gaussian_case(8, 4, 20008, dt, 1.0, seed=47, target_std=2.5, draft_noise=1.0)
+    if dt == "bf16":
+        t, d = W.bf16_bits_to_f32(case.target), W.bf16_bits_to_f32(case.draft)
+    else:
+        t, d = case.target, case.draft
+    _check(dev, t, d, dt, 1.0, 0, 0.9, f"near-band rows {dt}")

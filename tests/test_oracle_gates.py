@@ -207,3 +207,18 @@ def test_planted_mistakes_in_the_margins_are_caught(mutant, monkeypatch):
         monkeypatch.setattr(adjust, "topp_threshold", lambda *a, **k: (orig(*a, **k)[0], val))
     with pytest.raises(AssertionError):
         _run_all()
+
+
+# ------------------------------------------------ in-band threshold choices
+
+def test_adjacent_values_are_one_tie_group_either_side():
+    """A row within the nucleus band may keep one tie group more or less than
+    the oracle: the allowed thresholds are the oracle's and the next distinct
+    finite logit on either side, never a logit two groups away."""
+    from tests import parity
+    x = np.array([1.0, 3.0, 2.0, 2.0, -np.inf, 5.0, 3.0])
+    np.testing.assert_array_equal(parity.adjacent_values(x, 2.0), np.float32([1, 2, 3]))
+    np.testing.assert_array_equal(parity.adjacent_values(x, 1.0), np.float32([1, 2]))
+    np.testing.assert_array_equal(parity.adjacent_values(x, 5.0), np.float32([3, 5]))
+    assert 5.0 not in parity.adjacent_values(x, 2.0)
+    assert 1.0 not in parity.adjacent_values(x, 3.0)
