@@ -525,6 +525,88 @@ __device__ int row_search(const typename E::storage* r0, const typename E::stora
   return range_search<E, VEC, kThreads>(r0, r1, 0, V, (float)(u * total), weight, lds_f, lds_i);
 }
 
+// Bytes [o, o + 16) of the 32 bytes a || b (o < 16, the same in every lane
+// of the workgroup): each output word is one v_alignbyte of two input words.
+__device__ inline u32x4 cut_vector(const u32x4& a, const u32x4& b, int o) {
+  const uint32_t c[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  const uint32_t r = (uint32_t)o & 3u;
+  auto w = [&](int k) { return __builtin_amdgcn_alignbyte(c[k + 1], c[k], r); };
+  switch (o >> 2) {
+    case 0: return u32x4{w(0), w(1), w(2), w(3)};
+    case 1: return u32x4{w(1), w(2), w(3), w(4)};
+    case 2: return u32x4{w(2), w(3), w(4), w(5)};
+    default: return u32x4{w(3), w(4), w(5), w(6)};
+  }
+}
+
+// Tokens [j0, j0 + kVec) of a row that need not start on 16 bytes (its tensor
+// does), as floats; tokens at or past V read as -inf.  Cut from the two
+// aligned vectors that cover them when both lie in the row, else token by token.
+template <class E>
+__device__ inline void shifted_vector(const typename E::storage* row, int j0, int V, float* out) {
+  const int sh = (int)(((uintptr_t)row & 15u) / sizeof(typename E::storage));
+  if (j0 + 2 * E::kVec - sh <= V) {
+    const auto* ra = row - sh;
+    E::unpack(cut_vector(load_cached(ra + j0), load_cached(ra + j0 + E::kVec), sh * (int)sizeof(typename E::storage)),
+              out);
+  } else {
+#pragma unroll
+    for (int v = 0; v < E::kVec; ++v) out[v] = j0 + v < V ? E::at(row, j0 + v) : -INFINITY;
+  }
+}
+
+// tile_search (inverse-CDF draw over one tile of kThreads * PER tokens, one
+// memory round trip and one workgroup scan) for rows that need not start on
+// 16 bytes: thread t owns the PER tokens from tile_lo + t * PER, each vector
+// from shifted_vector.  Tokens at or past V have weight 0.  Returns the first
+// token whose running weight exceeds theta, or the tile's last positive-weight
+// token if rounding leaves the whole tile at or below theta, or -1 if no
+// token has positive weight.  Called by the whole workgroup.
+template <class E, int PER, class W>
+__device__ int shifted_tile_search(const typename E::storage* r0, const typename E::storage* r1, int tile_lo, int V,
+                                   float theta, W&& weight, float* lds_f, int* lds_i) {
+  constexpr int NS = PER / E::kVec;
+  __shared__ int found;
+  const int base = tile_lo + (int)threadIdx.x * PER;
+  float x0[PER], x1[PER];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    shifted_vector<E>(r0, base + s * E::kVec, V, x0 + s * E::kVec);
+    if (r1) shifted_vector<E>(r1, base + s * E::kVec, V, x1 + s * E::kVec);
+  }
+  if (threadIdx.x == 0) found = -1;
+  float w[PER];
+  float sum = 0.f;
+  int last_pos = -1;
+#pragma unroll
+  for (int t = 0; t < PER; ++t) {
+    const float wv = base + t < V ? weight(x0[t], r1 ? x1[t] : 0.f) : 0.f;
+    w[t] = wv;
+    if (wv > 0.f) last_pos = base + t;
+    sum += wv;
+  }
+  float excl, total;
+  const float incl = block_scan(sum, lds_f, &excl, &total);
+  if (excl <= theta && theta < incl) {  // exactly one thread owns theta
+    float run = excl;
+    int pick = -1, lastp = -1;
+#pragma unroll
+    for (int t = 0; t < PER; ++t) {
+      if (w[t] > 0.f) lastp = base + t;
+      run += w[t];
+      if (pick < 0 && run > theta) pick = base + t;
+    }
+    found = pick >= 0 ? pick : lastp;
+  }
+  __syncthreads();
+  const int f = found;
+  __syncthreads();
+  if (f >= 0) return f;
+  ArgMax lp{last_pos >= 0 ? (float)(last_pos - tile_lo) : -1.f, last_pos};
+  lp = block_argmax(lp, lds_f, lds_i);
+  return lp.i;
+}
+
 // Row normaliser from nch chunk partials (max m_c, sum S_c relative to m_c),
 // computed by one wave in a fixed order: M = max m_c and
 // S = sum_c S_c exp2((m_c - M) k) accumulated in fp64.  Call from all 64

@@ -277,7 +277,9 @@ __device__ inline void load_raw(const typename E::storage* row, int tile_lo, int
   }
 }
 
-template <class E, int PER>
+// PER_TOKEN: V need not be a multiple of kVec, so the vector that straddles
+// V is masked token by token.
+template <class E, int PER, bool PER_TOKEN = false>
 __device__ inline void unpack_tile(const RawTile<E, PER>& r, int tile_lo, int V, float (&x)[PER]) {
   if (tile_lo + kWave * PER <= V) {  // the whole tile is in range: no per-token select
 #pragma unroll
@@ -295,8 +297,40 @@ __device__ inline void unpack_tile(const RawTile<E, PER>& r, int tile_lo, int V,
     float t[E::kVec];
     E::unpack(r.v[s], t);
 #pragma unroll
-    for (int v = 0; v < E::kVec; ++v) x[s * E::kVec + v] = j0 < V ? t[v] : -INFINITY;
+    for (int v = 0; v < E::kVec; ++v) x[s * E::kVec + v] = (PER_TOKEN ? j0 + v : j0) < V ? t[v] : -INFINITY;
   }
+}
+
+// A row that does not start on 16 bytes, copied from its aligned-down start
+// (sh tokens earlier): each vector is cut from the two aligned vectors that
+// cover it.  The copies run to the end of the tensor, so the vector that
+// straddles the row's end holds the next row's first tokens (unpack_tile
+// masks them to -inf).  Only where the second aligned vector would run past
+// the tensor's end (the tensor's last row; `avail` = tokens from the row's
+// start to the end of the tensor) are the tokens read one by one.
+template <class E, int PER, class Avail>
+__device__ inline void fix_shifted_tail(float (&x)[PER], int tile_lo, int V, const typename E::storage* row, int sh,
+                                        Avail&& avail_fn) {
+  if (tile_lo + kWave * PER <= V) return;  // not the row's last tile
+  const int avail = avail_fn();
+  if (tile_lo + kWave * PER + E::kVec - sh <= avail) return;
+#pragma unroll
+  for (int s = 0; s < PER / E::kVec; ++s) {
+    const int j0 = tile_lo + (s * kWave + (int)(threadIdx.x & (kWave - 1))) * E::kVec;
+    if (j0 + 2 * E::kVec - sh > avail) {
+#pragma unroll
+      for (int v = 0; v < E::kVec; ++v) x[s * E::kVec + v] = j0 + v < V ? E::at(row, j0 + v) : -INFINITY;
+    }
+  }
+}
+
+// Tokens from the start of target row i of sequence b, or of its draft row,
+// to the end of that logit tensor, at most 2^30.
+template <bool DRAFT>
+__device__ inline int tokens_to_end(const VerifyArgs& a, int b, int i) {
+  const long rows = DRAFT ? (long)a.B * a.gamma : (long)a.B * (a.gamma + 1);
+  const long r = DRAFT ? (long)b * a.gamma + i : (long)b * (a.gamma + 1) + i;
+  return (int)min((rows - r) * (long)a.V, 1L << 30);
 }
 
 template <int KVEC>
@@ -594,15 +628,24 @@ __device__ inline void mask_below(float (&x)[PER], float t) {
 
 // Pair item, T > 0, in three steps.  Phase 1 turns the wave tile into kept
 // weights and publishes the wave's (scaled max, sum) of both rows.
-template <class E, int PER, bool THR>
+template <class E, int PER, bool THR, bool SHIFT = false>
 __device__ __attribute__((always_inline)) void pair_phase1(const FusedParams& P, int item, int c, int lo,
                                                            const RawPair<E, PER>& raw, const ItemThr& th,
                                                            float (&ep)[PER], float (&eq)[PER], float& mp, float& mq,
                                                            float& sp, float& sq) {
   const VerifyArgs& a = P.a;
   const float k = a.k;
-  unpack_tile<E, PER>(raw.p, lo, a.V, ep);
-  unpack_tile<E, PER>(raw.q, lo, a.V, eq);
+  unpack_tile<E, PER, SHIFT>(raw.p, lo, a.V, ep);
+  unpack_tile<E, PER, SHIFT>(raw.q, lo, a.V, eq);
+  if constexpr (SHIFT) {  // rows that do not start on 16 bytes
+    const int b = item / a.gamma, i = item % a.gamma;
+    const auto* pr = trow<E>(a, b, i);
+    const auto* qr = drow<E>(a, b, i);
+    fix_shifted_tail<E, PER>(ep, lo, a.V, pr, (int)(((uintptr_t)pr & 15u) / sizeof(typename E::storage)),
+                             [&] { return tokens_to_end<false>(a, b, i); });
+    fix_shifted_tail<E, PER>(eq, lo, a.V, qr, (int)(((uintptr_t)qr & 15u) / sizeof(typename E::storage)),
+                             [&] { return tokens_to_end<true>(a, b, i); });
+  }
   if constexpr (THR) {
     mask_below<PER>(ep, th.p);
     mask_below<PER>(eq, th.q);
@@ -740,7 +783,7 @@ __device__ __attribute__((always_inline)) void pair_compute_sample(const FusedPa
 }
 
 // Pair item at T = 0, or a bonus item: one pass, no waiting.
-template <class E, int PER, bool ARGMAX, bool THR>
+template <class E, int PER, bool ARGMAX, bool THR, bool SHIFT = false>
 __device__ __attribute__((always_inline)) void single_pass_compute(const FusedParams& P, int item, int c, int lo,
                                                                    const RawPair<E, PER>& raw, const ItemThr& th) {
   const VerifyArgs& a = P.a;
@@ -755,7 +798,13 @@ __device__ __attribute__((always_inline)) void single_pass_compute(const FusedPa
     w1 = pack2i(nz_bits(aq.v), (uint32_t)aq.i);
   } else {
     float x[PER];
-    unpack_tile<E, PER>(raw.p, lo, a.V, x);
+    unpack_tile<E, PER, SHIFT>(raw.p, lo, a.V, x);
+    if constexpr (SHIFT) {  // the bonus row, not starting on 16 bytes
+      const int b = item - P.n_pairs, g = seq_gamma_of<true>(a, b);
+      const auto* r = trow<E>(a, b, g);
+      fix_shifted_tail<E, PER>(x, lo, a.V, r, (int)(((uintptr_t)r & 15u) / sizeof(typename E::storage)),
+                               [&] { return tokens_to_end<false>(a, b, g); });
+    }
     if constexpr (ARGMAX) {
       const ArgMax ab = wave_argmax(thread_argmax<E, PER>(x, lo));
       w0 = pack2i(nz_bits(ab.v), (uint32_t)ab.i);
@@ -789,10 +838,10 @@ __device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 //   copies; barrier (stage full).
 // Each of the 2 * 4 * NS wave loads of an item moves 1 KiB of one row into
 // 1 KiB of LDS, lane l writing bytes [16 l, 16 l + 16).
-template <int PER>
-constexpr int stage_vectors() { return 2 * kWavesPerGroup * (PER / BF16::kVec) * kWave; }
+template <int PER, bool SHIFT>
+constexpr int stage_vectors() { return 2 * (kWavesPerGroup * (PER / BF16::kVec) + (SHIFT ? 1 : 0)) * kWave; }
 
-template <int PER, bool ARGMAX, bool EXT, bool WIDE, bool THR>
+template <int PER, bool ARGMAX, bool EXT, bool WIDE, bool THR, bool SHIFT>
 __device__ __attribute__((always_inline)) void compute_loop_staged(const FusedParams& P, int team, int rank,
                                                                    u32x4* stage, uint64_t* w1, NormMsg* msg) {
   using E = BF16;
@@ -811,33 +860,52 @@ __device__ __attribute__((always_inline)) void compute_loop_staged(const FusedPa
   // first vector and ends at the end of the row, so vectors past V read as
   // zero (unpack_tile masks them to -inf) and all address arithmetic is
   // scalar; lane l moves bytes [16 l, 16 l + 16).
+  //
+  // Rows that do not start on 16 bytes (V not a multiple of kVec; the tensors
+  // themselves start on 16 bytes) are copied from their 16-byte aligned-down
+  // start: a row starting sh tokens past that boundary has token t at
+  // position t + sh of the copy.  Such rows take one KiB more per row, so the
+  // slot also holds the vector after the tile, and every lane cuts its
+  // vectors out of the two aligned vectors that cover them.
   constexpr int kCopyBytes = kWave * 16;                  // one copy: 16 bytes per lane
   constexpr int kRowLoads = kWavesPerGroup * NS;          // copies per row tile of the workgroup
+  constexpr int kSlotVec = (kRowLoads + (SHIFT ? 1 : 0)) * kWave;  // vectors per row slot of the stage
   static_assert(NS * E::kVec == PER && (kRowLoads & (kRowLoads - 1)) == 0, "stage copy shape");
+  constexpr bool shifted = SHIFT;  // V % kVec != 0
+  const int row_loads = shifted ? kRowLoads + 1 : kRowLoads;
   const unsigned tile_bytes = (unsigned)(rank * kWavesPerGroup * kWave * PER * (int)sizeof(E::storage));
+  auto shift_of = [](const E::storage* row) {  // tokens of the row's start past 16 bytes
+    return (int)(((uintptr_t)row & 15u) / sizeof(E::storage));
+  };
   auto issue = [&](int item) {  // waves 1..3
     const bool pair = item < P.n_pairs;
     const int b = pair ? item / a.gamma : item - P.n_pairs;
     // a bonus item reads row gamma_b (padding items are never issued)
     const int i = pair ? item % a.gamma : seq_gamma_of<EXT>(a, b);
-    const E::storage* prow = trow<E>(a, b, i);
-    const E::storage* qrow = pair ? drow<E>(a, b, i) : prow;
-    const int n = pair ? kLoads : kLoads / 2;
-    // Copy l moves the (l mod kRowLoads)-th KiB of this workgroup's tile of
-    // row l / kRowLoads (the four wave tiles are adjacent, vector s of wave w
-    // being KiB w * NS + s) into KiB l of the stage.
-    for (int l = wave - 1; l < n; l += kWavesPerGroup - 1) {
-      const unsigned off = tile_bytes + (unsigned)(l & (kRowLoads - 1)) * kCopyBytes;
-      const uint64_t addr = reinterpret_cast<uint64_t>(l < kRowLoads ? prow : qrow) + off;
-      const uint64_t uaddr = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(addr >> 32)) << 32) |
-                             (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)addr);
-      // bytes from the copy's first vector to the row's end (rows are shorter
-      // than 2^31 bytes); a signed max stays a scalar instruction
-      const int nrec = max((int)row_bytes - (int)off, 0);
-      const __amdgpu_buffer_rsrc_t rs =
-          __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(uaddr), (short)0, nrec, 0x00020000);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)&stage[l * kWave], 16,
-                                               (unsigned)lane * 16u, 0, 0, 0);
+    const E::storage* rows[2] = {trow<E>(a, b, i), pair ? drow<E>(a, b, i) : nullptr};
+    int first = wave - 1;  // this wave's first copy of the row: copies l with l mod 3 == wave - 1
+    for (int r = 0; r < (pair ? 2 : 1); ++r) {
+      const int sh = shift_of(rows[r]);
+      const E::storage* base = rows[r] - sh;  // 16-byte aligned
+      // bytes readable from base: the row (its sh leading tokens belong to the
+      // row before), or for a shifted row everything to the tensor's end
+      int ext = (sh + a.V) * (int)sizeof(E::storage);
+      if constexpr (shifted) ext = (sh + (r == 0 ? tokens_to_end<false>(a, b, i) : tokens_to_end<true>(a, b, i))) *
+                                   (int)sizeof(E::storage);
+      for (int l = first; l < row_loads; l += kWavesPerGroup - 1) {
+        const unsigned off = tile_bytes + (unsigned)l * kCopyBytes;
+        const uint64_t addr = reinterpret_cast<uint64_t>(base) + off;
+        const uint64_t uaddr = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(addr >> 32)) << 32) |
+                               (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)addr);
+        // bytes from the copy's first vector to the row's end (rows are shorter
+        // than 2^31 bytes); a signed max stays a scalar instruction
+        const int nrec = max(ext - (int)off, 0);
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(uaddr), (short)0, nrec, 0x00020000);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)&stage[r * kSlotVec + l * kWave],
+                                                 16, (unsigned)lane * 16u, 0, 0, 0);
+      }
+      first = (first + (kWavesPerGroup - 1) - row_loads % (kWavesPerGroup - 1)) % (kWavesPerGroup - 1);
     }
   };
 
@@ -868,10 +936,25 @@ __device__ __attribute__((always_inline)) void compute_loop_staged(const FusedPa
     }
     ++round;
     RawPair<E, PER> A;
+    int sh_p = 0, sh_q = 0;
+    if constexpr (shifted) {
+      const bool pair = item < P.n_pairs;
+      const int b = pair ? item / a.gamma : item - P.n_pairs;
+      const int i = pair ? item % a.gamma : seq_gamma_of<EXT>(a, b);
+      sh_p = shift_of(trow<E>(a, b, i));
+      sh_q = pair ? shift_of(drow<E>(a, b, i)) : 0;
 #pragma unroll
-    for (int v = 0; v < NS; ++v) {
-      A.p.v[v] = stage[(wave * NS + v) * kWave + lane];
-      A.q.v[v] = stage[((kWavesPerGroup + wave) * NS + v) * kWave + lane];
+      for (int v = 0; v < NS; ++v) {
+        const int j = (wave * NS + v) * kWave + lane;
+        A.p.v[v] = cut_vector(stage[j], stage[j + 1], sh_p * (int)sizeof(E::storage));
+        A.q.v[v] = cut_vector(stage[kSlotVec + j], stage[kSlotVec + j + 1], sh_q * (int)sizeof(E::storage));
+      }
+    } else {
+#pragma unroll
+      for (int v = 0; v < NS; ++v) {
+        A.p.v[v] = stage[(wave * NS + v) * kWave + lane];
+        A.q.v[v] = stage[kSlotVec + (wave * NS + v) * kWave + lane];
+      }
     }
     lds_barrier();
     const int next_d = team_dense(team, ++kth, P.nteams, n_live, n_lpairs);
@@ -888,7 +971,7 @@ __device__ __attribute__((always_inline)) void compute_loop_staged(const FusedPa
       if (empty_item<EXT>(P, item)) {
       } else if (item < P.n_pairs) {
         float xp[PER], xq[PER], cp, cq, s_p, s_q;
-        pair_phase1<E, PER, THR>(P, item, c, lo, A, th, xp, xq, cp, cq, s_p, s_q);
+        pair_phase1<E, PER, THR, SHIFT>(P, item, c, lo, A, th, xp, xq, cp, cq, s_p, s_q);
         if (pend >= 0) {
           const NormMsg m = pair_wait<WIDE>(P, pend, parity, w1, msg);
           pair_phase2<PER, EXT>(P, pend, c, m, ep, eq, mp, mq, sp, sq);
@@ -905,7 +988,7 @@ __device__ __attribute__((always_inline)) void compute_loop_staged(const FusedPa
         sq = s_q;
         pend = item;
       } else {
-        single_pass_compute<E, PER, ARGMAX, THR>(P, item, c, lo, A, th);
+        single_pass_compute<E, PER, ARGMAX, THR, SHIFT>(P, item, c, lo, A, th);
         if (pend >= 0) {
           const NormMsg m = pair_wait<WIDE>(P, pend, parity, w1, msg);
           pair_phase2<PER, EXT>(P, pend, c, m, ep, eq, mp, mq, sp, sq);
@@ -955,7 +1038,7 @@ __device__ inline ArgMax combine_argmax(const uint64_t* w, int W, int half) {
 
 // Pair item: alpha, the ratio test and, after a rejection, the residual
 // sample.  Publishes (accept, token) for the sequence's bonus finisher.
-template <class E, int PER, bool ARGMAX, bool EXT>
+template <class E, int PER, bool ARGMAX, bool EXT, bool SHIFT>
 __device__ void finish_pair(const FusedParams& P, int item, uint64_t* w1, uint64_t* w2) {
   using S = SearchShape<E, PER>;
   __shared__ float lds_f[kMaxWaves];
@@ -1101,6 +1184,9 @@ __device__ void finish_pair(const FusedParams& P, int item, uint64_t* w1, uint64
       }
     }
     int t = 0;
+    // rows that do not start on 16 bytes take the searches that cut each
+    // vector from the two aligned vectors covering it
+    constexpr bool shifted = SHIFT;
     if (mode) {
       const float invSp = (float)(1.0 / Sp), invSq = (float)((double)a.lenience / Sq);  // l / S_q
       // keep thresholds of the two rows (-inf: nothing filtered)
@@ -1114,12 +1200,15 @@ __device__ void finish_pair(const FusedParams& P, int item, uint64_t* w1, uint64
           // give exactly 0
           return fmaxf(__fmul_rn(wp, invSp) - __fmul_rn(wq, invSq), 0.f);
         };
-        t = tile_search<E, S::kPer, kThreads>(prow, qrow, tile_s * S::kTokens, a.V, rest_s, residual, lds_f, lds_i);
+        if constexpr (shifted)
+          t = shifted_tile_search<E, S::kPer>(prow, qrow, tile_s * S::kTokens, a.V, rest_s, residual, lds_f, lds_i);
+        else
+          t = tile_search<E, S::kPer, kThreads>(prow, qrow, tile_s * S::kTokens, a.V, rest_s, residual, lds_f, lds_i);
         // No token of the picked tile has a positive residual in this
         // arithmetic: the tile's mass, formed from the overlap identity over
         // whole tiles, was rounding noise.  Draw from the residual of the whole
         // row instead, token by token in the arithmetic of the search.
-        if (t < 0) t = row_search<E, true, kThreads>(prow, qrow, a.V, uf, residual, lds_f, lds_i, lds_d);
+        if (t < 0) t = row_search<E, !shifted, kThreads>(prow, qrow, a.V, uf, residual, lds_f, lds_i, lds_d);
         // No token of the row has a positive residual either: p_i and l q_i
         // agree to fp32 everywhere, the residual without mass.  Sample p_i.
         if (t < 0) {
@@ -1127,11 +1216,13 @@ __device__ void finish_pair(const FusedParams& P, int item, uint64_t* w1, uint64
           pick_p_tile();
         }
       }
-      if (mode == 2)
-        t = tile_search<E, S::kPer, kThreads>(prow, nullptr, tile_s * S::kTokens, a.V, rest_s,
-                                              [&](float xp, float) {
-          return xp >= tp ? fast_exp2(fmaf(xp, k, -Mp)) : 0.f;
-        }, lds_f, lds_i);
+      if (mode == 2) {
+        auto pw = [&](float xp, float) { return xp >= tp ? fast_exp2(fmaf(xp, k, -Mp)) : 0.f; };
+        if constexpr (shifted)
+          t = shifted_tile_search<E, S::kPer>(prow, nullptr, tile_s * S::kTokens, a.V, rest_s, pw, lds_f, lds_i);
+        else
+          t = tile_search<E, S::kPer, kThreads>(prow, nullptr, tile_s * S::kTokens, a.V, rest_s, pw, lds_f, lds_i);
+      }
     }
     if (threadIdx.x == 0) {
       st_u64(P.pair_res + item, pack2i((uint32_t)acc_s | kResMark, (uint32_t)t));
@@ -1157,7 +1248,7 @@ __device__ void finish_pair(const FusedParams& P, int item, uint64_t* w1, uint64
 
 // Bonus item: the token from p_gamma ([FI] Algorithm 1 step 4), then the
 // sequence's outputs once every pair result of the sequence is published.
-template <class E, int PER, bool ARGMAX, bool EXT>
+template <class E, int PER, bool ARGMAX, bool EXT, bool SHIFT>
 __device__ void finish_bonus(const FusedParams& P, int item, uint64_t* w1, uint64_t* res) {
   using S = SearchShape<E, PER>;
   __shared__ float lds_f[kMaxWaves];
@@ -1201,11 +1292,13 @@ __device__ void finish_bonus(const FusedParams& P, int item, uint64_t* w1, uint6
       for (int c = g * S::kGroup; c < min(W, (g + 1) * S::kGroup); ++c) m += p_tile_mass(w1, c, M);
       return m;
     }, &tile_s, &rest_s);
-    t_bonus = tile_search<E, S::kPer, kThreads>(row, nullptr, tile_s * S::kTokens, a.V, rest_s,
-                                                   [&](float xp, float) {
-                                                     return xp >= tb ? fast_exp2(fmaf(xp, k, -M)) : 0.f;
-                                                   },
-                                                   lds_f, lds_i);
+    auto bw = [&](float xp, float) { return xp >= tb ? fast_exp2(fmaf(xp, k, -M)) : 0.f; };
+    // rows that do not start on 16 bytes take the search that cuts each vector
+    // from the two aligned vectors covering it
+    if constexpr (SHIFT)
+      t_bonus = shifted_tile_search<E, S::kPer>(row, nullptr, tile_s * S::kTokens, a.V, rest_s, bw, lds_f, lds_i);
+    else
+      t_bonus = tile_search<E, S::kPer, kThreads>(row, nullptr, tile_s * S::kTokens, a.V, rest_s, bw, lds_f, lds_i);
   }
   if constexpr (EXT) {
     // the padding positions (never scheduled as items): NaN outputs
@@ -1247,7 +1340,7 @@ __device__ void finish_bonus(const FusedParams& P, int item, uint64_t* w1, uint6
 // the finisher's copies of an item's slots on a finisher (a workgroup is one
 // or the other); the compute workgroup's poll buffer and normaliser messages
 // follow it.
-template <class E, int PER, bool ARGMAX>
+template <class E, int PER, bool ARGMAX, bool SHIFT>
 struct Pool {
   // Only the bf16 T > 0 kernel stages.  In argmax mode each wave loads its own
   // tiles when their item comes up: with no team exchange to hide and little
@@ -1256,15 +1349,17 @@ struct Pool {
   // 41.8 us on the B=64 workload); at T > 0 the stage wins (42.5 vs 51.0 us).
   static constexpr bool kStaged = std::is_same<E, BF16>::value && !ARGMAX;
   static constexpr int kFinBytes = (3 * kMaxWaveTiles + SPEC_MAX_GAMMA) * 8;
-  static constexpr int kStageBytes = kStaged ? stage_vectors<PER>() * 16 : 0;
+  static constexpr int kStageBytes = kStaged ? stage_vectors<PER, SHIFT>() * 16 : 0;
   static constexpr int kABytes = kStageBytes > kFinBytes ? kStageBytes : kFinBytes;
   static constexpr int kBytes = kABytes + 2 * kMaxWaveTiles * 8 + 2 * (int)sizeof(NormMsg);
 };
 
 // THR: the launch filters by keep thresholds (extended kernels at T > 0 only).
-template <class E, int PER, bool ARGMAX, bool EXT, bool WIDE, bool THR>
+// SHIFT: bf16 rows that do not start on 16 bytes (V % kVec != 0), T > 0,
+// with none of the extensions.
+template <class E, int PER, bool ARGMAX, bool EXT, bool WIDE, bool THR, bool SHIFT>
 __global__ __launch_bounds__(kThreads, kMinWaves) void fused_kernel(FusedParams P) {
-  using L = Pool<E, PER, ARGMAX>;
+  using L = Pool<E, PER, ARGMAX, SHIFT>;
   __shared__ __align__(16) unsigned char pool[L::kBytes];
   uint64_t* poll_buf = reinterpret_cast<uint64_t*>(pool + L::kABytes);
   NormMsg* msg = reinterpret_cast<NormMsg*>(pool + L::kABytes + 2 * kMaxWaveTiles * 8);
@@ -1282,7 +1377,8 @@ __global__ __launch_bounds__(kThreads, kMinWaves) void fused_kernel(FusedParams 
   }
   if (team >= 0) {
     if constexpr (L::kStaged) {
-      compute_loop_staged<PER, ARGMAX, EXT, WIDE, THR>(P, team, rank, reinterpret_cast<u32x4*>(pool), poll_buf, msg);
+      compute_loop_staged<PER, ARGMAX, EXT, WIDE, THR, SHIFT>(P, team, rank, reinterpret_cast<u32x4*>(pool), poll_buf,
+                                                              msg);
     } else {
       const int c = rank * kWavesPerGroup + (int)threadIdx.x / kWave;  // this wave's tile
       const int lo = c * kWave * PER;
@@ -1311,9 +1407,9 @@ __global__ __launch_bounds__(kThreads, kMinWaves) void fused_kernel(FusedParams 
     for (int d = f; d < n_live; d += P.nfin) {
       const int item = live_item<EXT>(P, d);
       if (item < P.n_pairs)
-        finish_pair<E, PER, ARGMAX, EXT>(P, item, fin_w1, fin_w2);
+        finish_pair<E, PER, ARGMAX, EXT, SHIFT>(P, item, fin_w1, fin_w2);
       else
-        finish_bonus<E, PER, ARGMAX, EXT>(P, item, fin_w1, fin_res);
+        finish_bonus<E, PER, ARGMAX, EXT, SHIFT>(P, item, fin_w1, fin_res);
     }
   }
 }
@@ -1360,7 +1456,7 @@ hipError_t resident_blocks(Kern kern, long* out) {
   return e;
 }
 
-template <class E, bool ARGMAX, bool EXT = false>
+template <class E, bool ARGMAX, bool EXT = false, bool SHIFT = false>
 hipError_t launch(const VerifyArgs& a, hipStream_t s) {
   const Layout L = layout(a.B, a.gamma, a.V);
   char* ws = static_cast<char*>(a.ws);
@@ -1380,11 +1476,19 @@ hipError_t launch(const VerifyArgs& a, hipStream_t s) {
   // launches carry no code for them
   constexpr bool kThrOk = EXT && !ARGMAX;
   const bool thr = kThrOk && a.thr != nullptr;
-  auto kern = !ARGMAX && P.W > kWave
-                  ? (thr ? fused_kernel<E, per_of<E>(), ARGMAX, EXT, !ARGMAX, kThrOk>
-                         : fused_kernel<E, per_of<E>(), ARGMAX, EXT, !ARGMAX, false>)
-                  : (thr ? fused_kernel<E, per_of<E>(), ARGMAX, EXT, false, kThrOk>
-                         : fused_kernel<E, per_of<E>(), ARGMAX, EXT, false, false>);
+  using Kern = void (*)(FusedParams);
+  Kern kern;
+  if constexpr (SHIFT) {
+    static_assert(std::is_same<E, BF16>::value && !ARGMAX && !EXT, "shifted rows: the plain bf16 T > 0 kernel");
+    kern = P.W > kWave ? fused_kernel<E, per_of<E>(), false, false, true, false, true>
+                       : fused_kernel<E, per_of<E>(), false, false, false, false, true>;
+  } else {
+    kern = !ARGMAX && P.W > kWave
+               ? (thr ? fused_kernel<E, per_of<E>(), ARGMAX, EXT, !ARGMAX, kThrOk, false>
+                      : fused_kernel<E, per_of<E>(), ARGMAX, EXT, !ARGMAX, false, false>)
+               : (thr ? fused_kernel<E, per_of<E>(), ARGMAX, EXT, false, kThrOk, false>
+                      : fused_kernel<E, per_of<E>(), ARGMAX, EXT, false, false, false>);
+  }
   long resident = 0;
   hipError_t e = resident_blocks(kern, &resident);
   if (e != hipSuccess) return e;
@@ -1404,8 +1508,11 @@ unsigned wait_limit() { return g_wait_polls; }
 
 size_t fused_workspace_bytes(int B, int gamma, int V) { return layout(B, gamma, V).total; }
 
+// Shapes of the T > 0 path.  bf16 rows need not start on 16 bytes (the
+// staged kernel copies them from their aligned-down start); fp32 rows and the
+// argmax kernels load each lane's vectors directly and need V % kVec == 0.
 bool fused_supported(int B, int gamma, int V, int dtype) {
-  const int vec = dtype == SPEC_BF16 ? BF16::kVec : F32::kVec;
+  const int vec = dtype == SPEC_BF16 ? 1 : F32::kVec;
   return B >= 1 && V % vec == 0 && groups_for(V, per_for(dtype)) * kWavesPerGroup <= kMaxWaveTiles &&
          (size_t)B * (gamma + 1) < (1u << 30);
 }
@@ -1414,12 +1521,18 @@ hipError_t fused_launch(const VerifyArgs& a, hipStream_t s) {
   if (!fused_supported(a.B, a.gamma, a.V, a.dtype)) return hipErrorNotSupported;
   if ((uintptr_t)a.target % 16 != 0 || (a.gamma > 0 && (uintptr_t)a.draft % 16 != 0)) return hipErrorNotSupported;
   const bool argmax = a.temperature == 0.f;
+  const int vec = a.dtype == SPEC_BF16 ? BF16::kVec : F32::kVec;
+  const bool shifted = a.V % vec != 0;
   // The extended kernels take lenience below 1, per-sequence draft counts and
   // top-k / top-p thresholds; lenience and the filters do not change argmax
   // mode.
   const bool ext = a.gamma_seq != nullptr || (!argmax && (a.lenience != 1.f || a.thr != nullptr));
+  // rows that do not start on 16 bytes: only the plain bf16 T > 0 kernel
+  // takes them (the others fall back to the multipass path)
+  if (shifted && (argmax || ext || a.dtype != SPEC_BF16)) return hipErrorNotSupported;
   if (a.dtype == SPEC_BF16) {
     if (argmax) return ext ? launch<BF16, true, true>(a, s) : launch<BF16, true>(a, s);
+    if (shifted) return launch<BF16, false, false, true>(a, s);
     return ext ? launch<BF16, false, true>(a, s) : launch<BF16, false>(a, s);
   }
   if (argmax) return ext ? launch<F32, true, true>(a, s) : launch<F32, true>(a, s);

@@ -76,6 +76,30 @@ def test_config3_full_size(dev, algo, T):
 
 @pytest.mark.parametrize("algo", list(ALGOS))
 @pytest.mark.parametrize("T", [1.0, 0.0])
+def test_odd_vocabulary_every_sequence(dev, algo, T):
+    """The B=64 row recipe at V = 50257, an odd vocabulary: consecutive rows
+    start at every offset modulo 16 bytes.  At T > 0 the fused path copies each
+    row from its aligned-down start and cuts every lane's vectors out of two
+    aligned ones (the row's last vectors token by token); in argmax mode it
+    declines the shape.  All 16 sequences against the oracle."""
+    case, res = _full(("odd", T), lambda: W.config3(3, T, B=16, V=50257))
+    if algo == "fused" and T == 0.0:
+        sv = _sv()
+        t = gpu_util.case_tensors(case, dev)
+        with pytest.raises(sv.SpecVerifyError) as e:
+            sv.verify(t["target"], t["draft"], t["tokens"], t["uniforms"], T, algo=sv.ALGO_FUSED)
+        assert e.value.status == sv.SPEC_EUNSUPPORTED
+        return
+    gpu = gpu_util.run_case(case, ALGOS[algo], dev=dev)
+    rep = parity.check(case, gpu, where=f"odd V T{T}", res=res)
+    _banner(f"odd V {algo} T={T}: {rep}")
+    assert rep.u_band <= 1
+    assert rep.cdf_band <= case.B // 3
+    assert rep.token_mismatch_valid <= 1
+
+
+@pytest.mark.parametrize("algo", list(ALGOS))
+@pytest.mark.parametrize("T", [1.0, 0.0])
 def test_config5_full_size_every_sequence(dev, algo, T):
     """B=256, gamma=8, V=256000 bf16 with 5% confidently wrong draft rows: every
     sequence against the oracle."""
@@ -115,9 +139,11 @@ def test_shapes(dev, algo, shape):
     B, G, V, dt, T = shape
     case = W.gaussian_case(B, G, V, dt, T, seed=B * 1000 + G * 10 + V % 97, target_std=2.5,
                            draft_scale=0.9, draft_noise=0.8)
-    if algo == "fused" and V % (8 if dt == "bf16" else 4):
-        # rows that are not whole 16-byte vectors: the fused path declines them
-        # (the default algorithm then runs the multipass path, tested above)
+    if algo == "fused" and V % (8 if dt == "bf16" else 4) and (dt == "f32" or T == 0.0):
+        # rows that are not whole 16-byte vectors: the fused path takes them
+        # only in bf16 at T > 0 (it copies each row from its aligned-down
+        # start); elsewhere it declines them and the default algorithm runs
+        # the multipass path, tested above
         sv = _sv()
         t = gpu_util.case_tensors(case, dev)
         with pytest.raises(sv.SpecVerifyError) as e:
