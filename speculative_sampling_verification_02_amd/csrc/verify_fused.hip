@@ -872,7 +872,6 @@ __device__ __attribute__((always_inline)) void compute_loop_staged(const FusedPa
   constexpr int kSlotVec = (kRowLoads + (SHIFT ? 1 : 0)) * kWave;  // vectors per row slot of the stage
   static_assert(NS * E::kVec == PER && (kRowLoads & (kRowLoads - 1)) == 0, "stage copy shape");
   constexpr bool shifted = SHIFT;  // V % kVec != 0
-  const int row_loads = shifted ? kRowLoads + 1 : kRowLoads;
   const unsigned tile_bytes = (unsigned)(rank * kWavesPerGroup * kWave * PER * (int)sizeof(E::storage));
   auto shift_of = [](const E::storage* row) {  // tokens of the row's start past 16 bytes
     return (int)(((uintptr_t)row & 15u) / sizeof(E::storage));
@@ -882,30 +881,50 @@ __device__ __attribute__((always_inline)) void compute_loop_staged(const FusedPa
     const int b = pair ? item / a.gamma : item - P.n_pairs;
     // a bonus item reads row gamma_b (padding items are never issued)
     const int i = pair ? item % a.gamma : seq_gamma_of<EXT>(a, b);
-    const E::storage* rows[2] = {trow<E>(a, b, i), pair ? drow<E>(a, b, i) : nullptr};
-    int first = wave - 1;  // this wave's first copy of the row: copies l with l mod 3 == wave - 1
-    for (int r = 0; r < (pair ? 2 : 1); ++r) {
-      const int sh = shift_of(rows[r]);
-      const E::storage* base = rows[r] - sh;  // 16-byte aligned
-      // bytes readable from base: the row (its sh leading tokens belong to the
-      // row before), or for a shifted row everything to the tensor's end
-      int ext = (sh + a.V) * (int)sizeof(E::storage);
-      if constexpr (shifted) ext = (sh + (r == 0 ? tokens_to_end<false>(a, b, i) : tokens_to_end<true>(a, b, i))) *
-                                   (int)sizeof(E::storage);
-      for (int l = first; l < row_loads; l += kWavesPerGroup - 1) {
-        const unsigned off = tile_bytes + (unsigned)l * kCopyBytes;
-        const uint64_t addr = reinterpret_cast<uint64_t>(base) + off;
+    if constexpr (!shifted) {
+      const E::storage* prow = trow<E>(a, b, i);
+      const E::storage* qrow = pair ? drow<E>(a, b, i) : prow;
+      const int n = pair ? 2 * kRowLoads : kRowLoads;
+      // Copy l moves the (l mod kRowLoads)-th KiB of this workgroup's tile of
+      // row l / kRowLoads (the four wave tiles are adjacent, vector s of wave w
+      // being KiB w * NS + s) into KiB l of the stage.
+      for (int l = wave - 1; l < n; l += kWavesPerGroup - 1) {
+        const unsigned off = tile_bytes + (unsigned)(l & (kRowLoads - 1)) * kCopyBytes;
+        const uint64_t addr = reinterpret_cast<uint64_t>(l < kRowLoads ? prow : qrow) + off;
         const uint64_t uaddr = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(addr >> 32)) << 32) |
                                (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)addr);
-        // bytes from the copy's first vector to the row's end (rows are shorter
-        // than 2^31 bytes); a signed max stays a scalar instruction
-        const int nrec = max(ext - (int)off, 0);
+        // bytes from the copy's first vector to the row's end (rows are
+        // shorter than 2^31 bytes); a signed max stays a scalar instruction
+        const int nrec = max((int)row_bytes - (int)off, 0);
         const __amdgpu_buffer_rsrc_t rs =
             __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(uaddr), (short)0, nrec, 0x00020000);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)&stage[r * kSlotVec + l * kWave],
-                                                 16, (unsigned)lane * 16u, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)&stage[l * kWave], 16,
+                                                 (unsigned)lane * 16u, 0, 0, 0);
       }
-      first = (first + (kWavesPerGroup - 1) - row_loads % (kWavesPerGroup - 1)) % (kWavesPerGroup - 1);
+    } else {
+      // each row from its aligned-down start, kRowLoads + 1 copies into its
+      // own slot; copies bounded by the end of the tensor
+      const E::storage* rows[2] = {trow<E>(a, b, i), pair ? drow<E>(a, b, i) : nullptr};
+      int first = wave - 1;  // this wave's first copy of the row: copies l with l mod 3 == wave - 1
+      for (int r = 0; r < (pair ? 2 : 1); ++r) {
+        const int sh = shift_of(rows[r]);
+        const E::storage* base = rows[r] - sh;  // 16-byte aligned
+        const int ext = (sh + (r == 0 ? tokens_to_end<false>(a, b, i) : tokens_to_end<true>(a, b, i))) *
+                        (int)sizeof(E::storage);
+        for (int l = first; l < kRowLoads + 1; l += kWavesPerGroup - 1) {
+          const unsigned off = tile_bytes + (unsigned)l * kCopyBytes;
+          const uint64_t addr = reinterpret_cast<uint64_t>(base) + off;
+          const uint64_t uaddr = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(addr >> 32)) << 32) |
+                                 (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)addr);
+          const int nrec = max(ext - (int)off, 0);
+          const __amdgpu_buffer_rsrc_t rs =
+              __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(uaddr), (short)0, nrec, 0x00020000);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rs, (__attribute__((address_space(3))) void*)&stage[r * kSlotVec + l * kWave], 16, (unsigned)lane * 16u,
+              0, 0, 0);
+        }
+        first = (first + (kWavesPerGroup - 1) - (kRowLoads + 1) % (kWavesPerGroup - 1)) % (kWavesPerGroup - 1);
+      }
     }
   };
 
