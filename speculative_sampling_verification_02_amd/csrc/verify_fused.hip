@@ -1498,9 +1498,11 @@ hipError_t launch(const VerifyArgs& a, hipStream_t s) {
   using Kern = void (*)(FusedParams);
   Kern kern;
   if constexpr (SHIFT) {
-    static_assert(std::is_same<E, BF16>::value && !ARGMAX && !EXT, "shifted rows: the plain bf16 T > 0 kernel");
-    kern = P.W > kWave ? fused_kernel<E, per_of<E>(), false, false, true, false, true>
-                       : fused_kernel<E, per_of<E>(), false, false, false, false, true>;
+    static_assert(std::is_same<E, BF16>::value && !ARGMAX, "shifted rows: the bf16 T > 0 kernels");
+    kern = P.W > kWave ? (thr ? fused_kernel<E, per_of<E>(), false, EXT, true, kThrOk, true>
+                              : fused_kernel<E, per_of<E>(), false, EXT, true, false, true>)
+                       : (thr ? fused_kernel<E, per_of<E>(), false, EXT, false, kThrOk, true>
+                              : fused_kernel<E, per_of<E>(), false, EXT, false, false, true>);
   } else {
     kern = !ARGMAX && P.W > kWave
                ? (thr ? fused_kernel<E, per_of<E>(), ARGMAX, EXT, !ARGMAX, kThrOk, false>
@@ -1548,10 +1550,10 @@ hipError_t fused_launch(const VerifyArgs& a, hipStream_t s) {
   const bool ext = a.gamma_seq != nullptr || (!argmax && (a.lenience != 1.f || a.thr != nullptr));
   // rows that do not start on 16 bytes: only the plain bf16 T > 0 kernel
   // takes them (the others fall back to the multipass path)
-  if (shifted && (argmax || ext || a.dtype != SPEC_BF16)) return hipErrorNotSupported;
+  if (shifted && (argmax || a.dtype != SPEC_BF16)) return hipErrorNotSupported;
   if (a.dtype == SPEC_BF16) {
     if (argmax) return ext ? launch<BF16, true, true>(a, s) : launch<BF16, true>(a, s);
-    if (shifted) return launch<BF16, false, false, true>(a, s);
+    if (shifted) return ext ? launch<BF16, false, true, true>(a, s) : launch<BF16, false, false, true>(a, s);
     return ext ? launch<BF16, false, true>(a, s) : launch<BF16, false>(a, s);
   }
   if (argmax) return ext ? launch<F32, true, true>(a, s) : launch<F32, true>(a, s);

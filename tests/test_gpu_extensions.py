@@ -174,11 +174,15 @@ def test_filters_leave_argmax_mode_alone_and_workspace_zero(dev):
     assert int(ws.count_nonzero()) == 0
 
 
-@pytest.mark.parametrize("dt", ["f32", "bf16"])
-def test_filters_on_unaligned_rows(dev, dt):
-    """V = 50257 (an odd vocabulary): the rows are not 16-byte aligned, so the
-    fused path declines, the default algorithm runs the multipass path and the
-    thresholds take element loads; every extension at once, workspace left
+# (fp32 rows with V % 4 != 0 are declined by the fused path: test_gpu_parity.test_shapes)
+@pytest.mark.parametrize("dt,algo", [("f32", "auto"), ("f32", "multipass"), ("bf16", "auto"), ("bf16", "multipass"),
+                                     ("bf16", "fused")])
+def test_filters_on_unaligned_rows(dev, dt, algo):
+    """V = 50257 (an odd vocabulary): the rows do not all start on 16 bytes.
+    In bf16 the extended fused kernel copies each row from its aligned-down
+    start (and the default algorithm takes it); in fp32 the fused path
+    declines and the default algorithm runs the multipass path.  The
+    thresholds take element loads.  Every extension at once, workspace left
     zero."""
     import torch
     import speculative_sampling_verification_02_amd as sv
@@ -188,7 +192,8 @@ def test_filters_on_unaligned_rows(dev, dt):
     ws = torch.zeros(sv.workspace_size(case.B, case.gamma, case.V, sv.SPEC_BF16 if dt == "bf16" else sv.SPEC_F32),
                      dtype=torch.uint8, device=dev)
     _banner(f"unaligned {dt} filters")
-    gpu = gpu_util.run_case(case, 0, dev=dev, top_k=100, top_p=0.8, lenience=0.8, gamma_seq=g, workspace=ws)
+    algo_code = {"auto": 0, "multipass": ALGOS["multipass"], "fused": ALGOS["fused"]}[algo]
+    gpu = gpu_util.run_case(case, algo_code, dev=dev, top_k=100, top_p=0.8, lenience=0.8, gamma_seq=g, workspace=ws)
     thr = gpu_util.gpu_thresholds(case, 100, 0.8, dev=dev)
     rep = parity.check(case, gpu, where=f"unaligned {dt}", top_k=100, top_p=0.8, lenience=0.8, gamma_seq=g,
                        gpu_thresholds=thr)
