@@ -141,9 +141,10 @@ int spec_verify(const void* target_logits, const void* draft_logits, int dtype,
  * same outputs up to the floating-point rounding of their reductions.
  * SPEC_ALGO_FUSED returns SPEC_EUNSUPPORTED, with nothing queued, for logit
  * tensors that do not start on 16 bytes, rows longer than 256 * 64 * 32
- * tokens, fp32 rows with V % 4 != 0, and bf16 rows with V % 8 != 0 (rows that
- * do not all start on 16 bytes) in argmax mode; SPEC_ALGO_AUTO runs the
- * multipass path for those. */
+ * tokens, fp32 rows with V % 4 != 0, bf16 rows with V % 8 != 0 (rows that
+ * do not all start on 16 bytes) in argmax mode, and per-sequence draft counts
+ * (spec_verify_ex) with B > 2048; SPEC_ALGO_AUTO runs the multipass path for
+ * those. */
 int spec_verify_algo(int algo,
                      const void* target_logits, const void* draft_logits, int dtype,
                      const int32_t* draft_tokens, const float* uniforms,

@@ -46,6 +46,7 @@
 // via Speculative Decoding"; [SD] nonconvexcard "Speculative Decoding".
 
 #include <float.h>
+#include <limits.h>
 #include <math.h>
 
 #include <algorithm>
@@ -506,55 +507,66 @@ struct RawPair {
   RawTile<E, PER> p, q;
 };
 
-// A pair item past its sequence's draft count (a padding position): nothing
-// is read, computed or published for it.  Only the extended kernels (EXT:
-// lenience below 1 or per-sequence draft counts) look; the others run the
-// exact, fully padded step with none of this code.
-template <bool EXT>
-__device__ inline bool empty_item(const FusedParams& P, int item) {
-  if constexpr (!EXT) return false;
-  return P.a.gamma_seq && item < P.n_pairs && item % P.a.gamma >= seq_gamma(P.a, item / P.a.gamma);
+// Per-sequence draft counts in LDS.  Every workgroup of an extended launch
+// with draft counts (B <= kGammaLds; larger batches take the multipass path)
+// stages the prefix sums of the clamped gamma_b once, at its start:
+// gamma_pre[b] is the number of live pairs of the sequences before b.  Every
+// later lookup (an item's row, the dense walk over the live items) is then an
+// LDS read instead of a memory round trip on the path to the next item's
+// copies.
+constexpr int kGammaLds = 2048;
+__shared__ int gamma_pre[kGammaLds + 1];
+
+// Wave 0 of the workgroup fills gamma_pre; the caller then synchronises the
+// workgroup before any lookup.
+__device__ inline void stage_gamma(const VerifyArgs& a) {
+  if (!a.gamma_seq || threadIdx.x >= (unsigned)kWave) return;
+  const int lane = wave_lane();
+  if (lane == 0) gamma_pre[0] = 0;
+  int acc = 0;
+  for (int b0 = 0; b0 < a.B; b0 += kWave) {
+    const int b = b0 + lane;
+    const int g = b < a.B ? seq_gamma(a, b) : 0;
+    const int incl = (int)wave_inclusive_scan((float)g);  // exact: at most 2048
+    if (b < a.B) gamma_pre[b + 1] = acc + incl;
+    acc += __builtin_amdgcn_readlane(incl, kWave - 1);
+  }
 }
+
 template <bool EXT>
 __device__ inline int seq_gamma_of(const VerifyArgs& a, int b) {
   if constexpr (!EXT) return a.gamma;
-  return seq_gamma(a, b);
+  return a.gamma_seq ? gamma_pre[b + 1] - gamma_pre[b] : a.gamma;
 }
 
 // With per-sequence draft counts the teams and finishers walk the live items
 // only, densely: the pairs (b, i) with i < gamma_b, by b then i, then the B
 // bonus items (pairs first, so a finisher never waits on an item it has yet
 // to finish itself).  Every item keeps its own slots.  live_item maps a dense
-// index (the same in every lane) to its item by a wave scan over gamma_b; it
-// is called by whole waves.  Without draft counts both are the identity.
+// index (the same in every lane) to its item by two ballots over the staged
+// prefix sums; it is called by whole waves.  Without draft counts both are
+// the identity.
 template <bool EXT>
 __device__ inline int live_count(const FusedParams& P) {
   if constexpr (!EXT) return P.n_items;
-  const VerifyArgs& a = P.a;
-  if (!a.gamma_seq) return P.n_items;
-  float s = 0.f;  // exact: at most 32 per sequence
-  for (int b = wave_lane(); b < a.B; b += kWave) s += (float)seq_gamma(a, b);
-  return (int)wave_sum(s) + a.B;
+  return P.a.gamma_seq ? gamma_pre[P.a.B] + P.a.B : P.n_items;
 }
 template <bool EXT>
 __device__ inline int live_item(const FusedParams& P, int d) {
   if constexpr (!EXT) return d;
   const VerifyArgs& a = P.a;
   if (!a.gamma_seq) return d;
+  const int n_lpairs = gamma_pre[a.B];
+  if (d >= n_lpairs) return P.n_pairs + (d - n_lpairs);  // a bonus item
+  // the 64-sequence chunks wholly before d (each lane reads the prefix at the
+  // end of one chunk; at most 32 chunks), then the sequences of d's chunk
+  // wholly before d: both a prefix of the lanes
   const int lane = wave_lane();
-  int acc = 0;  // live pairs of the sequences before this chunk of 64
-  for (int b0 = 0; b0 < a.B; b0 += kWave) {
-    const int g = b0 + lane < a.B ? seq_gamma(a, b0 + lane) : 0;
-    const int incl = (int)wave_inclusive_scan((float)g);  // exact: at most 2048
-    const int total = __builtin_amdgcn_readlane(incl, kWave - 1);
-    if (d < acc + total) {
-      // the sequences wholly before d form a prefix of the lanes
-      const int l = __popcll(__ballot(acc + incl <= d));
-      return (b0 + l) * a.gamma + (d - acc - __builtin_amdgcn_readlane(incl - g, l));
-    }
-    acc += total;
-  }
-  return P.n_pairs + (d - acc);  // a bonus item
+  const int ce = lane * kWave < a.B ? gamma_pre[min((lane + 1) * kWave, a.B)] : INT_MAX;
+  const int b0 = __popcll(__ballot(ce <= d)) * kWave;
+  const int pe = b0 + lane < a.B ? gamma_pre[b0 + lane + 1] : INT_MAX;
+  const int b = b0 + __popcll(__ballot(pe <= d));
+  return b * a.gamma + (d - gamma_pre[b]);
 }
 
 
@@ -931,9 +943,16 @@ __device__ __attribute__((always_inline)) void compute_loop_staged(const FusedPa
   const int n_live = live_count<EXT>(P);
   const int n_lpairs = n_live - a.B;
   int kth = 0;
-  int d = team_dense(team, 0, P.nteams, n_live, n_lpairs);  // dense index over the live items
+  const int d = team_dense(team, 0, P.nteams, n_live, n_lpairs);  // dense index over the live items
   int item = d < n_live ? live_item<EXT>(P, d) : P.n_items;
-  if (wave != 0 && item < P.n_items && !empty_item<EXT>(P, item)) issue(item);
+  if (wave != 0 && item < P.n_items) issue(item);
+  // With draft counts the item after the next one is looked up a round
+  // ahead, so the LDS lookups of the walk stay off the path to the copies.
+  auto lookup = [&](int k) {
+    const int dk = team_dense(team, k, P.nteams, n_live, n_lpairs);
+    return dk < n_live ? live_item<EXT>(P, dk) : P.n_items;
+  };
+  int ahead = EXT ? lookup(1) : 0;
   if (wave != 0) wait_vmem();
   lds_barrier();
   // keep thresholds, loaded when the item's tiles are issued (one item ahead)
@@ -976,19 +995,18 @@ __device__ __attribute__((always_inline)) void compute_loop_staged(const FusedPa
       }
     }
     lds_barrier();
-    const int next_d = team_dense(team, ++kth, P.nteams, n_live, n_lpairs);
-    const int next = next_d < n_live ? live_item<EXT>(P, next_d) : P.n_items;
-    if (wave != 0 && next < P.n_items && !empty_item<EXT>(P, next)) issue(next);
+    ++kth;
+    const int next = EXT ? ahead : lookup(kth);
+    if (wave != 0 && next < P.n_items) issue(next);
+    if constexpr (EXT) ahead = lookup(kth + 1);
     const ItemThr th_next = item_thr<EXT, THR>(P, next);
     {
       // Two pair items in flight: phase 1 of this item runs while the team
       // exchange of the previous one completes, and only then is the previous
       // one finished.  (Copying the new weights into the pending set costs a
       // register move per token but needs fewer registers than two sets that
-      // swap roles.)  A padding item does nothing: the pending item stays
-      // pending until the next pair or bonus item, or the end.
-      if (empty_item<EXT>(P, item)) {
-      } else if (item < P.n_pairs) {
+      // swap roles.)
+      if (item < P.n_pairs) {
         float xp[PER], xq[PER], cp, cq, s_p, s_q;
         pair_phase1<E, PER, THR, SHIFT>(P, item, c, lo, A, th, xp, xq, cp, cq, s_p, s_q);
         if (pend >= 0) {
@@ -1019,7 +1037,6 @@ __device__ __attribute__((always_inline)) void compute_loop_staged(const FusedPa
     if (wave != 0) wait_vmem();
     lds_barrier();
     item = next;
-    d = next_d;
     th = th_next;
   }
   if (pend >= 0) {
@@ -1076,18 +1093,9 @@ __device__ void finish_pair(const FusedParams& P, int item, uint64_t* w1, uint64
   const size_t o = (size_t)b * G + i;
   uint64_t* part1 = P.part1 + (size_t)item * W * 2;
   uint64_t* part2 = P.part2 + (size_t)item * W;
+  // only live pairs (i < gamma_b) reach a finisher: the bonus finisher
+  // writes the padding positions' outputs
   const int gb = seq_gamma_of<EXT>(a, b);
-  if (i >= gb) {
-    // a padding position: no draft to test; its outputs say so with NaN, and
-    // the bonus finisher does not wait for it
-    if (threadIdx.x == 0) {
-      const float nan = __uint_as_float(0x7fc00000u);
-      if (a.alpha) a.alpha[o] = nan;
-      if (a.p_draft) a.p_draft[o] = nan;
-      if (a.q_draft) a.q_draft[o] = nan;
-    }
-    return;
-  }
 
   if constexpr (ARGMAX) {
     if (!gather(part1, 2 * W, w1, P.polls)) {
@@ -1385,6 +1393,10 @@ __global__ __launch_bounds__(kThreads, kMinWaves) void fused_kernel(FusedParams 
   uint64_t* fin_w1 = reinterpret_cast<uint64_t*>(pool);
   uint64_t* fin_w2 = fin_w1 + 2 * kMaxWaveTiles;
   uint64_t* fin_res = fin_w2 + kMaxWaveTiles;
+  if constexpr (EXT) {
+    stage_gamma(P.a);
+    __syncthreads();
+  }
   const int ncompute = P.nteams * P.K;
   // role of this workgroup: compute (team, rank) or finisher f
   int team = -1, rank = 0, f = 0;
@@ -1408,7 +1420,6 @@ __global__ __launch_bounds__(kThreads, kMinWaves) void fused_kernel(FusedParams 
         const int d = team_dense(team, kth, P.nteams, n_live, n_lpairs);
         if (d >= n_live) break;
         const int item = live_item<EXT>(P, d);
-        if (empty_item<EXT>(P, item)) continue;
         RawPair<E, PER> A;
         issue_item<E, PER, EXT>(P, item, lo, A);
         if (!ARGMAX && item < P.n_pairs) {
@@ -1540,6 +1551,7 @@ bool fused_supported(int B, int gamma, int V, int dtype) {
 
 hipError_t fused_launch(const VerifyArgs& a, hipStream_t s) {
   if (!fused_supported(a.B, a.gamma, a.V, a.dtype)) return hipErrorNotSupported;
+  if (a.gamma_seq && a.B > kGammaLds) return hipErrorNotSupported;
   if ((uintptr_t)a.target % 16 != 0 || (a.gamma > 0 && (uintptr_t)a.draft % 16 != 0)) return hipErrorNotSupported;
   const bool argmax = a.temperature == 0.f;
   const int vec = a.dtype == SPEC_BF16 ? BF16::kVec : F32::kVec;

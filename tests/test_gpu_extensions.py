@@ -56,6 +56,31 @@ def test_ragged_gamma(dev, algo, dt, T):
     _banner(f"  {rep}")
 
 
+@pytest.mark.parametrize("B", [2048, 2049])
+@pytest.mark.parametrize("T", [1.0, 0.0])
+def test_ragged_batch_at_the_fused_limit(dev, B, T):
+    """The fused kernels keep every sequence's draft count in LDS for batches of
+    up to 2048 sequences (32 chunks of 64, the last chunk full at 2048) and
+    decline larger ones with draft counts, which the automatic choice then
+    runs on the multipass path."""
+    import speculative_sampling_verification_02_amd as sv
+    rng = np.random.default_rng(B)
+    case = W.gaussian_case(B, 3, 136, "bf16", T, seed=B, target_std=2.0, draft_noise=0.7)
+    g = _gseq(rng, case.B, case.gamma)
+    _banner(f"ragged batch B={B} T={T} live pairs={int(g.sum())}")
+    if B > 2048:
+        t = gpu_util.case_tensors(case, dev)
+        gs = __import__("torch").from_numpy(g.astype(np.int32)).to(dev)
+        with pytest.raises(sv.SpecVerifyError) as e:
+            sv.verify(t["target"], t["draft"], t["tokens"], t["uniforms"], T, algo=sv.ALGO_FUSED, gamma_seq=gs)
+        assert e.value.status == sv.SPEC_EUNSUPPORTED
+    algo = sv.ALGO_FUSED if B <= 2048 else sv.ALGO_AUTO
+    gpu = gpu_util.run_case(case, algo, dev=dev, gamma_seq=g)
+    rep = parity.check(case, gpu, where=f"ragged B={B} T{T}", gamma_seq=g)
+    assert np.all(gpu["n_accepted"] <= g)
+    _banner(f"  {rep}")
+
+
 @pytest.mark.parametrize("algo", list(ALGOS))
 def test_ragged_and_lenient_together(dev, algo):
     rng = np.random.default_rng(43)
