@@ -84,6 +84,16 @@ constexpr uint32_t kEmpty = 0u;
 constexpr uint32_t kPoison = 0xffffffffu;
 constexpr uint32_t kResMark = 2u;  // pair result: bit 0 = accepted, bit 1 = published
 
+// The bf16 T > 0 kernels without extensions take the bonus items two at a
+// time (two sequences' bonus rows per team round) once the teams walk at
+// least this many pairs each: one bonus row alone costs about three quarters
+// of a pair's round, so pairing them saves rounds on long walks (B=256,
+// gamma=8, V=256000: 522 -> 510 us; B=256, gamma=4, V=128256: 139.9 -> 136.5
+// us), while on short walks the single bonus items, given to the teams with
+// fewer pairs, end the launch as soon (B=64, gamma=4: 42.9 either way).  The
+// extended kernels keep single bonus items (ragged B=64: 33.4 against 34.9).
+constexpr int kBonusUnitPairs = 10;
+
 struct FusedParams {
   VerifyArgs a;
   int K;          // workgroups per team
@@ -611,7 +621,7 @@ struct __align__(16) NormMsg {
 struct ItemThr {
   float p, q;
 };
-template <bool EXT, bool THR>
+template <bool EXT, bool THR, bool TWO_BONUS = false>
 __device__ inline ItemThr item_thr(const FusedParams& P, int item) {
   ItemThr t{-INFINITY, -INFINITY};
   if constexpr (THR) {
@@ -624,6 +634,8 @@ __device__ inline ItemThr item_thr(const FusedParams& P, int item) {
       } else {
         const int b = item - P.n_pairs;  // the bonus row is target row gamma_b
         t.p = thr_target(a, b, seq_gamma_of<EXT>(a, b));
+        // a unit of two bonus items: the second sequence's bonus row in q
+        if (TWO_BONUS && b + 1 < a.B) t.q = thr_target(a, b + 1, seq_gamma_of<EXT>(a, b + 1));
       }
     }
   }
@@ -853,7 +865,7 @@ __device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 template <int PER, bool SHIFT>
 constexpr int stage_vectors() { return 2 * (kWavesPerGroup * (PER / BF16::kVec) + (SHIFT ? 1 : 0)) * kWave; }
 
-template <int PER, bool ARGMAX, bool EXT, bool WIDE, bool THR, bool SHIFT>
+template <int PER, bool ARGMAX, bool EXT, bool WIDE, bool THR, bool SHIFT, bool UNITS>
 __device__ __attribute__((always_inline)) void compute_loop_staged(const FusedParams& P, int team, int rank,
                                                                    u32x4* stage, uint64_t* w1, NormMsg* msg) {
   using E = BF16;
@@ -884,6 +896,7 @@ __device__ __attribute__((always_inline)) void compute_loop_staged(const FusedPa
   constexpr int kSlotVec = (kRowLoads + (SHIFT ? 1 : 0)) * kWave;  // vectors per row slot of the stage
   static_assert(NS * E::kVec == PER && (kRowLoads & (kRowLoads - 1)) == 0, "stage copy shape");
   constexpr bool shifted = SHIFT;  // V % kVec != 0
+  constexpr bool units = UNITS;  // bonus items two at a time
   const unsigned tile_bytes = (unsigned)(rank * kWavesPerGroup * kWave * PER * (int)sizeof(E::storage));
   auto shift_of = [](const E::storage* row) {  // tokens of the row's start past 16 bytes
     return (int)(((uintptr_t)row & 15u) / sizeof(E::storage));
@@ -891,12 +904,15 @@ __device__ __attribute__((always_inline)) void compute_loop_staged(const FusedPa
   auto issue = [&](int item) {  // waves 1..3
     const bool pair = item < P.n_pairs;
     const int b = pair ? item / a.gamma : item - P.n_pairs;
-    // a bonus item reads row gamma_b (padding items are never issued)
+    // a bonus item reads row gamma_b (padding items are never issued); a
+    // bonus unit also reads the next sequence's bonus row into the q slot
     const int i = pair ? item % a.gamma : seq_gamma_of<EXT>(a, b);
+    const bool two = pair || (units && b + 1 < a.B);
+    const int i2 = pair ? i : (two ? seq_gamma_of<EXT>(a, b + 1) : 0);
     if constexpr (!shifted) {
       const E::storage* prow = trow<E>(a, b, i);
-      const E::storage* qrow = pair ? drow<E>(a, b, i) : prow;
-      const int n = pair ? 2 * kRowLoads : kRowLoads;
+      const E::storage* qrow = pair ? drow<E>(a, b, i) : (two ? trow<E>(a, b + 1, i2) : prow);
+      const int n = two ? 2 * kRowLoads : kRowLoads;
       // Copy l moves the (l mod kRowLoads)-th KiB of this workgroup's tile of
       // row l / kRowLoads (the four wave tiles are adjacent, vector s of wave w
       // being KiB w * NS + s) into KiB l of the stage.
@@ -916,13 +932,15 @@ __device__ __attribute__((always_inline)) void compute_loop_staged(const FusedPa
     } else {
       // each row from its aligned-down start, kRowLoads + 1 copies into its
       // own slot; copies bounded by the end of the tensor
-      const E::storage* rows[2] = {trow<E>(a, b, i), pair ? drow<E>(a, b, i) : nullptr};
+      const E::storage* rows[2] = {trow<E>(a, b, i),
+                                   pair ? drow<E>(a, b, i) : (two ? trow<E>(a, b + 1, i2) : nullptr)};
       int first = wave - 1;  // this wave's first copy of the row: copies l with l mod 3 == wave - 1
-      for (int r = 0; r < (pair ? 2 : 1); ++r) {
+      for (int r = 0; r < (two ? 2 : 1); ++r) {
         const int sh = shift_of(rows[r]);
         const E::storage* base = rows[r] - sh;  // 16-byte aligned
-        const int ext = (sh + (r == 0 ? tokens_to_end<false>(a, b, i) : tokens_to_end<true>(a, b, i))) *
-                        (int)sizeof(E::storage);
+        const int left = r == 0 ? tokens_to_end<false>(a, b, i)
+                                : (pair ? tokens_to_end<true>(a, b, i) : tokens_to_end<false>(a, b + 1, i2));
+        const int ext = (sh + left) * (int)sizeof(E::storage);
         for (int l = first; l < kRowLoads + 1; l += kWavesPerGroup - 1) {
           const unsigned off = tile_bytes + (unsigned)l * kCopyBytes;
           const uint64_t addr = reinterpret_cast<uint64_t>(base) + off;
@@ -940,23 +958,33 @@ __device__ __attribute__((always_inline)) void compute_loop_staged(const FusedPa
     }
   };
 
+  // The teams walk units round-robin: first the live pairs, then the bonus
+  // items two at a time (two sequences' bonus rows, a pair's worth of copies
+  // and arithmetic, where one bonus row alone took three quarters of a pair's
+  // round).  A unit is named by its first item; the last unit of an odd batch
+  // holds one bonus row.
   const int n_live = live_count<EXT>(P);
   const int n_lpairs = n_live - a.B;
-  int kth = 0;
-  const int d = team_dense(team, 0, P.nteams, n_live, n_lpairs);  // dense index over the live items
-  int item = d < n_live ? live_item<EXT>(P, d) : P.n_items;
-  if (wave != 0 && item < P.n_items) issue(item);
-  // With draft counts the item after the next one is looked up a round
-  // ahead, so the LDS lookups of the walk stay off the path to the copies.
   auto lookup = [&](int k) {
-    const int dk = team_dense(team, k, P.nteams, n_live, n_lpairs);
-    return dk < n_live ? live_item<EXT>(P, dk) : P.n_items;
+    if (!units) {
+      const int dk = team_dense(team, k, P.nteams, n_live, n_lpairs);
+      return dk < n_live ? live_item<EXT>(P, dk) : P.n_items;
+    }
+    const int u = k * P.nteams + team;
+    if (u < n_lpairs) return live_item<EXT>(P, u);
+    const int j = 2 * (u - n_lpairs);
+    return j < a.B ? P.n_pairs + j : P.n_items;
   };
+  int kth = 0;
+  int item = lookup(0);
+  if (wave != 0 && item < P.n_items) issue(item);
+  // With draft counts the unit after the next one is looked up a round
+  // ahead, so the LDS lookups of the walk stay off the path to the copies.
   int ahead = EXT ? lookup(1) : 0;
   if (wave != 0) wait_vmem();
   lds_barrier();
-  // keep thresholds, loaded when the item's tiles are issued (one item ahead)
-  ItemThr th = item_thr<EXT, THR>(P, item);
+  // keep thresholds, loaded when the unit's tiles are issued (one unit ahead)
+  ItemThr th = item_thr<EXT, THR, UNITS>(P, item);
   int parity = 0;
   int pend = -1;  // pipelined: the pair item whose kept weights wait in (ep, eq)
   float ep[PER], eq[PER], mp = 0.f, mq = 0.f, sp = 0.f, sq = 0.f;
@@ -980,7 +1008,8 @@ __device__ __attribute__((always_inline)) void compute_loop_staged(const FusedPa
       const int b = pair ? item / a.gamma : item - P.n_pairs;
       const int i = pair ? item % a.gamma : seq_gamma_of<EXT>(a, b);
       sh_p = shift_of(trow<E>(a, b, i));
-      sh_q = pair ? shift_of(drow<E>(a, b, i)) : 0;
+      sh_q = pair ? shift_of(drow<E>(a, b, i))
+                  : (units && b + 1 < a.B ? shift_of(trow<E>(a, b + 1, seq_gamma_of<EXT>(a, b + 1))) : 0);
 #pragma unroll
       for (int v = 0; v < NS; ++v) {
         const int j = (wave * NS + v) * kWave + lane;
@@ -999,7 +1028,7 @@ __device__ __attribute__((always_inline)) void compute_loop_staged(const FusedPa
     const int next = EXT ? ahead : lookup(kth);
     if (wave != 0 && next < P.n_items) issue(next);
     if constexpr (EXT) ahead = lookup(kth + 1);
-    const ItemThr th_next = item_thr<EXT, THR>(P, next);
+    const ItemThr th_next = item_thr<EXT, THR, UNITS>(P, next);
     {
       // Two pair items in flight: phase 1 of this item runs while the team
       // exchange of the previous one completes, and only then is the previous
@@ -1026,6 +1055,10 @@ __device__ __attribute__((always_inline)) void compute_loop_staged(const FusedPa
         pend = item;
       } else {
         single_pass_compute<E, PER, ARGMAX, THR, SHIFT>(P, item, c, lo, A, th);
+        if (units && item - P.n_pairs + 1 < a.B) {  // the unit's second bonus row, staged in q
+          const RawPair<E, PER> A2{A.q, A.q};
+          single_pass_compute<E, PER, ARGMAX, THR, SHIFT>(P, item + 1, c, lo, A2, ItemThr{th.q, -INFINITY});
+        }
         if (pend >= 0) {
           const NormMsg m = pair_wait<WIDE>(P, pend, parity, w1, msg);
           pair_phase2<PER, EXT>(P, pend, c, m, ep, eq, mp, mq, sp, sq);
@@ -1384,7 +1417,9 @@ struct Pool {
 // THR: the launch filters by keep thresholds (extended kernels at T > 0 only).
 // SHIFT: bf16 rows that do not start on 16 bytes (V % kVec != 0), T > 0,
 // with none of the extensions.
-template <class E, int PER, bool ARGMAX, bool EXT, bool WIDE, bool THR, bool SHIFT>
+// UNITS: the staged loop takes the bonus items two at a time (bf16, T > 0,
+// none of the extensions, long team walks).
+template <class E, int PER, bool ARGMAX, bool EXT, bool WIDE, bool THR, bool SHIFT, bool UNITS = false>
 __global__ __launch_bounds__(kThreads, kMinWaves) void fused_kernel(FusedParams P) {
   using L = Pool<E, PER, ARGMAX, SHIFT>;
   __shared__ __align__(16) unsigned char pool[L::kBytes];
@@ -1408,7 +1443,7 @@ __global__ __launch_bounds__(kThreads, kMinWaves) void fused_kernel(FusedParams 
   }
   if (team >= 0) {
     if constexpr (L::kStaged) {
-      compute_loop_staged<PER, ARGMAX, EXT, WIDE, THR, SHIFT>(P, team, rank, reinterpret_cast<u32x4*>(pool), poll_buf,
+      compute_loop_staged<PER, ARGMAX, EXT, WIDE, THR, SHIFT, UNITS>(P, team, rank, reinterpret_cast<u32x4*>(pool), poll_buf,
                                                               msg);
     } else {
       const int c = rank * kWavesPerGroup + (int)threadIdx.x / kWave;  // this wave's tile
@@ -1529,6 +1564,19 @@ hipError_t launch(const VerifyArgs& a, hipStream_t s) {
   P.nfin = (int)std::min<long>(P.n_items, std::max<long>(1, resident / kFinisherDiv));
   P.nteams = (int)std::min<long>(P.n_items, (resident - P.nfin) / P.K);
   if (P.nteams < 1) return hipErrorNotSupported;
+  if constexpr (std::is_same<E, BF16>::value && !ARGMAX && !EXT && !SHIFT) {
+    if ((long)a.B * a.gamma >= (long)kBonusUnitPairs * P.nteams) {
+      // the same kernel with the bonus items two at a time (same resources;
+      // the grid is sized again from its own residency all the same)
+      kern = P.W > kWave ? fused_kernel<E, per_of<E>(), false, false, true, false, false, true>
+                         : fused_kernel<E, per_of<E>(), false, false, false, false, false, true>;
+      e = resident_blocks(kern, &resident);
+      if (e != hipSuccess) return e;
+      P.nfin = (int)std::min<long>(P.n_items, std::max<long>(1, resident / kFinisherDiv));
+      P.nteams = (int)std::min<long>(P.n_items, (resident - P.nfin) / P.K);
+      if (P.nteams < 1) return hipErrorNotSupported;
+    }
+  }
   kern<<<dim3(P.nteams * P.K + P.nfin), dim3(kThreads), 0, s>>>(P);
   return hipGetLastError();
 }

@@ -81,6 +81,23 @@ def test_ragged_batch_at_the_fused_limit(dev, B, T):
     _banner(f"  {rep}")
 
 
+@pytest.mark.parametrize("T", [1.0, 0.8])
+def test_long_walk_odd_batch_with_every_extension(dev, T):
+    """An odd batch with about ten pairs per team (85 * 5 over 42 teams), with
+    draft counts, lenience and a nucleus filter at once."""
+    rng = np.random.default_rng(85)
+    case = W.gaussian_case(85, 5, 128256, "bf16", T, seed=85, target_std=2.5, draft_noise=0.8)
+    g = _gseq(rng, case.B, case.gamma)
+    gpu = gpu_util.run_case(case, ALGOS["fused"], dev=dev, gamma_seq=g, lenience=0.8, top_p=0.9)
+    thr = gpu_util.gpu_thresholds(case, 0, 0.9, dev=dev)
+    rep = parity.check(case, gpu, where=f"bonus units ext T{T}", gamma_seq=g, lenience=0.8, top_p=0.9,
+                       gpu_thresholds=thr, workers=8)
+    assert np.all(gpu["n_accepted"] <= g)
+    _banner(f"  {rep}")
+    assert rep.thresholds_differ <= 2
+    assert rep.token_mismatch_valid <= 2
+
+
 @pytest.mark.parametrize("algo", list(ALGOS))
 def test_ragged_and_lenient_together(dev, algo):
     rng = np.random.default_rng(43)

@@ -154,6 +154,19 @@ def test_shapes(dev, algo, shape):
     _banner(f"shape {shape} {algo}: {rep}")
 
 
+@pytest.mark.parametrize("shape", [(85, 5, 128256), (67, 5, 160000)], ids=lambda s: "B{}g{}V{}".format(*s))
+def test_bonus_rows_two_per_round(dev, shape):
+    """Teams that walk at least ten pairs each (B * gamma >= 10 * teams: 42
+    teams of 16 workgroups at V=128256, 33 of 20 at V=160000, whose rows take
+    the wide team wait) take the bonus items two at a time; an odd batch ends
+    on a unit of one bonus row."""
+    B, G, V = shape
+    case = W.gaussian_case(B, G, V, "bf16", 1.0, seed=B * 7 + G, target_std=2.5, draft_scale=0.9,
+                           draft_noise=0.8)
+    rep = parity.check(case, gpu_util.run_case(case, ALGOS["fused"], dev=dev), where=f"bonus units {shape}")
+    _banner(f"bonus units {shape}: {rep}")
+
+
 @pytest.mark.parametrize("algo", list(ALGOS))
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_masked_logits(dev, algo, dt):
