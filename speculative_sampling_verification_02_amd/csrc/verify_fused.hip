@@ -84,14 +84,16 @@ constexpr uint32_t kEmpty = 0u;
 constexpr uint32_t kPoison = 0xffffffffu;
 constexpr uint32_t kResMark = 2u;  // pair result: bit 0 = accepted, bit 1 = published
 
-// The bf16 T > 0 kernels without extensions take the bonus items two at a
-// time (two sequences' bonus rows per team round) once the teams walk at
-// least this many pairs each: one bonus row alone costs about three quarters
-// of a pair's round, so pairing them saves rounds on long walks (B=256,
-// gamma=8, V=256000: 522 -> 510 us; B=256, gamma=4, V=128256: 139.9 -> 136.5
-// us), while on short walks the single bonus items, given to the teams with
-// fewer pairs, end the launch as soon (B=64, gamma=4: 42.9 either way).  The
-// extended kernels keep single bonus items (ragged B=64: 33.4 against 34.9).
+// The bf16 T > 0 kernel for 16-byte aligned rows without extensions takes
+// the bonus items two at a time (two sequences' bonus rows per team round)
+// once the teams walk at least this many pairs each: one bonus row alone
+// costs about three quarters of a pair's round, so pairing them saves rounds
+// on long walks (B=256, gamma=8, V=256000: 524 -> 512 us; B=256, gamma=4,
+// V=128256: 136.1 -> 135.7 us), while on short walks the single bonus items,
+// given to the teams with fewer pairs, end the launch as soon (B=64,
+// gamma=4: 42.9 either way).  The extended kernels keep single bonus items
+// (ragged B=64: 33.4 against 34.9), and so do the kernels for rows that do
+// not start on 16 bytes.
 constexpr int kBonusUnitPairs = 10;
 
 struct FusedParams {
